@@ -1,0 +1,74 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and names the workload shapes; it holds
+none of the attention arithmetic.  Tests, the smoke check and the benchmark
+use it to feed the same values to the HIP library and to the fp64 oracle.
+
+Recipe: one torch CPU ``Generator`` seeded per workload; draw order Q, K, V,
+dO; every tensor iid N(0, 1) in fp32; for bf16 workloads each value is rounded
+to bf16 (round-to-nearest-even), and both sides consume the rounded values.
+A query multiplier (a power of two, so exact) scales Q to produce extreme
+logits.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str  # "fp32" or "bf16"
+    q_mult: float = 1.0
+    backward: bool = False
+    seed: int = 0
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads of the task description, in order.
+WORKLOADS = {
+    1: Workload("single_head_fp32_B1_H1_N128_d64", 1, 1, 1, 128, 64, False, "fp32", seed=1),
+    2: Workload("noncausal_bf16_B8_H16_N1024_d64", 8, 16, 16, 1024, 64, False, "bf16", seed=2),
+    3: Workload("causal_bf16_B4_H32_N4000_d128", 4, 32, 32, 4000, 128, True, "bf16", seed=3),
+    4: Workload("causal_gqa_bf16_B1_Hq32_Hkv8_N16384_d128_q8", 1, 32, 8, 16384, 128, True,
+                "bf16", q_mult=8.0, seed=4),
+    5: Workload("causal_fwd_bwd_bf16_B8_H16_N2048_d64", 8, 16, 16, 2048, 64, True, "bf16",
+                backward=True, seed=5),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def make(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
+         q_mult: float = 1.0, with_dout: bool = False):
+    """Draw (q, k, v[, dout]) as CPU tensors of the workload dtype, [B, H, N, d]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    dout = torch.randn((B, Hq, N, d), generator=g, dtype=torch.float32) if with_dout else None
+    td = torch_dtype(dtype)
+    q, k, v = q.to(td), k.to(td), v.to(td)
+    if q_mult != 1.0:
+        q = q * q_mult  # power of two: exact in bf16 and fp32
+    if dout is not None:
+        dout = dout.to(td)
+    return (q, k, v, dout) if with_dout else (q, k, v)
+
+
+def make_workload(w: Workload, with_dout: bool | None = None):
+    wd = w.backward if with_dout is None else with_dout
+    return make(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.q_mult, wd)
