@@ -1,0 +1,164 @@
+"""Exact attention for AMD Instinct MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libattn.so`` (the C ABI in ``include/attn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only marshals arguments.  PyTorch provides device memory and the stream.
+
+Raw entry points with the C names (``attn_fwd``, ``attn_bwd``,
+``attn_bwd_workspace_bytes``, ``attn_status_str``, ``attn_abi_version``) take
+integer device addresses; ``fwd`` and ``bwd`` are conveniences over torch
+tensors.  Importing this package never falls back to another implementation:
+if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_UNSUPPORTED_DEVICE = 3
+ATTN_ERR_HIP = 4
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {attn_status_str(status)}")
+
+
+def lib():
+    """The loaded libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with exact_attention_87_amd._build.build() "
+                "(or __graft_entry__.build()); there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_abi_version.argtypes = []
+        L.attn_abi_version.restype = ci
+        L.attn_status_str.argtypes = [ci]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+        L.attn_fwd.restype = ci
+        L.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
+        L.attn_bwd_workspace_bytes.restype = sz
+        L.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
+        L.attn_bwd.restype = ci
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------ raw C entry points
+def attn_abi_version() -> int:
+    return int(lib().attn_abi_version())
+
+
+def attn_status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, dtype, stream) -> int:
+    return int(lib().attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
+                              int(dtype), stream))
+
+
+def attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype) -> int:
+    n = int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, int(dtype)))
+    return -1 if n == (1 << 64) - 1 else n
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, scale,
+             dtype, stream) -> int:
+    return int(lib().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d,
+                              int(causal), float(scale), int(dtype), stream))
+
+
+# ------------------------------------------------------------ torch conveniences
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _check_qkv(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    return B, Hq, k.shape[1], N, d
+
+
+def _stream_ptr(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention forward of device tensors q [B,Hq,N,d], k/v [B,Hkv,N,d]."""
+    import torch
+
+    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                  B, Hq, Hkv, N, d, causal, scale, _dtype_code(q), _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+        workspace=None):
+    """dQ, dK, dV of attention given the forward's O and LSE and upstream dO."""
+    import torch
+
+    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must match q")
+    if lse.shape != (B, Hq, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, Hq, N]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    nbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, code)
+    if nbytes < 0:
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_bwd_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                  workspace.data_ptr(), B, Hq, Hkv, N, d, causal, scale, code, _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,148 @@
+// C ABI of the exact-attention library (declared in include/attn.h):
+// argument validation, the per-device architecture check and dispatch to the
+// gfx950 kernels.  Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_arch_state[kMaxDevices];
+
+attn_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_HIP;
+  if (dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_HIP;
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED_DEVICE;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks common to both passes.  Returns ATTN_OK and sets *empty when
+// the problem has no rows.
+attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                        attn_dtype dtype, bool* empty) {
+  if (B < 0 || N < 0 || Hq < 1 || Hkv < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // 32-bit grid and row-index limits of the kernels.
+  if ((int64_t)B * Hq > (1 << 24) || N > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  *empty = (B == 0 || N == 0);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return 1; }
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_UNSUPPORTED_DEVICE: return "ATTN_ERR_UNSUPPORTED_DEVICE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "unknown attn_status";
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int N, int d, int causal, float scale, attn_dtype dtype,
+                     void* stream) {
+  bool empty = false;
+  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t qbytes = (size_t)B * Hq * N * d * es;
+  const size_t kvbytes = (size_t)B * Hkv * N * d * es;
+  const size_t lbytes = (size_t)B * Hq * N * sizeof(float);
+  const Range rq{(uintptr_t)q, (uintptr_t)q + qbytes}, rk{(uintptr_t)k, (uintptr_t)k + kvbytes},
+      rv{(uintptr_t)v, (uintptr_t)v + kvbytes}, ro{(uintptr_t)o, (uintptr_t)o + qbytes},
+      rl{(uintptr_t)lse, (uintptr_t)lse + lbytes};
+  for (Range in : {rq, rk, rv})
+    if (overlaps(ro, in) || overlaps(rl, in)) return ATTN_ERR_INVALID_ARG;
+  if (overlaps(ro, rl)) return ATTN_ERR_INVALID_ARG;
+
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, dtype == ATTN_BF16,
+                  (hipStream_t)stream};
+  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype) {
+  bool empty = false;
+  if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
+  if (dtype != ATTN_BF16) return (size_t)-1;
+  if (empty) return 0;
+  const size_t bytes = (size_t)B * Hq * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
+                     float scale, attn_dtype dtype, void* stream) {
+  bool empty = false;
+  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (empty) return ATTN_OK;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  const size_t es = 2;
+  const size_t qbytes = (size_t)B * Hq * N * d * es;
+  const size_t kvbytes = (size_t)B * Hkv * N * d * es;
+  const size_t lbytes = (size_t)B * Hq * N * sizeof(float);
+  const size_t wbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype);
+  auto R = [](const void* p, size_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
+  const Range ins[] = {R(q, qbytes), R(k, kvbytes), R(v, kvbytes), R(o, qbytes), R(lse, lbytes),
+                       R(dout, qbytes)};
+  const Range outs[] = {R(dq, qbytes), R(dk, kvbytes), R(dv, kvbytes), R(workspace, wbytes)};
+  for (const Range& a : outs) {
+    for (const Range& b : ins)
+      if (overlaps(a, b)) return ATTN_ERR_INVALID_ARG;
+    for (const Range& b : outs)
+      if (&a != &b && overlaps(a, b)) return ATTN_ERR_INVALID_ARG;
+  }
+
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::BwdArgs a{q,  k, v, o,  lse, dout, dq, dk,        dv,       (float*)workspace,
+                  B,  Hq, Hkv, N, d,  causal == 1, scale, dtype == ATTN_BF16,
+                  (hipStream_t)stream};
+  return attn::launch_bwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

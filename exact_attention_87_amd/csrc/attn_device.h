@@ -1,0 +1,104 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// vector types, the gfx950 matrix-core and LDS-transpose builtins, the LDS
+// tile swizzle and small lane helpers.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& x) {
+  static_assert(sizeof(To) == sizeof(From), "bitcast size");
+  return __builtin_bit_cast(To, x);
+}
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).
+// Lane l holds A[l%32][8*(l/32) + 0..7], B[8*(l/32) + 0..7][l%32] and
+// D[8*(r/4) + 4*(l/32) + r%4][l%32] in element r.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Accumulator row held in element r of lane l of a 32x32 MFMA result.
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// output lane i element r is the (i%4)-th 16-bit value of the 8 bytes
+// addressed by lane 4*r + i/4 of the same group.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return bitcast<u32x2>(v);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* p) { return *(const lds_u32x4*)(p); }
+__device__ __forceinline__ void lds_write16(char* p, u32x4 v) { *(lds_u32x4*)(p) = v; }
+
+// Value of x held by lane (l ^ 32).
+__device__ __forceinline__ float xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const uint32_t other = (threadIdx.x & 32) ? r[0] : r[1];
+  return __uint_as_float(other);
+}
+
+// Two fp32 -> packed bf16x2 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return bitcast<uint32_t>(v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS tile swizzle.  A tile row (one key or query) of D bf16 is D/8 chunks of
+// 16 bytes; logical chunk ch of row `row` is stored at chunk ch ^ swz(row).
+// The map makes both access patterns of the kernels conflict-free on the 64
+// banks: 16 consecutive rows reading one logical chunk (matrix-core operand
+// loads), and 4 consecutive rows x 4 aligned chunks (transposing reads).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    static_assert(D == 64, "head dim");
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int ch) {
+  return row * (D * 2) + ((ch ^ swz<D>(row)) << 4);
+}
+
+// Byte offset, inside a swizzled [rows][D] tile, of the 8 bytes this lane
+// feeds to a transposing read that yields the 32x16 operand
+//   A[m][k] = T[kbase + key(k)][dbase + m],   m = lane%32,
+// with k ordered like the accumulator rows of a 32x32 MFMA result:
+// element j of lane l is row kbase + 8*(j/4) + 4*(l/32) + j%4.  Call with
+// t = 0 for elements 0..3 and t = 1 for elements 4..7.
+template <int D>
+__device__ __forceinline__ int tr_off(int lane, int kbase, int dbase, int t) {
+  const int G = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int row = kbase + 8 * t + 4 * (G >> 1) + r;
+  const int d = dbase + 16 * (G & 1) + 4 * q;
+  return tile_off<D>(row, d >> 3) + ((d & 7) << 1);
+}
+
+}  // namespace attn

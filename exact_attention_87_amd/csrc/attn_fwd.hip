@@ -1,0 +1,344 @@
+// Forward pass of exact attention for gfx950.
+//
+// Method (FlashAttention pages: "FlashAttention" paper story, tiling and
+// online-softmax passages and the conceptual forward pass; wineandchord.com
+// page, section "Online softmax"): a workgroup keeps a block of query rows on
+// chip and streams key/value tiles through LDS.  For every tile it forms the
+// scores, updates each row's running maximum m and normaliser l, rescales the
+// output accumulator by 2^(m_old - m_new) when m grows, and accumulates P V.
+// The N x N score matrix never leaves the chip; only O and the per-row
+// logsumexp are written.
+//
+// bf16 kernel layout (one wave = 32 query rows, 4 waves per workgroup):
+//   S^T = K Q^T on the 32x32x16 bf16 matrix cores: K tile rows come from LDS,
+//     Q^T stays in registers for the whole key loop.  Each lane then owns one
+//     query column and 32 of the tile's 64 keys, so the row max and sum are
+//     in-lane reductions plus one exchange with lane l^32.
+//   O^T += V^T P^T: P^T is reused straight from the score registers (the key
+//     order of the accumulator is carried into V's transposing LDS read), so
+//     the per-row rescale is a per-lane multiply.
+//   Softmax runs in base 2: p = 2^(s*c - m) with c = |scale|*log2(e), one FMA
+//   and one v_exp_f32 per score.  The running maximum is only moved when a
+//   row's tile maximum exceeds it by more than kTau (then p <= 2^kTau); the
+//   final O = acc / l and LSE use the same m, so the result is unchanged.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+constexpr float kTau = 8.0f;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb,
+    float c, uint32_t qsign) {
+  constexpr int NW = 4;
+  constexpr int BR = 32 * NW;   // query rows per workgroup
+  constexpr int BC = 64;        // keys per tile
+  constexpr int NCH = D / 8;    // 16-byte chunks per row
+  constexpr int TILEB = BC * D * 2;
+  constexpr int RPP = 256 / NCH;  // tile rows loaded per pass
+  constexpr int PASSES = BC / RPP;
+  constexpr int NQC = D / 16;   // k-chunks of the S contraction
+  constexpr int NMB = D / 32;   // 32-row blocks of O^T
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [2][K tile | V tile]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  // Work map: heaviest query blocks first for the causal case; the heads of
+  // one key/value group are adjacent so they share K/V in cache.
+  const int BH = gridDim.x / nqb;
+  const int id = blockIdx.x;
+  const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
+  const int bh = id % BH;
+  const int b = bh / Hq;
+  const int h = bh - b * Hq;
+  const int g = h / (Hq / Hkv);
+  const int64_t qoff = (int64_t)bh * N * D;
+  const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
+  const int q0 = qb * BR + w * 32;  // first query row of this wave
+  const int qrow = q0 + l32;        // query row owned by this lane
+
+  // Q^T operand, resident for the whole key loop.
+  bf16x8 qreg[NQC];
+  {
+    const bool ok = qrow < N;
+    const __bf16* src = Q + qoff + (int64_t)(ok ? qrow : 0) * D + hf * 8;
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      u32x4 t = *(const u32x4*)(src + cc * 16);
+      if (!ok) t = u32x4{0, 0, 0, 0};
+      t ^= qsign;
+      qreg[cc] = bitcast<bf16x8>(t);
+    }
+  }
+
+  const int ntiles_all = (N + BC - 1) / BC;
+  int ntiles = ntiles_all;
+  int wtiles = ntiles_all;
+  if (CAUSAL) {
+    ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
+    wtiles = min(ntiles, (q0 + 31) / BC + 1);
+  }
+
+  // Cooperative tile loader: thread -> (row tid/NCH + pass*RPP, chunk tid%NCH).
+  const int lrow = tid / NCH;
+  const int lch = tid % NCH;
+  u32x4 kst[PASSES], vst[PASSES];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = j * BC + p * RPP + lrow;
+      const bool ok = row < N;
+      const int64_t off = kvoff + (int64_t)(ok ? row : 0) * D + lch * 8;
+      u32x4 kv = *(const u32x4*)(K + off);
+      u32x4 vv = *(const u32x4*)(V + off);
+      if (!ok) {
+        kv = u32x4{0, 0, 0, 0};
+        vv = u32x4{0, 0, 0, 0};
+      }
+      kst[p] = kv;
+      vst[p] = vv;
+    }
+  };
+  auto swrite = [&](int buf) {
+    char* kb = smem + buf * 2 * TILEB;
+    char* vb = kb + TILEB;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int off = tile_off<D>(p * RPP + lrow, lch);
+      lds_write16(kb + off, kst[p]);
+      lds_write16(vb + off, vst[p]);
+    }
+  };
+
+  float ms = -__builtin_inff();  // running max, scaled base-2 units
+  float lsum = 0.f;              // this lane's share of the normaliser
+  f32x16 oacc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
+
+  if (ntiles > 0) {
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    if (j < wtiles) {
+      const char* kb = smem + buf * 2 * TILEB;
+      const char* vb = kb + TILEB;
+      // ---- S^T = K Q^T for the tile's two 32-key blocks
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        sacc[kbk] = f32x16{};
+        const int key = kbk * 32 + l32;
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc) {
+          const bf16x8 a = bitcast<bf16x8>(lds_read16(kb + tile_off<D>(key, 2 * cc + hf)));
+          sacc[kbk] = mfma32(a, qreg[cc], sacc[kbk]);
+        }
+      }
+      // ---- mask (diagonal and tail tiles only)
+      const int k0 = j * BC;
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0));
+      if (need_mask) {
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kbk * 32 + acc_row(r, hf);
+            const bool dead = (key >= N) || (CAUSAL && key > qrow);
+            if (dead) sacc[kbk][r] = -__builtin_inff();
+          }
+      }
+      // ---- row max over the tile (raw scores; c > 0)
+      float mloc = sacc[0][0];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kbk][r]);
+      mloc = fmaxf(mloc, xor32(mloc));
+      const float tmax = mloc * c;
+      // ---- move the running max only when it is exceeded by more than kTau
+      if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
+        const float mnew = fmaxf(ms, tmax);
+        const float alpha = fast_exp2(ms - mnew);
+        ms = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
+      }
+      // ---- p = 2^(s*c - m), row sums, bf16 P^T operand
+      uint32_t pk[2][8];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -ms));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -ms));
+          lsum += p0 + p1;
+          pk[kbk][r >> 1] = pack_bf16(p0, p1);
+        }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int cp = 0; cp < 2; ++cp) {
+            const int kbase = kbk * 32 + cp * 16;
+            const u32x2 lo = lds_read_tr(vb + tr_off<D>(lane, kbase, mb * 32, 0));
+            const u32x2 hi = lds_read_tr(vb + tr_off<D>(lane, kbase, mb * 32, 1));
+            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const bf16x8 bp = bitcast<bf16x8>(
+                u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
+            oacc[mb] = mfma32(a, bp, oacc[mb]);
+          }
+    }
+    if (j + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
+  const float lfull = lsum + xor32(lsum);
+  if (qrow < N) {
+    const float inv = 1.0f / lfull;
+    __bf16* dst = O + qoff + (int64_t)qrow * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = mb * 32 + rg * 8 + hf * 4;
+        u32x2 v;
+        v[0] = pack_bf16(oacc[mb][4 * rg] * inv, oacc[mb][4 * rg + 1] * inv);
+        v[1] = pack_bf16(oacc[mb][4 * rg + 2] * inv, oacc[mb][4 * rg + 3] * inv);
+        *(u32x2*)(dst + d0) = v;
+      }
+    if (hf == 0) LSE[(int64_t)bh * N + qrow] = (ms + __builtin_log2f(lfull)) * kLn2;
+  }
+}
+
+// fp32 forward on the vector ALUs: 32 query rows per workgroup, 8 lanes per
+// row, each lane owning D/8 consecutive features; key/value tiles of 32 rows
+// in LDS.  Exact online softmax (the maximum moves on every increase).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb,
+    float cl2) {
+  constexpr int BR = 32, BC = 32, DS = D / 8;
+  __shared__ float ks[BC][D + 4];
+  __shared__ float vs[BC][D + 4];
+  const int tid = threadIdx.x;
+  const int BH = gridDim.x / nqb;
+  const int qb = blockIdx.x / BH;
+  const int bh = blockIdx.x % BH;
+  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  const int64_t qoff = (int64_t)bh * N * D;
+  const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
+  const int qi = qb * BR + tid / 8;
+  const int part = tid % 8;
+  const bool qok = qi < N;
+  float qv[DS], acc[DS];
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    qv[e] = qok ? Q[qoff + (int64_t)qi * D + part * DS + e] : 0.f;
+    acc[e] = 0.f;
+  }
+  float m = -__builtin_inff(), l = 0.f;
+  int ntiles = (N + BC - 1) / BC;
+  if (CAUSAL) ntiles = min(ntiles, (qb * BR + BR - 1) / BC + 1);
+  for (int j = 0; j < ntiles; ++j) {
+    __syncthreads();
+    for (int idx = tid; idx < BC * D; idx += 256) {
+      const int r = idx / D, cidx = idx % D;
+      const int key = j * BC + r;
+      const bool ok = key < N;
+      ks[r][cidx] = ok ? K[kvoff + (int64_t)key * D + cidx] : 0.f;
+      vs[r][cidx] = ok ? V[kvoff + (int64_t)key * D + cidx] : 0.f;
+    }
+    __syncthreads();
+    float s[BC];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int jj = 0; jj < BC; ++jj) {
+      float part_dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) part_dot = __builtin_fmaf(qv[e], ks[jj][part * DS + e], part_dot);
+      part_dot += __shfl_xor(part_dot, 1);
+      part_dot += __shfl_xor(part_dot, 2);
+      part_dot += __shfl_xor(part_dot, 4);
+      const int key = j * BC + jj;
+      const bool dead = (key >= N) || (CAUSAL && key > qi);
+      s[jj] = dead ? -__builtin_inff() : part_dot * cl2;
+      tmax = fmaxf(tmax, s[jj]);
+    }
+    const float mnew = fmaxf(m, tmax);
+    const float alpha = exp2f(m - mnew);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int jj = 0; jj < BC; ++jj) {
+      const float p = exp2f(s[jj] - mnew);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) acc[e] = __builtin_fmaf(p, vs[jj][part * DS + e], acc[e]);
+    }
+    m = mnew;
+  }
+  if (qok) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) O[qoff + (int64_t)qi * D + part * DS + e] = acc[e] * inv;
+    if (part == 0) LSE[(int64_t)bh * N + qi] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int D, bool CAUSAL>
+static hipError_t launch_bf16(const FwdArgs& a) {
+  constexpr int BR = 128, BC = 64;
+  const int nqb = (a.N + BR - 1) / BR;
+  const int64_t grid = (int64_t)nqb * a.B * a.Hq;
+  const size_t lds = 2 * 2 * BC * D * 2;
+  float c = fabsf(a.scale) * kLog2e;
+  if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
+  const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, a.stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
+                     a.Hq, a.Hkv, a.N, nqb, c, qsign);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_f32(const FwdArgs& a) {
+  constexpr int BR = 32;
+  const int nqb = (a.N + BR - 1) / BR;
+  const int64_t grid = (int64_t)nqb * a.B * a.Hq;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                     a.Hq, a.Hkv, a.N, nqb, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.bf16) {
+    if (a.d == 64) return a.causal ? launch_bf16<64, true>(a) : launch_bf16<64, false>(a);
+    return a.causal ? launch_bf16<128, true>(a) : launch_bf16<128, false>(a);
+  }
+  if (a.d == 64) return a.causal ? launch_f32<64, true>(a) : launch_f32<64, false>(a);
+  return a.causal ? launch_f32<128, true>(a) : launch_f32<128, false>(a);
+}
+
+}  // namespace attn

@@ -1,0 +1,44 @@
+// Host-side launch interface between the C ABI (attn_api.cpp) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float scale;
+  bool bf16;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;  // workspace: D_i = dO_i . O_i, [B, Hq, N] fp32
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float scale;
+  bool bf16;
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
+
+}  // namespace attn

@@ -1,0 +1,117 @@
+/*
+ * attn.h — C ABI of the exact-attention library for AMD Instinct MI355X
+ * (gfx950).  Build: libattn.so (hipcc --offload-arch=gfx950).
+ *
+ * The operation is exact softmax attention, computed tile by tile without
+ * ever storing the N x N score matrix:
+ *
+ *   O = softmax(scale * Q K^T [+ causal mask]) V
+ *
+ * (FlashAttention pages: the formula at the top of "FlashAttention：让精确注意力
+ * 服从内存层次" (wineandchord.com); the tiling and online-softmax passages and
+ * the conceptual forward pass of the "FlashAttention" paper story
+ * (ai.tomabc.com)).  Alongside O the forward stores one statistic per query
+ * row, the natural-log logsumexp of that row's scaled scores; the backward
+ * recomputes the probabilities from it (the recomputation paragraph of the
+ * same paper story) instead of reading an N x N matrix.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, contiguous, row-major:
+ *        Q, O, dQ, dO : [B, Hq,  N, d]
+ *        K, V, dK, dV : [B, Hkv, N, d]
+ *        LSE          : [B, Hq,  N]      (fp32, natural log)
+ *    Query head h reads key/value head h / (Hq / Hkv) (grouped-query
+ *    attention; Hq must be a multiple of Hkv; Hq == Hkv is plain multi-head).
+ *  - Causal mask (causal = 1): key j is visible to query i iff j <= i.
+ *  - scale multiplies Q K^T; any finite value is accepted (callers usually
+ *    pass 1/sqrt(d)).
+ *  - Every pointer is a DEVICE pointer on the current HIP device, 16-byte
+ *    aligned.  The caller owns and allocates all memory (including the
+ *    backward workspace); the library allocates nothing, keeps no state
+ *    between calls other than a per-device architecture check, and is safe
+ *    to call from several host threads on different streams.
+ *  - Outputs must not overlap inputs or each other.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream).  The call returns once the kernels are launched;
+ *    it never synchronises.
+ *  - B == 0 or N == 0 is an empty problem: nothing is launched and ATTN_OK
+ *    is returned (pointers may then be NULL).
+ *  - Arguments are validated on the host before any HIP call.  On error no
+ *    kernel is launched and no output is touched.
+ *
+ * Supported: dtype ATTN_BF16 (bf16 inputs/outputs, fp32 accumulation on
+ * matrix cores) with d in {64, 128}; dtype ATTN_F32 (fp32 throughout) with
+ * d in {64, 128}.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,        /* bad pointer, size, alignment or overlap */
+  ATTN_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  ATTN_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 */
+  ATTN_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Version of this ABI; bumped on any incompatible change. */
+int attn_abi_version(void);
+
+/*
+ * Forward pass.
+ *   q    [B,Hq,N,d]  in   (dtype)
+ *   k, v [B,Hkv,N,d] in   (dtype)
+ *   o    [B,Hq,N,d]  out  (dtype)  softmax(scale*q k^T [+mask]) v, per head
+ *   lse  [B,Hq,N]    out  (fp32)   ln sum_j exp(scale * q_i . k_j) over the
+ *                                  visible keys j of row i
+ * Tiling: each workgroup holds a block of query rows on chip while key/value
+ * tiles stream through LDS; the running row maximum and normaliser rescale
+ * the on-chip accumulator (online softmax), so only O and LSE reach memory.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     attn_dtype dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for this problem (a multiple of
+ * 256).  0 for an empty problem.  Returns (size_t)-1 for arguments attn_bwd
+ * would reject.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype);
+
+/*
+ * Backward pass with recomputation.
+ *   q, k, v, o, lse  in   as produced for / by attn_fwd with the same
+ *                         B, Hq, Hkv, N, d, causal, scale, dtype
+ *   dout [B,Hq,N,d]  in   upstream gradient dL/dO (dtype)
+ *   dq   [B,Hq,N,d]  out  dL/dQ (dtype)
+ *   dk, dv [B,Hkv,N,d] out dL/dK, dL/dV (dtype), summed over the query heads
+ *                         that share each key/value head
+ *   workspace        scratch of attn_bwd_workspace_bytes(...) bytes, owned by
+ *                    the caller, contents need not be initialised; it must
+ *                    stay allocated until the launched work completes.
+ * The softmax probabilities are recomputed tile by tile from q, k and lse;
+ * no N x N matrix is read or written.  Deterministic (no atomics).
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
+                     float scale, attn_dtype dtype, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_str(attn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

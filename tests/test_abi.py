@@ -1,0 +1,125 @@
+"""The C ABI library on the host: it loads, exports every entry point the
+header declares, and rejects bad arguments before touching the GPU (CPU only;
+no call here launches a kernel)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_87_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# Fake, 16-byte aligned, non-overlapping addresses: validation must fail
+# before anything dereferences them.
+Q, K, V, O, L, DO, DQ, DK, DV, WS = (0x10000000 * (i + 1) for i in range(10))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_workspace_bytes",
+                                  "attn_fwd", "attn_status_str"]
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = ea.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, flags=re.M))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert ea.attn_abi_version() == 1
+
+
+def test_status_strings():
+    assert ea.attn_status_str(ea.ATTN_OK) == "ATTN_OK"
+    assert ea.attn_status_str(ea.ATTN_ERR_INVALID_ARG) == "ATTN_ERR_INVALID_ARG"
+    assert ea.attn_status_str(ea.ATTN_ERR_UNSUPPORTED_DEVICE) == "ATTN_ERR_UNSUPPORTED_DEVICE"
+    assert ea.attn_status_str(99) == "unknown attn_status"
+
+
+def fwd(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=4, Hkv=2, N=100, d=64, causal=0, scale=0.125,
+             dtype=ea.ATTN_BF16, stream=None)
+    a.update(kw)
+    return ea.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                       a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+def bwd(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, B=2, Hq=4, Hkv=2,
+             N=100, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16, stream=None)
+    a.update(kw)
+    return ea.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                       a["dv"], a["ws"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                       a["scale"], a["dtype"], a["stream"])
+
+
+INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+    dict(B=-1), dict(N=-3), dict(Hq=0), dict(Hkv=0), dict(Hq=6, Hkv=4),
+    dict(causal=2), dict(causal=-1), dict(scale=float("inf")), dict(scale=float("nan")),
+    dict(dtype=7), dict(q=Q + 8), dict(o=O + 4), dict(lse=L + 2),
+    dict(o=Q), dict(o=K + 64), dict(lse=Q + 1024), dict(lse=O + 16),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID, ids=[str(k) for k in INVALID])
+def test_fwd_rejects_bad_arguments(kw):
+    assert fwd(**kw) == ea.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [0, 32, 96, 256])
+def test_fwd_unsupported_head_dim(d):
+    assert fwd(d=d) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_fwd_too_large_is_unsupported():
+    assert fwd(N=(1 << 24) + 1) == ea.ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=0)])
+def test_empty_problem_is_ok_without_pointers(kw):
+    assert fwd(q=None, k=None, v=None, o=None, lse=None, **kw) == ea.ATTN_OK
+    assert bwd(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None,
+               ws=None, **kw) == ea.ATTN_OK
+
+
+BWD_INVALID = [
+    dict(dout=None), dict(dq=None), dict(ws=None), dict(dk=DK + 8), dict(dq=DO),
+    dict(dk=DV), dict(ws=Q + 256), dict(dv=DK + 1024), dict(Hq=3, Hkv=2), dict(causal=5),
+]
+
+
+@pytest.mark.parametrize("kw", BWD_INVALID, ids=[str(k) for k in BWD_INVALID])
+def test_bwd_rejects_bad_arguments(kw):
+    assert bwd(**kw) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_bwd_fp32_is_unsupported():
+    assert bwd(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert ea.attn_bwd_workspace_bytes(1, 1, 1, 16, 64, ea.ATTN_F32) == -1
+
+
+def test_workspace_bytes():
+    assert ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_BF16) == 3328  # 3200 -> 256
+    assert ea.attn_bwd_workspace_bytes(8, 16, 16, 2048, 64, ea.ATTN_BF16) == 8 * 16 * 2048 * 4
+    assert ea.attn_bwd_workspace_bytes(0, 4, 2, 100, 64, ea.ATTN_BF16) == 0
+    assert ea.attn_bwd_workspace_bytes(1, 3, 2, 100, 64, ea.ATTN_BF16) == -1
+    assert ea.attn_bwd_workspace_bytes(1, 4, 2, 100, 80, ea.ATTN_BF16) == -1
+
+
+def test_torch_wrapper_rejects_host_tensors():
+    import torch
+
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.fwd(x, x, x)

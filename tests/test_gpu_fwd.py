@@ -1,0 +1,182 @@
+"""Forward parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 path max |error| <= 1e-5 on O and LSE; bf16 I/O path
+|O - O_ref| <= 2e-2 + 1e-2 |O_ref| element-wise and |LSE - LSE_ref| <= 1e-3
+(LSE is fp32 and never passes through bf16).  Small shapes are compared in
+full; the full-size workloads on sampled rows that the oracle computes one by
+one, in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs
+import exact_attention_87_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device(DEV)
+
+
+def run(q, k, v, causal, scale=None):
+    dev = gpu()
+    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def check_bf16(o, lse, ro, rl, what=""):
+    err = np.abs(o - ro)
+    bound = 2e-2 + 1e-2 * np.abs(ro)
+    bad = err > bound
+    assert not bad.any(), f"{what} O: {bad.sum()} elements out of tolerance, max err {err.max()}"
+    lerr = np.abs(lse - rl)
+    assert lerr.max() <= 1e-3, f"{what} LSE max err {lerr.max()}"
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def check_f32(o, lse, ro, rl, what=""):
+    assert np.abs(o - ro).max() <= 1e-5, f"{what} O max err {np.abs(o - ro).max()}"
+    assert np.abs(lse - rl).max() <= 1e-5, f"{what} LSE max err {np.abs(lse - rl).max()}"
+
+
+# ---------------------------------------------------------------- fp32 path
+def test_workload1_fp32_single_head(oracle_mod):
+    w = attn_inputs.WORKLOADS[1]
+    q, k, v = attn_inputs.make_workload(w)
+    o, lse = run(q, k, v, w.causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=w.causal)
+    check_f32(o, lse, ro, rl, w.name)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 64), (2, 4, 2, 33, 64), (1, 2, 1, 100, 128),
+                                   (1, 3, 3, 257, 128), (2, 2, 2, 64, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_shapes(oracle_mod, shape, causal):
+    B, Hq, Hkv, N, d = shape
+    q, k, v = attn_inputs.make(B, Hq, Hkv, N, d, "fp32", seed=N + d)
+    o, lse = run(q, k, v, causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    check_f32(o, lse, ro, rl)
+
+
+# ---------------------------------------------------------------- bf16 small
+SMALL_N = [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 257, 383]
+
+
+@pytest.mark.parametrize("N", SMALL_N)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_small_full_compare(oracle_mod, N, d, causal):
+    q, k, v = attn_inputs.make(2, 4, 2, N, d, "bf16", seed=1000 + N)
+    o, lse = run(q, k, v, causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    check_bf16(o, lse, ro, rl, f"N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("heads", [(1, 1), (8, 1), (8, 2), (6, 3), (5, 5)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_head_maps(oracle_mod, heads, causal):
+    Hq, Hkv = heads
+    q, k, v = attn_inputs.make(3, Hq, Hkv, 150, 64, "bf16", seed=7 * Hq + Hkv)
+    o, lse = run(q, k, v, causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    check_bf16(o, lse, ro, rl)
+
+
+@pytest.mark.parametrize("mult", [8.0, 64.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_extreme_logits(oracle_mod, mult, causal):
+    q, k, v = attn_inputs.make(1, 4, 2, 700, 128, "bf16", seed=77, q_mult=mult)
+    o, lse = run(q, k, v, causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    check_bf16(o, lse, ro, rl, f"q x{mult}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1e-3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_scales(oracle_mod, scale, causal):
+    q, k, v = attn_inputs.make(1, 2, 2, 190, 64, "bf16", seed=5)
+    o, lse = run(q, k, v, causal, scale=scale)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal, scale=scale)
+    check_bf16(o, lse, ro, rl, f"scale={scale}")
+
+
+# ---------------------------------------------------------------- properties
+def test_bf16_deterministic_bitwise():
+    dev = gpu()
+    q, k, v = (t.to(dev) for t in attn_inputs.make(2, 8, 2, 1000, 128, "bf16", seed=3))
+    o1, l1 = ea.fwd(q, k, v, causal=True)
+    for _ in range(5):
+        o2, l2 = ea.fwd(q, k, v, causal=True)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_gqa_equals_repeated_mha_bitwise(causal):
+    dev = gpu()
+    q, k, v = (t.to(dev) for t in attn_inputs.make(2, 8, 2, 300, 128, "bf16", seed=4))
+    o1, l1 = ea.fwd(q, k, v, causal=causal)
+    kr = k.repeat_interleave(4, dim=1).contiguous()
+    vr = v.repeat_interleave(4, dim=1).contiguous()
+    o2, l2 = ea.fwd(q, kr, vr, causal=causal)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_constant_value_column(causal):
+    dev = gpu()
+    q, k, v = attn_inputs.make(1, 4, 4, 333, 64, "bf16", seed=6)
+    v[..., 5] = 3.0
+    o, _ = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    col = o[..., 5].float()
+    assert torch.all(col == 3.0), (col - 3.0).abs().max()
+
+
+def test_empty_problems():
+    dev = gpu()
+    for shape in [(0, 2, 16, 64), (1, 2, 0, 64)]:
+        q = torch.empty(shape, device=dev, dtype=torch.bfloat16)
+        o, lse = ea.fwd(q, q.clone(), q.clone())
+        assert o.shape == shape and lse.numel() == 0
+
+
+def test_unsupported_head_dim_raises():
+    dev = gpu()
+    q = torch.zeros(1, 1, 16, 96, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(ea.AttnError) as e:
+        ea.fwd(q, q.clone(), q.clone())
+    assert e.value.status == ea.ATTN_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- full-size workloads
+def sample_rows(B, Hq, N, n_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.integers(0, B * Hq * N, n_random).tolist())
+    for b, h in [(0, 0), (B - 1, Hq - 1), (B // 2, Hq // 2)]:
+        base = (b * Hq + h) * N
+        for i in [0, 1, 2, 63, 64, 127, 128, N // 2, N - 129, N - 65, N - 64, N - 33, N - 2, N - 1]:
+            if 0 <= i < N:
+                rows.add(base + i)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_full_size_workload_sampled_rows(oracle_mod, wid):
+    w = attn_inputs.WORKLOADS[wid]
+    q, k, v = attn_inputs.make_workload(w, with_dout=False)
+    dev = gpu()
+    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=w.causal)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rows = sample_rows(w.B, w.Hq, w.N, 384, seed=wid)
+    o_s = o.reshape(-1, w.d)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    l_s = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    ro, rl = oracle_mod.fwd_rows(q, k, v, rows, causal=w.causal)
+    check_bf16(o_s, l_s, ro, rl, w.name)
