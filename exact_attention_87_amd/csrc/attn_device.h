@@ -101,4 +101,13 @@ __device__ __forceinline__ int tr_off(int lane, int kbase, int dbase, int t) {
   return tile_off<D>(row, d >> 3) + ((d & 7) << 1);
 }
 
+// Allow a kernel to use more than the default 64 KiB of dynamic LDS (gfx950
+// has 160 KiB per workgroup).  Idempotent; cheap after the first call.
+template <typename Kernel>
+inline hipError_t allow_lds(Kernel* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 }  // namespace attn

@@ -1,0 +1,165 @@
+"""Backward parity: dQ, dK, dV from the HIP kernels against the fp64 oracle.
+
+Tolerance (bf16 I/O): per gradient tensor, max |g - g_ref| <= 5e-2 * max |g_ref|.
+The relative Frobenius error is also checked (<= 2e-2).  The GPU backward
+consumes the GPU forward's O and LSE (as a caller would); the oracle
+recomputes everything itself in fp64.  Small problems are compared in full;
+the full-size workload on whole (batch, kv-group) slices the oracle computes
+separately.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs
+import exact_attention_87_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run(q, k, v, do, causal, scale=None):
+    dev = gpu()
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o, lse = ea.fwd(qg, kg, vg, causal=causal, scale=scale)
+    dq, dk, dv = ea.bwd(qg, kg, vg, o, lse, dog, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return tuple(t.float().cpu().numpy() for t in (dq, dk, dv))
+
+
+def check_grad(name, g, r):
+    assert np.all(np.isfinite(g)), f"{name}: non-finite"
+    ref_max = np.abs(r).max()
+    err = np.abs(g - r).max()
+    if ref_max == 0:
+        assert err <= 1e-6, f"{name}: max err {err} with zero reference"
+        return
+    assert err <= 5e-2 * ref_max, f"{name}: max err {err} vs max ref {ref_max}"
+    fro = np.linalg.norm(g - r) / np.linalg.norm(r)
+    assert fro <= 2e-2, f"{name}: relative Frobenius error {fro}"
+
+
+@pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 128, 129, 200, 257, 383])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_small_full_compare(oracle_mod, N, d, causal):
+    q, k, v, do = attn_inputs.make(2, 4, 2, N, d, "bf16", seed=2000 + N, with_dout=True)
+    dq, dk, dv = run(q, k, v, do, causal)
+    rq, rk, rv = oracle_mod.bwd(q, k, v, do, causal=causal)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_grad(f"{name} N={N} d={d} causal={causal}", g, r)
+
+
+@pytest.mark.parametrize("heads", [(1, 1), (8, 1), (8, 2), (6, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_head_maps(oracle_mod, heads, causal):
+    Hq, Hkv = heads
+    q, k, v, do = attn_inputs.make(2, Hq, Hkv, 150, 64, "bf16", seed=3 * Hq + Hkv, with_dout=True)
+    dq, dk, dv = run(q, k, v, do, causal)
+    rq, rk, rv = oracle_mod.bwd(q, k, v, do, causal=causal)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_grad(name, g, r)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_scales(oracle_mod, scale, causal):
+    q, k, v, do = attn_inputs.make(1, 2, 1, 170, 128, "bf16", seed=9, with_dout=True)
+    dq, dk, dv = run(q, k, v, do, causal, scale=scale)
+    rq, rk, rv = oracle_mod.bwd(q, k, v, do, causal=causal, scale=scale)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_grad(f"{name} scale={scale}", g, r)
+
+
+def test_bwd_extreme_logits(oracle_mod):
+    q, k, v, do = attn_inputs.make(1, 4, 1, 300, 128, "bf16", seed=10, q_mult=8.0, with_dout=True)
+    dq, dk, dv = run(q, k, v, do, True)
+    rq, rk, rv = oracle_mod.bwd(q, k, v, do, causal=True)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_grad(name, g, r)
+
+
+def test_bwd_deterministic_bitwise():
+    dev = gpu()
+    q, k, v, do = (t.to(dev) for t in attn_inputs.make(2, 8, 2, 700, 128, "bf16", seed=12,
+                                                       with_dout=True))
+    o, lse = ea.fwd(q, k, v, causal=True)
+    ref = ea.bwd(q, k, v, o, lse, do, causal=True)
+    for _ in range(3):
+        again = ea.bwd(q, k, v, o, lse, do, causal=True)
+        for a, b in zip(ref, again):
+            assert torch.equal(a, b)
+
+
+def test_bwd_gqa_equals_summed_mha():
+    """dK/dV of a shared kv head equal the sum over its query heads' MHA gradients."""
+    dev = gpu()
+    q, k, v, do = (t.to(dev) for t in attn_inputs.make(1, 8, 2, 260, 64, "bf16", seed=13,
+                                                       with_dout=True))
+    o, lse = ea.fwd(q, k, v, causal=True)
+    dq, dk, dv = ea.bwd(q, k, v, o, lse, do, causal=True)
+    kr = k.repeat_interleave(4, dim=1).contiguous()
+    vr = v.repeat_interleave(4, dim=1).contiguous()
+    o2, lse2 = ea.fwd(q, kr, vr, causal=True)
+    dq2, dk2, dv2 = ea.bwd(q, kr, vr, o2, lse2, do, causal=True)
+    assert torch.equal(dq, dq2)
+    dk_sum = dk2.float().reshape(1, 2, 4, 260, 64).sum(2)
+    dv_sum = dv2.float().reshape(1, 2, 4, 260, 64).sum(2)
+    assert (dk.float() - dk_sum).abs().max() <= 2e-2 * dk_sum.abs().max()
+    assert (dv.float() - dv_sum).abs().max() <= 2e-2 * dv_sum.abs().max()
+
+
+def test_bwd_constant_values_give_zero_dq_dk():
+    dev = gpu()
+    q, k, v, do = attn_inputs.make(1, 2, 2, 200, 64, "bf16", seed=14, with_dout=True)
+    v[:] = v[:, :, :1, :]
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o, lse = ea.fwd(qg, kg, vg, causal=True)
+    dq, dk, dv = ea.bwd(qg, kg, vg, o, lse, dog, causal=True)
+    # D_i = dO_i . O_i uses the bf16-rounded O, so dP - D is only ~1e-3 relative
+    assert dq.float().abs().max() <= 1e-2 * dv.float().abs().max()
+    assert dk.float().abs().max() <= 1e-2 * dv.float().abs().max()
+
+
+def test_bwd_empty():
+    dev = gpu()
+    q = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
+    lse = torch.empty(1, 2, 0, device=dev, dtype=torch.float32)
+    dq, dk, dv = ea.bwd(q, q.clone(), q.clone(), q.clone(), lse, q.clone())
+    assert dq.numel() == 0
+
+
+# ---------------------------------------------------------------- full-size
+def full_size_slices(oracle_mod, w, slices):
+    q, k, v, do = attn_inputs.make_workload(w, with_dout=True)
+    dev = gpu()
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o, lse = ea.fwd(qg, kg, vg, causal=w.causal)
+    dq, dk, dv = ea.bwd(qg, kg, vg, o, lse, dog, causal=w.causal)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    rq, rk, rv = oracle_mod.bwd_slices(q, k, v, do, slices, causal=w.causal)
+    grp = w.Hq // w.Hkv
+    for t, s in enumerate(slices):
+        b, g = divmod(int(s), w.Hkv)
+        gq = dq[b, g * grp:(g + 1) * grp].float().cpu().numpy()
+        check_grad(f"{w.name} dQ slice {s}", gq, rq[t])
+        check_grad(f"{w.name} dK slice {s}", dk[b, g].float().cpu().numpy(), rk[t])
+        check_grad(f"{w.name} dV slice {s}", dv[b, g].float().cpu().numpy(), rv[t])
+
+
+def test_workload5_fwd_bwd_full_size_sampled(oracle_mod):
+    w = attn_inputs.WORKLOADS[5]
+    full_size_slices(oracle_mod, w, [0, 37, 8 * 16 - 1])
+
+
+def test_gqa_backward_reduced_length(oracle_mod):
+    """Workload 4's heads (Hq=32, Hkv=8, d=128, Q x 8, causal) at N=2048."""
+    w = attn_inputs.WORKLOADS[4].scaled(N=2048, backward=True, seed=41)
+    full_size_slices(oracle_mod, w, [0, 5, 7])
