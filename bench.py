@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Attention throughput on one MI355X: forward + recompute backward.
+
+One step is the whole hot path once over one batch of seeded synthetic input:
+attn_fwd, then the backward's three stages (attn_bwd_preprocess,
+attn_bwd_dkdv, attn_bwd_dq), all through the C ABI on one stream.  The
+workload is the causal forward + backward problem B=8, H=16, N=2048, d=64
+(bf16 I/O, fp32 accumulation).  Inputs are resident in device memory before
+the timed region starts.
+
+FLOP convention (algorithmic): forward 4*B*H*N^2*d, backward 10*B*H*N^2*d
+(the five products S, dV, dP, dK, dQ), both halved for a causal mask.  The
+backward's recomputation of S and dP inside the dQ kernel is executed but not
+counted.
+
+Printed: one JSON line with the step throughput, the roofline of the dominant
+kernel (durations from HIP events on the launch stream), every kernel's
+duration, a forward sweep over the other workloads, and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # dense bf16 MFMA: CUs x FLOP/clk/CU x clock
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd(+bwd) TFLOP/s on 1 MI355X; % of peak bf16 MFMA"
+CSRC = os.path.join(ROOT, "exact_attention_87_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (forward + backward) on whole (batch, head) slices of
+    the workload, one after another until the time budget is spent."""
+    import oracle
+
+    import attn_inputs
+
+    q, k, v, do = attn_inputs.make_workload(w, with_dout=True)
+    slices = w.B * w.Hkv
+    per_slice = (fwd_flops(1, w.Hq // w.Hkv, w.N, w.d, w.causal) * 3.5)  # fwd + bwd (4 + 10)
+    done = 0
+    t0 = time.perf_counter()
+    while done < slices and (time.perf_counter() - t0) < budget_s:
+        oracle.bwd_slices(q, k, v, do, [done], causal=w.causal)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": per_slice * done / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.omp_threads(),
+        "kind": "oracle",
+        "sample": f"{done} of {slices} (batch, head) slices of the same workload, "
+                  f"full fp64 forward+backward each, {dt:.1f} s",
+        "seconds": round(dt, 3),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; use --gpus 1"}))
+        print("bench.py: only --gpus 1 is supported (single-GPU kernel library)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attn_inputs
+    import exact_attention_87_amd as ea
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    ea.lib()  # fail loudly if the HIP library is missing
+
+    w = attn_inputs.WORKLOADS[5]
+    B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
+    scale = 1.0 / math.sqrt(d)
+    causal = int(w.causal)
+    q, k, v, do = (t.to(dev) for t in attn_inputs.make_workload(w, with_dout=True))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), device=dev, dtype=torch.float32)
+    dsum = torch.empty((B, Hq, N), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    BF = ea.ATTN_BF16
+
+    def check(st, what):
+        if st != ea.ATTN_OK:
+            raise ea.AttnError(st, what)
+
+    launches = [
+        ("fwd", lambda: check(ea.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                          lse.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF,
+                                          sp), "attn_fwd")),
+        ("bwd_preprocess", lambda: check(ea.attn_bwd_preprocess(
+            o.data_ptr(), do.data_ptr(), dsum.data_ptr(), B, Hq, N, d, BF, sp),
+            "attn_bwd_preprocess")),
+        ("bwd_dkdv", lambda: check(ea.attn_bwd_dkdv(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            dsum.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF,
+            sp), "attn_bwd_dkdv")),
+        ("bwd_dq", lambda: check(ea.attn_bwd_dq(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            dsum.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF, sp),
+            "attn_bwd_dq")),
+    ]
+    f1 = fwd_flops(B, Hq, N, d, w.causal)  # = 4*B*H*N^2*d/2
+    unit = f1 / 4.0  # B*H*N^2*d/2
+    algo = {  # algorithmic FLOPs and HBM bytes per launch
+        "fwd": {"flops": 4 * unit, "bytes": (2 * B * Hq + 2 * B * Hkv) * N * d * 2 + B * Hq * N * 4},
+        "bwd_preprocess": {"flops": 0.0, "bytes": 2 * B * Hq * N * d * 2 + B * Hq * N * 4},
+        "bwd_dkdv": {"flops": 8 * unit,
+                     "bytes": (2 * B * Hq + 4 * B * Hkv) * N * d * 2 + 2 * B * Hq * N * 4},
+        "bwd_dq": {"flops": 2 * unit,
+                   "bytes": (3 * B * Hq + 2 * B * Hkv) * N * d * 2 + 2 * B * Hq * N * 4},
+    }
+    step_flops = 14 * unit
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(launches):
+            fn()
+            if events is not None:
+                events[i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if args.copy_mib > 0:  # plain copy of known size, for HBM counter calibration
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in launches] for _ in range(K)]
+    start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        start[s].record(stream)
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+
+    kern_ms = {name: 0.0 for name, _ in launches}
+    for s in range(K):
+        prev = start[s]
+        for i, (name, _) in enumerate(launches):
+            kern_ms[name] += prev.elapsed_time(evs[s][i]) / K
+            prev = evs[s][i]
+    gpu_ms = sum(kern_ms.values())
+
+    kernels = {}
+    for name, _ in launches:
+        t = kern_ms[name] / 1e3
+        rec = {"ms": round(kern_ms[name], 5)}
+        if algo[name]["flops"] > 0:
+            rec["tflops"] = round(algo[name]["flops"] / t / 1e12, 2)
+            rec["frac_of_peak"] = round(algo[name]["flops"] / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        rec["gbs"] = round(algo[name]["bytes"] / t / 1e9, 1)
+        kernels[name] = rec
+    dom = max(kern_ms, key=kern_ms.get)
+    t_dom = kern_ms[dom] / 1e3
+    if algo[dom]["flops"] > 0:
+        ach = algo[dom]["flops"] / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = algo[dom]["bytes"] / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = load_traffic(dom)
+    roof["kernel"] = dom
+
+    # forward sweep over the other workloads (parity-tested separately)
+    sweep = {}
+    if not args.no_sweep:
+        cases = [attn_inputs.WORKLOADS[i] for i in (2, 3, 4)] + [
+            attn_inputs.Workload("noncausal_bf16_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, False,
+                                 "bf16", seed=6),
+            attn_inputs.Workload("noncausal_bf16_B1_H32_N8192_d128", 1, 32, 32, 8192, 128, False,
+                                 "bf16", seed=7),
+        ]
+        for cw in cases:
+            cq, ck, cv = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=False))
+            co, cl = ea.fwd(cq, ck, cv, causal=cw.causal)
+            for _ in range(3):
+                ea.fwd(cq, ck, cv, causal=cw.causal, out=co, lse=cl)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record(stream)
+            for _ in range(reps):
+                ea.fwd(cq, ck, cv, causal=cw.causal, out=co, lse=cl)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = fwd_flops(cw.B, cw.Hq, cw.N, cw.d, cw.causal) / (ms / 1e3) / 1e12
+            sweep[cw.name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del cq, ck, cv, co, cl
+        torch.cuda.synchronize()
+
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    value = step_flops / (ms_per_step / 1e3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d,
+                   "causal": bool(causal), "scale": scale, "seed": w.seed,
+                   "step": "attn_fwd + attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "peak_tflops_bf16": round(PEAK_BF16_TFLOPS, 1),
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "roofline": roof,
+        "kernels": kernels,
+        "forward_sweep": sweep,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(dev),
+        "torch": torch.__version__,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

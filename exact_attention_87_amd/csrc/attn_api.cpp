@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "../../include/attn.h"
 #include "attn_launch.h"
@@ -52,6 +53,53 @@ attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float 
   // 32-bit grid and row-index limits of the kernels.
   if ((int64_t)B * Hq > (1 << 24) || N > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
   *empty = (B == 0 || N == 0);
+  return ATTN_OK;
+}
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+};
+
+// Every buffer non-null and 16-byte aligned; no output overlaps an input or
+// another output.
+attn_status check_buffers(std::initializer_list<Buf> ins, std::initializer_list<Buf> outs) {
+  for (const Buf& b : ins)
+    if (!b.p || !aligned16(b.p)) return ATTN_ERR_INVALID_ARG;
+  for (const Buf& b : outs)
+    if (!b.p || !aligned16(b.p)) return ATTN_ERR_INVALID_ARG;
+  auto R = [](const Buf& b) { return Range{(uintptr_t)b.p, (uintptr_t)b.p + b.bytes}; };
+  for (const Buf& o : outs) {
+    for (const Buf& i : ins)
+      if (overlaps(R(o), R(i))) return ATTN_ERR_INVALID_ARG;
+    for (const Buf& o2 : outs)
+      if (&o != &o2 && overlaps(R(o), R(o2))) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
+struct Sizes {
+  size_t q, kv, l;  // bytes of a [B,Hq,N,d] bf16 tensor, a [B,Hkv,N,d] one, [B,Hq,N] fp32
+};
+
+Sizes sizes(int B, int Hq, int Hkv, int N, int d) {
+  return Sizes{(size_t)B * Hq * N * d * 2, (size_t)B * Hkv * N * d * 2,
+               (size_t)B * Hq * N * sizeof(float)};
+}
+
+// Checks shared by the backward entry points.  On success fills *a's shape
+// fields; a->N == 0 marks an empty problem (nothing to launch).
+attn_status bwd_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       attn_dtype dtype, void* stream, attn::BwdArgs* a) {
+  *a = attn::BwdArgs{};
+  bool empty = false;
+  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (empty) return ATTN_OK;  // a->N stays 0
+  a->B = B, a->Hq = Hq, a->Hkv = Hkv, a->N = N, a->d = d;
+  a->causal = causal == 1, a->scale = scale, a->bf16 = true;
+  a->stream = (hipStream_t)stream;
   return ATTN_OK;
 }
 
@@ -113,36 +161,74 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
                      void* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
                      float scale, attn_dtype dtype, void* stream) {
-  bool empty = false;
-  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
-  if (st != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (empty) return ATTN_OK;
-  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
-  for (const void* p : ptrs)
-    if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
-  const size_t es = 2;
-  const size_t qbytes = (size_t)B * Hq * N * d * es;
-  const size_t kvbytes = (size_t)B * Hkv * N * d * es;
-  const size_t lbytes = (size_t)B * Hq * N * sizeof(float);
+  attn::BwdArgs a;
   const size_t wbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype);
-  auto R = [](const void* p, size_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
-  const Range ins[] = {R(q, qbytes), R(k, kvbytes), R(v, kvbytes), R(o, qbytes), R(lse, lbytes),
-                       R(dout, qbytes)};
-  const Range outs[] = {R(dq, qbytes), R(dk, kvbytes), R(dv, kvbytes), R(workspace, wbytes)};
-  for (const Range& a : outs) {
-    for (const Range& b : ins)
-      if (overlaps(a, b)) return ATTN_ERR_INVALID_ARG;
-    for (const Range& b : outs)
-      if (&a != &b && overlaps(a, b)) return ATTN_ERR_INVALID_ARG;
-  }
-
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if (a.N == 0) return ATTN_OK;  // empty problem
+  const Sizes z = sizes(B, Hq, Hkv, N, d);
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {lse, z.l}, {dout, z.q}},
+                     {{dq, z.q}, {dk, z.kv}, {dv, z.kv}, {workspace, wbytes}});
+  if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  attn::BwdArgs a{q,  k, v, o,  lse, dout, dq, dk,        dv,       (float*)workspace,
-                  B,  Hq, Hkv, N, d,  causal == 1, scale, dtype == ATTN_BF16,
-                  (hipStream_t)stream};
-  return attn::launch_bwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
+  a.dq = dq, a.dk = dk, a.dv = dv, a.dsum = (float*)workspace;
+  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_preprocess(const void* o, const void* dout, float* dsum, int B, int Hq,
+                                int N, int d, attn_dtype dtype, void* stream) {
+  attn::BwdArgs a;
+  attn_status st = bwd_common(B, Hq, Hq, N, d, 0, 1.0f, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if (a.N == 0) return ATTN_OK;  // empty problem
+  const Sizes z = sizes(B, Hq, Hq, N, d);
+  st = check_buffers({{o, z.q}, {dout, z.q}}, {{dsum, z.l}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  a.o = o, a.dout = dout, a.dsum = dsum;
+  return attn::launch_bwd_pre(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* dsum, void* dk, void* dv, int B,
+                          int Hq, int Hkv, int N, int d, int causal, float scale,
+                          attn_dtype dtype, void* stream) {
+  attn::BwdArgs a;
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if (a.N == 0) return ATTN_OK;  // empty problem
+  const Sizes z = sizes(B, Hq, Hkv, N, d);
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {lse, z.l}, {dsum, z.l}},
+                     {{dk, z.kv}, {dv, z.kv}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  a.q = q, a.k = k, a.v = v, a.dout = dout, a.lse = lse, a.dsum = (float*)dsum;
+  a.dk = dk, a.dv = dv;
+  return attn::launch_bwd_dkdv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, const float* dsum, void* dq, int B, int Hq, int Hkv,
+                        int N, int d, int causal, float scale, attn_dtype dtype, void* stream) {
+  attn::BwdArgs a;
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if (a.N == 0) return ATTN_OK;  // empty problem
+  const Sizes z = sizes(B, Hq, Hkv, N, d);
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {lse, z.l}, {dsum, z.l}},
+                     {{dq, z.q}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  a.q = q, a.k = k, a.v = v, a.dout = dout, a.lse = lse, a.dsum = (float*)dsum, a.dq = dq;
+  return attn::launch_bwd_dq(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // extern "C"

@@ -422,47 +422,72 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdArgs& a) {
-  float c = fabsf(a.scale) * kLog2e;
+struct BwdConsts {
+  float c;         // |scale| log2(e), at least the smallest normal
+  uint32_t qsign;  // sign bits XORed into Q when scale < 0
+};
+
+static BwdConsts bwd_consts(float scale) {
+  float c = fabsf(scale) * kLog2e;
   if (!(c >= kTiny)) c = kTiny;  // scale 0: uniform probabilities, zero dQ/dK
-  const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
+  return BwdConsts{c, (scale < 0.f) ? 0x80008000u : 0u};
+}
+
+template <int D>
+static hipError_t pre_t(const BwdArgs& a) {
+  constexpr int RPB = 256 / (D / 8);
   const int64_t rows = (int64_t)a.B * a.Hq * a.N;
-  {
-    constexpr int RPB = 256 / (D / 8);
-    const int64_t grid = (rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                       (const __bf16*)a.o, (const __bf16*)a.dout, a.dsum, rows);
-  }
-  {
-    constexpr int BKV = 128, BQ = 64;
-    const int nkb = (a.N + BKV - 1) / BKV;
-    const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
-    const size_t lds = 2 * (2 * BQ * D * 2 + 2 * BQ * 4);
-    const hipError_t e = allow_lds(bwd_dkdv_kernel<D, CAUSAL>, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds,
-                       a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, a.lse, a.dsum, (__bf16*)a.dk, (__bf16*)a.dv, a.Hq,
-                       a.Hkv, a.N, nkb, c, fabsf(a.scale), qsign);
-  }
-  {
-    constexpr int BR = 128, BC = 64;
-    const int nqb = (a.N + BR - 1) / BR;
-    const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-    const size_t lds = 2 * 2 * BC * D * 2;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, a.stream,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.dout, a.lse, a.dsum, (__bf16*)a.dq, a.Hq, a.Hkv, a.N, nqb,
-                       c, a.scale, qsign);
-  }
+  const int64_t grid = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                     (const __bf16*)a.o, (const __bf16*)a.dout, a.dsum, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a) {
+template <int D, bool CAUSAL>
+static hipError_t dkdv_t(const BwdArgs& a) {
+  constexpr int BKV = 128, BQ = 64;
+  const BwdConsts k = bwd_consts(a.scale);
+  const int nkb = (a.N + BKV - 1) / BKV;
+  const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
+  const size_t lds = 2 * (2 * BQ * D * 2 + 2 * BQ * 4);
+  const hipError_t e = allow_lds(bwd_dkdv_kernel<D, CAUSAL>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, a.stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                     (const __bf16*)a.dout, a.lse, a.dsum, (__bf16*)a.dk, (__bf16*)a.dv, a.Hq,
+                     a.Hkv, a.N, nkb, k.c, fabsf(a.scale), k.qsign);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t dq_t(const BwdArgs& a) {
+  constexpr int BR = 128, BC = 64;
+  const BwdConsts k = bwd_consts(a.scale);
+  const int nqb = (a.N + BR - 1) / BR;
+  const int64_t grid = (int64_t)nqb * a.B * a.Hq;
+  const size_t lds = 2 * 2 * BC * D * 2;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, a.stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                     (const __bf16*)a.dout, a.lse, a.dsum, (__bf16*)a.dq, a.Hq, a.Hkv, a.N, nqb,
+                     k.c, a.scale, k.qsign);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const BwdArgs& a) {
   if (!a.bf16) return hipErrorNotSupported;
-  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
-  return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
+  return a.d == 64 ? pre_t<64>(a) : pre_t<128>(a);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+  if (!a.bf16) return hipErrorNotSupported;
+  if (a.d == 64) return a.causal ? dkdv_t<64, true>(a) : dkdv_t<64, false>(a);
+  return a.causal ? dkdv_t<128, true>(a) : dkdv_t<128, false>(a);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  if (!a.bf16) return hipErrorNotSupported;
+  if (a.d == 64) return a.causal ? dq_t<64, true>(a) : dq_t<64, false>(a);
+  return a.causal ? dq_t<128, true>(a) : dq_t<128, false>(a);
 }
 
 }  // namespace attn

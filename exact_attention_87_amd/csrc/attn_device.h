@@ -67,6 +67,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2 with (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(pair), bitcast<bf16x2>(0x3f803f80u), acc,
+                                         false);
+}
+
 // LDS tile swizzle.  A tile row (one key or query) of D bf16 is D/8 chunks of
 // 16 bytes; logical chunk ch of row `row` is stored at chunk ch ^ swz(row).
 // The map makes both access patterns of the kernels conflict-free on the 64
@@ -99,6 +105,37 @@ __device__ __forceinline__ int tr_off(int lane, int kbase, int dbase, int t) {
   const int row = kbase + 8 * t + 4 * (G >> 1) + r;
   const int d = dbase + 16 * (G & 1) + 4 * q;
   return tile_off<D>(row, d >> 3) + ((d & 7) << 1);
+}
+
+// Raw buffer resource over [base, base + bytes): loads beyond the range
+// return zeros, which is how tail rows and keys are padded.  Word 3 is the
+// gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// 16 bytes per lane from the buffer straight into LDS: lane l's data lands at
+// lds + 16*l (lds must be the same for the whole wave).
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16,
+                                           off, 0, 0, 0);
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding, then
+// synchronise the workgroup.  Compiler fences keep LDS accesses on their side.
+template <int n>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt");
+  constexpr int imm = (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(imm);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Allow a kernel to use more than the default 64 KiB of dynamic LDS (gfx950

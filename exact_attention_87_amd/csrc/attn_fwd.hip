@@ -24,30 +24,52 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+#include <type_traits>
+
 namespace attn {
 
 constexpr float kTau = 8.0f;
 
+// Tuning knobs (compile-time; the defaults are the shipped configuration).
+#ifndef ATTN_FWD_WPE64
+#define ATTN_FWD_WPE64 3
+#endif
+#ifndef ATTN_FWD_WPE128
+#define ATTN_FWD_WPE128 2
+#endif
+#ifndef ATTN_FWD_NBUF64
+#define ATTN_FWD_NBUF64 3
+#endif
+#ifndef ATTN_FWD_NBUF128
+#define ATTN_FWD_NBUF128 2
+#endif
+
+template <int D>
+struct FwdCfg {
+  static constexpr int BR = 128;  // query rows per workgroup (4 waves x 32)
+  static constexpr int BC = 64;   // keys per tile
+  static constexpr int NBUF = D == 64 ? ATTN_FWD_NBUF64 : ATTN_FWD_NBUF128;  // LDS stages
+  static constexpr int WPE = D == 64 ? ATTN_FWD_WPE64 : ATTN_FWD_WPE128;     // waves per SIMD
+  static constexpr int TILEB = BC * D * 2;
+  static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb,
-    float c, uint32_t qsign) {
-  constexpr int NW = 4;
-  constexpr int BR = 32 * NW;   // query rows per workgroup
-  constexpr int BC = 64;        // keys per tile
-  constexpr int NCH = D / 8;    // 16-byte chunks per row
-  constexpr int TILEB = BC * D * 2;
-  constexpr int RPP = 256 / NCH;  // tile rows loaded per pass
-  constexpr int PASSES = BC / RPP;
-  constexpr int NQC = D / 16;   // k-chunks of the S contraction
-  constexpr int NMB = D / 32;   // 32-row blocks of O^T
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
+void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
+                     int Hq, int Hkv, int N, int nqb, float c, uint32_t qsign) {
+  using Cfg = FwdCfg<D>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
+  constexpr int ROWB = D * 2;
+  constexpr int PW = TILEB / 1024 / 4;  // 1 KiB direct loads per wave per tensor per tile
+  constexpr int NQC = D / 16;           // k-chunks of the S contraction
+  constexpr int NMB = D / 32;           // 32-row blocks of O^T
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // [2][K tile | V tile]
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [NBUF][K tile | V tile]
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -65,19 +87,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int q0 = qb * BR + w * 32;  // first query row of this wave
   const int qrow = q0 + l32;        // query row owned by this lane
 
+  // Each (batch, head) slice is one raw buffer; rows past N read as zero.
+  const uint32_t slice_bytes = (uint32_t)N * ROWB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
+
   // Q^T operand, resident for the whole key loop.
   bf16x8 qreg[NQC];
-  {
-    const bool ok = qrow < N;
-    const __bf16* src = Q + qoff + (int64_t)(ok ? qrow : 0) * D + hf * 8;
 #pragma unroll
-    for (int cc = 0; cc < NQC; ++cc) {
-      u32x4 t = *(const u32x4*)(src + cc * 16);
-      if (!ok) t = u32x4{0, 0, 0, 0};
-      t ^= qsign;
-      qreg[cc] = bitcast<bf16x8>(t);
-    }
-  }
+  for (int cc = 0; cc < NQC; ++cc)
+    qreg[cc] = bitcast<bf16x8>(buf_load16(rq, (uint32_t)(qrow * D + cc * 16 + hf * 8) * 2) ^ qsign);
 
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all;
@@ -87,36 +107,40 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     wtiles = min(ntiles, (q0 + 31) / BC + 1);
   }
 
-  // Cooperative tile loader: thread -> (row tid/NCH + pass*RPP, chunk tid%NCH).
-  const int lrow = tid / NCH;
-  const int lch = tid % NCH;
-  u32x4 kst[PASSES], vst[PASSES];
-  auto gload = [&](int j) {
+  // Direct global->LDS tile loads.  Wave w fills the 1 KiB pieces
+  // w*PW .. w*PW+PW-1 of each tile; lane l of piece i lands at byte
+  // 1024*i' + 16*l, i.e. at (row, physical chunk), and fetches the logical
+  // chunk the swizzle stores there.
+  uint32_t goff[PW];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = j * BC + p * RPP + lrow;
-      const bool ok = row < N;
-      const int64_t off = kvoff + (int64_t)(ok ? row : 0) * D + lch * 8;
-      u32x4 kv = *(const u32x4*)(K + off);
-      u32x4 vv = *(const u32x4*)(V + off);
-      if (!ok) {
-        kv = u32x4{0, 0, 0, 0};
-        vv = u32x4{0, 0, 0, 0};
-      }
-      kst[p] = kv;
-      vst[p] = vv;
+  for (int i = 0; i < PW; ++i) {
+    const int o = (w * PW + i) * 1024 + lane * 16;
+    const int row = o / ROWB;
+    const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
+    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+  }
+  auto issue = [&](int j) {
+    char* kt = smem + (j % NBUF) * 2 * TILEB;  // j % NBUF is the stage tile j uses
+    char* vt = kt + TILEB;
+    const uint32_t tbase = (uint32_t)j * BC * ROWB;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      buf_load16_lds(rk, kt + (w * PW + i) * 1024, goff[i] + tbase);
+      buf_load16_lds(rv, vt + (w * PW + i) * 1024, goff[i] + tbase);
     }
   };
-  auto swrite = [&](int buf) {
-    char* kb = smem + buf * 2 * TILEB;
-    char* vb = kb + TILEB;
+
+  // Per-lane LDS byte offsets inside one tile, fixed for the whole loop: the
+  // K operand rows (l32, +32) at chunk 2cc+hf, and the transposing-read
+  // addresses of the V^T operand for key block 0 (other key blocks are
+  // multiples of 16 rows further, which the swizzle leaves unchanged).
+  int koff[NQC], voff[2][NMB];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int off = tile_off<D>(p * RPP + lrow, lch);
-      lds_write16(kb + off, kst[p]);
-      lds_write16(vb + off, vst[p]);
-    }
-  };
+  for (int cc = 0; cc < NQC; ++cc) koff[cc] = tile_off<D>(l32, 2 * cc + hf);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) voff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
 
   float ms = -__builtin_inff();  // running max, scaled base-2 units
   float lsum = 0.f;              // this lane's share of the normaliser
@@ -124,34 +148,33 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
 
-  if (ntiles > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  // One key tile; BUF (the LDS stage) is a compile-time constant so every LDS
+  // address is a fixed per-lane register plus an immediate.
+  auto tile = [&](auto bufc, int j) {
+    constexpr int BUF = decltype(bufc)::value;
+    const char* kt = smem + BUF * 2 * TILEB;
+    const char* vt = kt + TILEB;
+    if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (j < wtiles) {
-      const char* kb = smem + buf * 2 * TILEB;
-      const char* vb = kb + TILEB;
       // ---- S^T = K Q^T for the tile's two 32-key blocks
+      u32x4 kfrag[2][NQC];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc) kfrag[kbk][cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
       f32x16 sacc[2];
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
         sacc[kbk] = f32x16{};
-        const int key = kbk * 32 + l32;
 #pragma unroll
-        for (int cc = 0; cc < NQC; ++cc) {
-          const bf16x8 a = bitcast<bf16x8>(lds_read16(kb + tile_off<D>(key, 2 * cc + hf)));
-          sacc[kbk] = mfma32(a, qreg[cc], sacc[kbk]);
-        }
+        for (int cc = 0; cc < NQC; ++cc)
+          sacc[kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
       }
-      // ---- mask (diagonal and tail tiles only)
+      // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
+      // and kept as a branch rather than flattened into selects)
       const int k0 = j * BC;
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0));
-      if (need_mask) {
+      if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {
+        __asm__ volatile("");
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
@@ -166,19 +189,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kbk][r]);
-      mloc = fmaxf(mloc, xor32(mloc));
+        for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[kbk][r]);
+      mloc = __builtin_fmaxf(mloc, xor32(mloc));
       const float tmax = mloc * c;
       // ---- move the running max only when it is exceeded by more than kTau
       if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
-        const float mnew = fmaxf(ms, tmax);
+        const float mnew = __builtin_fmaxf(ms, tmax);
         const float alpha = fast_exp2(ms - mnew);
         ms = mnew;
         lsum *= alpha;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
       }
-      // ---- p = 2^(s*c - m), row sums, bf16 P^T operand
+      // ---- p = 2^(s*c - m) -> bf16 P^T operand; fp32 row sums (an LSE
+      // accurate to fp32, not to the bf16 rounding of P)
       uint32_t pk[2][8];
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
@@ -186,8 +210,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         for (int r = 0; r < 16; r += 2) {
           const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -ms));
           const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -ms));
-          lsum += p0 + p1;
           pk[kbk][r >> 1] = pack_bf16(p0, p1);
+          lsum += p0 + p1;
         }
       // ---- O^T += V^T P^T
 #pragma unroll
@@ -196,17 +220,38 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
           for (int cp = 0; cp < 2; ++cp) {
-            const int kbase = kbk * 32 + cp * 16;
-            const u32x2 lo = lds_read_tr(vb + tr_off<D>(lane, kbase, mb * 32, 0));
-            const u32x2 hi = lds_read_tr(vb + tr_off<D>(lane, kbase, mb * 32, 1));
+            const int rows = (kbk * 32 + cp * 16) * ROWB;
+            const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
+            const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
             const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
             const bf16x8 bp = bitcast<bf16x8>(
                 u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
             oacc[mb] = mfma32(a, bp, oacc[mb]);
           }
     }
-    if (j + 1 < ntiles) swrite(buf ^ 1);
-    __syncthreads();
+    if (j + 1 < ntiles) {
+      // tile j+1 must have landed; tile j+2 (three stages) may stay in flight
+      if (NBUF == 3 && j + 2 < ntiles)
+        wait_vm_barrier<2 * PW>();
+      else
+        wait_vm_barrier<0>();
+    }
+  };
+
+  // Prologue: tiles 0 .. NBUF-2 in flight, then wait for tile 0.
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < ntiles) issue(j);
+  if (NBUF == 3 && ntiles > 1)
+    wait_vm_barrier<2 * PW>();
+  else
+    wait_vm_barrier<0>();
+
+  for (int j = 0; j < ntiles; j += NBUF) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
+    if constexpr (NBUF == 3)
+      if (j + 2 < ntiles) tile(std::integral_constant<int, 2 % NBUF>{}, j + 2);
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
@@ -308,10 +353,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // ---------------------------------------------------------------- launchers
 template <int D, bool CAUSAL>
 static hipError_t launch_bf16(const FwdArgs& a) {
-  constexpr int BR = 128, BC = 64;
-  const int nqb = (a.N + BR - 1) / BR;
+  const int nqb = (a.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const size_t lds = 2 * 2 * BC * D * 2;
+  const size_t lds = FwdCfg<D>::LDS;
+  const hipError_t e = allow_lds(fwd_bf16_kernel<D, CAUSAL>, lds);
+  if (e != hipSuccess) return e;
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;

@@ -39,6 +39,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+// Backward stages; each launches one kernel on a.stream.
+hipError_t launch_bwd_pre(const BwdArgs& a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
 
 }  // namespace attn

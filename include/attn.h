@@ -107,6 +107,29 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
                      float scale, attn_dtype dtype, void* stream);
 
+/*
+ * The three stages attn_bwd runs, in order, on one stream.  Exposed so a
+ * caller can schedule or time them separately; calling them in this order
+ * with the same arguments gives exactly attn_bwd's results.  `dsum` is an
+ * fp32 [B,Hq,N] buffer (attn_bwd keeps it at the start of its workspace).
+ *
+ *   attn_bwd_preprocess: dsum_i = dO_i . O_i for every query row.
+ *   attn_bwd_dkdv:       dK, dV (recomputing P and dP tile by tile from q, k,
+ *                        lse; reads dsum).  dK/dV of a key/value head are
+ *                        summed over its query heads on chip.
+ *   attn_bwd_dq:         dQ (recomputing P and dP; reads dsum).
+ * Validation, ownership and error behaviour are those of attn_bwd.
+ */
+attn_status attn_bwd_preprocess(const void* o, const void* dout, float* dsum, int B, int Hq,
+                                int N, int d, attn_dtype dtype, void* stream);
+attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* dsum, void* dk, void* dv, int B,
+                          int Hq, int Hkv, int N, int d, int causal, float scale,
+                          attn_dtype dtype, void* stream);
+attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, const float* dsum, void* dq, int B, int Hq, int Hkv,
+                        int N, int d, int causal, float scale, attn_dtype dtype, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

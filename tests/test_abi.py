@@ -24,8 +24,9 @@ def header_functions():
 
 
 def test_header_declares_the_boundary():
-    assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_workspace_bytes",
-                                  "attn_fwd", "attn_status_str"]
+    assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
+                                  "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd",
+                                  "attn_status_str"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -123,3 +124,29 @@ def test_torch_wrapper_rejects_host_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.fwd(x, x, x)
+
+
+def test_staged_backward_validation():
+    ok = dict(B=2, Hq=4, Hkv=2, N=100, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16, stream=None)
+    # empty problems are fine without pointers
+    assert ea.attn_bwd_preprocess(None, None, None, 0, 4, 100, 64, ea.ATTN_BF16, None) == ea.ATTN_OK
+    assert ea.attn_bwd_dkdv(*([None] * 8), 2, 4, 2, 0, 64, 1, 0.1, ea.ATTN_BF16, None) == ea.ATTN_OK
+    assert ea.attn_bwd_dq(*([None] * 7), 2, 4, 2, 0, 64, 1, 0.1, ea.ATTN_BF16, None) == ea.ATTN_OK
+    # missing / misaligned / overlapping buffers
+    assert ea.attn_bwd_preprocess(O, None, WS, 2, 4, 100, 64, ea.ATTN_BF16, None) == \
+        ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_preprocess(O, DO, O + 64, 2, 4, 100, 64, ea.ATTN_BF16, None) == \
+        ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_preprocess(O, DO, WS + 4, 2, 4, 100, 64, ea.ATTN_BF16, None) == \
+        ea.ATTN_ERR_INVALID_ARG
+    args = [ok[x] for x in ("B", "Hq", "Hkv", "N", "d", "causal", "scale", "dtype", "stream")]
+    assert ea.attn_bwd_dkdv(Q, K, V, DO, L, WS, DK, K, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dkdv(Q, K, V, DO, L, WS, DK, DK, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq(Q, K, V, DO, L, WS, WS, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq(Q, K, V, DO, None, WS, DQ, *args) == ea.ATTN_ERR_INVALID_ARG
+    bad = list(args)
+    bad[2] = 3  # Hq % Hkv != 0
+    assert ea.attn_bwd_dq(Q, K, V, DO, L, WS, DQ, *bad) == ea.ATTN_ERR_INVALID_ARG
+    f32 = list(args)
+    f32[7] = ea.ATTN_F32
+    assert ea.attn_bwd_dkdv(Q, K, V, DO, L, WS, DK, DV, *f32) == ea.ATTN_ERR_UNSUPPORTED

@@ -126,6 +126,33 @@ def test_bwd_constant_values_give_zero_dq_dk():
     assert dk.float().abs().max() <= 1e-2 * dv.float().abs().max()
 
 
+def test_staged_backward_equals_attn_bwd():
+    dev = gpu()
+    B, Hq, Hkv, N, d = 2, 8, 2, 333, 128
+    q, k, v, do = (t.to(dev) for t in attn_inputs.make(B, Hq, Hkv, N, d, "bf16", seed=15,
+                                                       with_dout=True))
+    o, lse = ea.fwd(q, k, v, causal=True)
+    ref = ea.bwd(q, k, v, o, lse, do, causal=True)
+    dsum = torch.empty(B, Hq, N, device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    s = torch.cuda.current_stream().cuda_stream
+    sc = d ** -0.5
+    assert ea.attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), dsum.data_ptr(), B, Hq, N, d,
+                                  ea.ATTN_BF16, s) == ea.ATTN_OK
+    assert ea.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                            lse.data_ptr(), dsum.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            B, Hq, Hkv, N, d, 1, sc, ea.ATTN_BF16, s) == ea.ATTN_OK
+    assert ea.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                          lse.data_ptr(), dsum.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, 1,
+                          sc, ea.ATTN_BF16, s) == ea.ATTN_OK
+    torch.cuda.synchronize()
+    for a, b in zip(ref, (dq, dk, dv)):
+        assert torch.equal(a, b)
+    # D_i = dO_i . O_i
+    ref_d = (do.float() * o.float()).sum(-1)
+    assert (dsum - ref_d).abs().max() <= 1e-3 * ref_d.abs().max()
+
+
 def test_bwd_empty():
     dev = gpu()
     q = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
