@@ -130,7 +130,8 @@ def main():
     q, k, v, do = (t.to(dev) for t in attn_inputs.make_workload(w, with_dout=True))
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), device=dev, dtype=torch.float32)
-    dsum = torch.empty((B, Hq, N), device=dev, dtype=torch.float32)
+    stats = torch.empty(ea.attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, ea.ATTN_BF16) // 4,
+                        device=dev, dtype=torch.float32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -145,22 +146,21 @@ def main():
                                           lse.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF,
                                           sp), "attn_fwd")),
         ("bwd_preprocess", lambda: check(ea.attn_bwd_preprocess(
-            o.data_ptr(), do.data_ptr(), dsum.data_ptr(), B, Hq, N, d, BF, sp),
+            o.data_ptr(), do.data_ptr(), lse.data_ptr(), stats.data_ptr(), B, Hq, N, d, BF, sp),
             "attn_bwd_preprocess")),
         ("bwd_dkdv", lambda: check(ea.attn_bwd_dkdv(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-            dsum.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF,
-            sp), "attn_bwd_dkdv")),
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), stats.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF, sp),
+            "attn_bwd_dkdv")),
         ("bwd_dq", lambda: check(ea.attn_bwd_dq(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
-            dsum.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF, sp),
-            "attn_bwd_dq")),
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), stats.data_ptr(),
+            dq.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF, sp), "attn_bwd_dq")),
     ]
     f1 = fwd_flops(B, Hq, N, d, w.causal)  # = 4*B*H*N^2*d/2
     unit = f1 / 4.0  # B*H*N^2*d/2
     algo = {  # algorithmic FLOPs and HBM bytes per launch
         "fwd": {"flops": 4 * unit, "bytes": (2 * B * Hq + 2 * B * Hkv) * N * d * 2 + B * Hq * N * 4},
-        "bwd_preprocess": {"flops": 0.0, "bytes": 2 * B * Hq * N * d * 2 + B * Hq * N * 4},
+        "bwd_preprocess": {"flops": 0.0, "bytes": 2 * B * Hq * N * d * 2 + 3 * B * Hq * N * 4},
         "bwd_dkdv": {"flops": 8 * unit,
                      "bytes": (2 * B * Hq + 4 * B * Hkv) * N * d * 2 + 2 * B * Hq * N * 4},
         "bwd_dq": {"flops": 2 * unit,

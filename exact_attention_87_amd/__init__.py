@@ -56,11 +56,11 @@ def lib():
         L.attn_bwd_workspace_bytes.restype = sz
         L.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd.restype = ci
-        L.attn_bwd_preprocess.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
+        L.attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
         L.attn_bwd_preprocess.restype = ci
-        L.attn_bwd_dkdv.argtypes = [vp] * 8 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
+        L.attn_bwd_dkdv.argtypes = [vp] * 7 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd_dkdv.restype = ci
-        L.attn_bwd_dq.argtypes = [vp] * 7 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
+        L.attn_bwd_dq.argtypes = [vp] * 6 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd_dq.restype = ci
         _lib = L
     return _lib
@@ -91,19 +91,19 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, cau
                               int(causal), float(scale), int(dtype), stream))
 
 
-def attn_bwd_preprocess(o, dout, dsum, B, Hq, N, d, dtype, stream) -> int:
-    return int(lib().attn_bwd_preprocess(o, dout, dsum, B, Hq, N, d, int(dtype), stream))
+def attn_bwd_preprocess(o, dout, lse, stats, B, Hq, N, d, dtype, stream) -> int:
+    return int(lib().attn_bwd_preprocess(o, dout, lse, stats, B, Hq, N, d, int(dtype), stream))
 
 
-def attn_bwd_dkdv(q, k, v, dout, lse, dsum, dk, dv, B, Hq, Hkv, N, d, causal, scale, dtype,
+def attn_bwd_dkdv(q, k, v, dout, stats, dk, dv, B, Hq, Hkv, N, d, causal, scale, dtype,
                   stream) -> int:
-    return int(lib().attn_bwd_dkdv(q, k, v, dout, lse, dsum, dk, dv, B, Hq, Hkv, N, d,
+    return int(lib().attn_bwd_dkdv(q, k, v, dout, stats, dk, dv, B, Hq, Hkv, N, d,
                                    int(causal), float(scale), int(dtype), stream))
 
 
-def attn_bwd_dq(q, k, v, dout, lse, dsum, dq, B, Hq, Hkv, N, d, causal, scale, dtype,
+def attn_bwd_dq(q, k, v, dout, stats, dq, B, Hq, Hkv, N, d, causal, scale, dtype,
                 stream) -> int:
-    return int(lib().attn_bwd_dq(q, k, v, dout, lse, dsum, dq, B, Hq, Hkv, N, d, int(causal),
+    return int(lib().attn_bwd_dq(q, k, v, dout, stats, dq, B, Hq, Hkv, N, d, int(causal),
                                  float(scale), int(dtype), stream))
 
 

@@ -50,8 +50,9 @@ attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float 
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  // 32-bit grid and row-index limits of the kernels.
-  if ((int64_t)B * Hq > (1 << 24) || N > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  // Limits of the kernels' 32-bit grid, row and byte offsets: one (batch,
+  // head) slice stays below 1 GiB.
+  if ((int64_t)B * Hq > (1 << 24) || N > (1 << 22)) return ATTN_ERR_UNSUPPORTED;
   *empty = (B == 0 || N == 0);
   return ATTN_OK;
 }
@@ -79,12 +80,12 @@ attn_status check_buffers(std::initializer_list<Buf> ins, std::initializer_list<
 }
 
 struct Sizes {
-  size_t q, kv, l;  // bytes of a [B,Hq,N,d] bf16 tensor, a [B,Hkv,N,d] one, [B,Hq,N] fp32
+  size_t q, kv, l, st;  // bytes of [B,Hq,N,d] and [B,Hkv,N,d] bf16, [B,Hq,N] fp32, statistics
 };
 
 Sizes sizes(int B, int Hq, int Hkv, int N, int d) {
   return Sizes{(size_t)B * Hq * N * d * 2, (size_t)B * Hkv * N * d * 2,
-               (size_t)B * Hq * N * sizeof(float)};
+               (size_t)B * Hq * N * sizeof(float), attn::bwd_stats_bytes(B, Hq, N)};
 }
 
 // Checks shared by the backward entry points.  On success fills *a's shape
@@ -153,7 +154,7 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype
   if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
   if (dtype != ATTN_BF16) return (size_t)-1;
   if (empty) return 0;
-  const size_t bytes = (size_t)B * Hq * N * sizeof(float);
+  const size_t bytes = attn::bwd_stats_bytes(B, Hq, N);
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -173,61 +174,59 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   st = check_device();
   if (st != ATTN_OK) return st;
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
-  a.dq = dq, a.dk = dk, a.dv = dv, a.dsum = (float*)workspace;
+  a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
   if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
-attn_status attn_bwd_preprocess(const void* o, const void* dout, float* dsum, int B, int Hq,
-                                int N, int d, attn_dtype dtype, void* stream) {
+attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, float* stats,
+                                int B, int Hq, int N, int d, attn_dtype dtype, void* stream) {
   attn::BwdArgs a;
   attn_status st = bwd_common(B, Hq, Hq, N, d, 0, 1.0f, dtype, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hq, N, d);
-  st = check_buffers({{o, z.q}, {dout, z.q}}, {{dsum, z.l}});
+  st = check_buffers({{o, z.q}, {dout, z.q}, {lse, z.l}}, {{stats, z.st}});
   if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  a.o = o, a.dout = dout, a.dsum = dsum;
+  a.o = o, a.dout = dout, a.lse = lse, a.stats = stats;
   return attn::launch_bwd_pre(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                          const float* lse, const float* dsum, void* dk, void* dv, int B,
-                          int Hq, int Hkv, int N, int d, int causal, float scale,
-                          attn_dtype dtype, void* stream) {
+                          const float* stats, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                          int d, int causal, float scale, attn_dtype dtype, void* stream) {
   attn::BwdArgs a;
   attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hkv, N, d);
-  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {lse, z.l}, {dsum, z.l}},
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {stats, z.st}},
                      {{dk, z.kv}, {dv, z.kv}});
   if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  a.q = q, a.k = k, a.v = v, a.dout = dout, a.lse = lse, a.dsum = (float*)dsum;
+  a.q = q, a.k = k, a.v = v, a.dout = dout, a.stats = (float*)stats;
   a.dk = dk, a.dv = dv;
   return attn::launch_bwd_dkdv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                        const float* lse, const float* dsum, void* dq, int B, int Hq, int Hkv,
-                        int N, int d, int causal, float scale, attn_dtype dtype, void* stream) {
+                        const float* stats, void* dq, int B, int Hq, int Hkv, int N, int d,
+                        int causal, float scale, attn_dtype dtype, void* stream) {
   attn::BwdArgs a;
   attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hkv, N, d);
-  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {lse, z.l}, {dsum, z.l}},
-                     {{dq, z.q}});
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {stats, z.st}}, {{dq, z.q}});
   if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  a.q = q, a.k = k, a.v = v, a.dout = dout, a.lse = lse, a.dsum = (float*)dsum, a.dq = dq;
+  a.q = q, a.k = k, a.v = v, a.dout = dout, a.stats = (float*)stats, a.dq = dq;
   return attn::launch_bwd_dq(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

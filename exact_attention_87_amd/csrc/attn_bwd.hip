@@ -10,34 +10,64 @@
 //   dQ = scale dS K                 dK = scale dS^T Q
 //
 // Three kernels, all deterministic (no atomics):
-//   pre:  D_i = dO_i . O_i into the caller's workspace.
+//   pre:  per (batch, head) row statistics into the caller's workspace,
+//         laid out [B*Hq][2][Np] fp32 with Np = N rounded up to 64:
+//         [0] = D_i = dO_i . O_i, [1] = LSE_i * log2(e); padding rows are 0.
 //   dkdv: one workgroup per (batch, kv head, block of 128 keys); each wave
 //         keeps its 32 keys' K and V as matrix-core operands in registers and
 //         accumulates dK^T, dV^T over every query tile of every query head of
-//         the group (so grouped-query heads are summed on chip).
+//         the group (so grouped-query heads are summed on chip).  Query tiles
+//         (Q, dO and the statistics) stream through LDS.
 //   dq:   one workgroup per (batch, query head, block of 128 queries); the
-//         forward's tiling, with dQ^T accumulated over the key tiles.
-// Probabilities use base 2: P = 2^(s*c - LSE*log2 e), c = |scale| log2 e.
-// A negative scale is folded into Q's sign bit when Q is loaded.
+//         forward's tiling, with dQ^T accumulated over key tiles that stream
+//         through LDS.
+// Probabilities use base 2: P = 2^(s*c - LSE*log2 e), c = |scale| log2 e.  A
+// negative scale is folded into the sign bit of the register-resident operand
+// (Q in the dq kernel, K in the dkdv kernel) as it is loaded.  Query rows
+// past N read as zero (Q, dO) with zero statistics, so they add nothing to
+// dK and dV without a mask.
 #include "attn_device.h"
 #include "attn_launch.h"
+
+#include <type_traits>
 
 namespace attn {
 
 constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 
-// ---------------------------------------------------------------- D = rowsum(dO o O)
+#ifndef ATTN_BWD_WPE64
+#define ATTN_BWD_WPE64 2
+#endif
+#ifndef ATTN_BWD_WPE128
+#define ATTN_BWD_WPE128 1
+#endif
+#ifndef ATTN_DQ_WPE64
+#define ATTN_DQ_WPE64 2
+#endif
+#ifndef ATTN_DQ_WPE128
+#define ATTN_DQ_WPE128 1
+#endif
+
+__host__ __device__ constexpr int stat_rows(int N) { return (N + 63) / 64 * 64; }
+
+// ---------------------------------------------------------------- row statistics
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
                                                       const __bf16* __restrict__ dO,
-                                                      float* __restrict__ Dsum, int64_t rows) {
+                                                      const float* __restrict__ LSE,
+                                                      float* __restrict__ stats, int N, int Np,
+                                                      int64_t nslices) {
   constexpr int TPR = D / 8;  // lanes per row, 16 bytes each
   constexpr int RPB = 256 / TPR;
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+  const int64_t prow = (int64_t)blockIdx.x * RPB + tid / TPR;  // padded row index
   const int part = tid % TPR;
+  const int64_t slice = prow / Np;
+  const int i = (int)(prow - slice * Np);
+  const bool live = slice < nslices && i < N;
   float acc = 0.f;
-  if (row < rows) {
+  if (live) {
+    const int64_t row = slice * N + i;
     const u32x4 a = *(const u32x4*)(O + row * D + part * 8);
     const u32x4 b = *(const u32x4*)(dO + row * D + part * 8);
     const bf16x8 av = bitcast<bf16x8>(a), bv = bitcast<bf16x8>(b);
@@ -46,32 +76,44 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   }
 #pragma unroll
   for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && part == 0) Dsum[row] = acc;
+  if (slice < nslices && part == 0) {
+    float* st = stats + slice * 2 * Np;
+    st[i] = acc;
+    st[Np + i] = live ? LSE[slice * N + i] * kLog2e : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
+template <int D>
+struct DkdvCfg {
+  static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
+  static constexpr int BQ = 64;    // queries per tile
+  static constexpr int NBUF = D == 64 ? 3 : 2;
+  static constexpr int WPE = D == 64 ? ATTN_BWD_WPE64 : ATTN_BWD_WPE128;
+  static constexpr int TILEB = BQ * D * 2;
+  static constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q | dO | D | LSE*log2e
+  static constexpr size_t LDS = (size_t)NBUF * STAGEB;
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c,
-    float kscale, uint32_t qsign) {
-  constexpr int NW = 4;
-  constexpr int BKV = 32 * NW;  // keys per workgroup
-  constexpr int BQ = 64;        // queries per tile
-  constexpr int NCH = D / 8;
-  constexpr int TILEB = BQ * D * 2;
-  constexpr int RPP = 256 / NCH;
-  constexpr int PASSES = BQ / RPP;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D>::WPE, DkdvCfg<D>::WPE)))
+void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                     const float* __restrict__ stats, __bf16* __restrict__ dK,
+                     __bf16* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c,
+                     float dk_scale, uint32_t qsign) {
+  using Cfg = DkdvCfg<D>;
+  constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
+  constexpr int STAGEB = Cfg::STAGEB;
+  constexpr int ROWB = D * 2;
+  constexpr int PW = TILEB / 1024 / 4;  // 1 KiB direct loads per wave per tensor per tile
   constexpr int NQC = D / 16;
   constexpr int NMB = D / 32;
-  constexpr int BUFB = 2 * TILEB + 2 * BQ * 4;  // Q tile | dO tile | lse2 | dsum
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -81,25 +123,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
   const int group = Hq / Hkv;
+  const int Np = stat_rows(N);
   const int64_t kvoff = (int64_t)bg * N * D;
   const int key0 = kblk * BKV + w * 32;  // first key of this wave
   const int krow = key0 + l32;           // key owned by this lane
+  const uint32_t slice_bytes = (uint32_t)N * ROWB;
 
-  // K^T and V^T operands of this wave's 32 keys, resident.
+  // K^T and V^T operands of this wave's 32 keys, resident (zero past N).
   bf16x8 kreg[NQC], vreg[NQC];
   {
-    const bool ok = krow < N;
-    const int64_t off = kvoff + (int64_t)(ok ? krow : 0) * D + hf * 8;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
-      u32x4 kv = *(const u32x4*)(K + off + cc * 16);
-      u32x4 vv = *(const u32x4*)(V + off + cc * 16);
-      if (!ok) {
-        kv = u32x4{0, 0, 0, 0};
-        vv = u32x4{0, 0, 0, 0};
-      }
-      kreg[cc] = bitcast<bf16x8>(kv);
-      vreg[cc] = bitcast<bf16x8>(vv);
+      const uint32_t off = (uint32_t)(krow * D + cc * 16 + hf * 8) * 2;
+      kreg[cc] = bitcast<bf16x8>(buf_load16(rk, off) ^ qsign);  // scale's sign rides on K here
+      vreg[cc] = bitcast<bf16x8>(buf_load16(rv, off));
     }
   }
   f32x16 dkacc[NMB], dvacc[NMB];
@@ -112,96 +151,101 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kblk * BKV) / BQ : 0;
   const int per_head = nqt - qt0;
-  const int iters = per_head > 0 ? group * per_head : 0;
+  const int iters = group * per_head;
 
-  const int lrow = tid / NCH;
-  const int lch = tid % NCH;
-  u32x4 qst[PASSES], dost[PASSES];
-  float stat = 0.f;  // threads 0..63: lse2 of row tid; 64..127: dsum of row tid-64
-  auto gload = [&](int it) {
+  // Direct loads of a query tile: Q and dO pieces as in the forward, plus
+  // the 512 bytes of statistics (wave 0, lanes 0..31).
+  uint32_t goff[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int o = (w * PW + i) * 1024 + lane * 16;
+    const int row = o / ROWB;
+    const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
+    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+  }
+  const uint32_t soff = (uint32_t)((lane >> 4) * Np * 4 + (lane & 15) * 16);
+  auto issue = [&](int it) {
     const int hq = g * group + it / per_head;
     const int qt = qt0 + it % per_head;
-    const int64_t qoff = (int64_t)(b * Hq + hq) * N;
+    const int64_t bh = (int64_t)b * Hq + hq;
+    char* base = smem + (it % NBUF) * STAGEB;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + bh * N * D, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + bh * N * D, slice_bytes);
+    const uint32_t tbase = (uint32_t)qt * BQ * ROWB;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = qt * BQ + p * RPP + lrow;
-      const bool ok = row < N;
-      const int64_t off = (qoff + (ok ? row : 0)) * D + lch * 8;
-      u32x4 qv = *(const u32x4*)(Q + off);
-      u32x4 dv = *(const u32x4*)(dO + off);
-      if (!ok) {
-        qv = u32x4{0, 0, 0, 0};
-        dv = u32x4{0, 0, 0, 0};
-      }
-      qst[p] = qv ^ qsign;
-      dost[p] = dv;
+    for (int i = 0; i < PW; ++i) {
+      buf_load16_lds(rq, base + (w * PW + i) * 1024, goff[i] + tbase);
+      buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, goff[i] + tbase);
     }
-    if (tid < 2 * BQ) {
-      const int row = qt * BQ + (tid & (BQ - 1));
-      const bool ok = row < N;
-      if (tid < BQ)
-        stat = ok ? LSE[qoff + row] * kLog2e : __builtin_inff();
-      else
-        stat = ok ? Dsum[qoff + row] : 0.f;
+    if (w == 0 && lane < 32) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(stats + bh * 2 * Np, (uint32_t)(2 * Np * 4));
+      buf_load16_lds(rs, base + 2 * TILEB, soff + (uint32_t)qt * BQ * 4);
     }
   };
-  auto swrite = [&](int buf) {
-    char* base = smem + buf * BUFB;
+  // Loads per wave per stage, for the partial waits of a 3-stage pipeline.
+  // Wave 0 has one extra (the statistics); waiting for the larger count is
+  // only conservative for the others.
+  constexpr int LOADS = 2 * PW + 1;
+
+  // Per-lane LDS offsets inside a stage (fixed for the whole loop).
+  int qoff_[NQC], troff[2][NMB];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int off = tile_off<D>(p * RPP + lrow, lch);
-      lds_write16(base + off, qst[p]);
-      lds_write16(base + TILEB + off, dost[p]);
-    }
-    if (tid < 2 * BQ) ((float*)(base + 2 * TILEB))[tid] = stat;
-  };
+  for (int cc = 0; cc < NQC; ++cc) qoff_[cc] = tile_off<D>(l32, 2 * cc + hf);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) troff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
 
-  if (iters > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < iters; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < iters) gload(it + 1);
-    const int qt = qt0 + it % per_head;
-    const char* qtile = smem + buf * BUFB;
+  auto step = [&](auto bufc, int it) {
+    constexpr int BUF = decltype(bufc)::value;
+    const char* qtile = smem + BUF * STAGEB;
     const char* dotile = qtile + TILEB;
-    const float* lse2 = (const float*)(qtile + 2 * TILEB);
-    const float* dsum = lse2 + BQ;
+    const float* dsum = (const float*)(qtile + 2 * TILEB);
+    const float* lse2 = dsum + BQ;
+    if (it + NBUF - 1 < iters) issue(it + NBUF - 1);
+    const int qt = qt0 + it % per_head;
 #pragma unroll
     for (int qs = 0; qs < BQ / 32; ++qs) {
       const int qbase = qs * 32;
       const int qfirst = qt * BQ + qbase;
-      if (CAUSAL && qfirst + 31 < key0) continue;  // every query precedes every key
-      if (qfirst >= N) continue;
+      if ((CAUSAL && qfirst + 31 < key0) || qfirst >= N) continue;  // wave-uniform
       // S = Q K^T and dP = dO V^T (rows: queries, columns: this wave's keys)
+      u32x4 qa[NQC], da[NQC];
+#pragma unroll
+      for (int cc = 0; cc < NQC; ++cc) {
+        qa[cc] = lds_read16(qtile + qbase * ROWB + qoff_[cc]);
+        da[cc] = lds_read16(dotile + qbase * ROWB + qoff_[cc]);
+      }
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < NQC; ++cc) {
-        const int off = tile_off<D>(qbase + l32, 2 * cc + hf);
-        sacc = mfma32(bitcast<bf16x8>(lds_read16(qtile + off)), kreg[cc], sacc);
-        pacc = mfma32(bitcast<bf16x8>(lds_read16(dotile + off)), vreg[cc], pacc);
+        sacc = mfma32(bitcast<bf16x8>(qa[cc]), kreg[cc], sacc);
+        pacc = mfma32(bitcast<bf16x8>(da[cc]), vreg[cc], pacc);
       }
-      const bool need_mask = CAUSAL && (key0 + 31 > qfirst);
       uint32_t pk[8], dsk[8];
+      float pv[16];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int q4 = qbase + 8 * rg + 4 * hf;
         const f32x4 l4 = *(const f32x4*)(lse2 + q4);
-        const f32x4 d4 = *(const f32x4*)(dsum + q4);
-        float pv[4], dsv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rg + e;
-          float p = fast_exp2(__builtin_fmaf(sacc[r], c, -l4[e]));
-          if (need_mask && krow > qt * BQ + q4 + e) p = 0.f;
-          pv[e] = p;
-          dsv[e] = p * (pacc[r] - d4[e]);
-        }
-        pk[2 * rg] = pack_bf16(pv[0], pv[1]);
-        pk[2 * rg + 1] = pack_bf16(pv[2], pv[3]);
+        for (int e = 0; e < 4; ++e) pv[4 * rg + e] = fast_exp2(__builtin_fmaf(sacc[4 * rg + e], c, -l4[e]));
+      }
+      if (CAUSAL && key0 + 31 > qfirst) {  // diagonal block: keys after the query get 0
+        __asm__ volatile("");
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (krow > qfirst + acc_row(r, hf)) pv[r] = 0.f;
+      }
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int q4 = qbase + 8 * rg + 4 * hf;
+        const f32x4 d4 = *(const f32x4*)(dsum + q4);
+        float dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * rg + e] * (pacc[4 * rg + e] - d4[e]);
+        pk[2 * rg] = pack_bf16(pv[4 * rg], pv[4 * rg + 1]);
+        pk[2 * rg + 1] = pack_bf16(pv[4 * rg + 2], pv[4 * rg + 3]);
         dsk[2 * rg] = pack_bf16(dsv[0], dsv[1]);
         dsk[2 * rg + 1] = pack_bf16(dsv[2], dsv[3]);
       }
@@ -211,22 +255,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const bf16x8 pb = bitcast<bf16x8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
         const bf16x8 sb =
             bitcast<bf16x8>(u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
+        const int rows = (qbase + 16 * cp) * ROWB;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-          const int o0 = tr_off<D>(lane, qbase + 16 * cp, 32 * mb, 0);
-          const int o1 = tr_off<D>(lane, qbase + 16 * cp, 32 * mb, 1);
-          const u32x2 a0 = lds_read_tr(dotile + o0), a1 = lds_read_tr(dotile + o1);
+          const u32x2 a0 = lds_read_tr(dotile + rows + troff[0][mb]);
+          const u32x2 a1 = lds_read_tr(dotile + rows + troff[1][mb]);
           dvacc[mb] = mfma32(bitcast<bf16x8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, dvacc[mb]);
-          const u32x2 b0 = lds_read_tr(qtile + o0), b1 = lds_read_tr(qtile + o1);
+          const u32x2 b0 = lds_read_tr(qtile + rows + troff[0][mb]);
+          const u32x2 b1 = lds_read_tr(qtile + rows + troff[1][mb]);
           dkacc[mb] = mfma32(bitcast<bf16x8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
         }
       }
     }
-    if (it + 1 < iters) swrite(buf ^ 1);
-    __syncthreads();
+    if (it + 1 < iters) {
+      if (NBUF == 3 && it + 2 < iters)
+        wait_vm_barrier<LOADS>();
+      else
+        wait_vm_barrier<0>();
+    }
+  };
+
+#pragma unroll
+  for (int it = 0; it < NBUF - 1; ++it)
+    if (it < iters) issue(it);
+  if (NBUF == 3 && iters > 1)
+    wait_vm_barrier<LOADS>();
+  else
+    wait_vm_barrier<0>();
+  for (int it = 0; it < iters; it += NBUF) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < iters) step(std::integral_constant<int, 1>{}, it + 1);
+    if constexpr (NBUF == 3)
+      if (it + 2 < iters) step(std::integral_constant<int, 2 % NBUF>{}, it + 2);
   }
 
-  // ---- store dK = kscale * dK^T^T, dV (lane: key krow; element r: feature)
+  // ---- store dK = scale * (dK^T)^T (Q was not sign-flipped), dV
+  // (lane: key krow; element r: feature)
   if (krow < N) {
     __bf16* dkp = dK + kvoff + (int64_t)krow * D;
     __bf16* dvp = dV + kvoff + (int64_t)krow * D;
@@ -236,8 +300,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int rg = 0; rg < 4; ++rg) {
         const int d0 = mb * 32 + rg * 8 + hf * 4;
         u32x2 kv, vv;
-        kv[0] = pack_bf16(dkacc[mb][4 * rg] * kscale, dkacc[mb][4 * rg + 1] * kscale);
-        kv[1] = pack_bf16(dkacc[mb][4 * rg + 2] * kscale, dkacc[mb][4 * rg + 3] * kscale);
+        kv[0] = pack_bf16(dkacc[mb][4 * rg] * dk_scale, dkacc[mb][4 * rg + 1] * dk_scale);
+        kv[1] = pack_bf16(dkacc[mb][4 * rg + 2] * dk_scale, dkacc[mb][4 * rg + 3] * dk_scale);
         vv[0] = pack_bf16(dvacc[mb][4 * rg], dvacc[mb][4 * rg + 1]);
         vv[1] = pack_bf16(dvacc[mb][4 * rg + 2], dvacc[mb][4 * rg + 3]);
         *(u32x2*)(dkp + d0) = kv;
@@ -247,27 +311,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------- dQ
+template <int D>
+struct DqCfg {
+  static constexpr int BR = 128;  // queries per workgroup (4 waves x 32)
+  static constexpr int BC = 64;   // keys per tile
+  static constexpr int NBUF = D == 64 ? 3 : 2;
+  static constexpr int WPE = D == 64 ? ATTN_DQ_WPE64 : ATTN_DQ_WPE128;
+  static constexpr int TILEB = BC * D * 2;
+  static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dsum,
-    __bf16* __restrict__ dQ, int Hq, int Hkv, int N, int nqb, float c, float qscale,
-    uint32_t qsign) {
-  constexpr int NW = 4;
-  constexpr int BR = 32 * NW;
-  constexpr int BC = 64;
-  constexpr int NCH = D / 8;
-  constexpr int TILEB = BC * D * 2;
-  constexpr int RPP = 256 / NCH;
-  constexpr int PASSES = BC / RPP;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<D>::WPE, DqCfg<D>::WPE)))
+void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                   const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                   const float* __restrict__ stats, __bf16* __restrict__ dQ, int Hq, int Hkv,
+                   int N, int nqb, float c, float qscale, uint32_t qsign) {
+  using Cfg = DqCfg<D>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
+  constexpr int ROWB = D * 2;
+  constexpr int PW = TILEB / 1024 / 4;
   constexpr int NQC = D / 16;
   constexpr int NMB = D / 32;
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];  // [2][K tile | V tile]
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [NBUF][K tile | V tile]
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -278,29 +348,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int g = h / (Hq / Hkv);
+  const int Np = stat_rows(N);
   const int64_t qoff = (int64_t)bh * N * D;
   const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
   const int q0 = qb * BR + w * 32;
   const int qrow = q0 + l32;
-  const bool qok = qrow < N;
+  const uint32_t slice_bytes = (uint32_t)N * ROWB;
 
+  // Q^T and dO^T operands and this lane's row statistics, resident.
   bf16x8 qreg[NQC], doreg[NQC];
   {
-    const int64_t off = qoff + (int64_t)(qok ? qrow : 0) * D + hf * 8;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + qoff, slice_bytes);
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
-      u32x4 qv = *(const u32x4*)(Q + off + cc * 16);
-      u32x4 dv = *(const u32x4*)(dO + off + cc * 16);
-      if (!qok) {
-        qv = u32x4{0, 0, 0, 0};
-        dv = u32x4{0, 0, 0, 0};
-      }
-      qreg[cc] = bitcast<bf16x8>(qv ^ qsign);
-      doreg[cc] = bitcast<bf16x8>(dv);
+      const uint32_t off = (uint32_t)(qrow * D + cc * 16 + hf * 8) * 2;
+      qreg[cc] = bitcast<bf16x8>(buf_load16(rq, off) ^ qsign);
+      doreg[cc] = bitcast<bf16x8>(buf_load16(rdo, off));
     }
   }
-  const float lse2 = qok ? LSE[(int64_t)bh * N + qrow] * kLog2e : __builtin_inff();
-  const float dsum = qok ? Dsum[(int64_t)bh * N + qrow] : 0.f;
+  const float* st = stats + (int64_t)bh * 2 * Np;
+  const bool qok = qrow < N;
+  const float dsum = qok ? st[qrow] : 0.f;
+  const float lse2 = qok ? st[Np + qrow] : 0.f;
 
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all, wtiles = ntiles_all;
@@ -309,83 +379,85 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     wtiles = min(ntiles, (q0 + 31) / BC + 1);
   }
 
-  const int lrow = tid / NCH;
-  const int lch = tid % NCH;
-  u32x4 kst[PASSES], vst[PASSES];
-  auto gload = [&](int j) {
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
+  uint32_t goff[PW];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = j * BC + p * RPP + lrow;
-      const bool ok = row < N;
-      const int64_t off = kvoff + (int64_t)(ok ? row : 0) * D + lch * 8;
-      u32x4 kv = *(const u32x4*)(K + off);
-      u32x4 vv = *(const u32x4*)(V + off);
-      if (!ok) {
-        kv = u32x4{0, 0, 0, 0};
-        vv = u32x4{0, 0, 0, 0};
-      }
-      kst[p] = kv;
-      vst[p] = vv;
+  for (int i = 0; i < PW; ++i) {
+    const int o = (w * PW + i) * 1024 + lane * 16;
+    const int row = o / ROWB;
+    const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
+    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+  }
+  auto issue = [&](int j) {
+    char* kt = smem + (j % NBUF) * 2 * TILEB;
+    const uint32_t tbase = (uint32_t)j * BC * ROWB;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      buf_load16_lds(rk, kt + (w * PW + i) * 1024, goff[i] + tbase);
+      buf_load16_lds(rv, kt + TILEB + (w * PW + i) * 1024, goff[i] + tbase);
     }
   };
-  auto swrite = [&](int buf) {
-    char* kb = smem + buf * 2 * TILEB;
+
+  int koff[NQC], troff[2][NMB];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int off = tile_off<D>(p * RPP + lrow, lch);
-      lds_write16(kb + off, kst[p]);
-      lds_write16(kb + TILEB + off, vst[p]);
-    }
-  };
+  for (int cc = 0; cc < NQC; ++cc) koff[cc] = tile_off<D>(l32, 2 * cc + hf);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) troff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
 
   f32x16 dqacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
 
-  if (ntiles > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  auto tile = [&](auto bufc, int j) {
+    constexpr int BUF = decltype(bufc)::value;
+    const char* kt = smem + BUF * 2 * TILEB;
+    const char* vt = kt + TILEB;
+    if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (j < wtiles && q0 < N) {
-      const char* kt = smem + buf * 2 * TILEB;
-      const char* vt = kt + TILEB;
+      // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
-        sacc[kbk] = f32x16{};
-        pacc[kbk] = f32x16{};
-        const int key = kbk * 32 + l32;
+        u32x4 ka[NQC], va[NQC];
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc) {
-          const int off = tile_off<D>(key, 2 * cc + hf);
-          sacc[kbk] = mfma32(bitcast<bf16x8>(lds_read16(kt + off)), qreg[cc], sacc[kbk]);
-          pacc[kbk] = mfma32(bitcast<bf16x8>(lds_read16(vt + off)), doreg[cc], pacc[kbk]);
+          ka[cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
+          va[cc] = lds_read16(vt + kbk * 32 * ROWB + koff[cc]);
+        }
+        sacc[kbk] = f32x16{};
+        pacc[kbk] = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc) {
+          sacc[kbk] = mfma32(bitcast<bf16x8>(ka[cc]), qreg[cc], sacc[kbk]);
+          pacc[kbk] = mfma32(bitcast<bf16x8>(va[cc]), doreg[cc], pacc[kbk]);
         }
       }
+      float pv[2][16];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[kbk][r] = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -lse2));
       const int k0 = j * BC;
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0));
+      if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {  // diagonal and tail tiles
+        __asm__ volatile("");
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kbk * 32 + acc_row(r, hf);
+            if (key >= N || (CAUSAL && key > qrow)) pv[kbk][r] = 0.f;
+          }
+      }
       uint32_t dsk[2][8];
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float ds[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            float p = fast_exp2(__builtin_fmaf(sacc[kbk][r + e], c, -lse2));
-            if (need_mask) {
-              const int key = k0 + kbk * 32 + acc_row(r + e, hf);
-              if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-            }
-            ds[e] = p * (pacc[kbk][r + e] - dsum);
-          }
-          dsk[kbk][r >> 1] = pack_bf16(ds[0], ds[1]);
-        }
+        for (int r = 0; r < 16; r += 2)
+          dsk[kbk][r >> 1] = pack_bf16(pv[kbk][r] * (pacc[kbk][r] - dsum),
+                                       pv[kbk][r + 1] * (pacc[kbk][r + 1] - dsum));
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -393,17 +465,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
           for (int cp = 0; cp < 2; ++cp) {
-            const int kbase = kbk * 32 + cp * 16;
-            const u32x2 lo = lds_read_tr(kt + tr_off<D>(lane, kbase, mb * 32, 0));
-            const u32x2 hi = lds_read_tr(kt + tr_off<D>(lane, kbase, mb * 32, 1));
+            const int rows = (kbk * 32 + cp * 16) * ROWB;
+            const u32x2 lo = lds_read_tr(kt + rows + troff[0][mb]);
+            const u32x2 hi = lds_read_tr(kt + rows + troff[1][mb]);
             const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
             const bf16x8 sb = bitcast<bf16x8>(u32x4{dsk[kbk][4 * cp], dsk[kbk][4 * cp + 1],
                                                     dsk[kbk][4 * cp + 2], dsk[kbk][4 * cp + 3]});
             dqacc[mb] = mfma32(a, sb, dqacc[mb]);
           }
     }
-    if (j + 1 < ntiles) swrite(buf ^ 1);
-    __syncthreads();
+    if (j + 1 < ntiles) {
+      if (NBUF == 3 && j + 2 < ntiles)
+        wait_vm_barrier<2 * PW>();
+      else
+        wait_vm_barrier<0>();
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < ntiles) issue(j);
+  if (NBUF == 3 && ntiles > 1)
+    wait_vm_barrier<2 * PW>();
+  else
+    wait_vm_barrier<0>();
+  for (int j = 0; j < ntiles; j += NBUF) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
+    if constexpr (NBUF == 3)
+      if (j + 2 < ntiles) tile(std::integral_constant<int, 2 % NBUF>{}, j + 2);
   }
 
   if (qok) {
@@ -422,6 +512,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
+size_t bwd_stats_bytes(int B, int Hq, int N) {
+  return (size_t)B * Hq * 2 * stat_rows(N) * sizeof(float);
+}
+
 struct BwdConsts {
   float c;         // |scale| log2(e), at least the smallest normal
   uint32_t qsign;  // sign bits XORed into Q when scale < 0
@@ -436,40 +530,41 @@ static BwdConsts bwd_consts(float scale) {
 template <int D>
 static hipError_t pre_t(const BwdArgs& a) {
   constexpr int RPB = 256 / (D / 8);
-  const int64_t rows = (int64_t)a.B * a.Hq * a.N;
-  const int64_t grid = (rows + RPB - 1) / RPB;
+  const int Np = stat_rows(a.N);
+  const int64_t nslices = (int64_t)a.B * a.Hq;
+  const int64_t grid = (nslices * Np + RPB - 1) / RPB;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                     (const __bf16*)a.o, (const __bf16*)a.dout, a.dsum, rows);
+                     (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.stats, a.N, Np, nslices);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t dkdv_t(const BwdArgs& a) {
-  constexpr int BKV = 128, BQ = 64;
+  using Cfg = DkdvCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
-  const int nkb = (a.N + BKV - 1) / BKV;
+  const int nkb = (a.N + Cfg::BKV - 1) / Cfg::BKV;
   const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
-  const size_t lds = 2 * (2 * BQ * D * 2 + 2 * BQ * 4);
-  const hipError_t e = allow_lds(bwd_dkdv_kernel<D, CAUSAL>, lds);
+  const hipError_t e = allow_lds(bwd_dkdv_kernel<D, CAUSAL>, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, a.stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                     (const __bf16*)a.dout, a.lse, a.dsum, (__bf16*)a.dk, (__bf16*)a.dv, a.Hq,
-                     a.Hkv, a.N, nkb, k.c, fabsf(a.scale), k.qsign);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
+                     a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                     (const __bf16*)a.dout, a.stats, (__bf16*)a.dk, (__bf16*)a.dv, a.Hq, a.Hkv, a.N,
+                     nkb, k.c, a.scale, k.qsign);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t dq_t(const BwdArgs& a) {
-  constexpr int BR = 128, BC = 64;
+  using Cfg = DqCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
-  const int nqb = (a.N + BR - 1) / BR;
+  const int nqb = (a.N + Cfg::BR - 1) / Cfg::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const size_t lds = 2 * 2 * BC * D * 2;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, a.stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                     (const __bf16*)a.dout, a.lse, a.dsum, (__bf16*)a.dq, a.Hq, a.Hkv, a.N, nqb,
-                     k.c, a.scale, k.qsign);
+  const hipError_t e = allow_lds(bwd_dq_kernel<D, CAUSAL>, Cfg::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
+                     a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                     (const __bf16*)a.dout, a.stats, (__bf16*)a.dq, a.Hq, a.Hkv, a.N, nqb, k.c,
+                     a.scale, k.qsign);
   return hipGetLastError();
 }
 

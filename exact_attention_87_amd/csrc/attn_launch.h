@@ -30,7 +30,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;  // workspace: D_i = dO_i . O_i, [B, Hq, N] fp32
+  float* stats;  // workspace: [B*Hq][2][N rounded up to 64] fp32 row statistics
   int B, Hq, Hkv, N, d;
   bool causal;
   float scale;
@@ -39,6 +39,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
+// Bytes of the backward row-statistics workspace.
+size_t bwd_stats_bytes(int B, int Hq, int N);
 // Backward stages; each launches one kernel on a.stream.
 hipError_t launch_bwd_pre(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);

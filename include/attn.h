@@ -35,6 +35,8 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the default stream).  The call returns once the kernels are launched;
  *    it never synchronises.
+ *  - Sizes: N <= 2^22 and B * Hq <= 2^24 (larger requests return
+ *    ATTN_ERR_UNSUPPORTED).
  *  - B == 0 or N == 0 is an empty problem: nothing is launched and ATTN_OK
  *    is returned (pointers may then be NULL).
  *  - Arguments are validated on the host before any HIP call.  On error no
@@ -83,8 +85,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Bytes of device workspace attn_bwd needs for this problem (a multiple of
- * 256).  0 for an empty problem.  Returns (size_t)-1 for arguments attn_bwd
- * would reject.
+ * 256; 8 * B * Hq * (N rounded up to 64)).  0 for an empty problem.  Returns
+ * (size_t)-1 for arguments attn_bwd would reject.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype);
 
@@ -110,25 +112,28 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /*
  * The three stages attn_bwd runs, in order, on one stream.  Exposed so a
  * caller can schedule or time them separately; calling them in this order
- * with the same arguments gives exactly attn_bwd's results.  `dsum` is an
- * fp32 [B,Hq,N] buffer (attn_bwd keeps it at the start of its workspace).
+ * with the same arguments gives exactly attn_bwd's results.
  *
- *   attn_bwd_preprocess: dsum_i = dO_i . O_i for every query row.
- *   attn_bwd_dkdv:       dK, dV (recomputing P and dP tile by tile from q, k,
- *                        lse; reads dsum).  dK/dV of a key/value head are
+ * `stats` is the backward workspace (attn_bwd_workspace_bytes bytes, caller
+ * owned): per (batch, query head) two fp32 rows of Np = N rounded up to 64
+ * entries, [B*Hq][2][Np]: D_i = dO_i . O_i and LSE_i * log2(e), zero in the
+ * padding.  attn_bwd_preprocess writes it; the other two stages read it.
+ *
+ *   attn_bwd_preprocess: the row statistics from O, dO and LSE.
+ *   attn_bwd_dkdv:       dK, dV, recomputing P and dP tile by tile from q, k
+ *                        and the statistics; dK/dV of a key/value head are
  *                        summed over its query heads on chip.
- *   attn_bwd_dq:         dQ (recomputing P and dP; reads dsum).
+ *   attn_bwd_dq:         dQ, recomputing P and dP the same way.
  * Validation, ownership and error behaviour are those of attn_bwd.
  */
-attn_status attn_bwd_preprocess(const void* o, const void* dout, float* dsum, int B, int Hq,
-                                int N, int d, attn_dtype dtype, void* stream);
+attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, float* stats,
+                                int B, int Hq, int N, int d, attn_dtype dtype, void* stream);
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                          const float* lse, const float* dsum, void* dk, void* dv, int B,
-                          int Hq, int Hkv, int N, int d, int causal, float scale,
-                          attn_dtype dtype, void* stream);
+                          const float* stats, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                          int d, int causal, float scale, attn_dtype dtype, void* stream);
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                        const float* lse, const float* dsum, void* dq, int B, int Hq, int Hkv,
-                        int N, int d, int causal, float scale, attn_dtype dtype, void* stream);
+                        const float* stats, void* dq, int B, int Hq, int Hkv, int N, int d,
+                        int causal, float scale, attn_dtype dtype, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);

@@ -84,7 +84,8 @@ def test_fwd_unsupported_head_dim(d):
 
 
 def test_fwd_too_large_is_unsupported():
-    assert fwd(N=(1 << 24) + 1) == ea.ATTN_ERR_UNSUPPORTED
+    assert fwd(N=(1 << 22) + 1) == ea.ATTN_ERR_UNSUPPORTED
+    assert fwd(B=1 << 13, Hq=1 << 12, Hkv=1 << 12) == ea.ATTN_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(N=0)])
@@ -111,8 +112,10 @@ def test_bwd_fp32_is_unsupported():
 
 
 def test_workspace_bytes():
-    assert ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_BF16) == 3328  # 3200 -> 256
-    assert ea.attn_bwd_workspace_bytes(8, 16, 16, 2048, 64, ea.ATTN_BF16) == 8 * 16 * 2048 * 4
+    # [B*Hq][2][N rounded up to 64] fp32, rounded up to 256 bytes
+    assert ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_BF16) == 2 * 4 * 2 * 128 * 4
+    assert ea.attn_bwd_workspace_bytes(1, 1, 1, 1, 64, ea.ATTN_BF16) == 512
+    assert ea.attn_bwd_workspace_bytes(8, 16, 16, 2048, 64, ea.ATTN_BF16) == 8 * 16 * 2 * 2048 * 4
     assert ea.attn_bwd_workspace_bytes(0, 4, 2, 100, 64, ea.ATTN_BF16) == 0
     assert ea.attn_bwd_workspace_bytes(1, 3, 2, 100, 64, ea.ATTN_BF16) == -1
     assert ea.attn_bwd_workspace_bytes(1, 4, 2, 100, 80, ea.ATTN_BF16) == -1
@@ -129,24 +132,25 @@ def test_torch_wrapper_rejects_host_tensors():
 def test_staged_backward_validation():
     ok = dict(B=2, Hq=4, Hkv=2, N=100, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16, stream=None)
     # empty problems are fine without pointers
-    assert ea.attn_bwd_preprocess(None, None, None, 0, 4, 100, 64, ea.ATTN_BF16, None) == ea.ATTN_OK
-    assert ea.attn_bwd_dkdv(*([None] * 8), 2, 4, 2, 0, 64, 1, 0.1, ea.ATTN_BF16, None) == ea.ATTN_OK
-    assert ea.attn_bwd_dq(*([None] * 7), 2, 4, 2, 0, 64, 1, 0.1, ea.ATTN_BF16, None) == ea.ATTN_OK
+    assert ea.attn_bwd_preprocess(None, None, None, None, 0, 4, 100, 64, ea.ATTN_BF16,
+                                  None) == ea.ATTN_OK
+    assert ea.attn_bwd_dkdv(*([None] * 7), 2, 4, 2, 0, 64, 1, 0.1, ea.ATTN_BF16, None) == ea.ATTN_OK
+    assert ea.attn_bwd_dq(*([None] * 6), 2, 4, 2, 0, 64, 1, 0.1, ea.ATTN_BF16, None) == ea.ATTN_OK
     # missing / misaligned / overlapping buffers
-    assert ea.attn_bwd_preprocess(O, None, WS, 2, 4, 100, 64, ea.ATTN_BF16, None) == \
-        ea.ATTN_ERR_INVALID_ARG
-    assert ea.attn_bwd_preprocess(O, DO, O + 64, 2, 4, 100, 64, ea.ATTN_BF16, None) == \
-        ea.ATTN_ERR_INVALID_ARG
-    assert ea.attn_bwd_preprocess(O, DO, WS + 4, 2, 4, 100, 64, ea.ATTN_BF16, None) == \
-        ea.ATTN_ERR_INVALID_ARG
+    bad_pre = [(O, None, L, WS), (O, DO, None, WS), (O, DO, L, O + 64), (O, DO, L, WS + 4),
+               (O, DO, L, L + 512)]
+    for o, do, lse, st in bad_pre:
+        assert ea.attn_bwd_preprocess(o, do, lse, st, 2, 4, 100, 64, ea.ATTN_BF16, None) == \
+            ea.ATTN_ERR_INVALID_ARG
     args = [ok[x] for x in ("B", "Hq", "Hkv", "N", "d", "causal", "scale", "dtype", "stream")]
-    assert ea.attn_bwd_dkdv(Q, K, V, DO, L, WS, DK, K, *args) == ea.ATTN_ERR_INVALID_ARG
-    assert ea.attn_bwd_dkdv(Q, K, V, DO, L, WS, DK, DK, *args) == ea.ATTN_ERR_INVALID_ARG
-    assert ea.attn_bwd_dq(Q, K, V, DO, L, WS, WS, *args) == ea.ATTN_ERR_INVALID_ARG
-    assert ea.attn_bwd_dq(Q, K, V, DO, None, WS, DQ, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dkdv(Q, K, V, DO, WS, DK, K, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dkdv(Q, K, V, DO, WS, DK, DK, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dkdv(Q, K, V, DO, WS, WS + 256, DV, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq(Q, K, V, DO, WS, WS, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq(Q, K, V, DO, None, DQ, *args) == ea.ATTN_ERR_INVALID_ARG
     bad = list(args)
     bad[2] = 3  # Hq % Hkv != 0
-    assert ea.attn_bwd_dq(Q, K, V, DO, L, WS, DQ, *bad) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq(Q, K, V, DO, WS, DQ, *bad) == ea.ATTN_ERR_INVALID_ARG
     f32 = list(args)
     f32[7] = ea.ATTN_F32
-    assert ea.attn_bwd_dkdv(Q, K, V, DO, L, WS, DK, DV, *f32) == ea.ATTN_ERR_UNSUPPORTED
+    assert ea.attn_bwd_dkdv(Q, K, V, DO, WS, DK, DV, *f32) == ea.ATTN_ERR_UNSUPPORTED

@@ -133,24 +133,30 @@ def test_staged_backward_equals_attn_bwd():
                                                        with_dout=True))
     o, lse = ea.fwd(q, k, v, causal=True)
     ref = ea.bwd(q, k, v, o, lse, do, causal=True)
-    dsum = torch.empty(B, Hq, N, device=dev, dtype=torch.float32)
+    nbytes = ea.attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, ea.ATTN_BF16)
+    Np = (N + 63) // 64 * 64
+    assert nbytes == B * Hq * 2 * Np * 4
+    stats = torch.full((B * Hq, 2, Np), float("nan"), device=dev, dtype=torch.float32)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     s = torch.cuda.current_stream().cuda_stream
     sc = d ** -0.5
-    assert ea.attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), dsum.data_ptr(), B, Hq, N, d,
-                                  ea.ATTN_BF16, s) == ea.ATTN_OK
+    assert ea.attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), stats.data_ptr(),
+                                  B, Hq, N, d, ea.ATTN_BF16, s) == ea.ATTN_OK
     assert ea.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                            lse.data_ptr(), dsum.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            stats.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                             B, Hq, Hkv, N, d, 1, sc, ea.ATTN_BF16, s) == ea.ATTN_OK
     assert ea.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                          lse.data_ptr(), dsum.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, 1,
+                          stats.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, 1,
                           sc, ea.ATTN_BF16, s) == ea.ATTN_OK
     torch.cuda.synchronize()
     for a, b in zip(ref, (dq, dk, dv)):
         assert torch.equal(a, b)
-    # D_i = dO_i . O_i
-    ref_d = (do.float() * o.float()).sum(-1)
-    assert (dsum - ref_d).abs().max() <= 1e-3 * ref_d.abs().max()
+    # row statistics: D_i = dO_i . O_i, LSE_i * log2(e), zero padding
+    ref_d = (do.float() * o.float()).sum(-1).reshape(B * Hq, N)
+    assert (stats[:, 0, :N] - ref_d).abs().max() <= 1e-3 * ref_d.abs().max()
+    ref_l = lse.reshape(B * Hq, N) * 1.4426950408889634
+    assert (stats[:, 1, :N] - ref_l).abs().max() <= 1e-5 * ref_l.abs().max()
+    assert bool((stats[:, :, N:] == 0).all())
 
 
 def test_bwd_empty():
