@@ -94,6 +94,39 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def forward_only(w, args, dev):
+    """Forward of one workload: K timed launches of attn_fwd (events on the stream)."""
+    import torch
+
+    import attn_inputs
+    import exact_attention_87_amd as ea
+
+    q, k, v = (t.to(dev) for t in attn_inputs.make_workload(w, with_dout=False))
+    o, lse = ea.fwd(q, k, v, causal=w.causal)
+    for _ in range(args.warmup):
+        ea.fwd(q, k, v, causal=w.causal, out=o, lse=lse)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        ea.fwd(q, k, v, causal=w.causal, out=o, lse=lse)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    fl = fwd_flops(w.B, w.Hq, w.N, w.d, w.causal)
+    print(json.dumps({
+        "metric": "attention forward TFLOP/s on 1 MI355X", "value": round(fl / ms / 1e9, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "kernel_ms": round(ms, 5),
+        "frac_of_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "higher_is_better": True,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "q_mult": w.q_mult, "seed": w.seed}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +137,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--fwd-only", type=int, default=0, metavar="ID",
+                    help="time only the forward of workload ID (1-5) and print its JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -122,6 +157,10 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     ea.lib()  # fail loudly if the HIP library is missing
+
+    if args.fwd_only:
+        forward_only(attn_inputs.WORKLOADS[args.fwd_only], args, dev)
+        return
 
     w = attn_inputs.WORKLOADS[5]
     B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
