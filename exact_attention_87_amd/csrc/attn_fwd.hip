@@ -29,6 +29,7 @@
 namespace attn {
 
 constexpr float kTau = 8.0f;
+constexpr float kSumMax = 256.0f;  // 2^kTau
 
 // Tuning knobs (compile-time; the defaults are the shipped configuration).
 #ifndef ATTN_FWD_WPE64
@@ -36,6 +37,12 @@ constexpr float kTau = 8.0f;
 #endif
 #ifndef ATTN_FWD_WPE128
 #define ATTN_FWD_WPE128 2
+#endif
+#ifndef ATTN_FWD_OPTIMISTIC
+#define ATTN_FWD_OPTIMISTIC 1
+#endif
+#ifndef ATTN_FWD_SETPRIO
+#define ATTN_FWD_SETPRIO 1
 #endif
 #ifndef ATTN_FWD_NBUF64
 #define ATTN_FWD_NBUF64 3
@@ -163,6 +170,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc) kfrag[kbk][cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
       f32x16 sacc[2];
+      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
         sacc[kbk] = f32x16{};
@@ -170,6 +178,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int cc = 0; cc < NQC; ++cc)
           sacc[kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
       }
+      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
       // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
       // and kept as a branch rather than flattened into selects)
       const int k0 = j * BC;
@@ -184,6 +193,51 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             if (dead) sacc[kbk][r] = -__builtin_inff();
           }
       }
+#if ATTN_FWD_OPTIMISTIC
+      // ---- p = 2^(s*c - m) with the current running max; fp32 row sums.  A
+      // lane whose tile sum exceeds 2^kTau may hold a p above 2^kTau (or the
+      // max was never set): only then take the max and maybe rescale.
+      uint32_t pk[2][8];
+      float tsum = 0.f;
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -ms));
+          const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -ms));
+          pk[kbk][r >> 1] = pack_bf16(p0, p1);
+          tsum += p0 + p1;
+        }
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax)) != 0) {
+        __asm__ volatile("");
+        float mloc = sacc[0][0];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[kbk][r]);
+        mloc = __builtin_fmaxf(mloc, xor32(mloc));
+        const float tmax = mloc * c;
+        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
+          const float mnew = __builtin_fmaxf(ms, tmax);
+          const float alpha = fast_exp2(ms - mnew);
+          ms = mnew;
+          lsum *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
+          tsum = 0.f;
+#pragma unroll
+          for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -ms));
+              const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -ms));
+              pk[kbk][r >> 1] = pack_bf16(p0, p1);
+              tsum += p0 + p1;
+            }
+        }
+      }
+      lsum += tsum;
+#else
       // ---- row max over the tile (raw scores; c > 0)
       float mloc = sacc[0][0];
 #pragma unroll
@@ -213,7 +267,9 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           pk[kbk][r >> 1] = pack_bf16(p0, p1);
           lsum += p0 + p1;
         }
+#endif
       // ---- O^T += V^T P^T
+      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -228,6 +284,7 @@ void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
             oacc[mb] = mfma32(a, bp, oacc[mb]);
           }
+      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
     }
     if (j + 1 < ntiles) {
       // tile j+1 must have landed; tile j+2 (three stages) may stay in flight
