@@ -19,6 +19,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # The direct global->LDS loads set M0 in inline assembly; no other code in
+    # these kernels keeps a value in M0 (checked in the generated assembly).
+    "-Wno-inline-asm",
 ]
 
 

@@ -120,10 +120,19 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 
 // 16 bytes per lane from the buffer straight into LDS: lane l's data lands at
-// lds + 16*l (lds must be the same for the whole wave).
+// lds + 16*l (lds must be the same for the whole wave; it goes through M0,
+// with the one wait state a following LDS load needs after an M0 write).
+// Written as inline assembly on purpose: the compiler's own waitcnt
+// insertion treats every later LDS read as possibly aliasing a pending
+// buffer-to-LDS load and waits for all of them, which would serialise the
+// prefetch of the next tiles into every tile.  The kernels instead wait with
+// explicit vmcnt counts before each workgroup barrier (wait_vm_barrier).
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16,
-                                           off, 0, 0, 0);
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(m0), "v"(off), "s"(r)
+                   : "memory", "m0");
 }
 
 // Wait until at most n vector-memory loads of this wave are outstanding, then

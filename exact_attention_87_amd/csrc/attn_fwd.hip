@@ -51,9 +51,17 @@ constexpr float kSumMax = 256.0f;  // 2^kTau
 #define ATTN_FWD_NBUF128 2
 #endif
 
+#ifndef ATTN_FWD_NW64
+#define ATTN_FWD_NW64 4
+#endif
+#ifndef ATTN_FWD_NW128
+#define ATTN_FWD_NW128 4
+#endif
+
 template <int D>
 struct FwdCfg {
-  static constexpr int BR = 128;  // query rows per workgroup (4 waves x 32)
+  static constexpr int NW = D == 64 ? ATTN_FWD_NW64 : ATTN_FWD_NW128;  // waves per workgroup
+  static constexpr int BR = 32 * NW;  // query rows per workgroup (32 per wave)
   static constexpr int BC = 64;   // keys per tile
   static constexpr int NBUF = D == 64 ? ATTN_FWD_NBUF64 : ATTN_FWD_NBUF128;  // LDS stages
   static constexpr int WPE = D == 64 ? ATTN_FWD_WPE64 : ATTN_FWD_WPE128;     // waves per SIMD
@@ -62,14 +70,16 @@ struct FwdCfg {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE)))
-void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(64 * FwdCfg<D>::NW)
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                      const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                      int Hq, int Hkv, int N, int nqb, float c, uint32_t qsign) {
   using Cfg = FwdCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
   constexpr int ROWB = D * 2;
-  constexpr int PW = TILEB / 1024 / 4;  // 1 KiB direct loads per wave per tensor per tile
+  constexpr int NW = Cfg::NW;
+  constexpr int PW = TILEB / 1024 / NW;  // 1 KiB direct loads per wave per tensor per tile
+  static_assert(PW * NW * 1024 == TILEB, "tile pieces");
   constexpr int NQC = D / 16;           // k-chunks of the S contraction
   constexpr int NMB = D / 32;           // 32-row blocks of O^T
 
@@ -418,7 +428,8 @@ static hipError_t launch_bf16(const FwdArgs& a) {
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), lds, a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * FwdCfg<D>::NW),
+                     lds, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
                      a.Hq, a.Hkv, a.N, nqb, c, qsign);
   return hipGetLastError();
