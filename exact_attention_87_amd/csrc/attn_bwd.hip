@@ -12,7 +12,9 @@
 // Three kernels, all deterministic (no atomics):
 //   pre:  per (batch, head) row statistics into the caller's workspace,
 //         laid out [B*Hq][2][Np] fp32 with Np = N rounded up to 64:
-//         [0] = D_i = dO_i . O_i, [1] = LSE_i * log2(e); padding rows are 0.
+//         [0] = -D_i = -(dO_i . O_i), [1] = LSE_i * log2(e); padding rows
+//         are 0.  -D seeds the accumulator of dP = dO V^T, so the matrix
+//         cores return dP - D directly.
 //   dkdv: one workgroup per (batch, kv head, block of 128 keys); each wave
 //         keeps its 32 keys' K and V as matrix-core operands in registers and
 //         accumulates dK^T, dV^T over every query tile of every query head of
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
   if (slice < nslices && part == 0) {
     float* st = stats + slice * 2 * Np;
-    st[i] = acc;
+    st[i] = -acc;
     st[Np + i] = live ? LSE[slice * N + i] * kLog2e : 0.f;
   }
 }
@@ -200,7 +202,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     constexpr int BUF = decltype(bufc)::value;
     const char* qtile = smem + BUF * STAGEB;
     const char* dotile = qtile + TILEB;
-    const float* dsum = (const float*)(qtile + 2 * TILEB);
+    const float* dsum = (const float*)(qtile + 2 * TILEB);  // -D of the tile's rows
     const float* lse2 = dsum + BQ;
     if (it + NBUF - 1 < iters) issue(it + NBUF - 1);
     const int qt = qt0 + it % per_head;
@@ -216,7 +218,16 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         qa[cc] = lds_read16(qtile + qbase * ROWB + qoff_[cc]);
         da[cc] = lds_read16(dotile + qbase * ROWB + qoff_[cc]);
       }
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      // dP - D: the accumulator starts at -D of each row (element 4*rg+e is
+      // row qbase + 8*rg + 4*hf + e)
+      f32x16 pacc;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 nd = *(const f32x4*)(dsum + qbase + 8 * rg + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
+      }
+      f32x16 sacc = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < NQC; ++cc) {
         sacc = mfma32(bitcast<bf16x8>(qa[cc]), kreg[cc], sacc);
@@ -239,11 +250,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       }
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int q4 = qbase + 8 * rg + 4 * hf;
-        const f32x4 d4 = *(const f32x4*)(dsum + q4);
         float dsv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * rg + e] * (pacc[4 * rg + e] - d4[e]);
+        for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * rg + e] * pacc[4 * rg + e];
         pk[2 * rg] = pack_bf16(pv[4 * rg], pv[4 * rg + 1]);
         pk[2 * rg + 1] = pack_bf16(pv[4 * rg + 2], pv[4 * rg + 3]);
         dsk[2 * rg] = pack_bf16(dsv[0], dsv[1]);
@@ -369,8 +378,11 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
   const float* st = stats + (int64_t)bh * 2 * Np;
   const bool qok = qrow < N;
-  const float dsum = qok ? st[qrow] : 0.f;
+  const float ndsum = qok ? st[qrow] : 0.f;  // -D of this lane's row
   const float lse2 = qok ? st[Np + qrow] : 0.f;
+  f32x16 pinit;  // seeds dP^T - D
+#pragma unroll
+  for (int r = 0; r < 16; ++r) pinit[r] = ndsum;
 
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all, wtiles = ntiles_all;
@@ -428,7 +440,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
           va[cc] = lds_read16(vt + kbk * 32 * ROWB + koff[cc]);
         }
         sacc[kbk] = f32x16{};
-        pacc[kbk] = f32x16{};
+        pacc[kbk] = pinit;
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc) {
           sacc[kbk] = mfma32(bitcast<bf16x8>(ka[cc]), qreg[cc], sacc[kbk]);
@@ -456,8 +468,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
-          dsk[kbk][r >> 1] = pack_bf16(pv[kbk][r] * (pacc[kbk][r] - dsum),
-                                       pv[kbk][r + 1] * (pacc[kbk][r + 1] - dsum));
+          dsk[kbk][r >> 1] = pack_bf16(pv[kbk][r] * pacc[kbk][r], pv[kbk][r + 1] * pacc[kbk][r + 1]);
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)

@@ -116,8 +116,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
  *
  * `stats` is the backward workspace (attn_bwd_workspace_bytes bytes, caller
  * owned): per (batch, query head) two fp32 rows of Np = N rounded up to 64
- * entries, [B*Hq][2][Np]: D_i = dO_i . O_i and LSE_i * log2(e), zero in the
- * padding.  attn_bwd_preprocess writes it; the other two stages read it.
+ * entries, [B*Hq][2][Np]: -D_i = -(dO_i . O_i) and LSE_i * log2(e), zero in
+ * the padding.  attn_bwd_preprocess writes it; the other two stages read it.
  *
  *   attn_bwd_preprocess: the row statistics from O, dO and LSE.
  *   attn_bwd_dkdv:       dK, dV, recomputing P and dP tile by tile from q, k

@@ -151,8 +151,8 @@ def test_staged_backward_equals_attn_bwd():
     torch.cuda.synchronize()
     for a, b in zip(ref, (dq, dk, dv)):
         assert torch.equal(a, b)
-    # row statistics: D_i = dO_i . O_i, LSE_i * log2(e), zero padding
-    ref_d = (do.float() * o.float()).sum(-1).reshape(B * Hq, N)
+    # row statistics: -D_i = -(dO_i . O_i), LSE_i * log2(e), zero padding
+    ref_d = -(do.float() * o.float()).sum(-1).reshape(B * Hq, N)
     assert (stats[:, 0, :N] - ref_d).abs().max() <= 1e-3 * ref_d.abs().max()
     ref_l = lse.reshape(B * Hq, N) * 1.4426950408889634
     assert (stats[:, 1, :N] - ref_l).abs().max() <= 1e-5 * ref_l.abs().max()
