@@ -38,9 +38,6 @@ constexpr float kSumMax = 256.0f;  // 2^kTau
 #ifndef ATTN_FWD_WPE128
 #define ATTN_FWD_WPE128 2
 #endif
-#ifndef ATTN_FWD_OPTIMISTIC
-#define ATTN_FWD_OPTIMISTIC 1
-#endif
 #ifndef ATTN_FWD_SETPRIO
 #define ATTN_FWD_SETPRIO 1
 #endif
@@ -51,6 +48,12 @@ constexpr float kSumMax = 256.0f;  // 2^kTau
 #define ATTN_FWD_NBUF128 2
 #endif
 
+#ifndef ATTN_FWD_NB64
+#define ATTN_FWD_NB64 1
+#endif
+#ifndef ATTN_FWD_NB128
+#define ATTN_FWD_NB128 1
+#endif
 #ifndef ATTN_FWD_NW64
 #define ATTN_FWD_NW64 4
 #endif
@@ -61,7 +64,8 @@ constexpr float kSumMax = 256.0f;  // 2^kTau
 template <int D>
 struct FwdCfg {
   static constexpr int NW = D == 64 ? ATTN_FWD_NW64 : ATTN_FWD_NW128;  // waves per workgroup
-  static constexpr int BR = 32 * NW;  // query rows per workgroup (32 per wave)
+  static constexpr int NB = D == 64 ? ATTN_FWD_NB64 : ATTN_FWD_NB128;  // 32-row blocks per wave
+  static constexpr int BR = 32 * NB * NW;  // query rows per workgroup
   static constexpr int BC = 64;   // keys per tile
   static constexpr int NBUF = D == 64 ? ATTN_FWD_NBUF64 : ATTN_FWD_NBUF128;  // LDS stages
   static constexpr int WPE = D == 64 ? ATTN_FWD_WPE64 : ATTN_FWD_WPE128;     // waves per SIMD
@@ -71,17 +75,19 @@ struct FwdCfg {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * FwdCfg<D>::NW)
-__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                     const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                     int Hq, int Hkv, int N, int nqb, float c, uint32_t qsign) {
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb, float c,
+    uint32_t qsign) {
   using Cfg = FwdCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
+  constexpr int NB = Cfg::NB;  // 32-row query blocks per wave (each K/V fragment feeds NB products)
   constexpr int ROWB = D * 2;
   constexpr int NW = Cfg::NW;
   constexpr int PW = TILEB / 1024 / NW;  // 1 KiB direct loads per wave per tensor per tile
   static_assert(PW * NW * 1024 == TILEB, "tile pieces");
-  constexpr int NQC = D / 16;           // k-chunks of the S contraction
-  constexpr int NMB = D / 32;           // 32-row blocks of O^T
+  constexpr int NQC = D / 16;  // k-chunks of the S contraction
+  constexpr int NMB = D / 32;  // 32-row blocks of O^T
 
   extern __shared__ __attribute__((aligned(16))) char smem[];  // [NBUF][K tile | V tile]
 
@@ -101,8 +107,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   const int g = h / (Hq / Hkv);
   const int64_t qoff = (int64_t)bh * N * D;
   const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
-  const int q0 = qb * BR + w * 32;  // first query row of this wave
-  const int qrow = q0 + l32;        // query row owned by this lane
+  const int q0 = qb * BR + w * 32 * NB;  // first query row of this wave
 
   // Each (batch, head) slice is one raw buffer; rows past N read as zero.
   const uint32_t slice_bytes = (uint32_t)N * ROWB;
@@ -110,18 +115,21 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
 
-  // Q^T operand, resident for the whole key loop.
-  bf16x8 qreg[NQC];
+  // Q^T operands (one per 32-row block), resident for the whole key loop.
+  bf16x8 qreg[NB][NQC];
 #pragma unroll
-  for (int cc = 0; cc < NQC; ++cc)
-    qreg[cc] = bitcast<bf16x8>(buf_load16(rq, (uint32_t)(qrow * D + cc * 16 + hf * 8) * 2) ^ qsign);
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc)
+      qreg[nb][cc] = bitcast<bf16x8>(
+          buf_load16(rq, (uint32_t)((q0 + nb * 32 + l32) * D + cc * 16 + hf * 8) * 2) ^ qsign);
 
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all;
   int wtiles = ntiles_all;
   if (CAUSAL) {
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
-    wtiles = min(ntiles, (q0 + 31) / BC + 1);
+    wtiles = min(ntiles, (q0 + 32 * NB - 1) / BC + 1);
   }
 
   // Direct global->LDS tile loads.  Wave w fills the 1 KiB pieces
@@ -159,11 +167,30 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) voff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
 
-  float ms = -__builtin_inff();  // running max, scaled base-2 units
-  float lsum = 0.f;              // this lane's share of the normaliser
-  f32x16 oacc[NMB];
+  float ms[NB], lsum[NB];  // running max (scaled base-2 units), this lane's share of l
+  f32x16 oacc[NB][NMB];
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
+  for (int nb = 0; nb < NB; ++nb) {
+    ms[nb] = -__builtin_inff();
+    lsum[nb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) oacc[nb][mb] = f32x16{};
+  }
+
+  // p = 2^(s*c - m) -> bf16 P^T operand and this lane's tile sum.
+  auto softmax_exp = [&](const f32x16 (&sacc)[2], float m, uint32_t (&pk)[2][8]) {
+    float tsum = 0.f;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -m));
+        pk[kbk][r >> 1] = pack_bf16(p0, p1);
+        tsum += p0 + p1;
+      }
+    return tsum;
+  };
 
   // One key tile; BUF (the LDS stage) is a compile-time constant so every LDS
   // address is a fixed per-lane register plus an immediate.
@@ -173,21 +200,23 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
     const char* vt = kt + TILEB;
     if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (j < wtiles) {
-      // ---- S^T = K Q^T for the tile's two 32-key blocks
+      // ---- S^T = K Q^T for the tile's two 32-key blocks and every query block
       u32x4 kfrag[2][NQC];
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc) kfrag[kbk][cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
-      f32x16 sacc[2];
+      f32x16 sacc[NB][2];
       if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) {
-        sacc[kbk] = f32x16{};
+      for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-        for (int cc = 0; cc < NQC; ++cc)
-          sacc[kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
-      }
+        for (int nb = 0; nb < NB; ++nb) {
+          sacc[nb][kbk] = f32x16{};
+#pragma unroll
+          for (int cc = 0; cc < NQC; ++cc)
+            sacc[nb][kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[nb][cc], sacc[nb][kbk]);
+        }
       if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
       // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
       // and kept as a branch rather than flattened into selects)
@@ -195,90 +224,52 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
       if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {
         __asm__ volatile("");
 #pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kbk * 32 + acc_row(r, hf);
-            const bool dead = (key >= N) || (CAUSAL && key > qrow);
-            if (dead) sacc[kbk][r] = -__builtin_inff();
-          }
-      }
-#if ATTN_FWD_OPTIMISTIC
-      // ---- p = 2^(s*c - m) with the current running max; fp32 row sums.  A
-      // lane whose tile sum exceeds 2^kTau may hold a p above 2^kTau (or the
-      // max was never set): only then take the max and maybe rescale.
-      uint32_t pk[2][8];
-      float tsum = 0.f;
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -ms));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -ms));
-          pk[kbk][r >> 1] = pack_bf16(p0, p1);
-          tsum += p0 + p1;
-        }
-      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax)) != 0) {
-        __asm__ volatile("");
-        float mloc = sacc[0][0];
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[kbk][r]);
-        mloc = __builtin_fmaxf(mloc, xor32(mloc));
-        const float tmax = mloc * c;
-        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
-          const float mnew = __builtin_fmaxf(ms, tmax);
-          const float alpha = fast_exp2(ms - mnew);
-          ms = mnew;
-          lsum *= alpha;
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
-          tsum = 0.f;
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -ms));
-              const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -ms));
-              pk[kbk][r >> 1] = pack_bf16(p0, p1);
-              tsum += p0 + p1;
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + kbk * 32 + acc_row(r, hf);
+              const bool dead = (key >= N) || (CAUSAL && key > q0 + nb * 32 + l32);
+              if (dead) sacc[nb][kbk][r] = -__builtin_inff();
             }
+      }
+      // ---- p with the current running max.  A lane whose tile sum exceeds
+      // 2^kTau may hold a p above 2^kTau (or the max was never set): only
+      // then take the row max and, if it grew by more than kTau, rescale.
+      uint32_t pk[NB][2][8];
+      float tsum[NB];
+      bool redo = false;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        tsum[nb] = softmax_exp(sacc[nb], ms[nb], pk[nb]);
+        redo |= !(tsum[nb] <= kSumMax);
+      }
+      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          float mloc = sacc[nb][0][0];
+#pragma unroll
+          for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[nb][kbk][r]);
+          mloc = __builtin_fmaxf(mloc, xor32(mloc));
+          const float tmax = mloc * c;
+          if (__builtin_amdgcn_ballot_w64(tmax > ms[nb] + kTau) != 0) {
+            const float mnew = __builtin_fmaxf(ms[nb], tmax);
+            const float alpha = fast_exp2(ms[nb] - mnew);
+            ms[nb] = mnew;
+            lsum[nb] *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) oacc[nb][mb] *= alpha;
+            tsum[nb] = softmax_exp(sacc[nb], ms[nb], pk[nb]);
+          }
         }
       }
-      lsum += tsum;
-#else
-      // ---- row max over the tile (raw scores; c > 0)
-      float mloc = sacc[0][0];
 #pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[kbk][r]);
-      mloc = __builtin_fmaxf(mloc, xor32(mloc));
-      const float tmax = mloc * c;
-      // ---- move the running max only when it is exceeded by more than kTau
-      if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
-        const float mnew = __builtin_fmaxf(ms, tmax);
-        const float alpha = fast_exp2(ms - mnew);
-        ms = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
-      }
-      // ---- p = 2^(s*c - m) -> bf16 P^T operand; fp32 row sums (an LSE
-      // accurate to fp32, not to the bf16 rounding of P)
-      uint32_t pk[2][8];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -ms));
-          const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -ms));
-          pk[kbk][r >> 1] = pack_bf16(p0, p1);
-          lsum += p0 + p1;
-        }
-#endif
-      // ---- O^T += V^T P^T
+      for (int nb = 0; nb < NB; ++nb) lsum[nb] += tsum[nb];
+      // ---- O^T += V^T P^T (each V^T fragment feeds every query block)
       if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -290,9 +281,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
             const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
             const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
             const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            const bf16x8 bp = bitcast<bf16x8>(
-                u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
-            oacc[mb] = mfma32(a, bp, oacc[mb]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              const bf16x8 bp = bitcast<bf16x8>(u32x4{pk[nb][kbk][4 * cp], pk[nb][kbk][4 * cp + 1],
+                                                      pk[nb][kbk][4 * cp + 2], pk[nb][kbk][4 * cp + 3]});
+              oacc[nb][mb] = mfma32(a, bp, oacc[nb][mb]);
+            }
           }
       if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
     }
@@ -322,21 +316,25 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l)
-  const float lfull = lsum + xor32(lsum);
-  if (qrow < N) {
-    const float inv = 1.0f / lfull;
-    __bf16* dst = O + qoff + (int64_t)qrow * D;
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+  for (int nb = 0; nb < NB; ++nb) {
+    const int qrow = q0 + nb * 32 + l32;
+    const float lfull = lsum[nb] + xor32(lsum[nb]);
+    if (qrow < N) {
+      const float inv = 1.0f / lfull;
+      __bf16* dst = O + qoff + (int64_t)qrow * D;
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = mb * 32 + rg * 8 + hf * 4;
-        u32x2 v;
-        v[0] = pack_bf16(oacc[mb][4 * rg] * inv, oacc[mb][4 * rg + 1] * inv);
-        v[1] = pack_bf16(oacc[mb][4 * rg + 2] * inv, oacc[mb][4 * rg + 3] * inv);
-        *(u32x2*)(dst + d0) = v;
-      }
-    if (hf == 0) LSE[(int64_t)bh * N + qrow] = (ms + __builtin_log2f(lfull)) * kLn2;
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = mb * 32 + rg * 8 + hf * 4;
+          u32x2 v;
+          v[0] = pack_bf16(oacc[nb][mb][4 * rg] * inv, oacc[nb][mb][4 * rg + 1] * inv);
+          v[1] = pack_bf16(oacc[nb][mb][4 * rg + 2] * inv, oacc[nb][mb][4 * rg + 3] * inv);
+          *(u32x2*)(dst + d0) = v;
+        }
+      if (hf == 0) LSE[(int64_t)bh * N + qrow] = (ms[nb] + __builtin_log2f(lfull)) * kLn2;
+    }
   }
 }
 
