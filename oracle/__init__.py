@@ -54,12 +54,13 @@ def _bind(path: str):
     ci, cd, c64 = ctypes.c_int, ctypes.c_double, ctypes.c_int64
     dims = [ci] * 7 + [ci, cd]  # B Hq Hkv Nq Nk dk dv causal scale
     lib.oracle_fwd.argtypes = [d, d, d, d, d] + dims
+    lib.oracle_fwd_bottom_right.argtypes = [d, d, d, d, d] + dims
     lib.oracle_fwd_rows.argtypes = [d, d, d, i64p, c64, d, d] + dims
     lib.oracle_fwd_blockwise.argtypes = [d, d, d, d, d] + dims + [ci, ci]
     lib.oracle_bwd.argtypes = [d] * 10 + dims
     lib.oracle_bwd_slices.argtypes = [d, d, d, d, i64p, c64, d, d, d] + dims
     lib.oracle_threads.argtypes = []
-    for f in (lib.oracle_threads, lib.oracle_fwd, lib.oracle_fwd_rows,
+    for f in (lib.oracle_threads, lib.oracle_fwd, lib.oracle_fwd_bottom_right, lib.oracle_fwd_rows,
               lib.oracle_fwd_blockwise, lib.oracle_bwd, lib.oracle_bwd_slices):
         f.restype = ci
     return lib
@@ -129,6 +130,19 @@ class Oracle:
         _check(self.lib.oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                    B, Hq, Hkv, Nq, Nk, dk, dv, int(bool(causal)), scale),
                "oracle_fwd")
+        return o, lse
+
+    def fwd_bottom_right(self, q, k, v, causal: bool = False, scale: float | None = None):
+        """Dense forward with the causal mask aligned bottom-right (query i of Nq
+        sees keys j <= i + Nk - Nq). Returns (O, LSE) in float64."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, Hq, Hkv, Nq, Nk, dk, dv = _shapes(q, k, v)
+        scale = default_scale(dk) if scale is None else float(scale)
+        o = np.empty((B, Hq, Nq, dv), np.float64)
+        lse = np.empty((B, Hq, Nq), np.float64)
+        _check(self.lib.oracle_fwd_bottom_right(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                B, Hq, Hkv, Nq, Nk, dk, dv, int(bool(causal)),
+                                                scale), "oracle_fwd_bottom_right")
         return o, lse
 
     def fwd_rows(self, q, k, v, rows, causal: bool = False, scale: float | None = None):
@@ -217,6 +231,7 @@ def from_library(path: str) -> Oracle:
 _default = Oracle()
 fwd = _default.fwd
 fwd_rows = _default.fwd_rows
+fwd_bottom_right = _default.fwd_bottom_right
 fwd_blockwise = _default.fwd_blockwise
 bwd = _default.bwd
 bwd_slices = _default.bwd_slices

@@ -51,10 +51,18 @@ static int check_args(int B, int Hq, int Hkv, int Nq, int Nk, int dk, int dv) {
   return ORACLE_OK;
 }
 
-/* Number of keys visible to query row i. */
-static int64_t visible_keys(int64_t i, int64_t Nk, int causal) {
+/* Number of keys visible to query row i: all of them, or with the causal
+ * mask keys j <= i + off (off = 0: top-left alignment; off = Nk - Nq:
+ * bottom-right alignment, the last query sees every key). */
+static int64_t visible_keys_off(int64_t i, int64_t Nk, int causal, int64_t off) {
   if (!causal) return Nk;
-  return (i + 1 < Nk) ? i + 1 : Nk;
+  const int64_t n = i + 1 + off;
+  if (n < 0) return 0;
+  return (n < Nk) ? n : Nk;
+}
+
+static int64_t visible_keys(int64_t i, int64_t Nk, int causal) {
+  return visible_keys_off(i, Nk, causal, 0);
 }
 
 /* Plain dot product in index order. */
@@ -122,6 +130,45 @@ int oracle_fwd(const double* q, const double* k, const double* v, double* o,
         const double* Vh = v + (b * Hkv + g) * (int64_t)Nk * dv;
         dense_row(q + r * dk, Kh, Vh, visible_keys(i, Nk, causal), dk, dv,
                   scale, scores, o + r * dv, lse + r);
+      }
+      free(scores);
+    }
+  }
+  return bad ? ORACLE_NO_MEM : ORACLE_OK;
+}
+
+/*
+ * Dense forward with the causal mask aligned to the bottom-right corner:
+ * query i (of Nq) sees keys j <= i + (Nk - Nq), as when the Nq queries are
+ * the last Nq positions of a sequence of Nk keys (decode and append).  For
+ * Nq == Nk this is oracle_fwd.  Rows that see no key get O = 0, LSE = -inf.
+ */
+int oracle_fwd_bottom_right(const double* q, const double* k, const double* v, double* o,
+                            double* lse, int B, int Hq, int Hkv, int Nq, int Nk, int dk,
+                            int dv, int causal, double scale) {
+  int rc = check_args(B, Hq, Hkv, Nq, Nk, dk, dv);
+  if (rc) return rc;
+  const int64_t rows = (int64_t)B * Hq * Nq;
+  const int group = Hq / Hkv;
+  const int64_t off = (int64_t)Nk - Nq;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* scores = (double*)malloc(sizeof(double) * (Nk > 0 ? Nk : 1));
+    if (!scores) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < rows; ++r) {
+        const int64_t i = r % Nq;
+        const int64_t h = (r / Nq) % Hq;
+        const int64_t b = r / ((int64_t)Nq * Hq);
+        const int64_t g = h / group;
+        const double* Kh = k + (b * Hkv + g) * (int64_t)Nk * dk;
+        const double* Vh = v + (b * Hkv + g) * (int64_t)Nk * dv;
+        dense_row(q + r * dk, Kh, Vh, visible_keys_off(i, Nk, causal, off), dk, dv, scale,
+                  scores, o + r * dv, lse + r);
       }
       free(scores);
     }

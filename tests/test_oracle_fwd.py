@@ -313,3 +313,47 @@ def test_blockwise_survives_extreme_logits(oracle_mod, causal):
     assert np.all(np.isfinite(o2)) and np.all(np.isfinite(l2))
     np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l2, l1, rtol=1e-15, atol=1e-9)
+
+
+# ---------------------------------------------------------------- bottom-right causal
+@pytest.mark.parametrize("nq,nk", [(1, 9), (3, 9), (9, 9), (12, 5)])
+def test_bottom_right_is_top_left_on_the_suffix(oracle_mod, nq, nk):
+    """Query i of Nq sees keys j <= i + Nk - Nq: the same rows as the last Nq
+    rows of the (pinned) top-left causal problem with Nk queries."""
+    q = rand((2, 4, nq, 6), 60)
+    k = rand((2, 2, nk, 6), 61)
+    v = rand((2, 2, nk, 5), 62)
+    o, lse = oracle_mod.fwd_bottom_right(q, k, v, causal=True)
+    if nq <= nk:
+        qfull = np.concatenate([rand((2, 4, nk - nq, 6), 63), q], axis=2)
+        of, lf = oracle_mod.fwd(qfull, k, v, causal=True)
+        np.testing.assert_array_equal(o, of[:, :, nk - nq:])
+        np.testing.assert_array_equal(lse, lf[:, :, nk - nq:])
+    else:  # the first Nq - Nk queries see nothing; the rest see keys 0..i-(Nq-Nk)
+        assert np.all(o[:, :, : nq - nk] == 0) and np.all(lse[:, :, : nq - nk] == -np.inf)
+        of, lf = oracle_mod.fwd(q[:, :, nq - nk:], k, v, causal=True)
+        np.testing.assert_array_equal(o[:, :, nq - nk:], of)
+        np.testing.assert_array_equal(lse[:, :, nq - nk:], lf)
+
+
+def test_bottom_right_single_query_sees_every_key(oracle_mod):
+    q = rand((1, 2, 1, 8), 64)
+    k = rand((1, 2, 33, 8), 65)
+    v = rand((1, 2, 33, 8), 66)
+    o1, l1 = oracle_mod.fwd_bottom_right(q, k, v, causal=True)
+    o2, l2 = oracle_mod.fwd(q, k, v, causal=False)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    for h in range(2):
+        ref_o, ref_l = scipy_attention(q[0, h], k[0, h], v[0, h], 1 / np.sqrt(8))
+        np.testing.assert_allclose(o1[0, h], ref_o, rtol=0, atol=1e-13)
+
+
+def test_bottom_right_non_causal_equals_dense(oracle_mod):
+    q = rand((1, 2, 4, 8), 67)
+    k = rand((1, 1, 20, 8), 68)
+    v = rand((1, 1, 20, 8), 69)
+    o1, l1 = oracle_mod.fwd_bottom_right(q, k, v, causal=False)
+    o2, l2 = oracle_mod.fwd(q, k, v, causal=False)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)

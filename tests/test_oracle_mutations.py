@@ -40,6 +40,9 @@ MUTANTS = [
     ("bwd_dv_uses_ds", "for (int c = 0; c < dv; ++c) dvj[c] += p * doi[c];",
      "for (int c = 0; c < dv; ++c) dvj[c] += ds * doi[c];", 1),
     ("bwd_dsum_drops", "dsum[r] = dot(dout + r * dv, obuf + r * dv, dv);", "dsum[r] = 0.0;", 1),
+    ("bottom_right_offset_sign", "const int64_t off = (int64_t)Nk - Nq;",
+     "const int64_t off = (int64_t)Nq - Nk;", 1),
+    ("bottom_right_off_by_one", "const int64_t n = i + 1 + off;", "const int64_t n = i + off;", 1),
     ("bwd_dk_skips_group", "for (int64_t hh = 0; hh < group; ++hh) {",
      "for (int64_t hh = 0; hh < 1; ++hh) {", 1),
 ]
@@ -61,6 +64,8 @@ def run_pins(om):
         ("blockwise", lambda: pf.test_blockwise_equals_dense(om, True, 13, 7, 3, 2)),
         ("blockwise_nc", lambda: pf.test_blockwise_equals_dense(om, False, 7, 13, 2, 3)),
         ("blockwise_extreme", lambda: pf.test_blockwise_survives_extreme_logits(om, False)),
+        ("bottom_right", lambda: pf.test_bottom_right_is_top_left_on_the_suffix(om, 3, 9)),
+        ("bottom_right_long", lambda: pf.test_bottom_right_is_top_left_on_the_suffix(om, 12, 5)),
         ("fd", lambda: pb.test_gradients_match_central_differences(om, True, pb.SHAPES[3])),
         ("autograd", lambda: pb.test_gradients_match_torch_autograd(
             om, True, (1, 3, 1, 9, 12, 5, 7))),
