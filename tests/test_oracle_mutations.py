@@ -23,9 +23,8 @@ MUTANTS = [
     ("drop_normalise", "for (int c = 0; c < dv; ++c) orow[c] /= l;", "", 1),
     ("drop_scale", "scores[j] = scale * dot(qi, Kh + j * dk, dk);",
      "scores[j] = dot(qi, Kh + j * dk, dk);", 1),
-    ("causal_excludes_diagonal", "return (i + 1 < Nk) ? i + 1 : Nk;", "return (i < Nk) ? i : Nk;", 1),
-    ("causal_one_extra_key", "return (i + 1 < Nk) ? i + 1 : Nk;",
-     "return (i + 2 < Nk) ? i + 2 : Nk;", 1),
+    ("causal_excludes_diagonal", "const int64_t n = i + 1 + off;", "const int64_t n = i + off;", 1),
+    ("causal_one_extra_key", "const int64_t n = i + 1 + off;", "const int64_t n = i + 2 + off;", 1),
     ("gqa_modulo_map", "const int64_t g = h / group;", "const int64_t g = h % Hkv;", 5),
     ("key_index_slip", "scores[j] = scale * dot(qi, Kh + j * dk, dk);",
      "scores[j] = scale * dot(qi, Kh + j, dk);", 1),
@@ -42,7 +41,6 @@ MUTANTS = [
     ("bwd_dsum_drops", "dsum[r] = dot(dout + r * dv, obuf + r * dv, dv);", "dsum[r] = 0.0;", 1),
     ("bottom_right_offset_sign", "const int64_t off = (int64_t)Nk - Nq;",
      "const int64_t off = (int64_t)Nq - Nk;", 1),
-    ("bottom_right_off_by_one", "const int64_t n = i + 1 + off;", "const int64_t n = i + off;", 1),
     ("bwd_dk_skips_group", "for (int64_t hh = 0; hh < group; ++hh) {",
      "for (int64_t hh = 0; hh < 1; ++hh) {", 1),
 ]
