@@ -25,7 +25,7 @@ MUTANTS = [
      "scores[j] = dot(qi, Kh + j * dk, dk);", 1),
     ("causal_excludes_diagonal", "const int64_t n = i + 1 + off;", "const int64_t n = i + off;", 1),
     ("causal_one_extra_key", "const int64_t n = i + 1 + off;", "const int64_t n = i + 2 + off;", 1),
-    ("gqa_modulo_map", "const int64_t g = h / group;", "const int64_t g = h % Hkv;", 5),
+    ("gqa_modulo_map", "const int64_t g = h / group;", "const int64_t g = h % Hkv;", 6),
     ("key_index_slip", "scores[j] = scale * dot(qi, Kh + j * dk, dk);",
      "scores[j] = scale * dot(qi, Kh + j, dk);", 1),
     ("value_transposed", "const double* vj = Vh + j * dv;", "const double* vj = Vh + j;", 1),
