@@ -72,3 +72,43 @@ def make(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "bf16", seed: i
 def make_workload(w: Workload, with_dout: bool | None = None):
     wd = w.backward if with_dout is None else with_dout
     return make(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype, w.seed, w.q_mult, wd)
+
+
+# Few queries against a long key/value cache (decode and chunked append), for
+# the split-K/V forward.  Same recipe; Q is [B, Hq, Nq, d], K/V [B, Hkv, Nk, d].
+@dataclass(frozen=True)
+class CacheWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int = 0
+
+
+CACHE_WORKLOADS = {
+    "decode": CacheWorkload("decode_bf16_B8_Hq32_Hkv8_Nq1_Nk32768_d128", 8, 32, 8, 1, 32768, 128,
+                            True, seed=11),
+    "append": CacheWorkload("append_causal_bf16_B4_Hq32_Hkv8_Nq64_Nk16384_d128", 4, 32, 8, 64,
+                            16384, 128, True, seed=12),
+}
+
+
+def make_cache(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int = 0,
+               q_mult: float = 1.0):
+    """Draw bf16 (q [B,Hq,Nq,d], k [B,Hkv,Nk,d], v [B,Hkv,Nk,d]) as CPU tensors."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, Nq, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    if q_mult != 1.0:
+        q = q * q_mult  # power of two: exact
+    return q, k, v
+
+
+def make_cache_workload(w: CacheWorkload):
+    return make_cache(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed)

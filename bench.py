@@ -15,8 +15,9 @@ counted.
 
 Printed: one JSON line with the step throughput, the roofline of the dominant
 kernel (durations from HIP events on the launch stream), every kernel's
-duration, a forward sweep over the other workloads, and the fp64 CPU oracle
-timed on a bounded sample of the same workload.
+duration, a forward sweep over the other workloads, the split-K/V forward on
+the key/value-cache workloads (decode, append; GB/s against HBM), and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -127,6 +128,77 @@ def forward_only(w, args, dev):
                    "causal": w.causal, "q_mult": w.q_mult, "seed": w.seed}}), flush=True)
 
 
+def splitkv_visible_pairs(Nq, Nk, causal):
+    """(query, key) pairs the bottom-right aligned mask leaves visible per head."""
+    if not causal:
+        return Nq * Nk
+    return sum(max(0, min(Nk, i + 1 + Nk - Nq)) for i in range(Nq))
+
+
+def splitkv_case(cw, dev, steps, warmup, num_splits=0):
+    """attn_fwd_splitkv on one cache workload: `steps` timed calls (split kernel
+    + merge kernel), HIP events on the launch stream.  HBM-bound: the
+    algorithmic bytes are K and V once, plus Q, O and LSE."""
+    import torch
+
+    import attn_inputs
+    import exact_attention_87_amd as ea
+
+    q, k, v = (t.to(dev) for t in attn_inputs.make_cache_workload(cw))
+    o = torch.empty_like(q)
+    lse = torch.empty((cw.B, cw.Hq, cw.Nq), device=dev, dtype=torch.float32)
+    nbytes = ea.attn_fwd_splitkv_workspace_bytes(cw.B, cw.Hq, cw.Hkv, cw.Nq, cw.Nk, cw.d,
+                                                 num_splits)
+    ws = torch.empty(max(nbytes, 256), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    scale = 1.0 / math.sqrt(cw.d)
+
+    def call():
+        st = ea.attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), ws.data_ptr(), cw.B, cw.Hq, cw.Hkv, cw.Nq, cw.Nk,
+                                 cw.d, int(cw.causal), scale, num_splits, ea.ATTN_BF16,
+                                 stream.cuda_stream)
+        if st != ea.ATTN_OK:
+            raise ea.AttnError(st, "attn_fwd_splitkv")
+
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    byts = (2 * cw.B * cw.Hkv * cw.Nk * cw.d * 2 + 2 * cw.B * cw.Hq * cw.Nq * cw.d * 2
+            + cw.B * cw.Hq * cw.Nq * 4)
+    flops = 4.0 * cw.B * cw.Hq * cw.d * splitkv_visible_pairs(cw.Nq, cw.Nk, cw.causal)
+    gbs = byts / (ms / 1e3) / 1e9
+    return {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1), "algorithmic_bytes": byts,
+            "num_splits": ea.attn_fwd_splitkv_num_splits(cw.B, cw.Hq, cw.Hkv, cw.Nq, cw.Nk, cw.d,
+                                                         num_splits)}
+
+
+def splitkv_only(name, args, dev):
+    import attn_inputs
+
+    cw = attn_inputs.CACHE_WORKLOADS[name]
+    r = splitkv_case(cw, dev, args.steps, args.warmup)
+    print(json.dumps({
+        "metric": "split-K/V attention forward GB/s on 1 MI355X (HBM-bound)",
+        "value": r["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["us"] / 1e3, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": r["frac_of_hbm"], "traffic": None,
+                     "kernel": "fwd_split + split_combine (one call)"},
+        "detail": r,
+        "config": {"workload": cw.name, "B": cw.B, "Hq": cw.Hq, "Hkv": cw.Hkv, "Nq": cw.Nq,
+                   "Nk": cw.Nk, "d": cw.d, "causal": cw.causal, "seed": cw.seed}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +211,9 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--fwd-only", type=int, default=0, metavar="ID",
                     help="time only the forward of workload ID (1-5) and print its JSON line")
+    ap.add_argument("--splitkv-only", default="", metavar="NAME",
+                    help="time only the split-K/V forward of cache workload NAME "
+                         "(decode, append) and print its JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,6 +235,9 @@ def main():
 
     if args.fwd_only:
         forward_only(attn_inputs.WORKLOADS[args.fwd_only], args, dev)
+        return
+    if args.splitkv_only:
+        splitkv_only(args.splitkv_only, args, dev)
         return
 
     w = attn_inputs.WORKLOADS[5]
@@ -295,6 +373,13 @@ def main():
             del cq, ck, cv, co, cl
         torch.cuda.synchronize()
 
+    # split-K/V forward on the key/value-cache workloads (parity-tested separately)
+    splitkv = {}
+    if not args.no_sweep:
+        for name, cw in attn_inputs.CACHE_WORKLOADS.items():
+            splitkv[cw.name] = splitkv_case(cw, dev, steps=20, warmup=3)
+        torch.cuda.synchronize()
+
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
     value = step_flops / (ms_per_step / 1e3) / 1e12
     out = {
@@ -319,6 +404,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "forward_sweep": sweep,
+        "splitkv": splitkv,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
         "torch": torch.__version__,

@@ -4,10 +4,10 @@ A thin ctypes layer over ``libattn.so`` (the C ABI in ``include/attn.h``).
 Every step of the computation runs in the library's HIP kernels; this module
 only marshals arguments.  PyTorch provides device memory and the stream.
 
-Raw entry points with the C names (``attn_fwd``, ``attn_bwd``,
-``attn_bwd_workspace_bytes``, ``attn_status_str``, ``attn_abi_version``) take
-integer device addresses; ``fwd`` and ``bwd`` are conveniences over torch
-tensors.  Importing this package never falls back to another implementation:
+Raw entry points with the C names (``attn_fwd``, ``attn_bwd`` and its
+stages, ``attn_fwd_splitkv``, the workspace-size queries,
+``attn_status_str``, ``attn_abi_version``) take integer device addresses;
+``fwd``, ``fwd_splitkv`` and ``bwd`` are conveniences over torch tensors.  Importing this package never falls back to another implementation:
 if the library is missing or fails to load, every call raises.
 """
 from __future__ import annotations
@@ -62,6 +62,12 @@ def lib():
         L.attn_bwd_dkdv.restype = ci
         L.attn_bwd_dq.argtypes = [vp] * 6 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd_dq.restype = ci
+        L.attn_fwd_splitkv.argtypes = [vp] * 6 + [ci] * 7 + [cf, ci, ci, vp]
+        L.attn_fwd_splitkv.restype = ci
+        L.attn_fwd_splitkv_num_splits.argtypes = [ci] * 7
+        L.attn_fwd_splitkv_num_splits.restype = ci
+        L.attn_fwd_splitkv_workspace_bytes.argtypes = [ci] * 7
+        L.attn_fwd_splitkv_workspace_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -105,6 +111,22 @@ def attn_bwd_dq(q, k, v, dout, stats, dq, B, Hq, Hkv, N, d, causal, scale, dtype
                 stream) -> int:
     return int(lib().attn_bwd_dq(q, k, v, dout, stats, dq, B, Hq, Hkv, N, d, int(causal),
                                  float(scale), int(dtype), stream))
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                     num_splits, dtype, stream) -> int:
+    return int(lib().attn_fwd_splitkv(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d,
+                                      int(causal), float(scale), int(num_splits), int(dtype),
+                                      stream))
+
+
+def attn_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
+    return int(lib().attn_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, int(num_splits)))
+
+
+def attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
+    n = int(lib().attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, int(num_splits)))
+    return -1 if n == (1 << 64) - 1 else n
 
 
 # ------------------------------------------------------------ torch conveniences
@@ -153,6 +175,44 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
                   B, Hq, Hkv, N, d, causal, scale, _dtype_code(q), _stream_ptr(q))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
+                num_splits: int = 0, out=None, lse=None, workspace=None):
+    """O, LSE for q [B,Hq,Nq,d] against a key/value cache k/v [B,Hkv,Nk,d] (bf16),
+    with the keys cut into num_splits ranges (0: chosen from the shape) and the
+    causal mask aligned to the last query."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
+    nbytes = attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
+    if nbytes < 0:
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+    st = attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, Nq, Nk, d, causal,
+                          scale, num_splits, code, _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_splitkv")
     return out, lse
 
 

@@ -231,3 +231,72 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ split K/V
+namespace {
+
+// Shape checks of the split-K/V forward.  Sets *empty when there are no
+// query rows (Nk == 0 with query rows is a real problem: every row sees no
+// key).
+attn_status split_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        int num_splits, attn_dtype dtype, bool* empty) {
+  if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 0) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  // 32-bit offsets: one key/value slice and one head group's query rows
+  // stay below 1 GiB; the grid stays below 2^31 workgroups.
+  if ((int64_t)B * Hq > (1 << 24) || Nq > (1 << 22) || Nk > (1 << 22)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)(Hq / Hkv) * Nq > (1 << 22)) return ATTN_ERR_UNSUPPORTED;
+  *empty = (B == 0 || Nq == 0);
+  if (*empty) return ATTN_OK;
+  const attn::SplitPlan p = attn::split_plan(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  if ((int64_t)p.nrb * p.nsplit * B * Hkv >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  bool empty = false;
+  if (split_shape(B, Hq, Hkv, Nq, Nk, d, 0, 1.0f, num_splits, ATTN_BF16, &empty) != ATTN_OK)
+    return -1;
+  if (empty) return 0;
+  return attn::split_plan(B, Hq, Hkv, Nq, Nk, d, num_splits).nsplit;
+}
+
+size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                        int num_splits) {
+  const int ns = attn_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  if (ns < 0) return (size_t)-1;
+  if (ns == 0) return 0;
+  return attn::split_workspace_bytes(B, Hq, Nq, d, ns);
+}
+
+attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                             void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                             int causal, float scale, int num_splits, attn_dtype dtype,
+                             void* stream) {
+  bool empty = false;
+  attn_status st = split_shape(B, Hq, Hkv, Nq, Nk, d, causal, scale, num_splits, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  const size_t qb = (size_t)B * Hq * Nq * d * 2, kvb = (size_t)B * Hkv * Nk * d * 2;
+  const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
+  const size_t wb = attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  st = check_buffers({{q, qb}, {k, kvb}, {v, kvb}}, {{o, qb}, {lse, lb}, {workspace, wb}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::SplitArgs a{q,  k,  v,  o,  lse, workspace,       B,     Hq,        Hkv,
+                    Nq, Nk, d, causal == 1, scale, num_splits, (hipStream_t)stream};
+  return attn::launch_fwd_split(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"

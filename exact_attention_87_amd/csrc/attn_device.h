@@ -22,6 +22,11 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Online softmax: the running maximum only moves when a tile's maximum
+// exceeds it by more than kTau (base-2 units), so probabilities stay below
+// 2^kTau = kSumMax; a lane whose tile sum passes kSumMax takes the max path.
+constexpr float kTau = 8.0f;
+constexpr float kSumMax = 256.0f;
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From& x) {

@@ -28,8 +28,6 @@
 
 namespace attn {
 
-constexpr float kTau = 8.0f;
-constexpr float kSumMax = 256.0f;  // 2^kTau
 
 // Tuning knobs (compile-time; the defaults are the shipped configuration).
 #ifndef ATTN_FWD_WPE64

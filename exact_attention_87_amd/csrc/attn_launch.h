@@ -38,6 +38,32 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Split-K/V forward (bf16): queries [B,Hq,Nq,d], keys/values [B,Hkv,Nk,d],
+// bottom-right aligned causal mask; workspace holds the per-split partials.
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* workspace;
+  int B, Hq, Hkv, Nq, Nk, d;
+  bool causal;
+  float scale;
+  int num_splits;  // requested; <= 0 picks one from the shape
+  hipStream_t stream;
+};
+
+struct SplitPlan {
+  int nrb;        // 128-row blocks of one head group's packed query rows
+  int nsplit;     // splits actually used (every split holds at least one key)
+  int split_len;  // keys per split, a multiple of 64
+};
+
+SplitPlan split_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int nsplit);
+hipError_t launch_fwd_split(const SplitArgs& a);
+
 hipError_t launch_fwd(const FwdArgs& a);
 // Bytes of the backward row-statistics workspace.
 size_t bwd_stats_bytes(int B, int Hq, int N);

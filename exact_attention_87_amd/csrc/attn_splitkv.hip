@@ -1,0 +1,402 @@
+// Split-K/V forward for few queries against many keys (decode, append).
+//
+// The keys of every (batch, key/value head) are cut into splits; one
+// workgroup computes, for one split, the attention of all the query rows of
+// the head group (the group's query heads x Nq rows, contiguous in memory,
+// so K and V are read once per group).  Each split leaves a normalised
+// partial output O_s and its logsumexp LSE_s; a second kernel merges the
+// splits with the pairwise (m, l, u) merge of the online softmax
+// ("FlashAttention：让精确注意力服从内存层次", section "Online softmax"):
+//   LSE = log sum_s e^{LSE_s},  O = sum_s e^{LSE_s - LSE} O_s.
+// The causal mask is aligned to the bottom-right corner: query i of Nq sees
+// keys j <= i + (Nk - Nq), the last query sees every key.
+//
+// The tile loop is the forward kernel's (direct global->LDS K/V tiles,
+// S^T = K Q^T and O^T += V^T P^T on the 32x32x16 bf16 matrix cores, base-2
+// online softmax); here the loop covers one split and the running maximum
+// starts at -FLT_MAX, because a row may see no key at all inside a split.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+#include <float.h>
+
+#include <algorithm>
+#include <type_traits>
+
+namespace attn {
+
+// Tuning knobs (compile-time; the defaults are the shipped configuration).
+#ifndef ATTN_SPLIT_NBUF64
+#define ATTN_SPLIT_NBUF64 2
+#endif
+#ifndef ATTN_SPLIT_NBUF128
+#define ATTN_SPLIT_NBUF128 2
+#endif
+#ifndef ATTN_SPLIT_WPE64
+#define ATTN_SPLIT_WPE64 3
+#endif
+#ifndef ATTN_SPLIT_WPE128
+#define ATTN_SPLIT_WPE128 2
+#endif
+
+template <int D>
+struct SplitCfg {
+  static constexpr int NW = 4;
+  static constexpr int BR = 128;  // packed query rows per workgroup (32 per wave)
+  static constexpr int BC = 64;   // keys per tile
+  static constexpr int NBUF = D == 64 ? ATTN_SPLIT_NBUF64 : ATTN_SPLIT_NBUF128;  // LDS stages
+  static constexpr int WPE = D == 64 ? ATTN_SPLIT_WPE64 : ATTN_SPLIT_WPE128;     // waves per SIMD
+  static_assert(NBUF >= 2 && NBUF <= 4, "stages");
+  static constexpr int TILEB = BC * D * 2;
+  static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fwd_split_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    float* __restrict__ Opart, float* __restrict__ Lpart, int Hq, int Hkv, int Nq, int Nk,
+    int nrb, int nsplit, int split_len, int64_t rows_total, float c, uint32_t qsign) {
+  using Cfg = SplitCfg<D>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, TILEB = Cfg::TILEB, NW = Cfg::NW, NBUF = Cfg::NBUF;
+  constexpr int ROWB = D * 2;
+  constexpr int PW = TILEB / 1024 / NW;
+  constexpr int NQC = D / 16;
+  constexpr int NMB = D / 32;
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // [NBUF][K tile | V tile]
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  // Work map: row blocks of one split adjacent (they share the split's K/V).
+  const int id = blockIdx.x;
+  const int rb = id % nrb;
+  const int t = id / nrb;
+  const int split = t % nsplit;
+  const int bg = t / nsplit;
+  const int b = bg / Hkv;
+  const int g = bg - b * Hkv;
+  const int group = Hq / Hkv;
+  const int R = group * Nq;                         // packed rows of the group
+  const int64_t row0 = ((int64_t)b * Hq + (int64_t)g * group) * Nq;  // [B,Hq,Nq] index of row 0
+  const int64_t kvoff = (int64_t)bg * Nk * D;
+  const int r0 = rb * BR + w * 32;  // first packed row of this wave
+  const int r = r0 + l32;           // packed row of this lane
+  const int qi = r % Nq;            // its query index
+  const int off = Nk - Nq;          // bottom-right diagonal offset
+
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + row0 * D, (uint32_t)R * ROWB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, (uint32_t)Nk * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, (uint32_t)Nk * ROWB);
+
+  bf16x8 qreg[NQC];
+#pragma unroll
+  for (int cc = 0; cc < NQC; ++cc)
+    qreg[cc] = bitcast<bf16x8>(buf_load16(rq, (uint32_t)(r * D + cc * 16 + hf * 8) * 2) ^ qsign);
+
+  // Key range of the split.  With the causal mask the workgroup stops after
+  // the last key any of its rows sees, and each wave after its own last key;
+  // a wave holding no rows computes nothing (it still loads its share).
+  const int kbeg = split * split_len;
+  const int kend = min(Nk, kbeg + split_len);
+  auto tiles_upto = [&](int ra, int rb_) {  // tiles of this split rows [ra, rb_] can see
+    if (!CAUSAL) return (kend - kbeg + BC - 1) / BC;
+    const int maxi = (ra / Nq != rb_ / Nq) ? Nq - 1 : rb_ % Nq;
+    const int klim = min(maxi + off, kend - 1);  // last visible key of the range
+    return klim < kbeg ? 0 : (klim - kbeg) / BC + 1;
+  };
+  const int wg0 = rb * BR;
+  const int ntiles = tiles_upto(wg0, min(wg0 + BR - 1, R - 1));
+  const int wtiles = r0 < R ? tiles_upto(r0, min(r0 + 31, R - 1)) : 0;
+
+  uint32_t goff[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int o = (w * PW + i) * 1024 + lane * 16;
+    const int row = o / ROWB;
+    const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
+    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+  }
+  auto issue = [&](int j) {
+    char* kt = smem + (j % NBUF) * 2 * TILEB;
+    const uint32_t tbase = (uint32_t)(kbeg + j * BC) * ROWB;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      buf_load16_lds(rk, kt + (w * PW + i) * 1024, goff[i] + tbase);
+      buf_load16_lds(rv, kt + TILEB + (w * PW + i) * 1024, goff[i] + tbase);
+    }
+  };
+
+  // Wait until tile t has landed (tiles issued after it may stay in flight,
+  // 2*PW loads each), then synchronise the workgroup.
+  auto wait_next = [&](int t) {
+    const int later = min(NBUF - 2, ntiles - 1 - t);
+    if (NBUF >= 4 && later >= 2)
+      wait_vm_barrier<(NBUF >= 4 ? 4 * PW : 0)>();
+    else if (NBUF >= 3 && later >= 1)
+      wait_vm_barrier<(NBUF >= 3 ? 2 * PW : 0)>();
+    else
+      wait_vm_barrier<0>();
+  };
+
+  int koff[NQC], voff[2][NMB];
+#pragma unroll
+  for (int cc = 0; cc < NQC; ++cc) koff[cc] = tile_off<D>(l32, 2 * cc + hf);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) voff[tt][mb] = tr_off<D>(lane, 0, mb * 32, tt);
+
+  float ms = -FLT_MAX;  // finite: rows may see no key in this split
+  float lsum = 0.f;
+  f32x16 oacc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
+
+  auto softmax_exp = [&](const f32x16 (&sacc)[2], uint32_t (&pk)[2][8]) {
+    float tsum = 0.f;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int rr = 0; rr < 16; rr += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][rr], c, -ms));
+        const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][rr + 1], c, -ms));
+        pk[kbk][rr >> 1] = pack_bf16(p0, p1);
+        tsum += p0 + p1;
+      }
+    return tsum;
+  };
+
+  auto tile = [&](auto bufc, int j) {
+    constexpr int BUF = decltype(bufc)::value;
+    const char* kt = smem + BUF * 2 * TILEB;
+    const char* vt = kt + TILEB;
+    if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
+    if (j < wtiles) {
+      u32x4 kfrag[2][NQC];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc) kfrag[kbk][cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        sacc[kbk] = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc)
+          sacc[kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
+      }
+      // mask: keys past the split / past Nk, and (causal) keys after the row's diagonal
+      const int k0 = kbeg + j * BC;
+      if ((k0 + BC > kend) || (CAUSAL && (k0 + BC - 1 > off))) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = k0 + kbk * 32 + acc_row(rr, hf);
+            const bool dead = (key >= kend) || (CAUSAL && key > qi + off);
+            if (dead) sacc[kbk][rr] = -__builtin_inff();
+          }
+      }
+      uint32_t pk[2][8];
+      float tsum = softmax_exp(sacc, pk);
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax)) != 0) {
+        __asm__ volatile("");
+        float mloc = sacc[0][0];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) mloc = __builtin_fmaxf(mloc, sacc[kbk][rr]);
+        mloc = __builtin_fmaxf(mloc, xor32(mloc));
+        const float tmax = mloc * c;
+        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
+          const float mnew = __builtin_fmaxf(ms, tmax);
+          const float alpha = fast_exp2(ms - mnew);
+          ms = mnew;
+          lsum *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
+          tsum = softmax_exp(sacc, pk);
+        }
+      }
+      lsum += tsum;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int cp = 0; cp < 2; ++cp) {
+            const int rows = (kbk * 32 + cp * 16) * ROWB;
+            const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
+            const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
+            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const bf16x8 bp = bitcast<bf16x8>(
+                u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
+            oacc[mb] = mfma32(a, bp, oacc[mb]);
+          }
+    }
+    if (j + 1 < ntiles) wait_next(j + 1);
+  };
+
+  // Prologue: tiles 0 .. NBUF-2 in flight, then wait for tile 0.
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < ntiles) issue(j);
+  wait_next(0);
+  for (int j = 0; j < ntiles; j += NBUF) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
+    if constexpr (NBUF >= 3)
+      if (j + 2 < ntiles) tile(std::integral_constant<int, 2 % NBUF>{}, j + 2);
+    if constexpr (NBUF >= 4)
+      if (j + 3 < ntiles) tile(std::integral_constant<int, 3 % NBUF>{}, j + 3);
+  }
+
+  // Partial result of this split: O_s = acc / l (fp32), LSE_s (ln); a row
+  // that saw no key here gets O_s = 0, LSE_s = -inf.
+  const float lfull = lsum + xor32(lsum);
+  if (r < R) {
+    const int64_t prow = (int64_t)split * rows_total + row0 + r;
+    float* dst = Opart + prow * D;
+    const bool any = lfull > 0.f;
+    const float inv = any ? 1.0f / lfull : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = mb * 32 + rg * 8 + hf * 4;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = oacc[mb][4 * rg + e] * inv;
+        *(f32x4*)(dst + d0) = v;
+      }
+    if (hf == 0) Lpart[prow] = any ? (ms + __builtin_log2f(lfull)) * kLn2 : -__builtin_inff();
+  }
+}
+
+// Merge of the split partials, 64 / (D/4) rows per one-wave workgroup.  Each
+// lane owns 4 features of one row and folds the splits in with the
+// online-softmax merge
+//   m' = max(m, LSE_s),  w <- w e^{m - m'} + e^{LSE_s - m'},
+//   acc <- acc e^{m - m'} + e^{LSE_s - m'} O_s,
+// then O = acc / w and LSE = m + ln w.  Splits are read in groups of
+// SG whose loads are all issued before any is used, so a row costs a few
+// memory round trips whatever the split count.  A row no split saw gets
+// O = 0, LSE = -inf.
+template <int D>
+__global__ __launch_bounds__(64) void split_combine_kernel(const float* __restrict__ Opart,
+                                                           const float* __restrict__ Lpart,
+                                                           __bf16* __restrict__ O,
+                                                           float* __restrict__ LSE, int nsplit,
+                                                           int64_t rows) {
+  constexpr int TPR = D / 4;   // lanes per row
+  constexpr int RPW = 64 / TPR;  // rows per wave
+  constexpr int SG = 8;        // splits whose loads are in flight together
+  const int64_t row = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const float ninf = -__builtin_inff();
+  float m = ninf, wsum = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += SG) {
+    float ls[SG];
+    f32x4 os[SG];
+#pragma unroll
+    for (int t = 0; t < SG; ++t) {
+      const int s = s0 + t;
+      ls[t] = s < nsplit ? Lpart[(int64_t)s * rows + row] : ninf;
+      os[t] = s < nsplit ? *(const f32x4*)(Opart + ((int64_t)s * rows + row) * D + part * 4)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int t = 0; t < SG; ++t) {
+      if (ls[t] == ninf) continue;  // split saw no key of this row
+      if (ls[t] > m) {
+        const float r = expf(m - ls[t]);  // 0 while m is still -inf
+        acc *= r;
+        wsum *= r;
+        m = ls[t];
+      }
+      const float wgt = expf(ls[t] - m);
+      acc += wgt * os[t];
+      wsum += wgt;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  u32x2 outv;
+  outv[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
+  outv[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+  *(u32x2*)(O + row * D + part * 4) = outv;
+  if (part == 0) LSE[row] = wsum > 0.f ? m + logf(wsum) : ninf;
+}
+
+// ---------------------------------------------------------------- launchers
+SplitPlan split_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  constexpr int BC = 64, BR = 128;
+  SplitPlan p{};
+  const int R = (Hq / Hkv) * Nq;
+  p.nrb = (R + BR - 1) / BR;
+  if (Nk == 0) {  // nothing to see: one split that writes the empty result
+    p.nsplit = 1;
+    p.split_len = BC;
+    return p;
+  }
+  const int max_splits = (Nk + BC - 1) / BC;
+  int ns = num_splits;
+  if (ns <= 0) {
+    // One round of resident workgroups (256 CUs x workgroups per CU, which
+    // the waves-per-SIMD setting fixes); each split keeps at least 4 tiles.
+    // More splits only add partial-output traffic and merge work.
+    const int64_t resident = 256 * (d == 64 ? SplitCfg<64>::WPE : SplitCfg<128>::WPE);
+    const int64_t wgs = (int64_t)B * Hkv * p.nrb;
+    const int64_t want = (resident + wgs - 1) / wgs;
+    ns = (int)std::min<int64_t>(want, std::max(1, (Nk + 4 * BC - 1) / (4 * BC)));
+  }
+  ns = std::max(1, std::min(ns, max_splits));
+  const int tiles = (Nk + BC - 1) / BC;
+  p.split_len = ((tiles + ns - 1) / ns) * BC;
+  p.nsplit = (Nk + p.split_len - 1) / p.split_len;  // no empty splits
+  return p;
+}
+
+size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int nsplit) {
+  const size_t rows = (size_t)B * Hq * Nq;
+  const size_t obytes = ((size_t)nsplit * rows * d * 4 + 255) & ~(size_t)255;
+  const size_t lbytes = ((size_t)nsplit * rows * 4 + 255) & ~(size_t)255;
+  return obytes + lbytes;
+}
+
+template <int D, bool CAUSAL>
+static hipError_t split_t(const SplitArgs& a) {
+  const SplitPlan p = split_plan(a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d, a.num_splits);
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  float* opart = (float*)a.workspace;
+  float* lpart = (float*)((char*)a.workspace +
+                          (((size_t)p.nsplit * rows * D * 4 + 255) & ~(size_t)255));
+  float c = fabsf(a.scale) * kLog2e;
+  if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
+  const int64_t grid = (int64_t)p.nrb * p.nsplit * a.B * a.Hkv;
+  hipError_t e = allow_lds(fwd_split_kernel<D, CAUSAL>, SplitCfg<D>::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256),
+                     SplitCfg<D>::LDS, a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
+                     (const __bf16*)a.v, opart, lpart, a.Hq, a.Hkv, a.Nq, a.Nk, p.nrb, p.nsplit,
+                     p.split_len, rows, c, (a.scale < 0.f) ? 0x80008000u : 0u);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int RPW = 64 / (D / 4);
+  hipLaunchKernelGGL((split_combine_kernel<D>), dim3((unsigned)((rows + RPW - 1) / RPW)),
+                     dim3(64), 0, a.stream, opart, lpart, (__bf16*)a.o, a.lse, p.nsplit, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_split(const SplitArgs& a) {
+  if (a.d == 64) return a.causal ? split_t<64, true>(a) : split_t<64, false>(a);
+  return a.causal ? split_t<128, true>(a) : split_t<128, false>(a);
+}
+
+}  // namespace attn

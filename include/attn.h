@@ -135,6 +135,50 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
                         const float* stats, void* dq, int B, int Hq, int Hkv, int N, int d,
                         int causal, float scale, attn_dtype dtype, void* stream);
 
+/*
+ * Split-K/V forward, for few queries against many keys (decoding one token,
+ * or appending a short chunk, against a long key/value cache).
+ *   q    [B,Hq,Nq,d]  in   (bf16)
+ *   k, v [B,Hkv,Nk,d] in   (bf16)
+ *   o    [B,Hq,Nq,d]  out  (bf16)
+ *   lse  [B,Hq,Nq]    out  (fp32, natural log)
+ *   workspace         scratch of attn_fwd_splitkv_workspace_bytes(...) bytes
+ *                     with the same shape and num_splits; caller owned,
+ *                     contents need not be initialised, must stay allocated
+ *                     until the launched work completes.
+ * Same operation as attn_fwd, with Nq queries and Nk keys.  The causal mask
+ * is aligned to the bottom-right corner: query i sees key j iff
+ * j <= i + (Nk - Nq), so the last query sees every key (for Nq == Nk this is
+ * attn_fwd's mask).  A query row that sees no key (causal with Nq > Nk, or
+ * Nk == 0) gets o = 0 and lse = -inf.
+ * The keys of each (batch, key/value head) are cut into num_splits ranges
+ * of whole 64-key tiles (num_splits == 0 picks a count from the shape; the
+ * count used may be lower than asked, so that no range is empty).  Each range
+ * yields a normalised partial output and its logsumexp; a second kernel
+ * merges them with the online-softmax merge of ("FlashAttention：让精确注意力
+ * 服从内存层次", section "Online softmax"), so the result is the exact
+ * attention up to rounding.  The query heads of one key/value head are
+ * processed together, so K and V are read once per group.
+ * Supported: dtype ATTN_BF16, d in {64, 128}, Nq and Nk <= 2^22,
+ * (Hq/Hkv)*Nq <= 2^22, B*Hq <= 2^24 (else ATTN_ERR_UNSUPPORTED).  B == 0 or
+ * Nq == 0 is an empty problem (ATTN_OK, nothing launched).  Every other
+ * convention is attn_fwd's; pointers must be non-NULL even when Nk == 0.
+ */
+attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                             void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                             int causal, float scale, int num_splits, attn_dtype dtype,
+                             void* stream);
+
+/* Number of key ranges attn_fwd_splitkv uses for this shape and request; 0
+ * for an empty problem, -1 for arguments it would reject. */
+int attn_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+
+/* Bytes of workspace attn_fwd_splitkv needs (a multiple of 256: fp32 partial
+ * outputs and logsumexps of every split); 0 for an empty problem,
+ * (size_t)-1 for arguments it would reject. */
+size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                        int num_splits);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -26,7 +26,8 @@ def header_functions():
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
                                   "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd",
-                                  "attn_status_str"]
+                                  "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
+                                  "attn_fwd_splitkv_workspace_bytes", "attn_status_str"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -154,3 +155,69 @@ def test_staged_backward_validation():
     f32 = list(args)
     f32[7] = ea.ATTN_F32
     assert ea.attn_bwd_dkdv(Q, K, V, DO, WS, DK, DV, *f32) == ea.ATTN_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- split K/V
+def split(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, ws=WS, B=2, Hq=4, Hkv=2, Nq=3, Nk=1000, d=128, causal=1,
+             scale=0.125, ns=0, dtype=ea.ATTN_BF16, stream=None)
+    a.update(kw)
+    return ea.attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["B"], a["Hq"],
+                               a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                               a["ns"], a["dtype"], a["stream"])
+
+
+SPLIT_INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(ws=None),
+    dict(B=-1), dict(Nq=-1), dict(Nk=-5), dict(Hq=0), dict(Hkv=0), dict(Hq=6, Hkv=4),
+    dict(causal=2), dict(scale=float("nan")), dict(ns=-1), dict(dtype=5), dict(q=Q + 8),
+    dict(ws=WS + 4), dict(o=Q), dict(lse=O + 16), dict(ws=O), dict(ws=K + 256),
+]
+
+
+@pytest.mark.parametrize("kw", SPLIT_INVALID, ids=[str(k) for k in SPLIT_INVALID])
+def test_splitkv_rejects_bad_arguments(kw):
+    assert split(**kw) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_splitkv_unsupported():
+    assert split(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert split(d=96) == ea.ATTN_ERR_UNSUPPORTED
+    assert split(Nk=(1 << 22) + 1) == ea.ATTN_ERR_UNSUPPORTED
+    assert split(Nq=(1 << 22) + 1) == ea.ATTN_ERR_UNSUPPORTED
+    assert split(Hq=64, Hkv=1, Nq=(1 << 16) + 1) == ea.ATTN_ERR_UNSUPPORTED  # > 2^22 rows per group
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0)])
+def test_splitkv_empty_problem(kw):
+    assert split(q=None, k=None, v=None, o=None, lse=None, ws=None, **kw) == ea.ATTN_OK
+    assert ea.attn_fwd_splitkv_workspace_bytes(kw.get("B", 2), 4, 2, kw.get("Nq", 3), 100, 64,
+                                               0) == 0
+
+
+def test_splitkv_split_counts():
+    n = ea.attn_fwd_splitkv_num_splits
+    # 1000 keys = 16 tiles of 64: 7 asked -> ranges of 3 tiles -> 6 non-empty ranges
+    assert n(1, 4, 2, 3, 1000, 64, 7) == 6
+    assert n(1, 4, 2, 3, 1000, 64, 1) == 1
+    assert n(1, 4, 2, 3, 1000, 64, 16) == 16
+    assert n(1, 4, 2, 3, 1000, 64, 100) == 16  # at most one range per tile
+    assert n(1, 4, 2, 3, 1, 64, 5) == 1
+    assert n(1, 4, 2, 3, 0, 64, 5) == 1  # no keys: one (empty) range writes the result
+    assert n(0, 4, 2, 3, 100, 64, 5) == 0
+    assert n(1, 4, 2, 3, 100, 64, -1) == -1
+    # chosen from the shape: one round of resident workgroups (512 at d=128),
+    # at least 4 tiles per range
+    assert n(8, 32, 8, 1, 32768, 128, 0) == 8
+    assert n(1, 1, 1, 1, 256, 64, 0) == 1
+    for args in [(2, 8, 2, 5, 4000, 128), (1, 32, 8, 64, 16384, 128), (3, 4, 4, 1, 77, 64)]:
+        assert 1 <= n(*args, 0) <= (args[4] + 63) // 64
+
+
+def test_splitkv_workspace_bytes():
+    w = ea.attn_fwd_splitkv_workspace_bytes
+    # fp32 partial O [splits][rows][d] and LSE [splits][rows], each rounded up to 256 bytes
+    assert w(1, 2, 1, 3, 100, 64, 1) == 1536 + 256
+    assert w(2, 4, 2, 3, 1000, 128, 7) == 6 * 24 * 128 * 4 + 768
+    assert w(1, 3, 2, 1, 100, 64, 1) == -1
+    assert w(1, 4, 2, 1, 100, 80, 1) == -1
