@@ -45,11 +45,19 @@ def fwd_flops(B, H, N, d, causal):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank lines removed, so a
+    comment edit does not invalidate counters taken on the same code."""
+    import re
+
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(name.encode())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 
@@ -128,6 +136,21 @@ def forward_only(w, args, dev):
                    "causal": w.causal, "q_mult": w.q_mult, "seed": w.seed}}), flush=True)
 
 
+def calibration_copy(mib, dev):
+    """One plain device copy of `mib` MiB: a transfer of known size that
+    scales the HBM byte counters of a profiling run."""
+    import torch
+
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def splitkv_visible_pairs(Nq, Nk, causal):
     """(query, key) pairs the bottom-right aligned mask leaves visible per head."""
     if not causal:
@@ -192,7 +215,7 @@ def splitkv_only(name, args, dev):
         "warmup": args.warmup, "ms_per_step": round(r["us"] / 1e3, 5), "higher_is_better": True,
         "dtype": "bf16", "data": "synthetic",
         "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": r["frac_of_hbm"], "traffic": None,
+                     "frac": r["frac_of_hbm"], "traffic": load_traffic("splitkv_" + name),
                      "kernel": "fwd_split + split_combine (one call)"},
         "detail": r,
         "config": {"workload": cw.name, "B": cw.B, "Hq": cw.Hq, "Hkv": cw.Hkv, "Nq": cw.Nq,
@@ -233,6 +256,8 @@ def main():
     dev = torch.device("cuda:0")
     ea.lib()  # fail loudly if the HIP library is missing
 
+    if args.fwd_only or args.splitkv_only:
+        calibration_copy(args.copy_mib, dev)
     if args.fwd_only:
         forward_only(attn_inputs.WORKLOADS[args.fwd_only], args, dev)
         return
@@ -295,13 +320,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    if args.copy_mib > 0:  # plain copy of known size, for HBM counter calibration
-        n = args.copy_mib * (1 << 20) // 4
-        src = torch.ones(n, device=dev, dtype=torch.float32)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args.copy_mib, dev)
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in launches] for _ in range(K)]

@@ -1,4 +1,9 @@
 // Split-K/V forward for few queries against many keys (decode, append).
+// The shape table of "FlashAttention：让精确注意力服从内存层次", section
+// "训练与推理的形状不同", puts decoding at few queries against a long key
+// history, bound first by key/value bandwidth; the "FlashAttention" paper
+// story names FlashDecoding among the method's descendants.  Splitting the
+// keys gives such shapes enough workgroups to stream K/V at HBM speed.
 //
 // The keys of every (batch, key/value head) are cut into splits; one
 // workgroup computes, for one split, the attention of all the query rows of

@@ -137,7 +137,9 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
 
 /*
  * Split-K/V forward, for few queries against many keys (decoding one token,
- * or appending a short chunk, against a long key/value cache).
+ * or appending a short chunk, against a long key/value cache: the decode row
+ * of the shape table in "FlashAttention：让精确注意力服从内存层次", section
+ * "训练与推理的形状不同", whose first constraint is key/value bandwidth).
  *   q    [B,Hq,Nq,d]  in   (bf16)
  *   k, v [B,Hkv,Nk,d] in   (bf16)
  *   o    [B,Hq,Nq,d]  out  (bf16)
