@@ -336,6 +336,275 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   }
 }
 
+// Software-pipelined variant of the bf16 forward: while a wave turns the
+// scores of key tile j into probabilities (vector ALU work), the matrix cores
+// already compute the scores of tile j+1, so the two units overlap inside one
+// wave instead of only across waves.  K and V have separate double-buffered
+// LDS stages: K(j+2) and V(j+1) are loaded during tile j (K(j) was consumed
+// one tile earlier, by the look-ahead score product), so one barrier per tile
+// still suffices.  Same arithmetic and results as fwd_bf16_kernel.
+#ifndef ATTN_FWD_PIPE64
+#define ATTN_FWD_PIPE64 0
+#endif
+#ifndef ATTN_FWD_PIPE128
+#define ATTN_FWD_PIPE128 1
+#endif
+#ifndef ATTN_PIPE_WPE64
+#define ATTN_PIPE_WPE64 3
+#endif
+#ifndef ATTN_PIPE_WPE128
+#define ATTN_PIPE_WPE128 2
+#endif
+#ifndef ATTN_PIPE_SCHED
+#define ATTN_PIPE_SCHED 1
+#endif
+#ifndef ATTN_PIPE_VPM64
+#define ATTN_PIPE_VPM64 14  // VALU instructions placed after each look-ahead MFMA
+#endif
+#ifndef ATTN_PIPE_VPM128
+#define ATTN_PIPE_VPM128 12
+#endif
+
+template <int D>
+struct PipeCfg {
+  static constexpr int NW = 4;
+  static constexpr int BR = 32 * NW;
+  static constexpr int BC = 64;
+  static constexpr int WPE = D == 64 ? ATTN_PIPE_WPE64 : ATTN_PIPE_WPE128;
+  static constexpr int VPM = D == 64 ? ATTN_PIPE_VPM64 : ATTN_PIPE_VPM128;
+  static constexpr int TILEB = BC * D * 2;
+  static constexpr size_t LDS = (size_t)4 * TILEB;  // K[2] | V[2]
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * PipeCfg<D>::NW)
+__attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_bf16_pipe_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb, float c,
+    uint32_t qsign) {
+  using Cfg = PipeCfg<D>;
+  constexpr int BR = Cfg::BR, BC = Cfg::BC, TILEB = Cfg::TILEB, NW = Cfg::NW;
+  constexpr int ROWB = D * 2;
+  constexpr int PW = TILEB / 1024 / NW;
+  static_assert(PW * NW * 1024 == TILEB, "tile pieces");
+  constexpr int NQC = D / 16;
+  constexpr int NMB = D / 32;
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];  // K[2] | V[2]
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const int BH = gridDim.x / nqb;
+  const int id = blockIdx.x;
+  const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
+  const int bh = id % BH;
+  const int b = bh / Hq;
+  const int h = bh - b * Hq;
+  const int g = h / (Hq / Hkv);
+  const int64_t qoff = (int64_t)bh * N * D;
+  const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
+  const int q0 = qb * BR + w * 32;
+
+  const uint32_t slice_bytes = (uint32_t)N * ROWB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
+
+  bf16x8 qreg[NQC];
+#pragma unroll
+  for (int cc = 0; cc < NQC; ++cc)
+    qreg[cc] = bitcast<bf16x8>(buf_load16(rq, (uint32_t)((q0 + l32) * D + cc * 16 + hf * 8) * 2) ^ qsign);
+
+  const int ntiles_all = (N + BC - 1) / BC;
+  int ntiles = ntiles_all;
+  int wtiles = ntiles_all;
+  if (CAUSAL) {
+    ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
+    wtiles = min(ntiles, (q0 + 31) / BC + 1);
+  }
+
+  uint32_t goff[PW];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int o = (w * PW + i) * 1024 + lane * 16;
+    const int row = o / ROWB;
+    const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
+    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+  }
+  auto issue = [&](__amdgpu_buffer_rsrc_t r, char* dst, int j) {
+    const uint32_t tbase = (uint32_t)j * BC * ROWB;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) buf_load16_lds(r, dst + (w * PW + i) * 1024, goff[i] + tbase);
+  };
+  auto kstage = [&](int s) { return smem + s * TILEB; };
+  auto vstage = [&](int s) { return smem + (2 + s) * TILEB; };
+
+  int koff[NQC], voff[2][NMB];
+#pragma unroll
+  for (int cc = 0; cc < NQC; ++cc) koff[cc] = tile_off<D>(l32, 2 * cc + hf);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) voff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
+
+  float ms = -__builtin_inff(), lsum = 0.f;
+  f32x16 oacc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
+
+  // S^T of one tile from a K stage.
+  auto scores = [&](const char* kt, f32x16 (&sacc)[2]) {
+    u32x4 kfrag[2][NQC];
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int cc = 0; cc < NQC; ++cc) kfrag[kbk][cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk) {
+      sacc[kbk] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < NQC; ++cc)
+        sacc[kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
+    }
+  };
+  auto softmax_exp = [&](const f32x16 (&sacc)[2], float m, uint32_t (&pk)[2][8]) {
+    float tsum = 0.f;
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -m));
+        pk[kbk][r >> 1] = pack_bf16(p0, p1);
+        tsum += p0 + p1;
+      }
+    return tsum;
+  };
+
+  // Tile j: scores sc (already computed) -> P -> O += P V; meanwhile the
+  // scores of tile j+1 go to sn.  BUF = j % 2.
+  auto tile = [&](auto bufc, int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (j + 1 < ntiles) issue(rv, vstage(BUF ^ 1), j + 1);
+    if (j + 2 < ntiles) issue(rk, kstage(BUF), j + 2);
+    if (j < wtiles) {
+      const int k0 = j * BC;
+      if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kbk * 32 + acc_row(r, hf);
+            const bool dead = (key >= N) || (CAUSAL && key > q0 + l32);
+            if (dead) sc[kbk][r] = -__builtin_inff();
+          }
+      }
+      uint32_t pk[2][8];
+      float tsum;
+      if (j + 1 < wtiles) {
+        __builtin_amdgcn_sched_barrier(0);
+        scores(kstage(BUF ^ 1), sn);
+        tsum = softmax_exp(sc, ms, pk);
+        if (ATTN_PIPE_SCHED) {
+          // K fragments stream a few MFMAs ahead of their use; the softmax
+          // of tile j fills the matrix-core issue gaps.
+          constexpr int LA = 4;  // LDS reads ahead
+          __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * NQC; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (i + LA < 2 * NQC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x002, Cfg::VPM, 0);  // VALU
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        tsum = softmax_exp(sc, ms, pk);
+      }
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax)) != 0) {
+        __asm__ volatile("");
+        float mloc = sc[0][0];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sc[kbk][r]);
+        mloc = __builtin_fmaxf(mloc, xor32(mloc));
+        const float tmax = mloc * c;
+        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
+          const float mnew = __builtin_fmaxf(ms, tmax);
+          const float alpha = fast_exp2(ms - mnew);
+          ms = mnew;
+          lsum *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
+          tsum = softmax_exp(sc, ms, pk);
+        }
+      }
+      lsum += tsum;
+      const char* vt = vstage(BUF);
+      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int cp = 0; cp < 2; ++cp) {
+            const int rows = (kbk * 32 + cp * 16) * ROWB;
+            const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
+            const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
+            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const bf16x8 bp = bitcast<bf16x8>(
+                u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
+            oacc[mb] = mfma32(a, bp, oacc[mb]);
+          }
+      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    }
+    // V(j+1) and K(j+2) must have landed, and every wave be done with
+    // K(j+1) and V(j), before their stages are refilled.
+    if (j + 1 < ntiles) wait_vm_barrier<0>();
+  };
+
+  // Prologue: K(0), V(0), K(1) in flight; wait; scores of tile 0.
+  if (ntiles > 0) {
+    issue(rk, kstage(0), 0);
+    issue(rv, vstage(0), 0);
+  }
+  if (ntiles > 1) issue(rk, kstage(1), 1);
+  wait_vm_barrier<0>();
+  f32x16 s0[2], s1[2];
+  if (0 < wtiles) scores(kstage(0), s0);
+  // tile 0's first step refills K stage 0 with K(2): every wave must be done
+  // reading K(0) first
+  wait_vm_barrier<0>();
+
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j, s0, s1);
+    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1, s1, s0);
+  }
+
+  const int qrow = q0 + l32;
+  const float lfull = lsum + xor32(lsum);
+  if (qrow < N) {
+    const float inv = 1.0f / lfull;
+    __bf16* dst = O + qoff + (int64_t)qrow * D;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = mb * 32 + rg * 8 + hf * 4;
+        u32x2 v;
+        v[0] = pack_bf16(oacc[mb][4 * rg] * inv, oacc[mb][4 * rg + 1] * inv);
+        v[1] = pack_bf16(oacc[mb][4 * rg + 2] * inv, oacc[mb][4 * rg + 3] * inv);
+        *(u32x2*)(dst + d0) = v;
+      }
+    if (hf == 0) LSE[(int64_t)bh * N + qrow] = (ms + __builtin_log2f(lfull)) * kLn2;
+  }
+}
+
 // fp32 forward on the vector ALUs: 32 query rows per workgroup, 8 lanes per
 // row, each lane owning D/8 consecutive features; key/value tiles of 32 rows
 // in LDS.  Exact online softmax (the maximum moves on every increase).
@@ -415,7 +684,26 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 
 // ---------------------------------------------------------------- launchers
 template <int D, bool CAUSAL>
+static hipError_t launch_bf16_pipe(const FwdArgs& a) {
+  const int nqb = (a.N + PipeCfg<D>::BR - 1) / PipeCfg<D>::BR;
+  const int64_t grid = (int64_t)nqb * a.B * a.Hq;
+  const size_t lds = PipeCfg<D>::LDS;
+  const hipError_t e = allow_lds(fwd_bf16_pipe_kernel<D, CAUSAL>, lds);
+  if (e != hipSuccess) return e;
+  float c = fabsf(a.scale) * kLog2e;
+  if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
+  const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CAUSAL>), dim3((unsigned)grid),
+                     dim3(64 * PipeCfg<D>::NW), lds, a.stream, (const __bf16*)a.q,
+                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.Hq, a.Hkv, a.N,
+                     nqb, c, qsign);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
 static hipError_t launch_bf16(const FwdArgs& a) {
+  if constexpr ((D == 64 && ATTN_FWD_PIPE64) || (D == 128 && ATTN_FWD_PIPE128))
+    return launch_bf16_pipe<D, CAUSAL>(a);
   const int nqb = (a.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
   const size_t lds = FwdCfg<D>::LDS;
