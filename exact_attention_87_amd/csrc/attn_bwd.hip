@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 template <int D>
 struct DkdvCfg {
   static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
-  static constexpr int BQ = 64;    // queries per tile
+  static constexpr int BQ = 64;    // queries per tile (two 32-query sub-blocks)
   static constexpr int NBUF = D == 64 ? 3 : 2;
   static constexpr int WPE = D == 64 ? ATTN_BWD_WPE64 : ATTN_BWD_WPE128;
   static constexpr int TILEB = BQ * D * 2;
@@ -184,10 +184,19 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       buf_load16_lds(rs, base + 2 * TILEB, soff + (uint32_t)qt * BQ * 4);
     }
   };
-  // Loads per wave per stage, for the partial waits of a 3-stage pipeline.
-  // Wave 0 has one extra (the statistics); waiting for the larger count is
-  // only conservative for the others.
-  constexpr int LOADS = 2 * PW + 1;
+  // Loads per wave per stage, for the partial waits of a 3-stage pipeline:
+  // 2*PW for Q and dO, plus one for the statistics on wave 0.  Each wave
+  // must wait with its own count: allowing wave 0's count on the others
+  // would let one load of the stage about to be read still be in flight.
+  constexpr int LOADS = 2 * PW;
+  // Wait until only the newest stage's loads may be outstanding, then
+  // synchronise the workgroup (w is wave-uniform).
+  auto wait_stage = [&]() {
+    if (w == 0)
+      wait_vm_barrier<LOADS + 1>();
+    else
+      wait_vm_barrier<LOADS>();
+  };
 
   // Per-lane LDS offsets inside a stage (fixed for the whole loop).
   int qoff_[NQC], troff[2][NMB];
@@ -198,6 +207,79 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) troff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
 
+  // The three phases of one 32-query sub-block (rows qbase.. of the tile):
+  //   A: S = Q K^T and dP - D = dO V^T - D on the matrix cores;
+  //   V: P = 2^(S c - LSE), dS = P (dP - D), both packed to bf16 (vector ALU);
+  //   C: dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.
+  auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
+                    f32x16& sacc, f32x16& pacc) {
+    u32x4 qa[NQC], da[NQC];
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      qa[cc] = lds_read16(qtile + qbase * ROWB + qoff_[cc]);
+      da[cc] = lds_read16(dotile + qbase * ROWB + qoff_[cc]);
+    }
+    // the dP accumulator starts at -D of each row (element 4*rg+e is row
+    // qbase + 8*rg + 4*hf + e)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 nd = *(const f32x4*)(dsum + qbase + 8 * rg + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
+    }
+    sacc = f32x16{};
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      sacc = mfma32(bitcast<bf16x8>(qa[cc]), kreg[cc], sacc);
+      pacc = mfma32(bitcast<bf16x8>(da[cc]), vreg[cc], pacc);
+    }
+  };
+  auto phaseV = [&](const float* lse2, int qbase, int qfirst, bool diag, const f32x16& sacc,
+                    const f32x16& pacc, uint32_t (&pk)[8], uint32_t (&dsk)[8]) {
+    float pv[16];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const f32x4 l4 = *(const f32x4*)(lse2 + qbase + 8 * rg + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pv[4 * rg + e] = fast_exp2(__builtin_fmaf(sacc[4 * rg + e], c, -l4[e]));
+    }
+    if (diag) {  // diagonal block: keys after the query get 0
+      __asm__ volatile("");
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (krow > qfirst + acc_row(r, hf)) pv[r] = 0.f;
+    }
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      float dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * rg + e] * pacc[4 * rg + e];
+      pk[2 * rg] = pack_bf16(pv[4 * rg], pv[4 * rg + 1]);
+      pk[2 * rg + 1] = pack_bf16(pv[4 * rg + 2], pv[4 * rg + 3]);
+      dsk[2 * rg] = pack_bf16(dsv[0], dsv[1]);
+      dsk[2 * rg + 1] = pack_bf16(dsv[2], dsv[3]);
+    }
+  };
+  auto phaseC = [&](const char* qtile, const char* dotile, int qbase, const uint32_t (&pk)[8],
+                    const uint32_t (&dsk)[8]) {
+#pragma unroll
+    for (int cp = 0; cp < 2; ++cp) {
+      const bf16x8 pb = bitcast<bf16x8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
+      const bf16x8 sb =
+          bitcast<bf16x8>(u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
+      const int rows = (qbase + 16 * cp) * ROWB;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const u32x2 a0 = lds_read_tr(dotile + rows + troff[0][mb]);
+        const u32x2 a1 = lds_read_tr(dotile + rows + troff[1][mb]);
+        dvacc[mb] = mfma32(bitcast<bf16x8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, dvacc[mb]);
+        const u32x2 b0 = lds_read_tr(qtile + rows + troff[0][mb]);
+        const u32x2 b1 = lds_read_tr(qtile + rows + troff[1][mb]);
+        dkacc[mb] = mfma32(bitcast<bf16x8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
+      }
+    }
+  };
+
   auto step = [&](auto bufc, int it) {
     constexpr int BUF = decltype(bufc)::value;
     const char* qtile = smem + BUF * STAGEB;
@@ -206,79 +288,25 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const float* lse2 = dsum + BQ;
     if (it + NBUF - 1 < iters) issue(it + NBUF - 1);
     const int qt = qt0 + it % per_head;
+    const int qf0 = qt * BQ, qf1 = qf0 + 32;
+    // wave-uniform: which of the two 32-query sub-blocks have visible
+    // (query, key) pairs, and which touch the diagonal
+    const bool act0 = !((CAUSAL && qf0 + 31 < key0) || qf0 >= N);
+    const bool act1 = !((CAUSAL && qf1 + 31 < key0) || qf1 >= N);
+    const bool diag0 = CAUSAL && key0 + 31 > qf0;
+    const bool diag1 = CAUSAL && key0 + 31 > qf1;
 #pragma unroll
     for (int qs = 0; qs < BQ / 32; ++qs) {
-      const int qbase = qs * 32;
-      const int qfirst = qt * BQ + qbase;
-      if ((CAUSAL && qfirst + 31 < key0) || qfirst >= N) continue;  // wave-uniform
-      // S = Q K^T and dP = dO V^T (rows: queries, columns: this wave's keys)
-      u32x4 qa[NQC], da[NQC];
-#pragma unroll
-      for (int cc = 0; cc < NQC; ++cc) {
-        qa[cc] = lds_read16(qtile + qbase * ROWB + qoff_[cc]);
-        da[cc] = lds_read16(dotile + qbase * ROWB + qoff_[cc]);
-      }
-      // dP - D: the accumulator starts at -D of each row (element 4*rg+e is
-      // row qbase + 8*rg + 4*hf + e)
-      f32x16 pacc;
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 nd = *(const f32x4*)(dsum + qbase + 8 * rg + 4 * hf);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
-      }
-      f32x16 sacc = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < NQC; ++cc) {
-        sacc = mfma32(bitcast<bf16x8>(qa[cc]), kreg[cc], sacc);
-        pacc = mfma32(bitcast<bf16x8>(da[cc]), vreg[cc], pacc);
-      }
+      if (!(qs == 0 ? act0 : act1)) continue;  // wave-uniform
+      f32x16 sacc, pacc;
       uint32_t pk[8], dsk[8];
-      float pv[16];
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int q4 = qbase + 8 * rg + 4 * hf;
-        const f32x4 l4 = *(const f32x4*)(lse2 + q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[4 * rg + e] = fast_exp2(__builtin_fmaf(sacc[4 * rg + e], c, -l4[e]));
-      }
-      if (CAUSAL && key0 + 31 > qfirst) {  // diagonal block: keys after the query get 0
-        __asm__ volatile("");
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (krow > qfirst + acc_row(r, hf)) pv[r] = 0.f;
-      }
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        float dsv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * rg + e] * pacc[4 * rg + e];
-        pk[2 * rg] = pack_bf16(pv[4 * rg], pv[4 * rg + 1]);
-        pk[2 * rg + 1] = pack_bf16(pv[4 * rg + 2], pv[4 * rg + 3]);
-        dsk[2 * rg] = pack_bf16(dsv[0], dsv[1]);
-        dsk[2 * rg + 1] = pack_bf16(dsv[2], dsv[3]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 queries)
-#pragma unroll
-      for (int cp = 0; cp < 2; ++cp) {
-        const bf16x8 pb = bitcast<bf16x8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
-        const bf16x8 sb =
-            bitcast<bf16x8>(u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
-        const int rows = (qbase + 16 * cp) * ROWB;
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const u32x2 a0 = lds_read_tr(dotile + rows + troff[0][mb]);
-          const u32x2 a1 = lds_read_tr(dotile + rows + troff[1][mb]);
-          dvacc[mb] = mfma32(bitcast<bf16x8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, dvacc[mb]);
-          const u32x2 b0 = lds_read_tr(qtile + rows + troff[0][mb]);
-          const u32x2 b1 = lds_read_tr(qtile + rows + troff[1][mb]);
-          dkacc[mb] = mfma32(bitcast<bf16x8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
-        }
-      }
+      phaseA(qtile, dotile, dsum, qs * 32, sacc, pacc);
+      phaseV(lse2, qs * 32, qs == 0 ? qf0 : qf1, qs == 0 ? diag0 : diag1, sacc, pacc, pk, dsk);
+      phaseC(qtile, dotile, qs * 32, pk, dsk);
     }
     if (it + 1 < iters) {
       if (NBUF == 3 && it + 2 < iters)
-        wait_vm_barrier<LOADS>();
+        wait_stage();
       else
         wait_vm_barrier<0>();
     }
@@ -288,7 +316,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   for (int it = 0; it < NBUF - 1; ++it)
     if (it < iters) issue(it);
   if (NBUF == 3 && iters > 1)
-    wait_vm_barrier<LOADS>();
+    wait_stage();
   else
     wait_vm_barrier<0>();
   for (int it = 0; it < iters; it += NBUF) {
