@@ -56,11 +56,14 @@ def _bind(path: str):
     lib.oracle_fwd.argtypes = [d, d, d, d, d] + dims
     lib.oracle_fwd_bottom_right.argtypes = [d, d, d, d, d] + dims
     lib.oracle_fwd_rows.argtypes = [d, d, d, i64p, c64, d, d] + dims
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.oracle_fwd_blockmask.argtypes = [d, d, d, d, d, u8p, ci, ci, ci] + [ci] * 6 + [ci, cd]
     lib.oracle_fwd_blockwise.argtypes = [d, d, d, d, d] + dims + [ci, ci]
     lib.oracle_bwd.argtypes = [d] * 10 + dims
     lib.oracle_bwd_slices.argtypes = [d, d, d, d, i64p, c64, d, d, d] + dims
     lib.oracle_threads.argtypes = []
     for f in (lib.oracle_threads, lib.oracle_fwd, lib.oracle_fwd_bottom_right, lib.oracle_fwd_rows,
+              lib.oracle_fwd_blockmask,
               lib.oracle_fwd_blockwise, lib.oracle_bwd, lib.oracle_bwd_slices):
         f.restype = ci
     return lib
@@ -143,6 +146,29 @@ class Oracle:
         _check(self.lib.oracle_fwd_bottom_right(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                                 B, Hq, Hkv, Nq, Nk, dk, dv, int(bool(causal)),
                                                 scale), "oracle_fwd_bottom_right")
+        return o, lse
+
+    def fwd_blockmask(self, q, k, v, mask, bm: int, bn: int, causal: bool = False,
+                      scale: float | None = None):
+        """Block-sparse forward: query i of head h sees key j iff
+        mask[h or 0][i // bm][j // bn] (and j <= i when causal).  mask is uint8
+        [1 or Hq, ceil(N/bm), ceil(N/bn)]. Returns (O, LSE) in float64."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, Hq, Hkv, Nq, Nk, dk, dv = _shapes(q, k, v)
+        if Nq != Nk:
+            raise ValueError("block-sparse forward is square: Nq == Nk")
+        m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
+        nbq, nbk = -(-Nq // bm), -(-Nk // bn)
+        if m.ndim != 3 or m.shape[0] not in (1, Hq) or m.shape[1:] != (nbq, nbk):
+            raise ValueError(f"mask must be [1 or {Hq}, {nbq}, {nbk}], got {m.shape}")
+        scale = default_scale(dk) if scale is None else float(scale)
+        o = np.empty((B, Hq, Nq, dv), np.float64)
+        lse = np.empty((B, Hq, Nq), np.float64)
+        mp = m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        _check(self.lib.oracle_fwd_blockmask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), mp,
+                                             m.shape[0], int(bm), int(bn), B, Hq, Hkv, Nq, dk,
+                                             dv, int(bool(causal)), scale),
+               "oracle_fwd_blockmask")
         return o, lse
 
     def fwd_rows(self, q, k, v, rows, causal: bool = False, scale: float | None = None):
@@ -233,6 +259,7 @@ fwd = _default.fwd
 fwd_rows = _default.fwd_rows
 fwd_bottom_right = _default.fwd_bottom_right
 fwd_blockwise = _default.fwd_blockwise
+fwd_blockmask = _default.fwd_blockmask
 bwd = _default.bwd
 bwd_slices = _default.bwd_slices
 omp_threads = _default.omp_threads

@@ -177,6 +177,67 @@ int oracle_fwd_bottom_right(const double* q, const double* k, const double* v, d
 }
 
 /*
+ * Block-sparse forward ("FlashAttention" paper story, block-sparse
+ * paragraph: a 0/1 mask over the grid of (Br rows) x (Bc keys) score blocks,
+ * whose zero blocks are never computed).  Square problem, N queries and N
+ * keys.  Query i of head h sees key j iff
+ *     mask[hm][i / bm][j / bn] != 0   and   (causal == 0 or j <= i),
+ * with hm = h when mask_heads == Hq and hm = 0 when mask_heads == 1; the
+ * mask is row-major [mask_heads][ceil(N/bm)][ceil(N/bn)] bytes and is shared
+ * by every batch.  Each row's visible keys are gathered in index order and
+ * the dense softmax is taken over them (dense_row), so the result is the
+ * definition itself.  A row that sees no key gets O = 0 and LSE = -inf.
+ */
+int oracle_fwd_blockmask(const double* q, const double* k, const double* v, double* o,
+                         double* lse, const uint8_t* mask, int mask_heads, int bm, int bn,
+                         int B, int Hq, int Hkv, int N, int dk, int dv, int causal,
+                         double scale) {
+  int rc = check_args(B, Hq, Hkv, N, N, dk, dv);
+  if (rc) return rc;
+  if (!(mask_heads == 1 || mask_heads == Hq) || bm < 1 || bn < 1) return ORACLE_BAD_ARG;
+  const int64_t nbq = ((int64_t)N + bm - 1) / bm, nbk = ((int64_t)N + bn - 1) / bn;
+  const int64_t rows = (int64_t)B * Hq * N;
+  const int group = Hq / Hkv;
+  int bad = 0;
+#pragma omp parallel
+  {
+    const int64_t n1 = N > 0 ? N : 1;
+    double* scores = (double*)malloc(sizeof(double) * n1);
+    double* kg = (double*)malloc(sizeof(double) * n1 * dk);
+    double* vg = (double*)malloc(sizeof(double) * n1 * dv);
+    if (!scores || !kg || !vg) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < rows; ++r) {
+        const int64_t i = r % N;
+        const int64_t h = (r / N) % Hq;
+        const int64_t b = r / ((int64_t)N * Hq);
+        const int64_t g = h / group;
+        const int64_t hm = (mask_heads == 1) ? 0 : h;
+        const uint8_t* mrow = mask + (hm * nbq + i / bm) * nbk;
+        const double* Kh = k + (b * Hkv + g) * (int64_t)N * dk;
+        const double* Vh = v + (b * Hkv + g) * (int64_t)N * dv;
+        int64_t nvis = 0;
+        for (int64_t j = 0; j < N; ++j) {
+          if (!mrow[j / bn]) continue;
+          if (causal && j > i) continue;
+          memcpy(kg + nvis * dk, Kh + j * dk, sizeof(double) * dk);
+          memcpy(vg + nvis * dv, Vh + j * dv, sizeof(double) * dv);
+          ++nvis;
+        }
+        dense_row(q + r * dk, kg, vg, nvis, dk, dv, scale, scores, o + r * dv, lse + r);
+      }
+    }
+    free(scores);
+    free(kg);
+    free(vg);
+  }
+  return bad ? ORACLE_NO_MEM : ORACLE_OK;
+}
+
+/*
  * Dense forward on a chosen subset of rows.  rows[t] is the flat row index
  * (b * Hq + h) * Nq + i; o is [nrows, dv], lse is [nrows].  Used to check
  * sampled rows of large problems one by one.

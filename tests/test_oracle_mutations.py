@@ -12,6 +12,7 @@ import shutil
 import pytest
 
 import oracle
+import test_oracle_blockmask as pm
 import test_oracle_bwd as pb
 import test_oracle_fwd as pf
 
@@ -25,7 +26,7 @@ MUTANTS = [
      "scores[j] = dot(qi, Kh + j * dk, dk);", 1),
     ("causal_excludes_diagonal", "const int64_t n = i + 1 + off;", "const int64_t n = i + off;", 1),
     ("causal_one_extra_key", "const int64_t n = i + 1 + off;", "const int64_t n = i + 2 + off;", 1),
-    ("gqa_modulo_map", "const int64_t g = h / group;", "const int64_t g = h % Hkv;", 6),
+    ("gqa_modulo_map", "const int64_t g = h / group;", "const int64_t g = h % Hkv;", 7),
     ("key_index_slip", "scores[j] = scale * dot(qi, Kh + j * dk, dk);",
      "scores[j] = scale * dot(qi, Kh + j, dk);", 1),
     ("value_transposed", "const double* vj = Vh + j * dv;", "const double* vj = Vh + j;", 1),
@@ -43,6 +44,10 @@ MUTANTS = [
      "const int64_t off = (int64_t)Nq - Nk;", 1),
     ("bwd_dk_skips_group", "for (int64_t hh = 0; hh < group; ++hh) {",
      "for (int64_t hh = 0; hh < 1; ++hh) {", 1),
+    ("blockmask_inverted", "if (!mrow[j / bn]) continue;", "if (mrow[j / bn]) continue;", 1),
+    ("blockmask_head_zero", "const int64_t hm = (mask_heads == 1) ? 0 : h;",
+     "const int64_t hm = 0;", 1),
+    ("blockmask_ignores_causal", "if (causal && j > i) continue;", "", 1),
 ]
 
 
@@ -68,6 +73,9 @@ def run_pins(om):
         ("autograd", lambda: pb.test_gradients_match_torch_autograd(
             om, True, (1, 3, 1, 9, 12, 5, 7))),
         ("sums", lambda: pb.test_gradient_sum_identities(om, False)),
+        ("blockmask_full", lambda: pm.test_full_mask_is_the_dense_forward(om, True, 13, 4, 3)),
+        ("blockmask_scipy", lambda: pm.test_matches_scipy_on_the_expanded_mask(om, False, 1)),
+        ("blockmask_heads", lambda: pm.test_per_head_masks_act_head_by_head(om)),
     ]
     failed = []
     for name, fn in pins:
