@@ -112,3 +112,46 @@ def make_cache(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int = 
 
 def make_cache_workload(w: CacheWorkload):
     return make_cache(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.seed)
+
+
+# Block-sparse forward: a block mask over tiles of 128 queries x 64 keys.  The
+# mask is input data (which tiles exist), drawn here like the tensors.
+@dataclass(frozen=True)
+class SparseWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    window: int      # keys before each query block that it always sees
+    globals_: int    # leading key tiles every query block sees
+    stride: int      # every stride-th key tile is also present
+    density: float   # extra random tiles, per head
+    seed: int = 0
+
+
+SPARSE_WORKLOADS = {
+    "local_global": SparseWorkload("blocksparse_local_global_bf16_B1_Hq32_Hkv8_N16384_d128", 1, 32,
+                                   8, 16384, 128, True, window=1024, globals_=2, stride=16,
+                                   density=0.05, seed=13),
+}
+
+
+def sparse_mask(w: SparseWorkload, block_q: int = 128, block_k: int = 64):
+    """uint8 numpy mask [Hq, ceil(N/block_q), ceil(N/block_k)]: a local band of
+    `window` keys ending at each query block, `globals_` leading key tiles,
+    every `stride`-th key tile, and random tiles of the given density (seeded,
+    different per head)."""
+    import numpy as np
+
+    nbq, nbk = -(-w.N // block_q), -(-w.N // block_k)
+    qb = np.arange(nbq)[:, None]
+    t = np.arange(nbk)[None, :]
+    q_end = np.minimum((qb + 1) * block_q, w.N)  # one past the block's last query
+    local = (t * block_k < q_end) & ((t + 1) * block_k > q_end - w.window)
+    base = local | (t < w.globals_) | (t % w.stride == 0)
+    r = np.random.default_rng(w.seed)
+    rand = r.random((w.Hq, nbq, nbk)) < w.density
+    return (base[None] | rand).astype(np.uint8)

@@ -16,8 +16,10 @@ counted.
 Printed: one JSON line with the step throughput, the roofline of the dominant
 kernel (durations from HIP events on the launch stream), every kernel's
 duration, a forward sweep over the other workloads, the split-K/V forward on
-the key/value-cache workloads (decode, append; GB/s against HBM), and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+the key/value-cache workloads (decode, append; GB/s against HBM), the
+block-sparse forward on a local + global + random block mask (TFLOP/s over
+the visible pairs, and the dense forward of the same shape beside it), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -204,6 +206,84 @@ def splitkv_case(cw, dev, steps, warmup, num_splits=0):
                                                          num_splits)}
 
 
+def sparse_visible_pairs(mask, N, bq, bk, causal):
+    """(query, key) pairs a block mask (and the causal rule) leaves visible,
+    summed over the mask's heads."""
+    import numpy as np
+
+    nbq, nbk = mask.shape[1], mask.shape[2]
+    qb = np.arange(nbq)[:, None]
+    t = np.arange(nbk)[None, :]
+    q0, q1 = qb * bq, np.minimum((qb + 1) * bq, N)
+    k0, k1 = t * bk, np.minimum((t + 1) * bk, N)
+    if not causal:
+        pairs = (q1 - q0) * (k1 - k0)
+    else:
+        # rows i in [q0, q1) see keys [k0, min(k1, i + 1)): sum over the rows
+        pairs = np.zeros((nbq, nbk), np.int64)
+        for i in range(bq):
+            row = q0 + i
+            pairs += np.where(row < q1, np.clip(np.minimum(k1, row + 1) - k0, 0, None), 0)
+    return int((mask.astype(np.int64) * pairs[None]).sum())
+
+
+def sparse_case(sw, dev, steps, warmup):
+    """attn_fwd_blocksparse on a block-sparse workload (mask compaction +
+    forward, one call), timed with HIP events on the launch stream, and the
+    dense forward of the same shape for comparison.  TFLOP/s count the
+    visible (query, key) pairs only: 4*d per pair."""
+    import torch
+
+    import attn_inputs
+    import exact_attention_87_amd as ea
+
+    q, k, v = (t.to(dev) for t in attn_inputs.make(sw.B, sw.Hq, sw.Hkv, sw.N, sw.d, "bf16",
+                                                    seed=sw.seed))
+    mask_np = attn_inputs.sparse_mask(sw)
+    mask = torch.from_numpy(mask_np).to(dev)
+    o, lse = ea.fwd_blocksparse(q, k, v, mask, causal=sw.causal)
+    ws = torch.empty(ea.attn_fwd_blocksparse_workspace_bytes(sw.Hq, sw.N, mask.shape[0]),
+                     device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: ea.fwd_blocksparse(q, k, v, mask, causal=sw.causal, out=o, lse=lse,
+                                          workspace=ws))
+    ms_dense = timed(lambda: ea.fwd(q, k, v, causal=sw.causal, out=o, lse=lse))
+    pairs = sw.B * sparse_visible_pairs(mask_np, sw.N, ea.SPARSE_BLOCK_Q, ea.SPARSE_BLOCK_K,
+                                        sw.causal)
+    dense_pairs = sw.B * sw.Hq * (sw.N * (sw.N + 1) // 2 if sw.causal else sw.N * sw.N)
+    tf = 4.0 * sw.d * pairs / (ms / 1e3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "visible_fraction": round(pairs / dense_pairs, 4), "dense_ms": round(ms_dense, 4),
+            "speedup_vs_dense": round(ms_dense / ms, 2)}
+
+
+def sparse_only(name, args, dev):
+    import attn_inputs
+
+    sw = attn_inputs.SPARSE_WORKLOADS[name]
+    r = sparse_case(sw, dev, args.steps, args.warmup)
+    print(json.dumps({
+        "metric": "block-sparse attention forward TFLOP/s (visible pairs) on 1 MI355X",
+        "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic", "detail": r,
+        "config": {"workload": sw.name, "B": sw.B, "Hq": sw.Hq, "Hkv": sw.Hkv, "N": sw.N,
+                   "d": sw.d, "causal": sw.causal, "seed": sw.seed}}), flush=True)
+
+
 def splitkv_only(name, args, dev):
     import attn_inputs
 
@@ -234,6 +314,8 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--fwd-only", type=int, default=0, metavar="ID",
                     help="time only the forward of workload ID (1-5) and print its JSON line")
+    ap.add_argument("--sparse-only", default="", metavar="NAME",
+                    help="time only the block-sparse forward of workload NAME (local_global)")
     ap.add_argument("--splitkv-only", default="", metavar="NAME",
                     help="time only the split-K/V forward of cache workload NAME "
                          "(decode, append) and print its JSON line")
@@ -256,13 +338,16 @@ def main():
     dev = torch.device("cuda:0")
     ea.lib()  # fail loudly if the HIP library is missing
 
-    if args.fwd_only or args.splitkv_only:
+    if args.fwd_only or args.splitkv_only or args.sparse_only:
         calibration_copy(args.copy_mib, dev)
     if args.fwd_only:
         forward_only(attn_inputs.WORKLOADS[args.fwd_only], args, dev)
         return
     if args.splitkv_only:
         splitkv_only(args.splitkv_only, args, dev)
+        return
+    if args.sparse_only:
+        sparse_only(args.sparse_only, args, dev)
         return
 
     w = attn_inputs.WORKLOADS[5]
@@ -399,6 +484,13 @@ def main():
             splitkv[cw.name] = splitkv_case(cw, dev, steps=20, warmup=3)
         torch.cuda.synchronize()
 
+    # block-sparse forward (parity-tested separately)
+    blocksparse = {}
+    if not args.no_sweep:
+        for name, sw in attn_inputs.SPARSE_WORKLOADS.items():
+            blocksparse[sw.name] = sparse_case(sw, dev, steps=10, warmup=3)
+        torch.cuda.synchronize()
+
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
     value = step_flops / (ms_per_step / 1e3) / 1e12
     out = {
@@ -424,6 +516,7 @@ def main():
         "kernels": kernels,
         "forward_sweep": sweep,
         "splitkv": splitkv,
+        "blocksparse": blocksparse,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
         "torch": torch.__version__,

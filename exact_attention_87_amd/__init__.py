@@ -5,9 +5,10 @@ Every step of the computation runs in the library's HIP kernels; this module
 only marshals arguments.  PyTorch provides device memory and the stream.
 
 Raw entry points with the C names (``attn_fwd``, ``attn_bwd`` and its
-stages, ``attn_fwd_splitkv``, the workspace-size queries,
+stages, ``attn_fwd_splitkv``, ``attn_fwd_blocksparse``, the workspace-size queries,
 ``attn_status_str``, ``attn_abi_version``) take integer device addresses;
-``fwd``, ``fwd_splitkv`` and ``bwd`` are conveniences over torch tensors.  Importing this package never falls back to another implementation:
+``fwd``, ``fwd_splitkv``, ``fwd_blocksparse`` and ``bwd`` are conveniences over torch
+tensors.  Importing this package never falls back to another implementation:
 if the library is missing or fails to load, every call raises.
 """
 from __future__ import annotations
@@ -68,6 +69,10 @@ def lib():
         L.attn_fwd_splitkv_num_splits.restype = ci
         L.attn_fwd_splitkv_workspace_bytes.argtypes = [ci] * 7
         L.attn_fwd_splitkv_workspace_bytes.restype = sz
+        L.attn_fwd_blocksparse.argtypes = [vp] * 6 + [ci, vp] + [ci] * 6 + [cf, ci, vp]
+        L.attn_fwd_blocksparse.restype = ci
+        L.attn_fwd_blocksparse_workspace_bytes.argtypes = [ci, ci, ci]
+        L.attn_fwd_blocksparse_workspace_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -126,6 +131,22 @@ def attn_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
 
 def attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
     n = int(lib().attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, int(num_splits)))
+    return -1 if n == (1 << 64) - 1 else n
+
+
+SPARSE_BLOCK_Q = 128  # ATTN_SPARSE_BLOCK_Q
+SPARSE_BLOCK_K = 64   # ATTN_SPARSE_BLOCK_K
+
+
+def attn_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_heads, workspace, B, Hq, Hkv, N, d,
+                         causal, scale, dtype, stream) -> int:
+    return int(lib().attn_fwd_blocksparse(q, k, v, o, lse, block_mask, int(mask_heads), workspace,
+                                          B, Hq, Hkv, N, d, int(causal), float(scale), int(dtype),
+                                          stream))
+
+
+def attn_fwd_blocksparse_workspace_bytes(Hq, N, mask_heads) -> int:
+    n = int(lib().attn_fwd_blocksparse_workspace_bytes(Hq, N, int(mask_heads)))
     return -1 if n == (1 << 64) - 1 else n
 
 
@@ -213,6 +234,37 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
                           scale, num_splits, code, _stream_ptr(q))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_splitkv")
+    return out, lse
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None,
+                    out=None, lse=None, workspace=None):
+    """O, LSE of the block-sparse forward: block_mask is a device uint8 tensor
+    [1 or Hq, ceil(N/128), ceil(N/64)] over tiles of 128 queries x 64 keys."""
+    import torch
+
+    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nqb, nkt = -(-N // SPARSE_BLOCK_Q), -(-N // SPARSE_BLOCK_K)
+    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or block_mask.dim() != 3
+            or block_mask.shape[1:] != (nqb, nkt) or not block_mask.is_contiguous()):
+        raise ValueError(f"block_mask must be a contiguous device uint8 [1 or Hq, {nqb}, {nkt}]")
+    mh = block_mask.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    nbytes = attn_fwd_blocksparse_workspace_bytes(Hq, N, mh)
+    if nbytes < 0:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "attn_fwd_blocksparse_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+    st = attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), block_mask.data_ptr(), mh, workspace.data_ptr(), B,
+                              Hq, Hkv, N, d, causal, scale, _dtype_code(q), _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_blocksparse")
     return out, lse
 
 

@@ -71,12 +71,13 @@ struct FwdCfg {
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(64 * FwdCfg<D>::NW)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb, float c,
-    uint32_t qsign) {
+    uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
+    int mask_heads) {
   using Cfg = FwdCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
   constexpr int NB = Cfg::NB;  // 32-row query blocks per wave (each K/V fragment feeds NB products)
@@ -129,6 +130,30 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
     wtiles = min(ntiles, (q0 + 32 * NB - 1) / BC + 1);
   }
+  // Block-sparse: the key tiles of this query block's mask row (ascending,
+  // already cut at the causal diagonal), copied to LDS after the stages as
+  // 16-bit indices; loop position j then loads tile tiles[j].
+  unsigned short* tl = (unsigned short*)(smem + NBUF * 2 * TILEB);
+  if constexpr (SPARSE) {
+    const int64_t mrow = (int64_t)(mask_heads == 1 ? 0 : h) * nqb + qb;
+    ntiles = wtiles = tcount[mrow];
+    const int* src = tlist + mrow * ntiles_all;
+    for (int t = threadIdx.x; t < ntiles; t += 64 * NW) tl[t] = (unsigned short)src[t];
+    __syncthreads();
+  }
+  auto tile_of = [&](int j) -> int {
+    if constexpr (SPARSE)
+      return __builtin_amdgcn_readfirstlane((int)tl[j]);
+    else
+      return j;
+  };
+  // does this wave have visible keys in loop position j (< ntiles)?
+  auto wave_active = [&](int j) -> bool {
+    if constexpr (SPARSE)
+      return !CAUSAL || tile_of(j) * BC <= q0 + 32 * NB - 1;
+    else
+      return j < wtiles;
+  };
 
   // Direct global->LDS tile loads.  Wave w fills the 1 KiB pieces
   // w*PW .. w*PW+PW-1 of each tile; lane l of piece i lands at byte
@@ -145,7 +170,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   auto issue = [&](int j) {
     char* kt = smem + (j % NBUF) * 2 * TILEB;  // j % NBUF is the stage tile j uses
     char* vt = kt + TILEB;
-    const uint32_t tbase = (uint32_t)j * BC * ROWB;
+    const uint32_t tbase = (uint32_t)tile_of(j) * BC * ROWB;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       buf_load16_lds(rk, kt + (w * PW + i) * 1024, goff[i] + tbase);
@@ -169,7 +194,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   f32x16 oacc[NB][NMB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    ms[nb] = -__builtin_inff();
+    ms[nb] = -3.402823466e38f;  // finite: a row may see no key (block-sparse)
     lsum[nb] = 0.f;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) oacc[nb][mb] = f32x16{};
@@ -197,7 +222,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
     const char* kt = smem + BUF * 2 * TILEB;
     const char* vt = kt + TILEB;
     if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
-    if (j < wtiles) {
+    if (wave_active(j)) {
       // ---- S^T = K Q^T for the tile's two 32-key blocks and every query block
       u32x4 kfrag[2][NQC];
 #pragma unroll
@@ -218,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
       if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
       // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
       // and kept as a branch rather than flattened into selects)
-      const int k0 = j * BC;
+      const int k0 = tile_of(j) * BC;
       if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {
         __asm__ volatile("");
 #pragma unroll
@@ -319,7 +344,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
     const int qrow = q0 + nb * 32 + l32;
     const float lfull = lsum[nb] + xor32(lsum[nb]);
     if (qrow < N) {
-      const float inv = 1.0f / lfull;
+      const bool any = lfull > 0.f;  // else the row saw no key: O = 0, LSE = -inf
+      const float inv = any ? 1.0f / lfull : 0.f;
       __bf16* dst = O + qoff + (int64_t)qrow * D;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -331,7 +357,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
           v[1] = pack_bf16(oacc[nb][mb][4 * rg + 2] * inv, oacc[nb][mb][4 * rg + 3] * inv);
           *(u32x2*)(dst + d0) = v;
         }
-      if (hf == 0) LSE[(int64_t)bh * N + qrow] = (ms[nb] + __builtin_log2f(lfull)) * kLn2;
+      if (hf == 0)
+        LSE[(int64_t)bh * N + qrow] =
+            any ? (ms[nb] + __builtin_log2f(lfull)) * kLn2 : -__builtin_inff();
     }
   }
 }
@@ -376,12 +404,13 @@ struct PipeCfg {
   static constexpr size_t LDS = (size_t)4 * TILEB;  // K[2] | V[2]
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(64 * PipeCfg<D>::NW)
 __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_bf16_pipe_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb, float c,
-    uint32_t qsign) {
+    uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
+    int mask_heads) {
   using Cfg = PipeCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, TILEB = Cfg::TILEB, NW = Cfg::NW;
   constexpr int ROWB = D * 2;
@@ -425,6 +454,27 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
     wtiles = min(ntiles, (q0 + 31) / BC + 1);
   }
+  // Block-sparse tile list, as in fwd_bf16_kernel (LDS after the stages).
+  unsigned short* tl = (unsigned short*)(smem + 4 * TILEB);
+  if constexpr (SPARSE) {
+    const int64_t mrow = (int64_t)(mask_heads == 1 ? 0 : h) * nqb + qb;
+    ntiles = wtiles = tcount[mrow];
+    const int* src = tlist + mrow * ntiles_all;
+    for (int t = threadIdx.x; t < ntiles; t += 64 * NW) tl[t] = (unsigned short)src[t];
+    __syncthreads();
+  }
+  auto tile_of = [&](int j) -> int {
+    if constexpr (SPARSE)
+      return __builtin_amdgcn_readfirstlane((int)tl[j]);
+    else
+      return j;
+  };
+  auto wave_active = [&](int j) -> bool {  // j < ntiles
+    if constexpr (SPARSE)
+      return !CAUSAL || tile_of(j) * BC <= q0 + 31;
+    else
+      return j < wtiles;
+  };
 
   uint32_t goff[PW];
 #pragma unroll
@@ -435,7 +485,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     goff[i] = (uint32_t)(row * D + ch * 8) * 2;
   }
   auto issue = [&](__amdgpu_buffer_rsrc_t r, char* dst, int j) {
-    const uint32_t tbase = (uint32_t)j * BC * ROWB;
+    const uint32_t tbase = (uint32_t)tile_of(j) * BC * ROWB;
 #pragma unroll
     for (int i = 0; i < PW; ++i) buf_load16_lds(r, dst + (w * PW + i) * 1024, goff[i] + tbase);
   };
@@ -450,7 +500,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) voff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
 
-  float ms = -__builtin_inff(), lsum = 0.f;
+  float ms = -3.402823466e38f, lsum = 0.f;  // finite: a row may see no key (block-sparse)
   f32x16 oacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
@@ -490,8 +540,8 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     constexpr int BUF = decltype(bufc)::value;
     if (j + 1 < ntiles) issue(rv, vstage(BUF ^ 1), j + 1);
     if (j + 2 < ntiles) issue(rk, kstage(BUF), j + 2);
-    if (j < wtiles) {
-      const int k0 = j * BC;
+    if (wave_active(j)) {
+      const int k0 = tile_of(j) * BC;
       if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {
         __asm__ volatile("");
 #pragma unroll
@@ -505,7 +555,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
       }
       uint32_t pk[2][8];
       float tsum;
-      if (j + 1 < wtiles) {
+      if (j + 1 < ntiles && wave_active(j + 1)) {
         __builtin_amdgcn_sched_barrier(0);
         scores(kstage(BUF ^ 1), sn);
         tsum = softmax_exp(sc, ms, pk);
@@ -576,7 +626,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   if (ntiles > 1) issue(rk, kstage(1), 1);
   wait_vm_barrier<0>();
   f32x16 s0[2], s1[2];
-  if (0 < wtiles) scores(kstage(0), s0);
+  if (0 < ntiles && wave_active(0)) scores(kstage(0), s0);
   // tile 0's first step refills K stage 0 with K(2): every wave must be done
   // reading K(0) first
   wait_vm_barrier<0>();
@@ -589,7 +639,8 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   const int qrow = q0 + l32;
   const float lfull = lsum + xor32(lsum);
   if (qrow < N) {
-    const float inv = 1.0f / lfull;
+    const bool any = lfull > 0.f;  // else the row saw no key: O = 0, LSE = -inf
+    const float inv = any ? 1.0f / lfull : 0.f;
     __bf16* dst = O + qoff + (int64_t)qrow * D;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
@@ -601,7 +652,8 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
         v[1] = pack_bf16(oacc[mb][4 * rg + 2] * inv, oacc[mb][4 * rg + 3] * inv);
         *(u32x2*)(dst + d0) = v;
       }
-    if (hf == 0) LSE[(int64_t)bh * N + qrow] = (ms + __builtin_log2f(lfull)) * kLn2;
+    if (hf == 0)
+      LSE[(int64_t)bh * N + qrow] = any ? (ms + __builtin_log2f(lfull)) * kLn2 : -__builtin_inff();
   }
 }
 
@@ -683,39 +735,49 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, bool CAUSAL>
+// Dynamic LDS of a forward launch: the kernel's stages, plus the 16-bit tile
+// list of a block-sparse launch (one entry per key tile, rounded to 16 B).
+static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
+  return a.tlist ? ((size_t)((a.N + BC - 1) / BC) * 2 + 15) & ~(size_t)15 : 0;
+}
+
+template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bf16_pipe(const FwdArgs& a) {
+  static_assert(!SPARSE || (PipeCfg<D>::BR == kSparseBlockQ && PipeCfg<D>::BC == kSparseBlockK),
+                "block-sparse tiles are the forward's tiles");
   const int nqb = (a.N + PipeCfg<D>::BR - 1) / PipeCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const size_t lds = PipeCfg<D>::LDS;
-  const hipError_t e = allow_lds(fwd_bf16_pipe_kernel<D, CAUSAL>, lds);
+  const size_t lds = PipeCfg<D>::LDS + sparse_list_bytes(a, PipeCfg<D>::BC);
+  const hipError_t e = allow_lds(fwd_bf16_pipe_kernel<D, CAUSAL, SPARSE>, lds);
   if (e != hipSuccess) return e;
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CAUSAL>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)grid),
                      dim3(64 * PipeCfg<D>::NW), lds, a.stream, (const __bf16*)a.q,
                      (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.Hq, a.Hkv, a.N,
-                     nqb, c, qsign);
+                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bf16(const FwdArgs& a) {
   if constexpr ((D == 64 && ATTN_FWD_PIPE64) || (D == 128 && ATTN_FWD_PIPE128))
-    return launch_bf16_pipe<D, CAUSAL>(a);
+    return launch_bf16_pipe<D, CAUSAL, SPARSE>(a);
+  static_assert(!SPARSE || (FwdCfg<D>::BR == kSparseBlockQ && FwdCfg<D>::BC == kSparseBlockK),
+                "block-sparse tiles are the forward's tiles");
   const int nqb = (a.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const size_t lds = FwdCfg<D>::LDS;
-  const hipError_t e = allow_lds(fwd_bf16_kernel<D, CAUSAL>, lds);
+  const size_t lds = FwdCfg<D>::LDS + sparse_list_bytes(a, FwdCfg<D>::BC);
+  const hipError_t e = allow_lds(fwd_bf16_kernel<D, CAUSAL, SPARSE>, lds);
   if (e != hipSuccess) return e;
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * FwdCfg<D>::NW),
-                     lds, a.stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
-                     a.Hq, a.Hkv, a.N, nqb, c, qsign);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)grid),
+                     dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const __bf16*)a.q,
+                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.Hq, a.Hkv, a.N,
+                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads);
   return hipGetLastError();
 }
 
@@ -732,8 +794,13 @@ static hipError_t launch_f32(const FwdArgs& a) {
 
 hipError_t launch_fwd(const FwdArgs& a) {
   if (a.bf16) {
-    if (a.d == 64) return a.causal ? launch_bf16<64, true>(a) : launch_bf16<64, false>(a);
-    return a.causal ? launch_bf16<128, true>(a) : launch_bf16<128, false>(a);
+    if (a.tlist) {
+      if (a.d == 64)
+        return a.causal ? launch_bf16<64, true, true>(a) : launch_bf16<64, false, true>(a);
+      return a.causal ? launch_bf16<128, true, true>(a) : launch_bf16<128, false, true>(a);
+    }
+    if (a.d == 64) return a.causal ? launch_bf16<64, true, false>(a) : launch_bf16<64, false, false>(a);
+    return a.causal ? launch_bf16<128, true, false>(a) : launch_bf16<128, false, false>(a);
   }
   if (a.d == 64) return a.causal ? launch_f32<64, true>(a) : launch_f32<64, false>(a);
   return a.causal ? launch_f32<128, true>(a) : launch_f32<128, false>(a);

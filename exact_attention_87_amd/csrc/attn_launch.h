@@ -18,6 +18,12 @@ struct FwdArgs {
   float scale;
   bool bf16;
   hipStream_t stream;
+  // Block-sparse (bf16 only): per mask row (mask head, query block of 128
+  // rows) the number of active key tiles of 64 keys and their ascending
+  // indices, rows of ceil(N/64) entries.  Null for the dense forward.
+  const int* tlist = nullptr;
+  const int* tcount = nullptr;
+  int mask_heads = 0;
 };
 
 struct BwdArgs {
@@ -65,6 +71,11 @@ size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int nsplit);
 hipError_t launch_fwd_split(const SplitArgs& a);
 
 hipError_t launch_fwd(const FwdArgs& a);
+// Block-sparse forward: compacts the byte mask [mask_heads][ceil(N/128)]
+// [ceil(N/64)] into tile lists in the workspace, then runs the forward.
+constexpr int kSparseBlockQ = 128, kSparseBlockK = 64;
+size_t sparse_workspace_bytes(int Hq, int N, int mask_heads);
+hipError_t launch_fwd_sparse(const FwdArgs& a, const unsigned char* mask, void* workspace);
 // Bytes of the backward row-statistics workspace.
 size_t bwd_stats_bytes(int B, int Hq, int N);
 // Backward stages; each launches one kernel on a.stream.

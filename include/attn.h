@@ -181,6 +181,39 @@ int attn_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, i
 size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
                                         int num_splits);
 
+/*
+ * Block-sparse forward ("FlashAttention" paper story, block-sparse
+ * paragraph: a 0/1 mask over the grid of score blocks, whose zero blocks
+ * are never loaded or computed).  The blocks are the forward's tiles:
+ * ATTN_SPARSE_BLOCK_Q query rows by ATTN_SPARSE_BLOCK_K keys.
+ *   q, k, v, o, lse  as attn_fwd (bf16), square: N queries and N keys
+ *   block_mask  in   DEVICE bytes [mask_heads][ceil(N/128)][ceil(N/64)],
+ *                    row-major, any alignment; non-zero = block present.
+ *                    mask_heads is 1 (one mask for every head and batch) or
+ *                    Hq (one mask per query head, shared by the batch).
+ *   workspace        attn_fwd_blocksparse_workspace_bytes(Hq, N, mask_heads)
+ *                    bytes, caller owned, need not be initialised; holds the
+ *                    compacted list of present blocks of each mask row.
+ * Query i of head h sees key j iff
+ *   block_mask[h or 0][i / 128][j / 64] != 0  and  (causal == 0 or j <= i).
+ * A row that sees no key gets o = 0 and lse = -inf.  Two kernels run on
+ * `stream`: the mask compaction, then the forward.  Supported: ATTN_BF16,
+ * d in {64, 128}, N <= 2^21 (else ATTN_ERR_UNSUPPORTED).  mask_heads other
+ * than 1 or Hq, or a NULL mask, is ATTN_ERR_INVALID_ARG.  Every other
+ * convention is attn_fwd's.
+ */
+#define ATTN_SPARSE_BLOCK_Q 128
+#define ATTN_SPARSE_BLOCK_K 64
+attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const unsigned char* block_mask, int mask_heads, void* workspace,
+                                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                 attn_dtype dtype, void* stream);
+
+/* Bytes of workspace attn_fwd_blocksparse needs (a multiple of 256); 0 for
+ * N == 0; (size_t)-1 for Hq < 1, N outside [0, 2^21] or mask_heads other
+ * than 1 or Hq. */
+size_t attn_fwd_blocksparse_workspace_bytes(int Hq, int N, int mask_heads);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -26,6 +26,7 @@ def header_functions():
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
                                   "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd",
+                                  "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
                                   "attn_fwd_splitkv_workspace_bytes", "attn_status_str"]
 
@@ -221,3 +222,49 @@ def test_splitkv_workspace_bytes():
     assert w(2, 4, 2, 3, 1000, 128, 7) == 6 * 24 * 128 * 4 + 768
     assert w(1, 3, 2, 1, 100, 64, 1) == -1
     assert w(1, 4, 2, 1, 100, 80, 1) == -1
+
+
+# ---------------------------------------------------------------- block-sparse
+MASK = 0x10000000 * 11 + 3  # any alignment is fine for the byte mask
+
+
+def sparse(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, mask=MASK, mh=1, ws=WS, B=2, Hq=4, Hkv=2, N=1000, d=64,
+             causal=1, scale=0.125, dtype=ea.ATTN_BF16, stream=None)
+    a.update(kw)
+    return ea.attn_fwd_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["mh"],
+                                   a["ws"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                                   a["scale"], a["dtype"], a["stream"])
+
+
+SPARSE_INVALID = [
+    dict(q=None), dict(o=None), dict(lse=None), dict(ws=None), dict(mask=None), dict(mh=0),
+    dict(mh=2), dict(mh=3, Hq=4), dict(B=-1), dict(N=-1), dict(Hq=6, Hkv=4), dict(causal=3),
+    dict(scale=float("inf")), dict(o=Q), dict(ws=O + 256), dict(mask=O + 5), dict(mask=WS),
+    dict(mask=L + 100), dict(q=Q + 4),
+]
+
+
+@pytest.mark.parametrize("kw", SPARSE_INVALID, ids=[str(k) for k in SPARSE_INVALID])
+def test_blocksparse_rejects_bad_arguments(kw):
+    assert sparse(**kw) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_blocksparse_unsupported_and_empty():
+    assert sparse(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert sparse(d=96) == ea.ATTN_ERR_UNSUPPORTED
+    assert sparse(N=(1 << 21) + 1) == ea.ATTN_ERR_UNSUPPORTED
+    assert sparse(q=None, k=None, v=None, o=None, lse=None, mask=None, ws=None, N=0) == ea.ATTN_OK
+    assert sparse(q=None, k=None, v=None, o=None, lse=None, mask=None, ws=None, B=0) == ea.ATTN_OK
+    assert sparse(mh=4) != ea.ATTN_ERR_INVALID_ARG  # one mask per query head is accepted
+
+
+def test_blocksparse_workspace_bytes():
+    w = ea.attn_fwd_blocksparse_workspace_bytes
+    # counts [mask rows] int32 and lists [mask rows][ceil(N/64)] int32, each rounded to 256
+    assert w(4, 1000, 1) == 256 + 8 * 16 * 4
+    assert w(4, 1000, 4) == 256 + ((32 * 16 * 4 + 255) // 256) * 256
+    assert w(8, 16384, 8) == ((8 * 128 * 4 + 255) // 256) * 256 + 8 * 128 * 256 * 4
+    assert w(4, 0, 1) == 0
+    assert w(4, 100, 2) == -1
+    assert w(4, (1 << 21) + 1, 1) == -1
