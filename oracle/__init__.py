@@ -58,12 +58,14 @@ def _bind(path: str):
     lib.oracle_fwd_rows.argtypes = [d, d, d, i64p, c64, d, d] + dims
     u8p = ctypes.POINTER(ctypes.c_uint8)
     lib.oracle_fwd_blockmask.argtypes = [d, d, d, d, d, u8p, ci, ci, ci] + [ci] * 6 + [ci, cd]
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.oracle_fwd_varlen.argtypes = [d, d, d, d, d, i32p] + [ci] * 6 + [ci, cd]
     lib.oracle_fwd_blockwise.argtypes = [d, d, d, d, d] + dims + [ci, ci]
     lib.oracle_bwd.argtypes = [d] * 10 + dims
     lib.oracle_bwd_slices.argtypes = [d, d, d, d, i64p, c64, d, d, d] + dims
     lib.oracle_threads.argtypes = []
     for f in (lib.oracle_threads, lib.oracle_fwd, lib.oracle_fwd_bottom_right, lib.oracle_fwd_rows,
-              lib.oracle_fwd_blockmask,
+              lib.oracle_fwd_blockmask, lib.oracle_fwd_varlen,
               lib.oracle_fwd_blockwise, lib.oracle_bwd, lib.oracle_bwd_slices):
         f.restype = ci
     return lib
@@ -171,6 +173,24 @@ class Oracle:
                "oracle_fwd_blockmask")
         return o, lse
 
+    def fwd_varlen(self, q, k, v, cu_seqlens, causal: bool = False, scale: float | None = None):
+        """Packed variable-length forward: q [Hq, T, dk], k/v [Hkv, T, d], sequences
+        at token offsets cu_seqlens (0 = cu[0] <= ... <= cu[-1] = T), each attending
+        only within itself. Returns (O [Hq, T, dv], LSE [Hq, T]) in float64."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        if q.ndim != 3 or k.ndim != 3 or v.ndim != 3:
+            raise ValueError("varlen tensors are [H, T, d]")
+        _, Hq, Hkv, T, _, dk, dv = _shapes(q[None], k[None], v[None])
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        scale = default_scale(dk) if scale is None else float(scale)
+        o = np.empty((Hq, T, dv), np.float64)
+        lse = np.empty((Hq, T), np.float64)
+        _check(self.lib.oracle_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                          cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                          len(cu) - 1, Hq, Hkv, T, dk, dv, int(bool(causal)),
+                                          scale), "oracle_fwd_varlen")
+        return o, lse
+
     def fwd_rows(self, q, k, v, rows, causal: bool = False, scale: float | None = None):
         """Dense forward of selected flat rows ((b*Hq+h)*Nq+i). Returns (O [n,dv], LSE [n])."""
         q, k, v = _f64(q), _f64(k), _f64(v)
@@ -260,6 +280,7 @@ fwd_rows = _default.fwd_rows
 fwd_bottom_right = _default.fwd_bottom_right
 fwd_blockwise = _default.fwd_blockwise
 fwd_blockmask = _default.fwd_blockmask
+fwd_varlen = _default.fwd_varlen
 bwd = _default.bwd
 bwd_slices = _default.bwd_slices
 omp_threads = _default.omp_threads

@@ -238,6 +238,54 @@ int oracle_fwd_blockmask(const double* q, const double* k, const double* v, doub
 }
 
 /*
+ * Variable-length (packed) forward: nseq sequences laid end to end along the
+ * token axis, sequence s occupying tokens [cu[s], cu[s+1]) of T.  Each token
+ * attends only to keys of its own sequence (a document mask), with the
+ * causal rule inside the sequence.  q [Hq, T, dk], k [Hkv, T, dk],
+ * v [Hkv, T, dv]; o [Hq, T, dv], lse [Hq, T].  cu must be non-decreasing from
+ * 0 to T.  Every (sequence, head) is one dense problem (dense_row on that
+ * sequence's keys); an empty sequence has no rows.
+ */
+int oracle_fwd_varlen(const double* q, const double* k, const double* v, double* o, double* lse,
+                      const int32_t* cu, int nseq, int Hq, int Hkv, int T, int dk, int dv,
+                      int causal, double scale) {
+  int rc = check_args(1, Hq, Hkv, T, T, dk, dv);
+  if (rc) return rc;
+  if (nseq < 0 || (nseq == 0 && T != 0) || (nseq > 0 && (cu[0] != 0 || cu[nseq] != T)))
+    return ORACLE_BAD_ARG;
+  for (int s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s]) return ORACLE_BAD_ARG;
+  const int group = Hq / Hkv;
+  const int64_t rows = (int64_t)Hq * T;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* scores = (double*)malloc(sizeof(double) * (T > 0 ? T : 1));
+    if (!scores) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < rows; ++r) {
+        const int64_t h = r / T;
+        const int64_t t = r % T;
+        int s = 0;
+        while (cu[s + 1] <= t) ++s;  /* sequence holding token t */
+        const int64_t start = cu[s], len = (int64_t)cu[s + 1] - cu[s];
+        const int64_t i = t - start;  /* position inside the sequence */
+        const int64_t g = h / group;
+        const double* Kh = k + (g * T + start) * dk;
+        const double* Vh = v + (g * T + start) * dv;
+        dense_row(q + r * dk, Kh, Vh, visible_keys(i, len, causal), dk, dv, scale, scores,
+                  o + r * dv, lse + r);
+      }
+      free(scores);
+    }
+  }
+  return bad ? ORACLE_NO_MEM : ORACLE_OK;
+}
+
+/*
  * Dense forward on a chosen subset of rows.  rows[t] is the flat row index
  * (b * Hq + h) * Nq + i; o is [nrows, dv], lse is [nrows].  Used to check
  * sampled rows of large problems one by one.

@@ -15,6 +15,7 @@ import oracle
 import test_oracle_blockmask as pm
 import test_oracle_bwd as pb
 import test_oracle_fwd as pf
+import test_oracle_varlen as pv
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
@@ -26,7 +27,7 @@ MUTANTS = [
      "scores[j] = dot(qi, Kh + j * dk, dk);", 1),
     ("causal_excludes_diagonal", "const int64_t n = i + 1 + off;", "const int64_t n = i + off;", 1),
     ("causal_one_extra_key", "const int64_t n = i + 1 + off;", "const int64_t n = i + 2 + off;", 1),
-    ("gqa_modulo_map", "const int64_t g = h / group;", "const int64_t g = h % Hkv;", 7),
+    ("gqa_modulo_map", "const int64_t g = h / group;", "const int64_t g = h % Hkv;", 8),
     ("key_index_slip", "scores[j] = scale * dot(qi, Kh + j * dk, dk);",
      "scores[j] = scale * dot(qi, Kh + j, dk);", 1),
     ("value_transposed", "const double* vj = Vh + j * dv;", "const double* vj = Vh + j;", 1),
@@ -48,6 +49,10 @@ MUTANTS = [
     ("blockmask_head_zero", "const int64_t hm = (mask_heads == 1) ? 0 : h;",
      "const int64_t hm = 0;", 1),
     ("blockmask_ignores_causal", "if (causal && j > i) continue;", "", 1),
+    ("varlen_sequence_boundary", "while (cu[s + 1] <= t) ++s;", "while (cu[s + 1] < t) ++s;", 1),
+    ("varlen_global_position", "visible_keys(i, len, causal)", "visible_keys(t, len, causal)", 1),
+    ("varlen_kv_offset_dropped", "const double* Kh = k + (g * T + start) * dk;",
+     "const double* Kh = k + (g * T) * dk;", 1),
 ]
 
 
@@ -76,6 +81,8 @@ def run_pins(om):
         ("blockmask_full", lambda: pm.test_full_mask_is_the_dense_forward(om, True, 13, 4, 3)),
         ("blockmask_scipy", lambda: pm.test_matches_scipy_on_the_expanded_mask(om, False, 1)),
         ("blockmask_heads", lambda: pm.test_per_head_masks_act_head_by_head(om)),
+        ("varlen_scipy", lambda: pv.test_matches_scipy_with_a_document_mask(om, True, [5, 1, 9])),
+        ("varlen_single", lambda: pv.test_single_sequence_is_the_dense_forward(om, True)),
     ]
     failed = []
     for name, fn in pins:
