@@ -155,3 +155,54 @@ def sparse_mask(w: SparseWorkload, block_q: int = 128, block_k: int = 64):
     r = np.random.default_rng(w.seed)
     rand = r.random((w.Hq, nbq, nbk)) < w.density
     return (base[None] | rand).astype(np.uint8)
+
+
+# Packed variable-length batches: documents of different lengths laid end to
+# end, Q [Hq, T, d] and K/V [Hkv, T, d], with token offsets cu_seqlens.
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    Hq: int
+    Hkv: int
+    T: int
+    d: int
+    causal: bool
+    min_len: int
+    max_len: int
+    seed: int = 0
+
+
+VARLEN_WORKLOADS = {
+    "docs": VarlenWorkload("varlen_docs_bf16_Hq32_Hkv8_T16384_d128", 32, 8, 16384, 128, True,
+                           min_len=32, max_len=4096, seed=14),
+}
+
+
+def varlen_lengths(w: VarlenWorkload):
+    """Document lengths summing to w.T: log-uniform in [min_len, max_len]
+    (seeded), the last one cut to fit."""
+    import numpy as np
+
+    r = np.random.default_rng(w.seed)
+    lengths, total = [], 0
+    while total < w.T:
+        n = int(round(np.exp(r.uniform(np.log(w.min_len), np.log(w.max_len)))))
+        n = min(n, w.T - total)
+        lengths.append(n)
+        total += n
+    return lengths
+
+
+def make_varlen(Hq: int, Hkv: int, lengths, d: int, seed: int = 0):
+    """bf16 (q [Hq,T,d], k [Hkv,T,d], v [Hkv,T,d]) and int32 offsets cu_seqlens
+    for sequences of the given lengths, T = sum(lengths)."""
+    import numpy as np
+
+    T = int(sum(lengths))
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((Hq, T, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    return q, k, v, cu

@@ -18,8 +18,10 @@ kernel (durations from HIP events on the launch stream), every kernel's
 duration, a forward sweep over the other workloads, the split-K/V forward on
 the key/value-cache workloads (decode, append; GB/s against HBM), the
 block-sparse forward on a local + global + random block mask (TFLOP/s over
-the visible pairs, and the dense forward of the same shape beside it), and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+the visible pairs, and the dense forward of the same shape beside it), the
+packed variable-length forward on a document batch (and the same documents
+padded to the longest), and the fp64 CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -270,6 +272,66 @@ def sparse_case(sw, dev, steps, warmup):
             "speedup_vs_dense": round(ms_dense / ms, 2)}
 
 
+def varlen_case(vw, dev, steps, warmup):
+    """attn_fwd_varlen on a packed document batch, timed with HIP events, and
+    the same documents padded to the longest one through attn_fwd for
+    comparison.  TFLOP/s count the visible pairs of each document only."""
+    import torch
+
+    import attn_inputs
+    import exact_attention_87_amd as ea
+
+    lengths = attn_inputs.varlen_lengths(vw)
+    q, k, v, cu = (t.to(dev) for t in attn_inputs.make_varlen(vw.Hq, vw.Hkv, lengths, vw.d,
+                                                               seed=vw.seed))
+    mx = max(lengths)
+    o, lse = ea.fwd_varlen(q, k, v, cu, mx, causal=vw.causal)
+    nseq = len(lengths)
+    qp = torch.zeros((nseq, vw.Hq, mx, vw.d), device=dev, dtype=q.dtype)
+    kp = torch.zeros((nseq, vw.Hkv, mx, vw.d), device=dev, dtype=q.dtype)
+    vp_ = torch.zeros_like(kp)
+    for s_, (a, n) in enumerate(zip(cu.tolist()[:-1], lengths)):
+        qp[s_, :, :n] = q[:, a:a + n]
+        kp[s_, :, :n] = k[:, a:a + n]
+        vp_[s_, :, :n] = v[:, a:a + n]
+    op, lp = ea.fwd(qp, kp, vp_, causal=vw.causal)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(lambda: ea.fwd_varlen(q, k, v, cu, mx, causal=vw.causal, out=o, lse=lse))
+    ms_pad = timed(lambda: ea.fwd(qp, kp, vp_, causal=vw.causal, out=op, lse=lp))
+    pairs = sum(n * (n + 1) // 2 if vw.causal else n * n for n in lengths) * vw.Hq
+    tf = 4.0 * vw.d * pairs / (ms / 1e3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "sequences": nseq, "longest": mx, "padded_ms": round(ms_pad, 4),
+            "speedup_vs_padded": round(ms_pad / ms, 2)}
+
+
+def varlen_only(name, args, dev):
+    import attn_inputs
+
+    vw = attn_inputs.VARLEN_WORKLOADS[name]
+    r = varlen_case(vw, dev, args.steps, args.warmup)
+    print(json.dumps({
+        "metric": "packed variable-length attention forward TFLOP/s on 1 MI355X",
+        "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic", "detail": r,
+        "config": {"workload": vw.name, "Hq": vw.Hq, "Hkv": vw.Hkv, "T": vw.T, "d": vw.d,
+                   "causal": vw.causal, "seed": vw.seed}}), flush=True)
+
+
 def sparse_only(name, args, dev):
     import attn_inputs
 
@@ -316,6 +378,8 @@ def main():
                     help="time only the forward of workload ID (1-5) and print its JSON line")
     ap.add_argument("--sparse-only", default="", metavar="NAME",
                     help="time only the block-sparse forward of workload NAME (local_global)")
+    ap.add_argument("--varlen-only", default="", metavar="NAME",
+                    help="time only the packed variable-length forward of workload NAME (docs)")
     ap.add_argument("--splitkv-only", default="", metavar="NAME",
                     help="time only the split-K/V forward of cache workload NAME "
                          "(decode, append) and print its JSON line")
@@ -338,7 +402,7 @@ def main():
     dev = torch.device("cuda:0")
     ea.lib()  # fail loudly if the HIP library is missing
 
-    if args.fwd_only or args.splitkv_only or args.sparse_only:
+    if args.fwd_only or args.splitkv_only or args.sparse_only or args.varlen_only:
         calibration_copy(args.copy_mib, dev)
     if args.fwd_only:
         forward_only(attn_inputs.WORKLOADS[args.fwd_only], args, dev)
@@ -348,6 +412,9 @@ def main():
         return
     if args.sparse_only:
         sparse_only(args.sparse_only, args, dev)
+        return
+    if args.varlen_only:
+        varlen_only(args.varlen_only, args, dev)
         return
 
     w = attn_inputs.WORKLOADS[5]
@@ -491,6 +558,13 @@ def main():
             blocksparse[sw.name] = sparse_case(sw, dev, steps=10, warmup=3)
         torch.cuda.synchronize()
 
+    # packed variable-length forward (parity-tested separately)
+    varlen = {}
+    if not args.no_sweep:
+        for name, vw in attn_inputs.VARLEN_WORKLOADS.items():
+            varlen[vw.name] = varlen_case(vw, dev, steps=10, warmup=3)
+        torch.cuda.synchronize()
+
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
     value = step_flops / (ms_per_step / 1e3) / 1e12
     out = {
@@ -517,6 +591,7 @@ def main():
         "forward_sweep": sweep,
         "splitkv": splitkv,
         "blocksparse": blocksparse,
+        "varlen": varlen,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
         "torch": torch.__version__,

@@ -5,10 +5,11 @@ Every step of the computation runs in the library's HIP kernels; this module
 only marshals arguments.  PyTorch provides device memory and the stream.
 
 Raw entry points with the C names (``attn_fwd``, ``attn_bwd`` and its
-stages, ``attn_fwd_splitkv``, ``attn_fwd_blocksparse``, the workspace-size queries,
+stages, ``attn_fwd_splitkv``, ``attn_fwd_blocksparse``, ``attn_fwd_varlen``, the
+workspace-size queries,
 ``attn_status_str``, ``attn_abi_version``) take integer device addresses;
-``fwd``, ``fwd_splitkv``, ``fwd_blocksparse`` and ``bwd`` are conveniences over torch
-tensors.  Importing this package never falls back to another implementation:
+``fwd``, ``fwd_splitkv``, ``fwd_blocksparse``, ``fwd_varlen`` and ``bwd`` are
+conveniences over torch tensors.  Importing this package never falls back to another implementation:
 if the library is missing or fails to load, every call raises.
 """
 from __future__ import annotations
@@ -73,6 +74,8 @@ def lib():
         L.attn_fwd_blocksparse.restype = ci
         L.attn_fwd_blocksparse_workspace_bytes.argtypes = [ci, ci, ci]
         L.attn_fwd_blocksparse_workspace_bytes.restype = sz
+        L.attn_fwd_varlen.argtypes = [vp] * 6 + [ci] * 7 + [cf, ci, vp]
+        L.attn_fwd_varlen.restype = ci
         _lib = L
     return _lib
 
@@ -148,6 +151,12 @@ def attn_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_heads, workspace, B, 
 def attn_fwd_blocksparse_workspace_bytes(Hq, N, mask_heads) -> int:
     n = int(lib().attn_fwd_blocksparse_workspace_bytes(Hq, N, int(mask_heads)))
     return -1 if n == (1 << 64) - 1 else n
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, Hq, Hkv, T, d, causal, scale,
+                    dtype, stream) -> int:
+    return int(lib().attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, Hq, Hkv, T, d,
+                                     int(causal), float(scale), int(dtype), stream))
 
 
 # ------------------------------------------------------------ torch conveniences
@@ -265,6 +274,35 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
                               Hq, Hkv, N, d, causal, scale, _dtype_code(q), _stream_ptr(q))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_blocksparse")
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
+               scale: float | None = None, out=None, lse=None):
+    """O [Hq,T,d], LSE [Hq,T] of packed sequences: q [Hq,T,d], k/v [Hkv,T,d] (bf16),
+    cu_seqlens a device int32 tensor of nseq+1 token offsets."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor [H, T, d]")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    if k.shape != v.shape or k.shape[1:] != (T, d):
+        raise ValueError("k and v must be [Hkv, T, d] matching q")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a device int32 vector")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, T), device=q.device, dtype=torch.float32)
+    st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), Hq, Hkv, T,
+                         d, causal, scale, _dtype_code(q), _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_varlen")
     return out, lse
 
 

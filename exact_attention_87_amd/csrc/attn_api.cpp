@@ -350,3 +350,38 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ packed variable length
+extern "C" {
+
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens, int nseq, int max_seqlen, int Hq, int Hkv,
+                            int T, int d, int causal, float scale, attn_dtype dtype,
+                            void* stream) {
+  if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
+  bool empty = false;
+  attn_status st = check_shape(1, Hq, Hkv, T, d, causal, scale, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  if (nseq == 0 || T == 0 || max_seqlen == 0) return ATTN_OK;  // no rows to compute
+  const Sizes z = sizes(1, Hq, Hkv, T, d);
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}}, {{o, z.q}, {lse, z.l}});
+  if (st != ATTN_OK) return st;
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return ATTN_ERR_INVALID_ARG;
+  const Range rc{(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + ((size_t)nseq + 1) * 4};
+  if (overlaps(rc, Range{(uintptr_t)o, (uintptr_t)o + z.q}) ||
+      overlaps(rc, Range{(uintptr_t)lse, (uintptr_t)lse + z.l}))
+    return ATTN_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  // B = sequences and N = the longest sequence size the grid
+  attn::FwdArgs a{q, k, v, o, lse, nseq, Hq, Hkv, max_seqlen, d, causal == 1, scale, true,
+                  (hipStream_t)stream};
+  a.cu_seqlens = cu_seqlens;
+  a.T = T;
+  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"
+

@@ -71,13 +71,14 @@ struct FwdCfg {
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64 * FwdCfg<D>::NW)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb, float c,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
-    int mask_heads) {
+    int mask_heads, const int* __restrict__ cu_seqlens, int T) {
+  constexpr bool SPARSE = MODE == kFwdSparse;
   using Cfg = FwdCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
   constexpr int NB = Cfg::NB;  // 32-row query blocks per wave (each K/V fragment feeds NB products)
@@ -101,11 +102,30 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   const int id = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
   const int bh = id % BH;
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
-  const int g = h / (Hq / Hkv);
-  const int64_t qoff = (int64_t)bh * N * D;
-  const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
+  // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
+  // packed variable-length batch, one (sequence, head) of the packed tokens;
+  // offsets are in elements of Q/O, of K/V and in entries of LSE.
+  int N = Nmax, h;
+  int64_t qoff, kvoff, lbase;
+  if constexpr (MODE == kFwdVarlen) {
+    const int seq = bh / Hq;
+    h = bh - seq * Hq;
+    const int start = min(max(cu_seqlens[seq], 0), T);
+    const int end = min(max(cu_seqlens[seq + 1], start), T);
+    N = end - start;
+    if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
+    const int g = h / (Hq / Hkv);
+    qoff = ((int64_t)h * T + start) * D;
+    kvoff = ((int64_t)g * T + start) * D;
+    lbase = (int64_t)h * T + start;
+  } else {
+    const int b = bh / Hq;
+    h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    qoff = (int64_t)bh * N * D;
+    kvoff = (int64_t)(b * Hkv + g) * N * D;
+    lbase = (int64_t)bh * N;
+  }
   const int q0 = qb * BR + w * 32 * NB;  // first query row of this wave
 
   // Each (batch, head) slice is one raw buffer; rows past N read as zero.
@@ -358,7 +378,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
           *(u32x2*)(dst + d0) = v;
         }
       if (hf == 0)
-        LSE[(int64_t)bh * N + qrow] =
+        LSE[lbase + qrow] =
             any ? (ms[nb] + __builtin_log2f(lfull)) * kLn2 : -__builtin_inff();
     }
   }
@@ -404,13 +424,14 @@ struct PipeCfg {
   static constexpr size_t LDS = (size_t)4 * TILEB;  // K[2] | V[2]
 };
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64 * PipeCfg<D>::NW)
 __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_bf16_pipe_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N, int nqb, float c,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
-    int mask_heads) {
+    int mask_heads, const int* __restrict__ cu_seqlens, int T) {
+  constexpr bool SPARSE = MODE == kFwdSparse;
   using Cfg = PipeCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, TILEB = Cfg::TILEB, NW = Cfg::NW;
   constexpr int ROWB = D * 2;
@@ -430,11 +451,30 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   const int id = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
   const int bh = id % BH;
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
-  const int g = h / (Hq / Hkv);
-  const int64_t qoff = (int64_t)bh * N * D;
-  const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
+  // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
+  // packed variable-length batch, one (sequence, head) of the packed tokens;
+  // offsets are in elements of Q/O, of K/V and in entries of LSE.
+  int N = Nmax, h;
+  int64_t qoff, kvoff, lbase;
+  if constexpr (MODE == kFwdVarlen) {
+    const int seq = bh / Hq;
+    h = bh - seq * Hq;
+    const int start = min(max(cu_seqlens[seq], 0), T);
+    const int end = min(max(cu_seqlens[seq + 1], start), T);
+    N = end - start;
+    if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
+    const int g = h / (Hq / Hkv);
+    qoff = ((int64_t)h * T + start) * D;
+    kvoff = ((int64_t)g * T + start) * D;
+    lbase = (int64_t)h * T + start;
+  } else {
+    const int b = bh / Hq;
+    h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    qoff = (int64_t)bh * N * D;
+    kvoff = (int64_t)(b * Hkv + g) * N * D;
+    lbase = (int64_t)bh * N;
+  }
   const int q0 = qb * BR + w * 32;
 
   const uint32_t slice_bytes = (uint32_t)N * ROWB;
@@ -653,7 +693,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
         *(u32x2*)(dst + d0) = v;
       }
     if (hf == 0)
-      LSE[(int64_t)bh * N + qrow] = any ? (ms + __builtin_log2f(lfull)) * kLn2 : -__builtin_inff();
+      LSE[lbase + qrow] = any ? (ms + __builtin_log2f(lfull)) * kLn2 : -__builtin_inff();
   }
 }
 
@@ -741,43 +781,45 @@ static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
   return a.tlist ? ((size_t)((a.N + BC - 1) / BC) * 2 + 15) & ~(size_t)15 : 0;
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, int MODE>
 static hipError_t launch_bf16_pipe(const FwdArgs& a) {
+  constexpr bool SPARSE = MODE == kFwdSparse;
   static_assert(!SPARSE || (PipeCfg<D>::BR == kSparseBlockQ && PipeCfg<D>::BC == kSparseBlockK),
                 "block-sparse tiles are the forward's tiles");
   const int nqb = (a.N + PipeCfg<D>::BR - 1) / PipeCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
   const size_t lds = PipeCfg<D>::LDS + sparse_list_bytes(a, PipeCfg<D>::BC);
-  const hipError_t e = allow_lds(fwd_bf16_pipe_kernel<D, CAUSAL, SPARSE>, lds);
+  const hipError_t e = allow_lds(fwd_bf16_pipe_kernel<D, CAUSAL, MODE>, lds);
   if (e != hipSuccess) return e;
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid),
                      dim3(64 * PipeCfg<D>::NW), lds, a.stream, (const __bf16*)a.q,
                      (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.Hq, a.Hkv, a.N,
-                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads);
+                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, int MODE>
 static hipError_t launch_bf16(const FwdArgs& a) {
+  constexpr bool SPARSE = MODE == kFwdSparse;
   if constexpr ((D == 64 && ATTN_FWD_PIPE64) || (D == 128 && ATTN_FWD_PIPE128))
-    return launch_bf16_pipe<D, CAUSAL, SPARSE>(a);
+    return launch_bf16_pipe<D, CAUSAL, MODE>(a);
   static_assert(!SPARSE || (FwdCfg<D>::BR == kSparseBlockQ && FwdCfg<D>::BC == kSparseBlockK),
                 "block-sparse tiles are the forward's tiles");
   const int nqb = (a.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
   const size_t lds = FwdCfg<D>::LDS + sparse_list_bytes(a, FwdCfg<D>::BC);
-  const hipError_t e = allow_lds(fwd_bf16_kernel<D, CAUSAL, SPARSE>, lds);
+  const hipError_t e = allow_lds(fwd_bf16_kernel<D, CAUSAL, MODE>, lds);
   if (e != hipSuccess) return e;
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid),
                      dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const __bf16*)a.q,
                      (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.Hq, a.Hkv, a.N,
-                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads);
+                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 
@@ -794,13 +836,20 @@ static hipError_t launch_f32(const FwdArgs& a) {
 
 hipError_t launch_fwd(const FwdArgs& a) {
   if (a.bf16) {
+    // B is the number of sequences and N the longest one for a varlen launch
     if (a.tlist) {
       if (a.d == 64)
-        return a.causal ? launch_bf16<64, true, true>(a) : launch_bf16<64, false, true>(a);
-      return a.causal ? launch_bf16<128, true, true>(a) : launch_bf16<128, false, true>(a);
+        return a.causal ? launch_bf16<64, true, kFwdSparse>(a) : launch_bf16<64, false, kFwdSparse>(a);
+      return a.causal ? launch_bf16<128, true, kFwdSparse>(a) : launch_bf16<128, false, kFwdSparse>(a);
     }
-    if (a.d == 64) return a.causal ? launch_bf16<64, true, false>(a) : launch_bf16<64, false, false>(a);
-    return a.causal ? launch_bf16<128, true, false>(a) : launch_bf16<128, false, false>(a);
+    if (a.cu_seqlens) {
+      if (a.d == 64)
+        return a.causal ? launch_bf16<64, true, kFwdVarlen>(a) : launch_bf16<64, false, kFwdVarlen>(a);
+      return a.causal ? launch_bf16<128, true, kFwdVarlen>(a) : launch_bf16<128, false, kFwdVarlen>(a);
+    }
+    if (a.d == 64)
+      return a.causal ? launch_bf16<64, true, kFwdDense>(a) : launch_bf16<64, false, kFwdDense>(a);
+    return a.causal ? launch_bf16<128, true, kFwdDense>(a) : launch_bf16<128, false, kFwdDense>(a);
   }
   if (a.d == 64) return a.causal ? launch_f32<64, true>(a) : launch_f32<64, false>(a);
   return a.causal ? launch_f32<128, true>(a) : launch_f32<128, false>(a);

@@ -24,7 +24,16 @@ struct FwdArgs {
   const int* tlist = nullptr;
   const int* tcount = nullptr;
   int mask_heads = 0;
+  // Packed variable-length (bf16 only): sequence s is tokens
+  // [cu_seqlens[s], cu_seqlens[s+1]) of T; B is then the number of sequences
+  // and N the longest sequence.  Null for a batched problem.
+  const int* cu_seqlens = nullptr;
+  int T = 0;
 };
+
+// Forward kernel variants: every tile, a block-sparse tile list, or packed
+// variable-length sequences.
+enum FwdMode { kFwdDense = 0, kFwdSparse = 1, kFwdVarlen = 2 };
 
 struct BwdArgs {
   const void* q;

@@ -214,6 +214,33 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
  * than 1 or Hq. */
 size_t attn_fwd_blocksparse_workspace_bytes(int Hq, int N, int mask_heads);
 
+/*
+ * Packed variable-length forward: nseq sequences of different lengths laid
+ * end to end along the token axis (no padding), every token attending only
+ * to keys of its own sequence, causally within it if causal = 1.
+ *   q, o        [Hq,  T, d]  bf16, token-major within each head
+ *   k, v        [Hkv, T, d]  bf16
+ *   lse         [Hq,  T]     fp32
+ *   cu_seqlens  DEVICE int32 [nseq + 1], 4-byte aligned: sequence s is tokens
+ *               [cu_seqlens[s], cu_seqlens[s+1]); the caller guarantees
+ *               0 = cu_seqlens[0] <= ... <= cu_seqlens[nseq] = T.  The kernel
+ *               clamps every offset into [0, T], so inconsistent offsets
+ *               cannot read or write outside the tensors.
+ *   max_seqlen  host int, at least the longest sequence (it sizes the grid;
+ *               rows of a sequence beyond max_seqlen are not computed),
+ *               at most T.
+ * Each (sequence, head) is the attention of attn_fwd on that sequence alone;
+ * the sequences' key/value ranges are addressed through their own buffer
+ * descriptors, so no work is spent on other sequences' keys.  A sequence of
+ * length 0 has no rows.  Supported: ATTN_BF16, d in {64, 128}, T <= 2^22,
+ * nseq * Hq <= 2^24.  nseq == 0, T == 0 or max_seqlen == 0 launches nothing.
+ * Every other convention is attn_fwd's.
+ */
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens, int nseq, int max_seqlen, int Hq, int Hkv,
+                            int T, int d, int causal, float scale, attn_dtype dtype,
+                            void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

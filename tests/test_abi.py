@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                                   "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
-                                  "attn_fwd_splitkv_workspace_bytes", "attn_status_str"]
+                                  "attn_fwd_splitkv_workspace_bytes", "attn_fwd_varlen",
+                                  "attn_status_str"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -268,3 +269,40 @@ def test_blocksparse_workspace_bytes():
     assert w(4, 0, 1) == 0
     assert w(4, 100, 2) == -1
     assert w(4, (1 << 21) + 1, 1) == -1
+
+
+# ---------------------------------------------------------------- packed variable length
+CU = 0x10000000 * 12 + 4
+
+
+def varlen(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, cu=CU, nseq=3, maxlen=500, Hq=4, Hkv=2, T=1000, d=64,
+             causal=1, scale=0.125, dtype=ea.ATTN_BF16, stream=None)
+    a.update(kw)
+    return ea.attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["nseq"],
+                              a["maxlen"], a["Hq"], a["Hkv"], a["T"], a["d"], a["causal"],
+                              a["scale"], a["dtype"], a["stream"])
+
+
+VARLEN_INVALID = [
+    dict(q=None), dict(o=None), dict(lse=None), dict(cu=None), dict(cu=CU + 2), dict(nseq=-1),
+    dict(maxlen=-1), dict(maxlen=1001), dict(T=-1), dict(Hq=6, Hkv=4), dict(causal=2),
+    dict(scale=float("nan")), dict(o=Q + 64), dict(lse=O), dict(cu=O + 8), dict(cu=L + 4),
+    dict(k=K + 8),
+]
+
+
+@pytest.mark.parametrize("kw", VARLEN_INVALID, ids=[str(k) for k in VARLEN_INVALID])
+def test_varlen_rejects_bad_arguments(kw):
+    assert varlen(**kw) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_varlen_unsupported_and_empty():
+    assert varlen(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert varlen(d=80) == ea.ATTN_ERR_UNSUPPORTED
+    assert varlen(T=(1 << 22) + 1, maxlen=10) == ea.ATTN_ERR_UNSUPPORTED
+    assert varlen(nseq=(1 << 23), Hq=4) == ea.ATTN_ERR_UNSUPPORTED
+    none = dict(q=None, k=None, v=None, o=None, lse=None, cu=None)
+    assert varlen(nseq=0, **none) == ea.ATTN_OK
+    assert varlen(T=0, maxlen=0, **none) == ea.ATTN_OK
+    assert varlen(maxlen=0, **none) == ea.ATTN_OK
