@@ -25,8 +25,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Online softmax: the running maximum only moves when a tile's maximum
 // exceeds it by more than kTau (base-2 units), so probabilities stay below
 // 2^kTau = kSumMax; a lane whose tile sum passes kSumMax takes the max path.
-constexpr float kTau = 8.0f;
-constexpr float kSumMax = 256.0f;
+// Any kTau keeps the result: O and LSE use the same maximum, P keeps bf16's
+// relative precision at any magnitude, and the fp32 accumulators stay far
+// from overflow (at most 2^15 x N x |v|).  A large kTau makes the max path
+// rare for extreme logits; 15 keeps p within fp16's range as well.
+#ifndef ATTN_TAU
+#define ATTN_TAU 15
+#endif
+static_assert(ATTN_TAU >= 1 && ATTN_TAU <= 30, "rescale threshold");
+constexpr float kTau = (float)ATTN_TAU;
+constexpr float kSumMax = (float)(1u << ATTN_TAU);
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From& x) {
