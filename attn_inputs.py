@@ -5,8 +5,9 @@ none of the attention arithmetic.  Tests, the smoke check and the benchmark
 use it to feed the same values to the HIP library and to the fp64 oracle.
 
 Recipe: one torch CPU ``Generator`` seeded per workload; draw order Q, K, V,
-dO; every tensor iid N(0, 1) in fp32; for bf16 workloads each value is rounded
-to bf16 (round-to-nearest-even), and both sides consume the rounded values.
+dO; every tensor iid N(0, 1) in fp32; for bf16 (fp16) workloads each value is
+rounded to bf16 (fp16) round-to-nearest-even, and both sides consume the
+rounded values.
 A query multiplier (a power of two, so exact) scales Q to produce extreme
 logits.
 """
@@ -48,7 +49,7 @@ WORKLOADS = {
 
 
 def torch_dtype(name: str) -> torch.dtype:
-    return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
+    return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[name]
 
 
 def make(B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
@@ -98,13 +99,14 @@ CACHE_WORKLOADS = {
 
 
 def make_cache(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int = 0,
-               q_mult: float = 1.0):
-    """Draw bf16 (q [B,Hq,Nq,d], k [B,Hkv,Nk,d], v [B,Hkv,Nk,d]) as CPU tensors."""
+               q_mult: float = 1.0, dtype: str = "bf16"):
+    """Draw (q [B,Hq,Nq,d], k [B,Hkv,Nk,d], v [B,Hkv,Nk,d]) as CPU tensors (bf16 or fp16)."""
+    td = torch_dtype(dtype)
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    q = torch.randn((B, Hq, Nq, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
-    k = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((B, Hq, Nq, d), generator=g, dtype=torch.float32).to(td)
+    k = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(td)
+    v = torch.randn((B, Hkv, Nk, d), generator=g, dtype=torch.float32).to(td)
     if q_mult != 1.0:
         q = q * q_mult  # power of two: exact
     return q, k, v
@@ -193,16 +195,17 @@ def varlen_lengths(w: VarlenWorkload):
     return lengths
 
 
-def make_varlen(Hq: int, Hkv: int, lengths, d: int, seed: int = 0):
-    """bf16 (q [Hq,T,d], k [Hkv,T,d], v [Hkv,T,d]) and int32 offsets cu_seqlens
-    for sequences of the given lengths, T = sum(lengths)."""
+def make_varlen(Hq: int, Hkv: int, lengths, d: int, seed: int = 0, dtype: str = "bf16"):
+    """(q [Hq,T,d], k [Hkv,T,d], v [Hkv,T,d]) in bf16 or fp16 and int32 offsets
+    cu_seqlens for sequences of the given lengths, T = sum(lengths)."""
     import numpy as np
 
+    td = torch_dtype(dtype)
     T = int(sum(lengths))
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    q = torch.randn((Hq, T, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
-    k = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
-    v = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((Hq, T, d), generator=g, dtype=torch.float32).to(td)
+    k = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32).to(td)
+    v = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32).to(td)
     cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
     return q, k, v, cu

@@ -28,6 +28,7 @@ ATTN_ERR_UNSUPPORTED_DEVICE = 3
 ATTN_ERR_HIP = 4
 ATTN_F32 = 0
 ATTN_BF16 = 1
+ATTN_F16 = 2
 
 _lib = None
 
@@ -165,9 +166,12 @@ def _dtype_code(t) -> int:
 
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_F16
     if t.dtype == torch.float32:
         return ATTN_F32
-    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16, torch.float16 or "
+                    "torch.float32")
 
 
 def _check_qkv(q, k, v):

@@ -16,7 +16,7 @@ SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_splitkv.hip", "
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
     # The direct global->LDS loads set M0 in inline assembly; no other code in
@@ -25,15 +25,31 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles; returns the path of the library."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (one hipcc per source, in parallel, then a link);
+    returns the path of the library."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    with tempfile.TemporaryDirectory(prefix="attn_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        jobs = min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            outs = list(pool.map(_run, cmds))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
+    out = "\n".join(o for o in outs if o.strip())
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)

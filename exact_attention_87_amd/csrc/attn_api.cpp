@@ -48,7 +48,7 @@ attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float 
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   // Limits of the kernels' 32-bit grid, row and byte offsets: one (batch,
   // head) slice stays below 1 GiB.
@@ -80,7 +80,7 @@ attn_status check_buffers(std::initializer_list<Buf> ins, std::initializer_list<
 }
 
 struct Sizes {
-  size_t q, kv, l, st;  // bytes of [B,Hq,N,d] and [B,Hkv,N,d] bf16, [B,Hq,N] fp32, statistics
+  size_t q, kv, l, st;  // bytes of [B,Hq,N,d] and [B,Hkv,N,d] 16-bit, [B,Hq,N] fp32, statistics
 };
 
 Sizes sizes(int B, int Hq, int Hkv, int N, int d) {
@@ -96,10 +96,10 @@ attn_status bwd_common(int B, int Hq, int Hkv, int N, int d, int causal, float s
   bool empty = false;
   attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (empty) return ATTN_OK;  // a->N stays 0
   a->B = B, a->Hq = Hq, a->Hkv = Hkv, a->N = N, a->d = d;
-  a->causal = causal == 1, a->scale = scale, a->bf16 = true;
+  a->causal = causal == 1, a->scale = scale, a->dtype = (attn::Dtype)dtype;
   a->stream = (hipStream_t)stream;
   return ATTN_OK;
 }
@@ -131,7 +131,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_INVALID_ARG;
-  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t es = dtype == ATTN_F32 ? 4 : 2;
   const size_t qbytes = (size_t)B * Hq * N * d * es;
   const size_t kvbytes = (size_t)B * Hkv * N * d * es;
   const size_t lbytes = (size_t)B * Hq * N * sizeof(float);
@@ -144,7 +144,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
   st = check_device();
   if (st != ATTN_OK) return st;
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, dtype == ATTN_BF16,
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dtype,
                   (hipStream_t)stream};
   return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -152,7 +152,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype) {
   bool empty = false;
   if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
-  if (dtype != ATTN_BF16) return (size_t)-1;
+  if (dtype == ATTN_F32) return (size_t)-1;
   if (empty) return 0;
   const size_t bytes = attn::bwd_stats_bytes(B, Hq, N);
   return (bytes + 255) & ~(size_t)255;
@@ -244,10 +244,10 @@ attn_status split_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causa
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   if (num_splits < 0) return ATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   // 32-bit offsets: one key/value slice and one head group's query rows
   // stay below 1 GiB; the grid stays below 2^31 workgroups.
   if ((int64_t)B * Hq > (1 << 24) || Nq > (1 << 22) || Nk > (1 << 22)) return ATTN_ERR_UNSUPPORTED;
@@ -294,8 +294,9 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  attn::SplitArgs a{q,  k,  v,  o,  lse, workspace,       B,     Hq,        Hkv,
-                    Nq, Nk, d, causal == 1, scale, num_splits, (hipStream_t)stream};
+  attn::SplitArgs a{q,  k,  v, o,           lse,   workspace,  B,
+                    Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dtype,
+                    (hipStream_t)stream};
   return attn::launch_fwd_split(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -322,7 +323,7 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
   attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
   if (!(mask_heads == 1 || mask_heads == Hq)) return ATTN_ERR_INVALID_ARG;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (N > (1 << 21)) return ATTN_ERR_UNSUPPORTED;  // the tile list lives in LDS
   if (empty) return ATTN_OK;
   const size_t nqb = ((size_t)N + ATTN_SPARSE_BLOCK_Q - 1) / ATTN_SPARSE_BLOCK_Q;
@@ -343,7 +344,7 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
     if (overlaps(rm, r)) return ATTN_ERR_INVALID_ARG;
   st = check_device();
   if (st != ATTN_OK) return st;
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, true,
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dtype,
                   (hipStream_t)stream};
   a.mask_heads = mask_heads;
   return attn::launch_fwd_sparse(a, block_mask, workspace) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -362,7 +363,7 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   bool empty = false;
   attn_status st = check_shape(1, Hq, Hkv, T, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
   if (nseq == 0 || T == 0 || max_seqlen == 0) return ATTN_OK;  // no rows to compute
   const Sizes z = sizes(1, Hq, Hkv, T, d);
@@ -376,8 +377,8 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
   st = check_device();
   if (st != ATTN_OK) return st;
   // B = sequences and N = the longest sequence size the grid
-  attn::FwdArgs a{q, k, v, o, lse, nseq, Hq, Hkv, max_seqlen, d, causal == 1, scale, true,
-                  (hipStream_t)stream};
+  attn::FwdArgs a{q, k, v, o, lse, nseq, Hq, Hkv, max_seqlen, d, causal == 1, scale,
+                  (attn::Dtype)dtype, (hipStream_t)stream};
   a.cu_seqlens = cu_seqlens;
   a.T = T;
   return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

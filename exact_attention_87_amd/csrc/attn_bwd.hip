@@ -53,9 +53,9 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 __host__ __device__ constexpr int stat_rows(int N) { return (N + 63) / 64 * 64; }
 
 // ---------------------------------------------------------------- row statistics
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
-                                                      const __bf16* __restrict__ dO,
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
+                                                      const T* __restrict__ dO,
                                                       const float* __restrict__ LSE,
                                                       float* __restrict__ stats, int N, int Np,
                                                       int64_t nslices) {
@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
     const int64_t row = slice * N + i;
     const u32x4 a = *(const u32x4*)(O + row * D + part * 8);
     const u32x4 b = *(const u32x4*)(dO + row * D + part * 8);
-    const bf16x8 av = bitcast<bf16x8>(a), bv = bitcast<bf16x8>(b);
+    using V8 = typename Elem<T>::v8;
+    const V8 av = bitcast<V8>(a), bv = bitcast<V8>(b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)av[e], (float)bv[e], acc);
   }
@@ -97,14 +98,15 @@ struct DkdvCfg {
   static constexpr size_t LDS = (size_t)NBUF * STAGEB;
 };
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D>::WPE, DkdvCfg<D>::WPE)))
-void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                     const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                     const float* __restrict__ stats, __bf16* __restrict__ dK,
-                     __bf16* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c,
+void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                     const T* __restrict__ V, const T* __restrict__ dO,
+                     const float* __restrict__ stats, T* __restrict__ dK,
+                     T* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c,
                      float dk_scale, uint32_t qsign) {
   using Cfg = DkdvCfg<D>;
+  using V8 = typename Elem<T>::v8;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
   constexpr int STAGEB = Cfg::STAGEB;
   constexpr int ROWB = D * 2;
@@ -132,15 +134,15 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const uint32_t slice_bytes = (uint32_t)N * ROWB;
 
   // K^T and V^T operands of this wave's 32 keys, resident (zero past N).
-  bf16x8 kreg[NQC], vreg[NQC];
+  V8 kreg[NQC], vreg[NQC];
   {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
       const uint32_t off = (uint32_t)(krow * D + cc * 16 + hf * 8) * 2;
-      kreg[cc] = bitcast<bf16x8>(buf_load16(rk, off) ^ qsign);  // scale's sign rides on K here
-      vreg[cc] = bitcast<bf16x8>(buf_load16(rv, off));
+      kreg[cc] = bitcast<V8>(buf_load16(rk, off) ^ qsign);  // scale's sign rides on K here
+      vreg[cc] = bitcast<V8>(buf_load16(rv, off));
     }
   }
   f32x16 dkacc[NMB], dvacc[NMB];
@@ -230,8 +232,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     sacc = f32x16{};
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
-      sacc = mfma32(bitcast<bf16x8>(qa[cc]), kreg[cc], sacc);
-      pacc = mfma32(bitcast<bf16x8>(da[cc]), vreg[cc], pacc);
+      sacc = mfma32(bitcast<V8>(qa[cc]), kreg[cc], sacc);
+      pacc = mfma32(bitcast<V8>(da[cc]), vreg[cc], pacc);
     }
   };
   auto phaseV = [&](const float* lse2, int qbase, int qfirst, bool diag, const f32x16& sacc,
@@ -254,28 +256,28 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       float dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * rg + e] * pacc[4 * rg + e];
-      pk[2 * rg] = pack_bf16(pv[4 * rg], pv[4 * rg + 1]);
-      pk[2 * rg + 1] = pack_bf16(pv[4 * rg + 2], pv[4 * rg + 3]);
-      dsk[2 * rg] = pack_bf16(dsv[0], dsv[1]);
-      dsk[2 * rg + 1] = pack_bf16(dsv[2], dsv[3]);
+      pk[2 * rg] = pack2<T>(pv[4 * rg], pv[4 * rg + 1]);
+      pk[2 * rg + 1] = pack2<T>(pv[4 * rg + 2], pv[4 * rg + 3]);
+      dsk[2 * rg] = pack2<T>(dsv[0], dsv[1]);
+      dsk[2 * rg + 1] = pack2<T>(dsv[2], dsv[3]);
     }
   };
   auto phaseC = [&](const char* qtile, const char* dotile, int qbase, const uint32_t (&pk)[8],
                     const uint32_t (&dsk)[8]) {
 #pragma unroll
     for (int cp = 0; cp < 2; ++cp) {
-      const bf16x8 pb = bitcast<bf16x8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
-      const bf16x8 sb =
-          bitcast<bf16x8>(u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
+      const V8 pb = bitcast<V8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
+      const V8 sb =
+          bitcast<V8>(u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
       const int rows = (qbase + 16 * cp) * ROWB;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
         const u32x2 a0 = lds_read_tr(dotile + rows + troff[0][mb]);
         const u32x2 a1 = lds_read_tr(dotile + rows + troff[1][mb]);
-        dvacc[mb] = mfma32(bitcast<bf16x8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, dvacc[mb]);
+        dvacc[mb] = mfma32(bitcast<V8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, dvacc[mb]);
         const u32x2 b0 = lds_read_tr(qtile + rows + troff[0][mb]);
         const u32x2 b1 = lds_read_tr(qtile + rows + troff[1][mb]);
-        dkacc[mb] = mfma32(bitcast<bf16x8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
+        dkacc[mb] = mfma32(bitcast<V8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
       }
     }
   };
@@ -329,18 +331,18 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   // ---- store dK = scale * (dK^T)^T (Q was not sign-flipped), dV
   // (lane: key krow; element r: feature)
   if (krow < N) {
-    __bf16* dkp = dK + kvoff + (int64_t)krow * D;
-    __bf16* dvp = dV + kvoff + (int64_t)krow * D;
+    T* dkp = dK + kvoff + (int64_t)krow * D;
+    T* dvp = dV + kvoff + (int64_t)krow * D;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d0 = mb * 32 + rg * 8 + hf * 4;
         u32x2 kv, vv;
-        kv[0] = pack_bf16(dkacc[mb][4 * rg] * dk_scale, dkacc[mb][4 * rg + 1] * dk_scale);
-        kv[1] = pack_bf16(dkacc[mb][4 * rg + 2] * dk_scale, dkacc[mb][4 * rg + 3] * dk_scale);
-        vv[0] = pack_bf16(dvacc[mb][4 * rg], dvacc[mb][4 * rg + 1]);
-        vv[1] = pack_bf16(dvacc[mb][4 * rg + 2], dvacc[mb][4 * rg + 3]);
+        kv[0] = pack2<T>(dkacc[mb][4 * rg] * dk_scale, dkacc[mb][4 * rg + 1] * dk_scale);
+        kv[1] = pack2<T>(dkacc[mb][4 * rg + 2] * dk_scale, dkacc[mb][4 * rg + 3] * dk_scale);
+        vv[0] = pack2<T>(dvacc[mb][4 * rg], dvacc[mb][4 * rg + 1]);
+        vv[1] = pack2<T>(dvacc[mb][4 * rg + 2], dvacc[mb][4 * rg + 3]);
         *(u32x2*)(dkp + d0) = kv;
         *(u32x2*)(dvp + d0) = vv;
       }
@@ -358,13 +360,14 @@ struct DqCfg {
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<D>::WPE, DqCfg<D>::WPE)))
-void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                   const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
-                   const float* __restrict__ stats, __bf16* __restrict__ dQ, int Hq, int Hkv,
+void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                   const T* __restrict__ V, const T* __restrict__ dO,
+                   const float* __restrict__ stats, T* __restrict__ dQ, int Hq, int Hkv,
                    int N, int nqb, float c, float qscale, uint32_t qsign) {
   using Cfg = DqCfg<D>;
+  using V8 = typename Elem<T>::v8;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
   constexpr int ROWB = D * 2;
   constexpr int PW = TILEB / 1024 / 4;
@@ -393,15 +396,15 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   const uint32_t slice_bytes = (uint32_t)N * ROWB;
 
   // Q^T and dO^T operands and this lane's row statistics, resident.
-  bf16x8 qreg[NQC], doreg[NQC];
+  V8 qreg[NQC], doreg[NQC];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + qoff, slice_bytes);
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
       const uint32_t off = (uint32_t)(qrow * D + cc * 16 + hf * 8) * 2;
-      qreg[cc] = bitcast<bf16x8>(buf_load16(rq, off) ^ qsign);
-      doreg[cc] = bitcast<bf16x8>(buf_load16(rdo, off));
+      qreg[cc] = bitcast<V8>(buf_load16(rq, off) ^ qsign);
+      doreg[cc] = bitcast<V8>(buf_load16(rdo, off));
     }
   }
   const float* st = stats + (int64_t)bh * 2 * Np;
@@ -471,8 +474,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         pacc[kbk] = pinit;
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc) {
-          sacc[kbk] = mfma32(bitcast<bf16x8>(ka[cc]), qreg[cc], sacc[kbk]);
-          pacc[kbk] = mfma32(bitcast<bf16x8>(va[cc]), doreg[cc], pacc[kbk]);
+          sacc[kbk] = mfma32(bitcast<V8>(ka[cc]), qreg[cc], sacc[kbk]);
+          pacc[kbk] = mfma32(bitcast<V8>(va[cc]), doreg[cc], pacc[kbk]);
         }
       }
       float pv[2][16];
@@ -496,7 +499,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
       for (int kbk = 0; kbk < 2; ++kbk)
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
-          dsk[kbk][r >> 1] = pack_bf16(pv[kbk][r] * pacc[kbk][r], pv[kbk][r + 1] * pacc[kbk][r + 1]);
+          dsk[kbk][r >> 1] = pack2<T>(pv[kbk][r] * pacc[kbk][r], pv[kbk][r + 1] * pacc[kbk][r + 1]);
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -507,8 +510,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             const int rows = (kbk * 32 + cp * 16) * ROWB;
             const u32x2 lo = lds_read_tr(kt + rows + troff[0][mb]);
             const u32x2 hi = lds_read_tr(kt + rows + troff[1][mb]);
-            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            const bf16x8 sb = bitcast<bf16x8>(u32x4{dsk[kbk][4 * cp], dsk[kbk][4 * cp + 1],
+            const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const V8 sb = bitcast<V8>(u32x4{dsk[kbk][4 * cp], dsk[kbk][4 * cp + 1],
                                                     dsk[kbk][4 * cp + 2], dsk[kbk][4 * cp + 3]});
             dqacc[mb] = mfma32(a, sb, dqacc[mb]);
           }
@@ -536,15 +539,15 @@ void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
   }
 
   if (qok) {
-    __bf16* dst = dQ + qoff + (int64_t)qrow * D;
+    T* dst = dQ + qoff + (int64_t)qrow * D;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d0 = mb * 32 + rg * 8 + hf * 4;
         u32x2 v;
-        v[0] = pack_bf16(dqacc[mb][4 * rg] * qscale, dqacc[mb][4 * rg + 1] * qscale);
-        v[1] = pack_bf16(dqacc[mb][4 * rg + 2] * qscale, dqacc[mb][4 * rg + 3] * qscale);
+        v[0] = pack2<T>(dqacc[mb][4 * rg] * qscale, dqacc[mb][4 * rg + 1] * qscale);
+        v[1] = pack2<T>(dqacc[mb][4 * rg + 2] * qscale, dqacc[mb][4 * rg + 3] * qscale);
         *(u32x2*)(dst + d0) = v;
       }
   }
@@ -566,62 +569,76 @@ static BwdConsts bwd_consts(float scale) {
   return BwdConsts{c, (scale < 0.f) ? 0x80008000u : 0u};
 }
 
-template <int D>
+template <typename T, int D>
 static hipError_t pre_t(const BwdArgs& a) {
   constexpr int RPB = 256 / (D / 8);
   const int Np = stat_rows(a.N);
   const int64_t nslices = (int64_t)a.B * a.Hq;
   const int64_t grid = (nslices * Np + RPB - 1) / RPB;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                     (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, a.stats, a.N, Np, nslices);
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                     (const T*)a.o, (const T*)a.dout, a.lse, a.stats, a.N, Np, nslices);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 static hipError_t dkdv_t(const BwdArgs& a) {
   using Cfg = DkdvCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
   const int nkb = (a.N + Cfg::BKV - 1) / Cfg::BKV;
   const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
-  const hipError_t e = allow_lds(bwd_dkdv_kernel<D, CAUSAL>, Cfg::LDS);
+  const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL>, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
-                     a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                     (const __bf16*)a.dout, a.stats, (__bf16*)a.dk, (__bf16*)a.dv, a.Hq, a.Hkv, a.N,
-                     nkb, k.c, a.scale, k.qsign);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
+                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                     a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv, a.N, nkb, k.c, a.scale, k.qsign);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 static hipError_t dq_t(const BwdArgs& a) {
   using Cfg = DqCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
   const int nqb = (a.N + Cfg::BR - 1) / Cfg::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const hipError_t e = allow_lds(bwd_dq_kernel<D, CAUSAL>, Cfg::LDS);
+  const hipError_t e = allow_lds(bwd_dq_kernel<T, D, CAUSAL>, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
-                     a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                     (const __bf16*)a.dout, a.stats, (__bf16*)a.dq, a.Hq, a.Hkv, a.N, nqb, k.c,
-                     a.scale, k.qsign);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
+                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                     a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N, nqb, k.c, a.scale, k.qsign);
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t bwd_pre_for(const BwdArgs& a) {
+  return a.d == 64 ? pre_t<T, 64>(a) : pre_t<T, 128>(a);
+}
+template <typename T>
+static hipError_t bwd_dkdv_for(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dkdv_t<T, 64, true>(a) : dkdv_t<T, 64, false>(a);
+  return a.causal ? dkdv_t<T, 128, true>(a) : dkdv_t<T, 128, false>(a);
+}
+template <typename T>
+static hipError_t bwd_dq_for(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dq_t<T, 64, true>(a) : dq_t<T, 64, false>(a);
+  return a.causal ? dq_t<T, 128, true>(a) : dq_t<T, 128, false>(a);
+}
+
 hipError_t launch_bwd_pre(const BwdArgs& a) {
-  if (!a.bf16) return hipErrorNotSupported;
-  return a.d == 64 ? pre_t<64>(a) : pre_t<128>(a);
+  if (a.dtype == kBF16) return bwd_pre_for<__bf16>(a);
+  if (a.dtype == kF16) return bwd_pre_for<_Float16>(a);
+  return hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a) {
-  if (!a.bf16) return hipErrorNotSupported;
-  if (a.d == 64) return a.causal ? dkdv_t<64, true>(a) : dkdv_t<64, false>(a);
-  return a.causal ? dkdv_t<128, true>(a) : dkdv_t<128, false>(a);
+  if (a.dtype == kBF16) return bwd_dkdv_for<__bf16>(a);
+  if (a.dtype == kF16) return bwd_dkdv_for<_Float16>(a);
+  return hipErrorNotSupported;
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a) {
-  if (!a.bf16) return hipErrorNotSupported;
-  if (a.d == 64) return a.causal ? dq_t<64, true>(a) : dq_t<64, false>(a);
-  return a.causal ? dq_t<128, true>(a) : dq_t<128, false>(a);
+  if (a.dtype == kBF16) return bwd_dq_for<__bf16>(a);
+  if (a.dtype == kF16) return bwd_dq_for<_Float16>(a);
+  return hipErrorNotSupported;
 }
 
 }  // namespace attn

@@ -11,6 +11,8 @@ namespace attn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -49,6 +51,23 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product with fp16 operands (same operand and result layout).
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// 16-bit element types of the matrix-core kernels: T is __bf16 or _Float16.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  using v8 = bf16x8;
+};
+template <>
+struct Elem<_Float16> {
+  using v8 = f16x8;
+};
+
 // Accumulator row held in element r of lane l of a 32x32 MFMA result.
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
@@ -78,13 +97,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return bitcast<uint32_t>(v);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// acc + lo + hi of a packed bf16 pair, in fp32 (v_dot2 with (1, 1)).
-__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(pair), bitcast<bf16x2>(0x3f803f80u), acc,
-                                         false);
+// Two fp32 -> packed fp16x2 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 v;
+  v[0] = (_Float16)lo;
+  v[1] = (_Float16)hi;
+  return bitcast<uint32_t>(v);
 }
+
+// Two fp32 -> two packed 16-bit values of type T.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (__is_same(T, _Float16))
+    return pack_f16(lo, hi);
+  else
+    return pack_bf16(lo, hi);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // LDS tile swizzle.  A tile row (one key or query) of D bf16 is D/8 chunks of
 // 16 bytes; logical chunk ch of row `row` is stored at chunk ch ^ swz(row).

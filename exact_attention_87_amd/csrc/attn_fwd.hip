@@ -71,14 +71,15 @@ struct FwdCfg {
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
 
-template <int D, bool CAUSAL, int MODE>
+template <typename T, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64 * FwdCfg<D>::NW)
-__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf16_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mfma_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
-    int mask_heads, const int* __restrict__ cu_seqlens, int T) {
+    int mask_heads, const int* __restrict__ cu_seqlens, int ntok) {
   constexpr bool SPARSE = MODE == kFwdSparse;
+  using V8 = typename Elem<T>::v8;
   using Cfg = FwdCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
   constexpr int NB = Cfg::NB;  // 32-row query blocks per wave (each K/V fragment feeds NB products)
@@ -110,14 +111,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   if constexpr (MODE == kFwdVarlen) {
     const int seq = bh / Hq;
     h = bh - seq * Hq;
-    const int start = min(max(cu_seqlens[seq], 0), T);
-    const int end = min(max(cu_seqlens[seq + 1], start), T);
+    const int start = min(max(cu_seqlens[seq], 0), ntok);
+    const int end = min(max(cu_seqlens[seq + 1], start), ntok);
     N = end - start;
     if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
     const int g = h / (Hq / Hkv);
-    qoff = ((int64_t)h * T + start) * D;
-    kvoff = ((int64_t)g * T + start) * D;
-    lbase = (int64_t)h * T + start;
+    qoff = ((int64_t)h * ntok + start) * D;
+    kvoff = ((int64_t)g * ntok + start) * D;
+    lbase = (int64_t)h * ntok + start;
   } else {
     const int b = bh / Hq;
     h = bh - b * Hq;
@@ -135,12 +136,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
 
   // Q^T operands (one per 32-row block), resident for the whole key loop.
-  bf16x8 qreg[NB][NQC];
+  V8 qreg[NB][NQC];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc)
-      qreg[nb][cc] = bitcast<bf16x8>(
+      qreg[nb][cc] = bitcast<V8>(
           buf_load16(rq, (uint32_t)((q0 + nb * 32 + l32) * D + cc * 16 + hf * 8) * 2) ^ qsign);
 
   const int ntiles_all = (N + BC - 1) / BC;
@@ -229,7 +230,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -m));
         const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -m));
-        pk[kbk][r >> 1] = pack_bf16(p0, p1);
+        pk[kbk][r >> 1] = pack2<T>(p0, p1);
         tsum += p0 + p1;
       }
     return tsum;
@@ -258,7 +259,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
           sacc[nb][kbk] = f32x16{};
 #pragma unroll
           for (int cc = 0; cc < NQC; ++cc)
-            sacc[nb][kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[nb][cc], sacc[nb][kbk]);
+            sacc[nb][kbk] = mfma32(bitcast<V8>(kfrag[kbk][cc]), qreg[nb][cc], sacc[nb][kbk]);
         }
       if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
       // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
@@ -323,10 +324,10 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
             const int rows = (kbk * 32 + cp * 16) * ROWB;
             const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
             const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
-            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              const bf16x8 bp = bitcast<bf16x8>(u32x4{pk[nb][kbk][4 * cp], pk[nb][kbk][4 * cp + 1],
+              const V8 bp = bitcast<V8>(u32x4{pk[nb][kbk][4 * cp], pk[nb][kbk][4 * cp + 1],
                                                       pk[nb][kbk][4 * cp + 2], pk[nb][kbk][4 * cp + 3]});
               oacc[nb][mb] = mfma32(a, bp, oacc[nb][mb]);
             }
@@ -366,15 +367,15 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
     if (qrow < N) {
       const bool any = lfull > 0.f;  // else the row saw no key: O = 0, LSE = -inf
       const float inv = any ? 1.0f / lfull : 0.f;
-      __bf16* dst = O + qoff + (int64_t)qrow * D;
+      T* dst = O + qoff + (int64_t)qrow * D;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int d0 = mb * 32 + rg * 8 + hf * 4;
           u32x2 v;
-          v[0] = pack_bf16(oacc[nb][mb][4 * rg] * inv, oacc[nb][mb][4 * rg + 1] * inv);
-          v[1] = pack_bf16(oacc[nb][mb][4 * rg + 2] * inv, oacc[nb][mb][4 * rg + 3] * inv);
+          v[0] = pack2<T>(oacc[nb][mb][4 * rg] * inv, oacc[nb][mb][4 * rg + 1] * inv);
+          v[1] = pack2<T>(oacc[nb][mb][4 * rg + 2] * inv, oacc[nb][mb][4 * rg + 3] * inv);
           *(u32x2*)(dst + d0) = v;
         }
       if (hf == 0)
@@ -390,7 +391,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_bf
 // wave instead of only across waves.  K and V have separate double-buffered
 // LDS stages: K(j+2) and V(j+1) are loaded during tile j (K(j) was consumed
 // one tile earlier, by the look-ahead score product), so one barrier per tile
-// still suffices.  Same arithmetic and results as fwd_bf16_kernel.
+// still suffices.  Same arithmetic and results as fwd_mfma_kernel.
 #ifndef ATTN_FWD_PIPE64
 #define ATTN_FWD_PIPE64 0
 #endif
@@ -424,14 +425,15 @@ struct PipeCfg {
   static constexpr size_t LDS = (size_t)4 * TILEB;  // K[2] | V[2]
 };
 
-template <int D, bool CAUSAL, int MODE>
+template <typename T, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64 * PipeCfg<D>::NW)
-__attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_bf16_pipe_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
+__attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_mfma_pipe_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
-    int mask_heads, const int* __restrict__ cu_seqlens, int T) {
+    int mask_heads, const int* __restrict__ cu_seqlens, int ntok) {
   constexpr bool SPARSE = MODE == kFwdSparse;
+  using V8 = typename Elem<T>::v8;
   using Cfg = PipeCfg<D>;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, TILEB = Cfg::TILEB, NW = Cfg::NW;
   constexpr int ROWB = D * 2;
@@ -459,14 +461,14 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   if constexpr (MODE == kFwdVarlen) {
     const int seq = bh / Hq;
     h = bh - seq * Hq;
-    const int start = min(max(cu_seqlens[seq], 0), T);
-    const int end = min(max(cu_seqlens[seq + 1], start), T);
+    const int start = min(max(cu_seqlens[seq], 0), ntok);
+    const int end = min(max(cu_seqlens[seq + 1], start), ntok);
     N = end - start;
     if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
     const int g = h / (Hq / Hkv);
-    qoff = ((int64_t)h * T + start) * D;
-    kvoff = ((int64_t)g * T + start) * D;
-    lbase = (int64_t)h * T + start;
+    qoff = ((int64_t)h * ntok + start) * D;
+    kvoff = ((int64_t)g * ntok + start) * D;
+    lbase = (int64_t)h * ntok + start;
   } else {
     const int b = bh / Hq;
     h = bh - b * Hq;
@@ -482,10 +484,10 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
 
-  bf16x8 qreg[NQC];
+  V8 qreg[NQC];
 #pragma unroll
   for (int cc = 0; cc < NQC; ++cc)
-    qreg[cc] = bitcast<bf16x8>(buf_load16(rq, (uint32_t)((q0 + l32) * D + cc * 16 + hf * 8) * 2) ^ qsign);
+    qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)((q0 + l32) * D + cc * 16 + hf * 8) * 2) ^ qsign);
 
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all;
@@ -494,7 +496,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
     wtiles = min(ntiles, (q0 + 31) / BC + 1);
   }
-  // Block-sparse tile list, as in fwd_bf16_kernel (LDS after the stages).
+  // Block-sparse tile list, as in fwd_mfma_kernel (LDS after the stages).
   unsigned short* tl = (unsigned short*)(smem + 4 * TILEB);
   if constexpr (SPARSE) {
     const int64_t mrow = (int64_t)(mask_heads == 1 ? 0 : h) * nqb + qb;
@@ -557,7 +559,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
       sacc[kbk] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < NQC; ++cc)
-        sacc[kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
+        sacc[kbk] = mfma32(bitcast<V8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
     }
   };
   auto softmax_exp = [&](const f32x16 (&sacc)[2], float m, uint32_t (&pk)[2][8]) {
@@ -568,7 +570,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -m));
         const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -m));
-        pk[kbk][r >> 1] = pack_bf16(p0, p1);
+        pk[kbk][r >> 1] = pack2<T>(p0, p1);
         tsum += p0 + p1;
       }
     return tsum;
@@ -646,8 +648,8 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
             const int rows = (kbk * 32 + cp * 16) * ROWB;
             const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
             const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
-            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            const bf16x8 bp = bitcast<bf16x8>(
+            const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const V8 bp = bitcast<V8>(
                 u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
             oacc[mb] = mfma32(a, bp, oacc[mb]);
           }
@@ -681,15 +683,15 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   if (qrow < N) {
     const bool any = lfull > 0.f;  // else the row saw no key: O = 0, LSE = -inf
     const float inv = any ? 1.0f / lfull : 0.f;
-    __bf16* dst = O + qoff + (int64_t)qrow * D;
+    T* dst = O + qoff + (int64_t)qrow * D;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d0 = mb * 32 + rg * 8 + hf * 4;
         u32x2 v;
-        v[0] = pack_bf16(oacc[mb][4 * rg] * inv, oacc[mb][4 * rg + 1] * inv);
-        v[1] = pack_bf16(oacc[mb][4 * rg + 2] * inv, oacc[mb][4 * rg + 3] * inv);
+        v[0] = pack2<T>(oacc[mb][4 * rg] * inv, oacc[mb][4 * rg + 1] * inv);
+        v[1] = pack2<T>(oacc[mb][4 * rg + 2] * inv, oacc[mb][4 * rg + 3] * inv);
         *(u32x2*)(dst + d0) = v;
       }
     if (hf == 0)
@@ -781,46 +783,66 @@ static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
   return a.tlist ? ((size_t)((a.N + BC - 1) / BC) * 2 + 15) & ~(size_t)15 : 0;
 }
 
-template <int D, bool CAUSAL, int MODE>
-static hipError_t launch_bf16_pipe(const FwdArgs& a) {
+template <typename T, int D, bool CAUSAL, int MODE>
+static hipError_t launch_pipe(const FwdArgs& a) {
   constexpr bool SPARSE = MODE == kFwdSparse;
   static_assert(!SPARSE || (PipeCfg<D>::BR == kSparseBlockQ && PipeCfg<D>::BC == kSparseBlockK),
                 "block-sparse tiles are the forward's tiles");
   const int nqb = (a.N + PipeCfg<D>::BR - 1) / PipeCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
   const size_t lds = PipeCfg<D>::LDS + sparse_list_bytes(a, PipeCfg<D>::BC);
-  const hipError_t e = allow_lds(fwd_bf16_pipe_kernel<D, CAUSAL, MODE>, lds);
+  const hipError_t e = allow_lds(fwd_mfma_pipe_kernel<T, D, CAUSAL, MODE>, lds);
   if (e != hipSuccess) return e;
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid),
-                     dim3(64 * PipeCfg<D>::NW), lds, a.stream, (const __bf16*)a.q,
-                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.Hq, a.Hkv, a.N,
-                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads, a.cu_seqlens, a.T);
+  hipLaunchKernelGGL((fwd_mfma_pipe_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
+                     dim3(64 * PipeCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
+                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
+                     a.tcount, a.mask_heads, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int MODE>
-static hipError_t launch_bf16(const FwdArgs& a) {
+template <typename T, int D, bool CAUSAL, int MODE>
+static hipError_t launch_mfma(const FwdArgs& a) {
   constexpr bool SPARSE = MODE == kFwdSparse;
   if constexpr ((D == 64 && ATTN_FWD_PIPE64) || (D == 128 && ATTN_FWD_PIPE128))
-    return launch_bf16_pipe<D, CAUSAL, MODE>(a);
+    return launch_pipe<T, D, CAUSAL, MODE>(a);
   static_assert(!SPARSE || (FwdCfg<D>::BR == kSparseBlockQ && FwdCfg<D>::BC == kSparseBlockK),
                 "block-sparse tiles are the forward's tiles");
   const int nqb = (a.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
   const size_t lds = FwdCfg<D>::LDS + sparse_list_bytes(a, FwdCfg<D>::BC);
-  const hipError_t e = allow_lds(fwd_bf16_kernel<D, CAUSAL, MODE>, lds);
+  const hipError_t e = allow_lds(fwd_mfma_kernel<T, D, CAUSAL, MODE>, lds);
   if (e != hipSuccess) return e;
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, MODE>), dim3((unsigned)grid),
-                     dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const __bf16*)a.q,
-                     (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.Hq, a.Hkv, a.N,
-                     nqb, c, qsign, a.tlist, a.tcount, a.mask_heads, a.cu_seqlens, a.T);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
+                     dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
+                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
+                     a.tcount, a.mask_heads, a.cu_seqlens, a.T);
   return hipGetLastError();
+}
+
+// Runtime (head dim, causal, mode) -> kernel instantiation for element type T.
+template <typename T>
+static hipError_t dispatch_mfma(const FwdArgs& a) {
+  // B is the number of sequences and N the longest one for a varlen launch
+  const int mode = a.tlist ? kFwdSparse : a.cu_seqlens ? kFwdVarlen : kFwdDense;
+  auto pick = [&](auto dc, auto cc) -> hipError_t {
+    constexpr int D = decltype(dc)::value;
+    constexpr bool C = decltype(cc)::value;
+    if (mode == kFwdSparse) return launch_mfma<T, D, C, kFwdSparse>(a);
+    if (mode == kFwdVarlen) return launch_mfma<T, D, C, kFwdVarlen>(a);
+    return launch_mfma<T, D, C, kFwdDense>(a);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  if (a.d == 64) return a.causal ? pick(I64{}, Yes{}) : pick(I64{}, No{});
+  return a.causal ? pick(I128{}, Yes{}) : pick(I128{}, No{});
 }
 
 template <int D, bool CAUSAL>
@@ -835,22 +857,8 @@ static hipError_t launch_f32(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.bf16) {
-    // B is the number of sequences and N the longest one for a varlen launch
-    if (a.tlist) {
-      if (a.d == 64)
-        return a.causal ? launch_bf16<64, true, kFwdSparse>(a) : launch_bf16<64, false, kFwdSparse>(a);
-      return a.causal ? launch_bf16<128, true, kFwdSparse>(a) : launch_bf16<128, false, kFwdSparse>(a);
-    }
-    if (a.cu_seqlens) {
-      if (a.d == 64)
-        return a.causal ? launch_bf16<64, true, kFwdVarlen>(a) : launch_bf16<64, false, kFwdVarlen>(a);
-      return a.causal ? launch_bf16<128, true, kFwdVarlen>(a) : launch_bf16<128, false, kFwdVarlen>(a);
-    }
-    if (a.d == 64)
-      return a.causal ? launch_bf16<64, true, kFwdDense>(a) : launch_bf16<64, false, kFwdDense>(a);
-    return a.causal ? launch_bf16<128, true, kFwdDense>(a) : launch_bf16<128, false, kFwdDense>(a);
-  }
+  if (a.dtype == kBF16) return dispatch_mfma<__bf16>(a);
+  if (a.dtype == kF16) return dispatch_mfma<_Float16>(a);
   if (a.d == 64) return a.causal ? launch_f32<64, true>(a) : launch_f32<64, false>(a);
   return a.causal ? launch_f32<128, true>(a) : launch_f32<128, false>(a);
 }

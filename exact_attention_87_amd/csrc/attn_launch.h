@@ -7,6 +7,9 @@
 
 namespace attn {
 
+// Element types, numbered as the ABI's attn_dtype.
+enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -16,15 +19,15 @@ struct FwdArgs {
   int B, Hq, Hkv, N, d;
   bool causal;
   float scale;
-  bool bf16;
+  Dtype dtype;
   hipStream_t stream;
-  // Block-sparse (bf16 only): per mask row (mask head, query block of 128
+  // Block-sparse (16-bit types only): per mask row (mask head, query block of 128
   // rows) the number of active key tiles of 64 keys and their ascending
   // indices, rows of ceil(N/64) entries.  Null for the dense forward.
   const int* tlist = nullptr;
   const int* tcount = nullptr;
   int mask_heads = 0;
-  // Packed variable-length (bf16 only): sequence s is tokens
+  // Packed variable-length (16-bit types only): sequence s is tokens
   // [cu_seqlens[s], cu_seqlens[s+1]) of T; B is then the number of sequences
   // and N the longest sequence.  Null for a batched problem.
   const int* cu_seqlens = nullptr;
@@ -49,11 +52,11 @@ struct BwdArgs {
   int B, Hq, Hkv, N, d;
   bool causal;
   float scale;
-  bool bf16;
+  Dtype dtype;
   hipStream_t stream;
 };
 
-// Split-K/V forward (bf16): queries [B,Hq,Nq,d], keys/values [B,Hkv,Nk,d],
+// Split-K/V forward (16-bit types): queries [B,Hq,Nq,d], keys/values [B,Hkv,Nk,d],
 // bottom-right aligned causal mask; workspace holds the per-split partials.
 struct SplitArgs {
   const void* q;
@@ -66,6 +69,7 @@ struct SplitArgs {
   bool causal;
   float scale;
   int num_splits;  // requested; <= 0 picks one from the shape
+  Dtype dtype;     // kBF16 or kF16
   hipStream_t stream;
 };
 

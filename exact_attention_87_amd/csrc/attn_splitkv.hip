@@ -56,13 +56,14 @@ struct SplitCfg {
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fwd_split_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ Opart, float* __restrict__ Lpart, int Hq, int Hkv, int Nq, int Nk,
     int nrb, int nsplit, int split_len, int64_t rows_total, float c, uint32_t qsign) {
   using Cfg = SplitCfg<D>;
+  using V8 = typename Elem<T>::v8;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, TILEB = Cfg::TILEB, NW = Cfg::NW, NBUF = Cfg::NBUF;
   constexpr int ROWB = D * 2;
   constexpr int PW = TILEB / 1024 / NW;
@@ -97,10 +98,10 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, (uint32_t)Nk * ROWB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, (uint32_t)Nk * ROWB);
 
-  bf16x8 qreg[NQC];
+  V8 qreg[NQC];
 #pragma unroll
   for (int cc = 0; cc < NQC; ++cc)
-    qreg[cc] = bitcast<bf16x8>(buf_load16(rq, (uint32_t)(r * D + cc * 16 + hf * 8) * 2) ^ qsign);
+    qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)(r * D + cc * 16 + hf * 8) * 2) ^ qsign);
 
   // Key range of the split.  With the causal mask the workgroup stops after
   // the last key any of its rows sees, and each wave after its own last key;
@@ -169,7 +170,7 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
       for (int rr = 0; rr < 16; rr += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][rr], c, -ms));
         const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][rr + 1], c, -ms));
-        pk[kbk][rr >> 1] = pack_bf16(p0, p1);
+        pk[kbk][rr >> 1] = pack2<T>(p0, p1);
         tsum += p0 + p1;
       }
     return tsum;
@@ -192,7 +193,7 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
         sacc[kbk] = f32x16{};
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc)
-          sacc[kbk] = mfma32(bitcast<bf16x8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
+          sacc[kbk] = mfma32(bitcast<V8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
       }
       // mask: keys past the split / past Nk, and (causal) keys after the row's diagonal
       const int k0 = kbeg + j * BC;
@@ -238,8 +239,8 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
             const int rows = (kbk * 32 + cp * 16) * ROWB;
             const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
             const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
-            const bf16x8 a = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            const bf16x8 bp = bitcast<bf16x8>(
+            const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            const V8 bp = bitcast<V8>(
                 u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
             oacc[mb] = mfma32(a, bp, oacc[mb]);
           }
@@ -292,10 +293,10 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
 // SG whose loads are all issued before any is used, so a row costs a few
 // memory round trips whatever the split count.  A row no split saw gets
 // O = 0, LSE = -inf.
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restrict__ Opart,
                                                            const float* __restrict__ Lpart,
-                                                           __bf16* __restrict__ O,
+                                                           T* __restrict__ O,
                                                            float* __restrict__ LSE, int nsplit,
                                                            int64_t rows) {
   constexpr int TPR = D / 4;   // lanes per row
@@ -333,8 +334,8 @@ __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restri
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   u32x2 outv;
-  outv[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
-  outv[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+  outv[0] = pack2<T>(acc[0] * inv, acc[1] * inv);
+  outv[1] = pack2<T>(acc[2] * inv, acc[3] * inv);
   *(u32x2*)(O + row * D + part * 4) = outv;
   if (part == 0) LSE[row] = wsum > 0.f ? m + logf(wsum) : ninf;
 }
@@ -375,7 +376,7 @@ size_t split_workspace_bytes(int B, int Hq, int Nq, int d, int nsplit) {
   return obytes + lbytes;
 }
 
-template <int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 static hipError_t split_t(const SplitArgs& a) {
   const SplitPlan p = split_plan(a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d, a.num_splits);
   const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
@@ -385,23 +386,29 @@ static hipError_t split_t(const SplitArgs& a) {
   float c = fabsf(a.scale) * kLog2e;
   if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
   const int64_t grid = (int64_t)p.nrb * p.nsplit * a.B * a.Hkv;
-  hipError_t e = allow_lds(fwd_split_kernel<D, CAUSAL>, SplitCfg<D>::LDS);
+  hipError_t e = allow_lds(fwd_split_kernel<T, D, CAUSAL>, SplitCfg<D>::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fwd_split_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(256),
-                     SplitCfg<D>::LDS, a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
-                     (const __bf16*)a.v, opart, lpart, a.Hq, a.Hkv, a.Nq, a.Nk, p.nrb, p.nsplit,
+  hipLaunchKernelGGL((fwd_split_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256),
+                     SplitCfg<D>::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, opart, lpart, a.Hq, a.Hkv, a.Nq, a.Nk, p.nrb, p.nsplit,
                      p.split_len, rows, c, (a.scale < 0.f) ? 0x80008000u : 0u);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPW = 64 / (D / 4);
-  hipLaunchKernelGGL((split_combine_kernel<D>), dim3((unsigned)((rows + RPW - 1) / RPW)),
-                     dim3(64), 0, a.stream, opart, lpart, (__bf16*)a.o, a.lse, p.nsplit, rows);
+  hipLaunchKernelGGL((split_combine_kernel<T, D>), dim3((unsigned)((rows + RPW - 1) / RPW)),
+                     dim3(64), 0, a.stream, opart, lpart, (T*)a.o, a.lse, p.nsplit, rows);
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t split_for(const SplitArgs& a) {
+  if (a.d == 64) return a.causal ? split_t<T, 64, true>(a) : split_t<T, 64, false>(a);
+  return a.causal ? split_t<T, 128, true>(a) : split_t<T, 128, false>(a);
+}
+
 hipError_t launch_fwd_split(const SplitArgs& a) {
-  if (a.d == 64) return a.causal ? split_t<64, true>(a) : split_t<64, false>(a);
-  return a.causal ? split_t<128, true>(a) : split_t<128, false>(a);
+  if (a.dtype == kBF16) return split_for<__bf16>(a);
+  if (a.dtype == kF16) return split_for<_Float16>(a);
+  return hipErrorNotSupported;
 }
 
 }  // namespace attn

@@ -42,9 +42,10 @@
  *  - Arguments are validated on the host before any HIP call.  On error no
  *    kernel is launched and no output is touched.
  *
- * Supported: dtype ATTN_BF16 (bf16 inputs/outputs, fp32 accumulation on
- * matrix cores) with d in {64, 128}; dtype ATTN_F32 (fp32 throughout) with
- * d in {64, 128}.
+ * Supported: dtype ATTN_BF16 or ATTN_F16 (16-bit inputs/outputs, fp32
+ * accumulation on the matrix cores, probabilities rounded to the same 16-bit
+ * type for the P V product) with d in {64, 128}; dtype ATTN_F32 (fp32
+ * throughout, vector ALUs, forward only) with d in {64, 128}.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
 #define EXACT_ATTENTION_ATTN_H
@@ -63,7 +64,7 @@ typedef enum {
   ATTN_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } attn_status;
 
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 } attn_dtype;
 
 /* Version of this ABI; bumped on any incompatible change. */
 int attn_abi_version(void);
@@ -140,9 +141,9 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
  * or appending a short chunk, against a long key/value cache: the decode row
  * of the shape table in "FlashAttention：让精确注意力服从内存层次", section
  * "训练与推理的形状不同", whose first constraint is key/value bandwidth).
- *   q    [B,Hq,Nq,d]  in   (bf16)
- *   k, v [B,Hkv,Nk,d] in   (bf16)
- *   o    [B,Hq,Nq,d]  out  (bf16)
+ *   q    [B,Hq,Nq,d]  in   (dtype: bf16 or fp16)
+ *   k, v [B,Hkv,Nk,d] in   (dtype)
+ *   o    [B,Hq,Nq,d]  out  (dtype)
  *   lse  [B,Hq,Nq]    out  (fp32, natural log)
  *   workspace         scratch of attn_fwd_splitkv_workspace_bytes(...) bytes
  *                     with the same shape and num_splits; caller owned,
@@ -161,7 +162,7 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
  * 服从内存层次", section "Online softmax"), so the result is the exact
  * attention up to rounding.  The query heads of one key/value head are
  * processed together, so K and V are read once per group.
- * Supported: dtype ATTN_BF16, d in {64, 128}, Nq and Nk <= 2^22,
+ * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}, Nq and Nk <= 2^22,
  * (Hq/Hkv)*Nq <= 2^22, B*Hq <= 2^24 (else ATTN_ERR_UNSUPPORTED).  B == 0 or
  * Nq == 0 is an empty problem (ATTN_OK, nothing launched).  Every other
  * convention is attn_fwd's; pointers must be non-NULL even when Nk == 0.
@@ -186,7 +187,7 @@ size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, 
  * paragraph: a 0/1 mask over the grid of score blocks, whose zero blocks
  * are never loaded or computed).  The blocks are the forward's tiles:
  * ATTN_SPARSE_BLOCK_Q query rows by ATTN_SPARSE_BLOCK_K keys.
- *   q, k, v, o, lse  as attn_fwd (bf16), square: N queries and N keys
+ *   q, k, v, o, lse  as attn_fwd (bf16 or fp16), square: N queries and N keys
  *   block_mask  in   DEVICE bytes [mask_heads][ceil(N/128)][ceil(N/64)],
  *                    row-major, any alignment; non-zero = block present.
  *                    mask_heads is 1 (one mask for every head and batch) or
@@ -197,7 +198,7 @@ size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, 
  * Query i of head h sees key j iff
  *   block_mask[h or 0][i / 128][j / 64] != 0  and  (causal == 0 or j <= i).
  * A row that sees no key gets o = 0 and lse = -inf.  Two kernels run on
- * `stream`: the mask compaction, then the forward.  Supported: ATTN_BF16,
+ * `stream`: the mask compaction, then the forward.  Supported: ATTN_BF16 or ATTN_F16,
  * d in {64, 128}, N <= 2^21 (else ATTN_ERR_UNSUPPORTED).  mask_heads other
  * than 1 or Hq, or a NULL mask, is ATTN_ERR_INVALID_ARG.  Every other
  * convention is attn_fwd's.
@@ -218,8 +219,8 @@ size_t attn_fwd_blocksparse_workspace_bytes(int Hq, int N, int mask_heads);
  * Packed variable-length forward: nseq sequences of different lengths laid
  * end to end along the token axis (no padding), every token attending only
  * to keys of its own sequence, causally within it if causal = 1.
- *   q, o        [Hq,  T, d]  bf16, token-major within each head
- *   k, v        [Hkv, T, d]  bf16
+ *   q, o        [Hq,  T, d]  dtype (bf16 or fp16), token-major within each head
+ *   k, v        [Hkv, T, d]  dtype
  *   lse         [Hq,  T]     fp32
  *   cu_seqlens  DEVICE int32 [nseq + 1], 4-byte aligned: sequence s is tokens
  *               [cu_seqlens[s], cu_seqlens[s+1]); the caller guarantees
@@ -232,7 +233,7 @@ size_t attn_fwd_blocksparse_workspace_bytes(int Hq, int N, int mask_heads);
  * Each (sequence, head) is the attention of attn_fwd on that sequence alone;
  * the sequences' key/value ranges are addressed through their own buffer
  * descriptors, so no work is spent on other sequences' keys.  A sequence of
- * length 0 has no rows.  Supported: ATTN_BF16, d in {64, 128}, T <= 2^22,
+ * length 0 has no rows.  Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}, T <= 2^22,
  * nseq * Hq <= 2^24.  nseq == 0, T == 0 or max_seqlen == 0 launches nothing.
  * Every other convention is attn_fwd's.
  */

@@ -306,3 +306,15 @@ def test_varlen_unsupported_and_empty():
     assert varlen(nseq=0, **none) == ea.ATTN_OK
     assert varlen(T=0, maxlen=0, **none) == ea.ATTN_OK
     assert varlen(maxlen=0, **none) == ea.ATTN_OK
+
+
+def test_fp16_is_accepted_where_bf16_is():
+    assert ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_F16) == \
+        ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_BF16)
+    # validation passes for fp16 and stops only at the device check (no GPU here)
+    assert fwd(dtype=ea.ATTN_F16) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert bwd(dtype=ea.ATTN_F16) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert split(dtype=ea.ATTN_F16) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert sparse(dtype=ea.ATTN_F16) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert varlen(dtype=ea.ATTN_F16) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert fwd(dtype=3) == ea.ATTN_ERR_INVALID_ARG

@@ -1,0 +1,122 @@
+"""fp16 I/O parity for every entry point (16-bit inputs and outputs, fp32
+accumulation, probabilities rounded to fp16 for the P V product), against the
+fp64 oracle on the same fp16-rounded inputs.
+
+Tolerances are the 16-bit ones used for bf16 (fp16 rounds more finely):
+|O - O_ref| <= 2e-2 + 1e-2 |O_ref|, |LSE - LSE_ref| <= 1e-3, gradients
+max |g - g_ref| <= 5e-2 max |g_ref|.  Extreme logits (Q x 64) check that the
+online softmax keeps fp16 probabilities in range.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs
+import exact_attention_87_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device(DEV)
+
+
+def check(o, lse, ro, rl, what=""):
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: rows with no key differ"
+    assert np.all(o[empty] == 0.0)
+    o, ro, lse, rl = o[~empty], ro[~empty], lse[~empty], rl[~empty]
+    err = np.abs(o - ro)
+    bad = err > 2e-2 + 1e-2 * np.abs(ro)
+    assert not bad.any(), f"{what} O: {bad.sum()} out of tolerance, max err {err.max()}"
+    assert np.abs(lse - rl).max() <= 1e-3, f"{what} LSE max err {np.abs(lse - rl).max()}"
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("N", [1, 65, 200, 383])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward(oracle_mod, N, d, causal):
+    dev = gpu()
+    q, k, v = attn_inputs.make(2, 4, 2, N, d, "fp16", seed=300 + N)
+    assert q.dtype == torch.float16
+    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"N={N} d={d}")
+
+
+@pytest.mark.parametrize("mult", [8.0, 64.0])
+@pytest.mark.parametrize("d", [64, 128])
+def test_forward_extreme_logits(oracle_mod, mult, d):
+    dev = gpu()
+    q, k, v = attn_inputs.make(1, 4, 2, 700, d, "fp16", seed=77, q_mult=mult)
+    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.fwd(q, k, v, causal=True)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"q x{mult}")
+
+
+@pytest.mark.parametrize("N", [1, 100, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward(oracle_mod, N, d, causal):
+    dev = gpu()
+    q, k, v, do = attn_inputs.make(2, 4, 2, N, d, "fp16", seed=400 + N, with_dout=True)
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o, lse = ea.fwd(qg, kg, vg, causal=causal)
+    dq, dk, dv = ea.bwd(qg, kg, vg, o, lse, dog, causal=causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle_mod.bwd(q, k, v, do, causal=causal)
+    for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert g.dtype == torch.float16
+        g = g.float().cpu().numpy()
+        assert np.all(np.isfinite(g)), f"{name}: non-finite"
+        e, ref_max = np.abs(g - r).max(), np.abs(r).max()
+        if ref_max == 0:  # one key: dS = P (dP - D) is zero up to rounding
+            assert e <= 1e-6, f"{name} N={N} d={d}: {e} with zero reference"
+            continue
+        assert e <= 5e-2 * ref_max, f"{name} N={N} d={d}: {e} vs {ref_max}"
+        assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 2e-2, f"{name} Frobenius"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_splitkv(oracle_mod, d):
+    dev = gpu()
+    q, k, v = attn_inputs.make_cache(2, 8, 2, 3, 3000, d, seed=5, dtype="fp16")
+    for causal in (False, True):
+        o, lse = ea.fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), causal=causal, num_splits=5)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.fwd_bottom_right(q, k, v, causal=causal)
+        check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"split causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_blocksparse(oracle_mod, d):
+    dev = gpu()
+    N = 600
+    q, k, v = attn_inputs.make(1, 4, 2, N, d, "fp16", seed=9)
+    r = np.random.default_rng(4)
+    mask = (r.random((4, -(-N // 128), -(-N // 64))) < 0.4).astype(np.uint8)
+    for causal in (False, True):
+        o, lse = ea.fwd_blocksparse(q.to(dev), k.to(dev), v.to(dev),
+                                    torch.from_numpy(mask).to(dev), causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.fwd_blockmask(q, k, v, mask, 128, 64, causal=causal)
+        check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"sparse causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen(oracle_mod, d):
+    dev = gpu()
+    q, k, v, cu = attn_inputs.make_varlen(4, 2, [300, 1, 129, 0, 64], d, seed=3, dtype="fp16")
+    for causal in (False, True):
+        o, lse = ea.fwd_varlen(q.to(dev), k.to(dev), v.to(dev), cu.to(dev), 300, causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.fwd_varlen(q, k, v, cu.numpy(), causal=causal)
+        check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"varlen causal={causal}")
