@@ -524,6 +524,10 @@ def main():
                                  "bf16", seed=6),
             attn_inputs.Workload("noncausal_bf16_B1_H32_N8192_d128", 1, 32, 32, 8192, 128, False,
                                  "bf16", seed=7),
+            attn_inputs.Workload("causal_fp16_B1_H32_N8192_d128", 1, 32, 32, 8192, 128, True,
+                                 "fp16", seed=8),
+            attn_inputs.Workload("noncausal_bf16_B1_H16_N8192_d256", 1, 16, 16, 8192, 256, False,
+                                 "bf16", seed=9),
         ]
         for cw in cases:
             cq, ck, cv = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=False))

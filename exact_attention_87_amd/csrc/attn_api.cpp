@@ -49,7 +49,8 @@ attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float 
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // d = 256: 16-bit forward paths only (the callers below say which)
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   // Limits of the kernels' 32-bit grid, row and byte offsets: one (batch,
   // head) slice stays below 1 GiB.
   if ((int64_t)B * Hq > (1 << 24) || N > (1 << 22)) return ATTN_ERR_UNSUPPORTED;
@@ -96,7 +97,7 @@ attn_status bwd_common(int B, int Hq, int Hkv, int N, int d, int causal, float s
   bool empty = false;
   attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
-  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32 || d == 256) return ATTN_ERR_UNSUPPORTED;
   if (empty) return ATTN_OK;  // a->N stays 0
   a->B = B, a->Hq = Hq, a->Hkv = Hkv, a->N = N, a->d = d;
   a->causal = causal == 1, a->scale = scale, a->dtype = (attn::Dtype)dtype;
@@ -127,6 +128,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   bool empty = false;
   attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
+  if (dtype == ATTN_F32 && d == 256) return ATTN_ERR_UNSUPPORTED;
   if (empty) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -152,7 +154,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype) {
   bool empty = false;
   if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
-  if (dtype == ATTN_F32) return (size_t)-1;
+  if (dtype == ATTN_F32 || d == 256) return (size_t)-1;
   if (empty) return 0;
   const size_t bytes = attn::bwd_stats_bytes(B, Hq, N);
   return (bytes + 255) & ~(size_t)255;
@@ -246,7 +248,7 @@ attn_status split_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causa
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
   if (num_splits < 0) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   // 32-bit offsets: one key/value slice and one head group's query rows
   // stay below 1 GiB; the grid stays below 2^31 workgroups.
@@ -324,7 +326,8 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
   if (st != ATTN_OK) return st;
   if (!(mask_heads == 1 || mask_heads == Hq)) return ATTN_ERR_INVALID_ARG;
   if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  if (N > (1 << 21)) return ATTN_ERR_UNSUPPORTED;  // the tile list lives in LDS
+  // the tile list lives in LDS beside the stages (128 KiB of them at d = 256)
+  if (N > (d == 256 ? (1 << 20) : (1 << 21))) return ATTN_ERR_UNSUPPORTED;
   if (empty) return ATTN_OK;
   const size_t nqb = ((size_t)N + ATTN_SPARSE_BLOCK_Q - 1) / ATTN_SPARSE_BLOCK_Q;
   const size_t nkt = ((size_t)N + ATTN_SPARSE_BLOCK_K - 1) / ATTN_SPARSE_BLOCK_K;

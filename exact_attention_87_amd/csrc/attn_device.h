@@ -123,7 +123,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // loads), and 4 consecutive rows x 4 aligned chunks (transposing reads).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) {
+  if constexpr (D == 128 || D == 256) {
+    // rows of 256 or 512 bytes start on the same bank, so a 16-byte chunk's
+    // bank group is its index mod 16 and the same XOR serves both
     return ((row & 3) << 2) | ((row >> 2) & 3);
   } else {
     static_assert(D == 64, "head dim");

@@ -59,14 +59,20 @@ namespace attn {
 #define ATTN_FWD_NW128 4
 #endif
 
+// Per head dim: a value for d = 64, 128 and 256.
+template <int D>
+constexpr int by_dim(int v64, int v128, int v256) {
+  return D == 64 ? v64 : D == 128 ? v128 : v256;
+}
+
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = D == 64 ? ATTN_FWD_NW64 : ATTN_FWD_NW128;  // waves per workgroup
-  static constexpr int NB = D == 64 ? ATTN_FWD_NB64 : ATTN_FWD_NB128;  // 32-row blocks per wave
+  static constexpr int NW = by_dim<D>(ATTN_FWD_NW64, ATTN_FWD_NW128, 4);  // waves per workgroup
+  static constexpr int NB = by_dim<D>(ATTN_FWD_NB64, ATTN_FWD_NB128, 1);  // 32-row blocks per wave
   static constexpr int BR = 32 * NB * NW;  // query rows per workgroup
   static constexpr int BC = 64;   // keys per tile
-  static constexpr int NBUF = D == 64 ? ATTN_FWD_NBUF64 : ATTN_FWD_NBUF128;  // LDS stages
-  static constexpr int WPE = D == 64 ? ATTN_FWD_WPE64 : ATTN_FWD_WPE128;     // waves per SIMD
+  static constexpr int NBUF = by_dim<D>(ATTN_FWD_NBUF64, ATTN_FWD_NBUF128, 2);  // LDS stages
+  static constexpr int WPE = by_dim<D>(ATTN_FWD_WPE64, ATTN_FWD_WPE128, 1);     // waves per SIMD
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
@@ -245,23 +251,30 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (wave_active(j)) {
       // ---- S^T = K Q^T for the tile's two 32-key blocks and every query block
-      u32x4 kfrag[2][NQC];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-        for (int cc = 0; cc < NQC; ++cc) kfrag[kbk][cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
+      // (all K fragments are read up front; at d = 256 that would be 128
+      // registers, so there the fragments of one key block at a time)
+      constexpr int KF = D == 256 ? 1 : 2;  // key blocks whose fragments are held at once
       f32x16 sacc[NB][2];
-      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
+      for (int k0b = 0; k0b < 2; k0b += KF) {
+        u32x4 kfrag[KF][NQC];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          sacc[nb][kbk] = f32x16{};
+        for (int kk = 0; kk < KF; ++kk)
 #pragma unroll
           for (int cc = 0; cc < NQC; ++cc)
-            sacc[nb][kbk] = mfma32(bitcast<V8>(kfrag[kbk][cc]), qreg[nb][cc], sacc[nb][kbk]);
-        }
-      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
+            kfrag[kk][cc] = lds_read16(kt + (k0b + kk) * 32 * ROWB + koff[cc]);
+        if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kk = 0; kk < KF; ++kk)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            sacc[nb][k0b + kk] = f32x16{};
+#pragma unroll
+            for (int cc = 0; cc < NQC; ++cc)
+              sacc[nb][k0b + kk] = mfma32(bitcast<V8>(kfrag[kk][cc]), qreg[nb][cc], sacc[nb][k0b + kk]);
+          }
+        if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
+      }
       // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
       // and kept as a branch rather than flattened into selects)
       const int k0 = tile_of(j) * BC;
@@ -413,14 +426,20 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #ifndef ATTN_PIPE_VPM128
 #define ATTN_PIPE_VPM128 12
 #endif
+#ifndef ATTN_FWD_PIPE256
+#define ATTN_FWD_PIPE256 0
+#endif
+#ifndef ATTN_PIPE_VPM256
+#define ATTN_PIPE_VPM256 6
+#endif
 
 template <int D>
 struct PipeCfg {
   static constexpr int NW = 4;
   static constexpr int BR = 32 * NW;
   static constexpr int BC = 64;
-  static constexpr int WPE = D == 64 ? ATTN_PIPE_WPE64 : ATTN_PIPE_WPE128;
-  static constexpr int VPM = D == 64 ? ATTN_PIPE_VPM64 : ATTN_PIPE_VPM128;
+  static constexpr int WPE = by_dim<D>(ATTN_PIPE_WPE64, ATTN_PIPE_WPE128, 1);
+  static constexpr int VPM = by_dim<D>(ATTN_PIPE_VPM64, ATTN_PIPE_VPM128, ATTN_PIPE_VPM256);
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)4 * TILEB;  // K[2] | V[2]
 };
@@ -806,23 +825,26 @@ static hipError_t launch_pipe(const FwdArgs& a) {
 template <typename T, int D, bool CAUSAL, int MODE>
 static hipError_t launch_mfma(const FwdArgs& a) {
   constexpr bool SPARSE = MODE == kFwdSparse;
-  if constexpr ((D == 64 && ATTN_FWD_PIPE64) || (D == 128 && ATTN_FWD_PIPE128))
+  if constexpr ((D == 64 && ATTN_FWD_PIPE64) || (D == 128 && ATTN_FWD_PIPE128) ||
+                (D == 256 && ATTN_FWD_PIPE256)) {
     return launch_pipe<T, D, CAUSAL, MODE>(a);
-  static_assert(!SPARSE || (FwdCfg<D>::BR == kSparseBlockQ && FwdCfg<D>::BC == kSparseBlockK),
-                "block-sparse tiles are the forward's tiles");
-  const int nqb = (a.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
-  const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const size_t lds = FwdCfg<D>::LDS + sparse_list_bytes(a, FwdCfg<D>::BC);
-  const hipError_t e = allow_lds(fwd_mfma_kernel<T, D, CAUSAL, MODE>, lds);
-  if (e != hipSuccess) return e;
-  float c = fabsf(a.scale) * kLog2e;
-  if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
-  const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
-                     dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
-                     a.tcount, a.mask_heads, a.cu_seqlens, a.T);
-  return hipGetLastError();
+  } else {
+    static_assert(!SPARSE || (FwdCfg<D>::BR == kSparseBlockQ && FwdCfg<D>::BC == kSparseBlockK),
+                  "block-sparse tiles are the forward's tiles");
+    const int nqb = (a.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
+    const int64_t grid = (int64_t)nqb * a.B * a.Hq;
+    const size_t lds = FwdCfg<D>::LDS + sparse_list_bytes(a, FwdCfg<D>::BC);
+    const hipError_t e = allow_lds(fwd_mfma_kernel<T, D, CAUSAL, MODE>, lds);
+    if (e != hipSuccess) return e;
+    float c = fabsf(a.scale) * kLog2e;
+    if (!(c >= 1.17549435e-38f)) c = 1.17549435e-38f;  // scale 0: uniform weights
+    const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
+                       dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
+                       a.tcount, a.mask_heads, a.cu_seqlens, a.T);
+    return hipGetLastError();
+  }
 }
 
 // Runtime (head dim, causal, mode) -> kernel instantiation for element type T.
@@ -839,10 +861,12 @@ static hipError_t dispatch_mfma(const FwdArgs& a) {
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;
+  using I256 = std::integral_constant<int, 256>;
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   if (a.d == 64) return a.causal ? pick(I64{}, Yes{}) : pick(I64{}, No{});
-  return a.causal ? pick(I128{}, Yes{}) : pick(I128{}, No{});
+  if (a.d == 128) return a.causal ? pick(I128{}, Yes{}) : pick(I128{}, No{});
+  return a.causal ? pick(I256{}, Yes{}) : pick(I256{}, No{});
 }
 
 template <int D, bool CAUSAL>

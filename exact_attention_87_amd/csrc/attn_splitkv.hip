@@ -49,8 +49,8 @@ struct SplitCfg {
   static constexpr int NW = 4;
   static constexpr int BR = 128;  // packed query rows per workgroup (32 per wave)
   static constexpr int BC = 64;   // keys per tile
-  static constexpr int NBUF = D == 64 ? ATTN_SPLIT_NBUF64 : ATTN_SPLIT_NBUF128;  // LDS stages
-  static constexpr int WPE = D == 64 ? ATTN_SPLIT_WPE64 : ATTN_SPLIT_WPE128;     // waves per SIMD
+  static constexpr int NBUF = D == 64 ? ATTN_SPLIT_NBUF64 : D == 128 ? ATTN_SPLIT_NBUF128 : 2;
+  static constexpr int WPE = D == 64 ? ATTN_SPLIT_WPE64 : D == 128 ? ATTN_SPLIT_WPE128 : 1;
   static_assert(NBUF >= 2 && NBUF <= 4, "stages");
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
@@ -357,7 +357,8 @@ SplitPlan split_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_spli
     // One round of resident workgroups (256 CUs x workgroups per CU, which
     // the waves-per-SIMD setting fixes); each split keeps at least 4 tiles.
     // More splits only add partial-output traffic and merge work.
-    const int64_t resident = 256 * (d == 64 ? SplitCfg<64>::WPE : SplitCfg<128>::WPE);
+    const int64_t resident =
+        256 * (d == 64 ? SplitCfg<64>::WPE : d == 128 ? SplitCfg<128>::WPE : SplitCfg<256>::WPE);
     const int64_t wgs = (int64_t)B * Hkv * p.nrb;
     const int64_t want = (resident + wgs - 1) / wgs;
     ns = (int)std::min<int64_t>(want, std::max(1, (Nk + 4 * BC - 1) / (4 * BC)));
@@ -389,7 +390,8 @@ static hipError_t split_t(const SplitArgs& a) {
   hipError_t e = allow_lds(fwd_split_kernel<T, D, CAUSAL>, SplitCfg<D>::LDS);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fwd_split_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256),
-                     SplitCfg<D>::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, opart, lpart, a.Hq, a.Hkv, a.Nq, a.Nk, p.nrb, p.nsplit,
+                     SplitCfg<D>::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     opart, lpart, a.Hq, a.Hkv, a.Nq, a.Nk, p.nrb, p.nsplit,
                      p.split_len, rows, c, (a.scale < 0.f) ? 0x80008000u : 0u);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -402,7 +404,8 @@ static hipError_t split_t(const SplitArgs& a) {
 template <typename T>
 static hipError_t split_for(const SplitArgs& a) {
   if (a.d == 64) return a.causal ? split_t<T, 64, true>(a) : split_t<T, 64, false>(a);
-  return a.causal ? split_t<T, 128, true>(a) : split_t<T, 128, false>(a);
+  if (a.d == 128) return a.causal ? split_t<T, 128, true>(a) : split_t<T, 128, false>(a);
+  return a.causal ? split_t<T, 256, true>(a) : split_t<T, 256, false>(a);
 }
 
 hipError_t launch_fwd_split(const SplitArgs& a) {

@@ -44,7 +44,8 @@
  *
  * Supported: dtype ATTN_BF16 or ATTN_F16 (16-bit inputs/outputs, fp32
  * accumulation on the matrix cores, probabilities rounded to the same 16-bit
- * type for the P V product) with d in {64, 128}; dtype ATTN_F32 (fp32
+ * type for the P V product) with d in {64, 128, 256} for the forward entry
+ * points and d in {64, 128} for the backward; dtype ATTN_F32 (fp32
  * throughout, vector ALUs, forward only) with d in {64, 128}.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
@@ -162,7 +163,7 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
  * 服从内存层次", section "Online softmax"), so the result is the exact
  * attention up to rounding.  The query heads of one key/value head are
  * processed together, so K and V are read once per group.
- * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}, Nq and Nk <= 2^22,
+ * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128, 256}, Nq and Nk <= 2^22,
  * (Hq/Hkv)*Nq <= 2^22, B*Hq <= 2^24 (else ATTN_ERR_UNSUPPORTED).  B == 0 or
  * Nq == 0 is an empty problem (ATTN_OK, nothing launched).  Every other
  * convention is attn_fwd's; pointers must be non-NULL even when Nk == 0.
@@ -198,10 +199,10 @@ size_t attn_fwd_splitkv_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, 
  * Query i of head h sees key j iff
  *   block_mask[h or 0][i / 128][j / 64] != 0  and  (causal == 0 or j <= i).
  * A row that sees no key gets o = 0 and lse = -inf.  Two kernels run on
- * `stream`: the mask compaction, then the forward.  Supported: ATTN_BF16 or ATTN_F16,
- * d in {64, 128}, N <= 2^21 (else ATTN_ERR_UNSUPPORTED).  mask_heads other
- * than 1 or Hq, or a NULL mask, is ATTN_ERR_INVALID_ARG.  Every other
- * convention is attn_fwd's.
+ * `stream`: the mask compaction, then the forward.  Supported: ATTN_BF16 or
+ * ATTN_F16, d in {64, 128, 256}, N <= 2^21 (2^20 at d = 256; else
+ * ATTN_ERR_UNSUPPORTED).  mask_heads other than 1 or Hq, or a NULL mask, is
+ * ATTN_ERR_INVALID_ARG.  Every other convention is attn_fwd's.
  */
 #define ATTN_SPARSE_BLOCK_Q 128
 #define ATTN_SPARSE_BLOCK_K 64
@@ -233,7 +234,8 @@ size_t attn_fwd_blocksparse_workspace_bytes(int Hq, int N, int mask_heads);
  * Each (sequence, head) is the attention of attn_fwd on that sequence alone;
  * the sequences' key/value ranges are addressed through their own buffer
  * descriptors, so no work is spent on other sequences' keys.  A sequence of
- * length 0 has no rows.  Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}, T <= 2^22,
+ * length 0 has no rows.  Supported: ATTN_BF16 or ATTN_F16, d in {64, 128,
+ * 256}, T <= 2^22,
  * nseq * Hq <= 2^24.  nseq == 0, T == 0 or max_seqlen == 0 launches nothing.
  * Every other convention is attn_fwd's.
  */

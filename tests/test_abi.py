@@ -81,9 +81,22 @@ def test_fwd_rejects_bad_arguments(kw):
     assert fwd(**kw) == ea.ATTN_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("d", [0, 32, 96, 256])
+@pytest.mark.parametrize("d", [0, 32, 96, 512])
 def test_fwd_unsupported_head_dim(d):
     assert fwd(d=d) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_d256_is_forward_only_and_16_bit():
+    # accepted by the 16-bit forward paths (validation passes; no GPU here)
+    for dt in (ea.ATTN_BF16, ea.ATTN_F16):
+        assert fwd(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+        assert split(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+        assert sparse(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+        assert varlen(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert fwd(d=256, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert bwd(d=256) == ea.ATTN_ERR_UNSUPPORTED
+    assert ea.attn_bwd_workspace_bytes(1, 1, 1, 64, 256, ea.ATTN_BF16) == -1
+    assert sparse(d=256, N=(1 << 20) + 1) == ea.ATTN_ERR_UNSUPPORTED
 
 
 def test_fwd_too_large_is_unsupported():
