@@ -77,6 +77,8 @@ def lib():
         L.attn_fwd_blocksparse_workspace_bytes.restype = sz
         L.attn_fwd_varlen.argtypes = [vp] * 6 + [ci] * 7 + [cf, ci, vp]
         L.attn_fwd_varlen.restype = ci
+        L.attn_fwd_strided.argtypes = [vp] * 6 + [ci] * 6 + [cf, ci, vp]
+        L.attn_fwd_strided.restype = ci
         _lib = L
     return _lib
 
@@ -158,6 +160,14 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, Hq, Hkv, T, d
                     dtype, stream) -> int:
     return int(lib().attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, Hq, Hkv, T, d,
                                      int(causal), float(scale), int(dtype), stream))
+
+
+def attn_fwd_strided(q, k, v, o, lse, strides, B, Hq, Hkv, N, d, causal, scale, dtype,
+                     stream) -> int:
+    """strides: 9 element strides (q_b, q_h, q_row, kv_b, kv_h, kv_row, o_b, o_h, o_row)."""
+    arr = (ctypes.c_longlong * 9)(*[int(x) for x in strides])
+    return int(lib().attn_fwd_strided(q, k, v, o, lse, arr, B, Hq, Hkv, N, d, int(causal),
+                                      float(scale), int(dtype), stream))
 
 
 # ------------------------------------------------------------ torch conveniences
@@ -307,6 +317,42 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
                          d, causal, scale, _dtype_code(q), _stream_ptr(q))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_varlen")
+    return out, lse
+
+
+def _bhnd_strides(t):
+    """(batch, head, row) element strides of a [B, H, N, d] view with a unit
+    stride in d (any permutation of the first three axes in memory)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("tensors must be 4-D [B, H, N, d] views with contiguous d")
+    return [t.stride(0), t.stride(1), t.stride(2)]
+
+
+def fwd_strided(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Forward on [B, H, N, d] views of any (batch, head, row) strides, such as
+    [B, N, H, d] tensors transposed to [B, H, N, d] or slices of a packed QKV
+    projection.  k and v must share strides; out defaults to a [B, N, Hq, d]
+    tensor viewed as [B, Hq, N, d]."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_cuda:
+            raise ValueError(f"{name} must be a 4-D device tensor [B, H, N, d]")
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, N, Hq, d), device=q.device, dtype=q.dtype).transpose(1, 2)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    strides = _bhnd_strides(q) + _bhnd_strides(k) + _bhnd_strides(out)
+    st = attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          strides, B, Hq, Hkv, N, d, causal, scale, _dtype_code(q), _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_strided")
     return out, lse
 
 

@@ -389,3 +389,55 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
 
 }  // extern "C"
 
+// ------------------------------------------------------------ strided tensors
+namespace {
+
+// One tensor family's strides from the caller's array (batch, head, row).
+attn::Strides3 strides_at(const long long* s, int i) {
+  return attn::Strides3{(int64_t)s[3 * i], (int64_t)s[3 * i + 1], (int)s[3 * i + 2]};
+}
+
+// Strides the kernels can address: non-negative, 16-byte multiples, rows at
+// least d apart, and every row index up to N + 127 (the padded tail of a tile)
+// at a 32-bit byte offset.
+bool strides_ok(const long long* s, int i, int N, int d) {
+  const long long b = s[3 * i], h = s[3 * i + 1], r = s[3 * i + 2];
+  if (b < 0 || h < 0 || r < d || (b % 8) || (h % 8) || (r % 8)) return false;
+  return ((long long)(N + 127) * r + d) * 2 < (1ll << 31);
+}
+
+// Bytes from a tensor's base to the end of its last element.
+size_t extent(const long long* s, int i, int B, int H, int N, int d) {
+  return (size_t)(((long long)(B - 1) * s[3 * i] + (long long)(H - 1) * s[3 * i + 1] +
+                   (long long)(N - 1) * s[3 * i + 2] + d) * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const long long* strides, int B, int Hq, int Hkv, int N, int d,
+                             int causal, float scale, attn_dtype dtype, void* stream) {
+  bool empty = false;
+  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (empty) return ATTN_OK;
+  if (!strides) return ATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (!strides_ok(strides, i, N, d)) return ATTN_ERR_INVALID_ARG;
+  const size_t eq = extent(strides, 0, B, Hq, N, d), ek = extent(strides, 1, B, Hkv, N, d),
+               eo = extent(strides, 2, B, Hq, N, d), el = (size_t)B * Hq * N * sizeof(float);
+  st = check_buffers({{q, eq}, {k, ek}, {v, ek}}, {{o, eo}, {lse, el}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dtype,
+                  (hipStream_t)stream};
+  a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
+  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // extern "C"
+

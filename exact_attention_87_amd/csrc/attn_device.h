@@ -160,6 +160,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+// Bytes of a buffer over rows 0..n-1 of stride rs elements, d 16-bit
+// elements each (the last row ends the buffer).
+__device__ __forceinline__ uint32_t slice_bytes(int n, int rs, int d) {
+  return n > 0 ? (uint32_t)(((int64_t)(n - 1) * rs + d) * 2) : 0u;
+}
+
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

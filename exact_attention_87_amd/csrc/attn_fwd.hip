@@ -83,7 +83,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
-    int mask_heads, const int* __restrict__ cu_seqlens, int ntok) {
+    int mask_heads, const int* __restrict__ cu_seqlens, int ntok, Layout lay) {
   constexpr bool SPARSE = MODE == kFwdSparse;
   using V8 = typename Elem<T>::v8;
   using Cfg = FwdCfg<D>;
@@ -113,7 +113,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
   int N = Nmax, h;
-  int64_t qoff, kvoff, lbase;
+  int64_t qoff, kvoff, ooff, lbase;
+  int qrs = D, krs = D, ors = D;  // row strides (elements) of Q, K/V and O
   if constexpr (MODE == kFwdVarlen) {
     const int seq = bh / Hq;
     h = bh - seq * Hq;
@@ -122,24 +123,26 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     N = end - start;
     if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
     const int g = h / (Hq / Hkv);
-    qoff = ((int64_t)h * ntok + start) * D;
+    qoff = ooff = ((int64_t)h * ntok + start) * D;
     kvoff = ((int64_t)g * ntok + start) * D;
     lbase = (int64_t)h * ntok + start;
   } else {
     const int b = bh / Hq;
     h = bh - b * Hq;
     const int g = h / (Hq / Hkv);
-    qoff = (int64_t)bh * N * D;
-    kvoff = (int64_t)(b * Hkv + g) * N * D;
+    qoff = b * lay.q.b + h * lay.q.h;
+    kvoff = b * lay.kv.b + g * lay.kv.h;
+    ooff = b * lay.o.b + h * lay.o.h;
+    qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
     lbase = (int64_t)bh * N;
   }
   const int q0 = qb * BR + w * 32 * NB;  // first query row of this wave
 
-  // Each (batch, head) slice is one raw buffer; rows past N read as zero.
-  const uint32_t slice_bytes = (uint32_t)N * ROWB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
+  // Each (batch, head) slice is one raw buffer ending after row N-1; rows
+  // past N read as zero.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes(N, qrs, D));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes(N, krs, D));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes(N, krs, D));
 
   // Q^T operands (one per 32-row block), resident for the whole key loop.
   V8 qreg[NB][NQC];
@@ -148,7 +151,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc)
       qreg[nb][cc] = bitcast<V8>(
-          buf_load16(rq, (uint32_t)((q0 + nb * 32 + l32) * D + cc * 16 + hf * 8) * 2) ^ qsign);
+          buf_load16(rq, (uint32_t)(((q0 + nb * 32 + l32) * qrs + cc * 16 + hf * 8) * 2)) ^ qsign);
 
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all;
@@ -192,12 +195,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     const int o = (w * PW + i) * 1024 + lane * 16;
     const int row = o / ROWB;
     const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
-    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+    goff[i] = (uint32_t)((row * krs + ch * 8) * 2);
   }
   auto issue = [&](int j) {
     char* kt = smem + (j % NBUF) * 2 * TILEB;  // j % NBUF is the stage tile j uses
     char* vt = kt + TILEB;
-    const uint32_t tbase = (uint32_t)tile_of(j) * BC * ROWB;
+    const uint32_t tbase = (uint32_t)(tile_of(j) * BC * krs * 2);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       buf_load16_lds(rk, kt + (w * PW + i) * 1024, goff[i] + tbase);
@@ -380,7 +383,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     if (qrow < N) {
       const bool any = lfull > 0.f;  // else the row saw no key: O = 0, LSE = -inf
       const float inv = any ? 1.0f / lfull : 0.f;
-      T* dst = O + qoff + (int64_t)qrow * D;
+      T* dst = O + ooff + (int64_t)qrow * ors;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -450,7 +453,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
-    int mask_heads, const int* __restrict__ cu_seqlens, int ntok) {
+    int mask_heads, const int* __restrict__ cu_seqlens, int ntok, Layout lay) {
   constexpr bool SPARSE = MODE == kFwdSparse;
   using V8 = typename Elem<T>::v8;
   using Cfg = PipeCfg<D>;
@@ -476,7 +479,8 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
   int N = Nmax, h;
-  int64_t qoff, kvoff, lbase;
+  int64_t qoff, kvoff, ooff, lbase;
+  int qrs = D, krs = D, ors = D;  // row strides (elements) of Q, K/V and O
   if constexpr (MODE == kFwdVarlen) {
     const int seq = bh / Hq;
     h = bh - seq * Hq;
@@ -485,28 +489,31 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     N = end - start;
     if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
     const int g = h / (Hq / Hkv);
-    qoff = ((int64_t)h * ntok + start) * D;
+    qoff = ooff = ((int64_t)h * ntok + start) * D;
     kvoff = ((int64_t)g * ntok + start) * D;
     lbase = (int64_t)h * ntok + start;
   } else {
     const int b = bh / Hq;
     h = bh - b * Hq;
     const int g = h / (Hq / Hkv);
-    qoff = (int64_t)bh * N * D;
-    kvoff = (int64_t)(b * Hkv + g) * N * D;
+    qoff = b * lay.q.b + h * lay.q.h;
+    kvoff = b * lay.kv.b + g * lay.kv.h;
+    ooff = b * lay.o.b + h * lay.o.h;
+    qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
     lbase = (int64_t)bh * N;
   }
   const int q0 = qb * BR + w * 32;
 
-  const uint32_t slice_bytes = (uint32_t)N * ROWB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
+  // Each (batch, head) slice is one raw buffer ending after row N-1; rows
+  // past N read as zero.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes(N, qrs, D));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes(N, krs, D));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes(N, krs, D));
 
   V8 qreg[NQC];
 #pragma unroll
   for (int cc = 0; cc < NQC; ++cc)
-    qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)((q0 + l32) * D + cc * 16 + hf * 8) * 2) ^ qsign);
+    qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)(((q0 + l32) * qrs + cc * 16 + hf * 8) * 2)) ^ qsign);
 
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all;
@@ -543,10 +550,10 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     const int o = (w * PW + i) * 1024 + lane * 16;
     const int row = o / ROWB;
     const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
-    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+    goff[i] = (uint32_t)((row * krs + ch * 8) * 2);
   }
   auto issue = [&](__amdgpu_buffer_rsrc_t r, char* dst, int j) {
-    const uint32_t tbase = (uint32_t)tile_of(j) * BC * ROWB;
+    const uint32_t tbase = (uint32_t)(tile_of(j) * BC * krs * 2);
 #pragma unroll
     for (int i = 0; i < PW; ++i) buf_load16_lds(r, dst + (w * PW + i) * 1024, goff[i] + tbase);
   };
@@ -702,7 +709,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   if (qrow < N) {
     const bool any = lfull > 0.f;  // else the row saw no key: O = 0, LSE = -inf
     const float inv = any ? 1.0f / lfull : 0.f;
-    T* dst = O + qoff + (int64_t)qrow * D;
+    T* dst = O + ooff + (int64_t)qrow * ors;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -796,6 +803,11 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
+// The strides a launch uses: the caller's, or the dense [B, H, N, d] ones.
+static Layout layout_of(const FwdArgs& a) {
+  return a.lay.q.r ? a.lay : dense_layout(a.Hq, a.Hkv, a.N, a.d);
+}
+
 // Dynamic LDS of a forward launch: the kernel's stages, plus the 16-bit tile
 // list of a block-sparse launch (one entry per key tile, rounded to 16 B).
 static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
@@ -818,7 +830,7 @@ static hipError_t launch_pipe(const FwdArgs& a) {
   hipLaunchKernelGGL((fwd_mfma_pipe_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
                      dim3(64 * PipeCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
-                     a.tcount, a.mask_heads, a.cu_seqlens, a.T);
+                     a.tcount, a.mask_heads, a.cu_seqlens, a.T, layout_of(a));
   return hipGetLastError();
 }
 
@@ -842,7 +854,7 @@ static hipError_t launch_mfma(const FwdArgs& a) {
     hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
                        dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
-                       a.tcount, a.mask_heads, a.cu_seqlens, a.T);
+                       a.tcount, a.mask_heads, a.cu_seqlens, a.T, layout_of(a));
     return hipGetLastError();
   }
 }

@@ -10,6 +10,22 @@ namespace attn {
 // Element types, numbered as the ABI's attn_dtype.
 enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
 
+// Element strides of one [batch, head, row, d] tensor family (d contiguous).
+struct Strides3 {
+  int64_t b, h;
+  int r;
+};
+// Q (and dQ); K, V (and dK, dV); O (and dO).  r == 0 in q means "dense
+// [B, H, N, d]", which the launchers fill in.
+struct Layout {
+  Strides3 q, kv, o;
+};
+inline Layout dense_layout(int Hq, int Hkv, int N, int d) {
+  const Strides3 q{(int64_t)Hq * N * d, (int64_t)N * d, d};
+  const Strides3 kv{(int64_t)Hkv * N * d, (int64_t)N * d, d};
+  return Layout{q, kv, q};
+}
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -32,6 +48,8 @@ struct FwdArgs {
   // and N the longest sequence.  Null for a batched problem.
   const int* cu_seqlens = nullptr;
   int T = 0;
+  // Strided tensors (dense and block-sparse modes); zero = dense layout.
+  Layout lay{};
 };
 
 // Forward kernel variants: every tile, a block-sparse tile list, or packed

@@ -244,6 +244,30 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             int T, int d, int causal, float scale, attn_dtype dtype,
                             void* stream);
 
+/*
+ * Forward on strided tensors: every tensor is addressed as
+ *   base + b * stride_b + h * stride_h + i * stride_row + c     (elements)
+ * with the d elements of a row contiguous.  strides is a HOST array of 9
+ * element counts:
+ *   { q_b, q_h, q_row,   kv_b, kv_h, kv_row,   o_b, o_h, o_row }
+ * (K and V share one set).  Examples, for [B, N, H, d] tensors (token-major,
+ * as most model code lays them out): q = {N*Hq*d, d, Hq*d}; for Q, K, V
+ * sliced out of one packed projection [B, N, 3, H, d]: q = kv =
+ * {N*3*H*d, d, 3*H*d} with k = q + H*d, v = q + 2*H*d.  lse stays dense
+ * [B, Hq, N].  Every stride must be a non-negative multiple of 8 (16-byte
+ * aligned rows), row strides at least d, and ((N + 127) * row + d) * 2 <
+ * 2^31 (else ATTN_ERR_INVALID_ARG); distinct (b, h, i) must address distinct
+ * rows of o (not checked).  Inputs may share memory with each other; the
+ * outputs must not overlap the inputs or each other (checked on the extent
+ * from base to last element).  Supported: ATTN_BF16 or ATTN_F16 (ATTN_F32 is
+ * ATTN_ERR_UNSUPPORTED), d in {64, 128, 256}; every other convention is
+ * attn_fwd's, and with the dense strides the result is attn_fwd's bit for
+ * bit.
+ */
+attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const long long* strides, int B, int Hq, int Hkv, int N, int d,
+                             int causal, float scale, attn_dtype dtype, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                                   "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
-                                  "attn_fwd_splitkv_workspace_bytes", "attn_fwd_varlen",
+                                  "attn_fwd_splitkv_workspace_bytes", "attn_fwd_strided",
+                                  "attn_fwd_varlen",
                                   "attn_status_str"]
 
 
@@ -331,3 +332,34 @@ def test_fp16_is_accepted_where_bf16_is():
     assert sparse(dtype=ea.ATTN_F16) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
     assert varlen(dtype=ea.ATTN_F16) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
     assert fwd(dtype=3) == ea.ATTN_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- strided tensors
+def strided(strides, **kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=4, Hkv=2, N=100, d=64, causal=1, scale=0.125,
+             dtype=ea.ATTN_BF16, stream=None)
+    a.update(kw)
+    return ea.attn_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], strides, a["B"], a["Hq"],
+                               a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"],
+                               a["stream"])
+
+
+BNHD = [100 * 4 * 64, 64, 4 * 64, 100 * 2 * 64, 64, 2 * 64, 100 * 4 * 64, 64, 4 * 64]
+
+
+def test_strided_validation():
+    ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert strided(BNHD) not in ok  # passes validation, stops at the device check
+    for i, bad in [(2, 60), (2, 65), (1, 4), (0, -8), (5, 32), (8, 0)]:
+        s = list(BNHD)
+        s[i] = bad
+        assert strided(s) == ea.ATTN_ERR_INVALID_ARG, (i, bad)
+    huge = list(BNHD)
+    huge[2] = 1 << 23  # (N + 127) * row * 2 >= 2^31
+    assert strided(huge) == ea.ATTN_ERR_INVALID_ARG
+    assert strided(BNHD, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert strided(BNHD, o=Q + 64) == ea.ATTN_ERR_INVALID_ARG  # output overlaps an input
+    assert strided(BNHD, q=Q, k=Q + 128, v=Q + 256) not in ok  # inputs may share memory
+    assert strided(BNHD, B=0, q=None, k=None, v=None, o=None, lse=None) == ea.ATTN_OK
+    assert ea.lib().attn_fwd_strided(Q, K, V, O, L, None, 2, 4, 2, 100, 64, 1, 0.125, 1,
+                                     None) == ea.ATTN_ERR_INVALID_ARG  # no strides

@@ -1,0 +1,93 @@
+"""Strided-tensor forward parity: attn_fwd_strided (through the C ABI) on
+[B, N, H, d] tensors and on slices of a packed QKV projection, against the
+fp64 oracle on dense copies of the same values.
+
+Tolerances are the 16-bit forward's: |O - O_ref| <= 2e-2 + 1e-2 |O_ref|,
+|LSE - LSE_ref| <= 1e-3.  With the dense strides the result must be
+attn_fwd's bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs
+import exact_attention_87_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device(DEV)
+
+
+def check(o, lse, ro, rl, what=""):
+    err = np.abs(o - ro)
+    bad = err > 2e-2 + 1e-2 * np.abs(ro)
+    assert not bad.any(), f"{what} O: {bad.sum()} out of tolerance, max err {err.max()}"
+    assert np.abs(lse - rl).max() <= 1e-3, f"{what} LSE max err {np.abs(lse - rl).max()}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_strides_are_the_forward_bitwise(d, causal):
+    dev = gpu()
+    q, k, v = (t.to(dev) for t in attn_inputs.make(2, 4, 2, 333, d, "bf16", seed=3))
+    o, lse = ea.fwd_strided(q, k, v, causal=causal, out=torch.empty_like(q))
+    fo, fl = ea.fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o, fo) and torch.equal(lse, fl)
+
+
+@pytest.mark.parametrize("N", [1, 100, 257, 700])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_token_major_layout(oracle_mod, N, d, causal):
+    # [B, N, H, d] tensors, seen as [B, H, N, d] views; O written [B, N, Hq, d]
+    dev = gpu()
+    q, k, v = attn_inputs.make(2, 8, 2, N, d, "bf16", seed=N + d)
+    qt, kt, vt = (t.transpose(1, 2).contiguous().to(dev) for t in (q, k, v))  # [B, N, H, d]
+    o, lse = ea.fwd_strided(qt.transpose(1, 2), kt.transpose(1, 2), vt.transpose(1, 2),
+                            causal=causal)
+    torch.cuda.synchronize()
+    assert o.transpose(1, 2).is_contiguous()
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"N={N} d={d}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("heads", [(8, 8), (8, 2)])
+def test_packed_qkv_projection(oracle_mod, dtype, heads):
+    # one [B, N, Hq + 2*Hkv, d] buffer holding Q, K and V heads side by side
+    dev = gpu()
+    Hq, Hkv = heads
+    B, N, d = 2, 450, 128
+    q, k, v = attn_inputs.make(B, Hq, Hkv, N, d, dtype, seed=11)
+    packed = torch.cat([q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2)], dim=2)
+    packed = packed.contiguous().to(dev)  # [B, N, Hq + 2 Hkv, d]
+    qv = packed[:, :, :Hq].transpose(1, 2)
+    kv = packed[:, :, Hq:Hq + Hkv].transpose(1, 2)
+    vv = packed[:, :, Hq + Hkv:].transpose(1, 2)
+    for causal in (False, True):
+        o, lse = ea.fwd_strided(qv, kv, vv, causal=causal)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+        check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"packed {heads} {dtype}")
+
+
+def test_output_into_a_strided_view(oracle_mod):
+    # O written straight into the head slots of a wider [B, N, 2*Hq, d] buffer
+    dev = gpu()
+    q, k, v = attn_inputs.make(1, 4, 4, 300, 64, "bf16", seed=13)
+    big = torch.full((1, 300, 8, 64), 7.0, device=dev, dtype=torch.bfloat16)
+    out = big[:, :, 4:].transpose(1, 2)
+    ea.fwd_strided(q.to(dev), k.to(dev), v.to(dev), causal=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, :, :4] == 7.0)  # untouched neighbours
+    ro, rl = oracle_mod.fwd(q, k, v, causal=True)
+    o = big[:, :, 4:].transpose(1, 2).float().cpu().numpy()
+    err = np.abs(o - ro)
+    assert not (err > 2e-2 + 1e-2 * np.abs(ro)).any(), err.max()
