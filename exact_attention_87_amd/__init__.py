@@ -79,6 +79,8 @@ def lib():
         L.attn_fwd_varlen.restype = ci
         L.attn_fwd_strided.argtypes = [vp] * 6 + [ci] * 6 + [cf, ci, vp]
         L.attn_fwd_strided.restype = ci
+        L.attn_bwd_strided.argtypes = [vp] * 11 + [ci] * 6 + [cf, ci, vp]
+        L.attn_bwd_strided.restype = ci
         _lib = L
     return _lib
 
@@ -168,6 +170,14 @@ def attn_fwd_strided(q, k, v, o, lse, strides, B, Hq, Hkv, N, d, causal, scale, 
     arr = (ctypes.c_longlong * 9)(*[int(x) for x in strides])
     return int(lib().attn_fwd_strided(q, k, v, o, lse, arr, B, Hq, Hkv, N, d, int(causal),
                                       float(scale), int(dtype), stream))
+
+
+def attn_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, strides, B, Hq, Hkv, N, d,
+                     causal, scale, dtype, stream) -> int:
+    """strides: 9 element strides (q/dq, k/v/dk/dv, o/dout; batch, head, row each)."""
+    arr = (ctypes.c_longlong * 9)(*[int(x) for x in strides])
+    return int(lib().attn_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, arr, B, Hq,
+                                      Hkv, N, d, int(causal), float(scale), int(dtype), stream))
 
 
 # ------------------------------------------------------------ torch conveniences
@@ -354,6 +364,48 @@ def fwd_strided(q, k, v, causal: bool = False, scale: float | None = None, out=N
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_strided")
     return out, lse
+
+
+def bwd_strided(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV for [B, H, N, d] views of any strides (q and dq share strides,
+    k, v, dk, dv share strides, o and dout share strides).  Gradients default
+    to new tensors with their input's strides (for slices of a packed buffer,
+    pass slices of a packed gradient buffer instead)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dim() != 4 or not t.is_cuda:
+            raise ValueError(f"{name} must be a 4-D device tensor [B, H, N, d]")
+    if k.stride() != v.stride() or o.stride() != dout.stride():
+        raise ValueError("k/v and o/dout must share strides")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def like(t, grad):
+        if grad is not None:
+            if grad.stride() != t.stride() or grad.shape != t.shape:
+                raise ValueError("gradients must have their input's shape and strides")
+            return grad
+        return torch.empty_strided(t.shape, t.stride(), device=t.device, dtype=t.dtype)
+
+    dq, dk, dv = like(q, dq), like(k, dk), like(v, dv)
+    code = _dtype_code(q)
+    nbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, code)
+    if nbytes < 0:
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_bwd_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+    strides = _bhnd_strides(q) + _bhnd_strides(k) + _bhnd_strides(o)
+    st = attn_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          workspace.data_ptr(), strides, B, Hq, Hkv, N, d, causal, scale, code,
+                          _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_strided")
+    return dq, dk, dv
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,

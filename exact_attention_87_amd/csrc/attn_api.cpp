@@ -439,5 +439,48 @@ attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* 
   return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-}  // extern "C"
+attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             void* workspace, const long long* strides, int B, int Hq, int Hkv,
+                             int N, int d, int causal, float scale, attn_dtype dtype,
+                             void* stream) {
+  attn::BwdArgs a;
+  const size_t wbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype);
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if (a.N == 0) return ATTN_OK;  // empty problem
+  if (!strides) return ATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (!strides_ok(strides, i, N, d)) return ATTN_ERR_INVALID_ARG;
+  const size_t eq = extent(strides, 0, B, Hq, N, d), ek = extent(strides, 1, B, Hkv, N, d),
+               eo = extent(strides, 2, B, Hq, N, d), el = (size_t)B * Hq * N * sizeof(float);
+  // The gradients may be interleaved slices of one buffer (a packed dQKV), so
+  // their extents may overlap each other; each must still stay clear of every
+  // input and of the workspace.
+  const Buf ins[] = {{q, eq}, {k, ek}, {v, ek}, {o, eo}, {lse, el}, {dout, eo}};
+  const Buf grads[] = {{dq, eq}, {dk, ek}, {dv, ek}};
+  for (const Buf& b : ins)
+    if (!b.p || !aligned16(b.p)) return ATTN_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  const Range rw{(uintptr_t)workspace, (uintptr_t)workspace + wbytes};
+  for (const Buf& g : grads) {
+    if (!g.p || !aligned16(g.p)) return ATTN_ERR_INVALID_ARG;
+    const Range rg{(uintptr_t)g.p, (uintptr_t)g.p + g.bytes};
+    if (overlaps(rg, rw)) return ATTN_ERR_INVALID_ARG;
+    for (const Buf& b : ins)
+      if (overlaps(rg, Range{(uintptr_t)b.p, (uintptr_t)b.p + b.bytes})) return ATTN_ERR_INVALID_ARG;
+  }
+  for (const Buf& b : ins)
+    if (overlaps(rw, Range{(uintptr_t)b.p, (uintptr_t)b.p + b.bytes})) return ATTN_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
+  a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
+  a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
+  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
 
+}  // extern "C"

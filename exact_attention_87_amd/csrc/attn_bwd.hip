@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       const T* __restrict__ dO,
                                                       const float* __restrict__ LSE,
                                                       float* __restrict__ stats, int N, int Np,
-                                                      int64_t nslices) {
+                                                      int64_t nslices, int Hq, Strides3 os) {
   constexpr int TPR = D / 8;  // lanes per row, 16 bytes each
   constexpr int RPB = 256 / TPR;
   const int tid = threadIdx.x;
@@ -69,9 +69,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   const bool live = slice < nslices && i < N;
   float acc = 0.f;
   if (live) {
-    const int64_t row = slice * N + i;
-    const u32x4 a = *(const u32x4*)(O + row * D + part * 8);
-    const u32x4 b = *(const u32x4*)(dO + row * D + part * 8);
+    // O and dO share one stride set
+    const int64_t off = (slice / Hq) * os.b + (slice % Hq) * os.h + (int64_t)i * os.r + part * 8;
+    const u32x4 a = *(const u32x4*)(O + off);
+    const u32x4 b = *(const u32x4*)(dO + off);
     using V8 = typename Elem<T>::v8;
     const V8 av = bitcast<V8>(a), bv = bitcast<V8>(b);
 #pragma unroll
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D>:
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                      const T* __restrict__ V, const T* __restrict__ dO,
                      const float* __restrict__ stats, T* __restrict__ dK,
-                     T* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c,
+                     T* __restrict__ dV, int Hq, int Hkv, int N, int nkb, Layout lay, float c,
                      float dk_scale, uint32_t qsign) {
   using Cfg = DkdvCfg<D>;
   using V8 = typename Elem<T>::v8;
@@ -128,19 +129,20 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int g = bg - b * Hkv;
   const int group = Hq / Hkv;
   const int Np = stat_rows(N);
-  const int64_t kvoff = (int64_t)bg * N * D;
+  // K, V, dK, dV share one stride set; Q; O and dO share another
+  const int64_t kvoff = b * lay.kv.b + g * lay.kv.h;
+  const int krs = lay.kv.r, qrs = lay.q.r, ors = lay.o.r;
   const int key0 = kblk * BKV + w * 32;  // first key of this wave
   const int krow = key0 + l32;           // key owned by this lane
-  const uint32_t slice_bytes = (uint32_t)N * ROWB;
 
   // K^T and V^T operands of this wave's 32 keys, resident (zero past N).
   V8 kreg[NQC], vreg[NQC];
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes(N, krs, D));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes(N, krs, D));
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
-      const uint32_t off = (uint32_t)(krow * D + cc * 16 + hf * 8) * 2;
+      const uint32_t off = (uint32_t)((krow * krs + cc * 16 + hf * 8) * 2);
       kreg[cc] = bitcast<V8>(buf_load16(rk, off) ^ qsign);  // scale's sign rides on K here
       vreg[cc] = bitcast<V8>(buf_load16(rv, off));
     }
@@ -159,13 +161,14 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
   // Direct loads of a query tile: Q and dO pieces as in the forward, plus
   // the 512 bytes of statistics (wave 0, lanes 0..31).
-  uint32_t goff[PW];
+  uint32_t goffq[PW], goffo[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int o = (w * PW + i) * 1024 + lane * 16;
     const int row = o / ROWB;
     const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
-    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+    goffq[i] = (uint32_t)((row * qrs + ch * 8) * 2);
+    goffo[i] = (uint32_t)((row * ors + ch * 8) * 2);
   }
   const uint32_t soff = (uint32_t)((lane >> 4) * Np * 4 + (lane & 15) * 16);
   auto issue = [&](int it) {
@@ -173,13 +176,15 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     const int qt = qt0 + it % per_head;
     const int64_t bh = (int64_t)b * Hq + hq;
     char* base = smem + (it % NBUF) * STAGEB;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + bh * N * D, slice_bytes);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + bh * N * D, slice_bytes);
-    const uint32_t tbase = (uint32_t)qt * BQ * ROWB;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(Q + b * lay.q.b + hq * lay.q.h, slice_bytes(N, qrs, D));
+    const __amdgpu_buffer_rsrc_t rdo =
+        make_rsrc(dO + b * lay.o.b + hq * lay.o.h, slice_bytes(N, ors, D));
+    const uint32_t tq = (uint32_t)(qt * BQ * qrs * 2), to = (uint32_t)(qt * BQ * ors * 2);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      buf_load16_lds(rq, base + (w * PW + i) * 1024, goff[i] + tbase);
-      buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, goff[i] + tbase);
+      buf_load16_lds(rq, base + (w * PW + i) * 1024, goffq[i] + tq);
+      buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, goffo[i] + to);
     }
     if (w == 0 && lane < 32) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(stats + bh * 2 * Np, (uint32_t)(2 * Np * 4));
@@ -331,8 +336,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // ---- store dK = scale * (dK^T)^T (Q was not sign-flipped), dV
   // (lane: key krow; element r: feature)
   if (krow < N) {
-    T* dkp = dK + kvoff + (int64_t)krow * D;
-    T* dvp = dV + kvoff + (int64_t)krow * D;
+    T* dkp = dK + kvoff + (int64_t)krow * krs;
+    T* dvp = dV + kvoff + (int64_t)krow * krs;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<D>::W
 void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                    const T* __restrict__ V, const T* __restrict__ dO,
                    const float* __restrict__ stats, T* __restrict__ dQ, int Hq, int Hkv,
-                   int N, int nqb, float c, float qscale, uint32_t qsign) {
+                   int N, int nqb, Layout lay, float c, float qscale, uint32_t qsign) {
   using Cfg = DqCfg<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
@@ -389,22 +394,23 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int h = bh - b * Hq;
   const int g = h / (Hq / Hkv);
   const int Np = stat_rows(N);
-  const int64_t qoff = (int64_t)bh * N * D;
-  const int64_t kvoff = (int64_t)(b * Hkv + g) * N * D;
+  // Q and dQ share one stride set; K and V another; dO has O's
+  const int64_t qoff = b * lay.q.b + h * lay.q.h;
+  const int64_t kvoff = b * lay.kv.b + g * lay.kv.h;
+  const int qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
   const int q0 = qb * BR + w * 32;
   const int qrow = q0 + l32;
-  const uint32_t slice_bytes = (uint32_t)N * ROWB;
 
   // Q^T and dO^T operands and this lane's row statistics, resident.
   V8 qreg[NQC], doreg[NQC];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + qoff, slice_bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes(N, qrs, D));
+    const __amdgpu_buffer_rsrc_t rdo =
+        make_rsrc(dO + b * lay.o.b + h * lay.o.h, slice_bytes(N, ors, D));
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
-      const uint32_t off = (uint32_t)(qrow * D + cc * 16 + hf * 8) * 2;
-      qreg[cc] = bitcast<V8>(buf_load16(rq, off) ^ qsign);
-      doreg[cc] = bitcast<V8>(buf_load16(rdo, off));
+      qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)((qrow * qrs + cc * 16 + hf * 8) * 2)) ^ qsign);
+      doreg[cc] = bitcast<V8>(buf_load16(rdo, (uint32_t)((qrow * ors + cc * 16 + hf * 8) * 2)));
     }
   }
   const float* st = stats + (int64_t)bh * 2 * Np;
@@ -422,19 +428,19 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     wtiles = min(ntiles, (q0 + 31) / BC + 1);
   }
 
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes(N, krs, D));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes(N, krs, D));
   uint32_t goff[PW];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int o = (w * PW + i) * 1024 + lane * 16;
     const int row = o / ROWB;
     const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
-    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+    goff[i] = (uint32_t)((row * krs + ch * 8) * 2);
   }
   auto issue = [&](int j) {
     char* kt = smem + (j % NBUF) * 2 * TILEB;
-    const uint32_t tbase = (uint32_t)j * BC * ROWB;
+    const uint32_t tbase = (uint32_t)(j * BC * krs * 2);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       buf_load16_lds(rk, kt + (w * PW + i) * 1024, goff[i] + tbase);
@@ -539,7 +545,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   }
 
   if (qok) {
-    T* dst = dQ + qoff + (int64_t)qrow * D;
+    T* dst = dQ + qoff + (int64_t)qrow * qrs;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -554,6 +560,11 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 }
 
 // ---------------------------------------------------------------- launchers
+// The strides a launch uses: the caller's, or the dense [B, H, N, d] ones.
+static Layout layout_of(const BwdArgs& a) {
+  return a.lay.q.r ? a.lay : dense_layout(a.Hq, a.Hkv, a.N, a.d);
+}
+
 size_t bwd_stats_bytes(int B, int Hq, int N) {
   return (size_t)B * Hq * 2 * stat_rows(N) * sizeof(float);
 }
@@ -576,7 +587,8 @@ static hipError_t pre_t(const BwdArgs& a) {
   const int64_t nslices = (int64_t)a.B * a.Hq;
   const int64_t grid = (nslices * Np + RPB - 1) / RPB;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                     (const T*)a.o, (const T*)a.dout, a.lse, a.stats, a.N, Np, nslices);
+                     (const T*)a.o, (const T*)a.dout, a.lse, a.stats, a.N, Np, nslices, a.Hq,
+                     layout_of(a).o);
   return hipGetLastError();
 }
 
@@ -590,7 +602,8 @@ static hipError_t dkdv_t(const BwdArgs& a) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
                      a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                     a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv, a.N, nkb, k.c, a.scale, k.qsign);
+                     a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv, a.N, nkb, layout_of(a), k.c, a.scale,
+                     k.qsign);
   return hipGetLastError();
 }
 
@@ -604,7 +617,7 @@ static hipError_t dq_t(const BwdArgs& a) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
                      a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                     a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N, nqb, k.c, a.scale, k.qsign);
+                     a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N, nqb, layout_of(a), k.c, a.scale, k.qsign);
   return hipGetLastError();
 }
 

@@ -72,6 +72,8 @@ struct BwdArgs {
   float scale;
   Dtype dtype;
   hipStream_t stream;
+  // Q and dQ; K, V, dK and dV; O and dO.  Zero = dense [B, H, N, d].
+  Layout lay{};
 };
 
 // Split-K/V forward (16-bit types): queries [B,Hq,Nq,d], keys/values [B,Hkv,Nk,d],

@@ -268,6 +268,24 @@ attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* 
                              const long long* strides, int B, int Hq, int Hkv, int N, int d,
                              int causal, float scale, attn_dtype dtype, void* stream);
 
+/*
+ * Backward on strided tensors, with the strides' meaning of attn_fwd_strided:
+ * strides[0..2] address q and dq, strides[3..5] k, v, dk and dv,
+ * strides[6..8] o and dout; lse and the workspace stay dense (the workspace
+ * is attn_bwd_workspace_bytes(...) bytes).  Stride rules as for
+ * attn_fwd_strided.  Inputs may share memory (one packed QKV buffer); dq, dk
+ * and dv may be interleaved slices of one packed gradient buffer, so they are
+ * only required to address disjoint elements (not checked), while each must
+ * stay clear of every input and of the workspace (checked on extents).
+ * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}; with the dense strides the
+ * result is attn_bwd's bit for bit.
+ */
+attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             void* workspace, const long long* strides, int B, int Hq, int Hkv,
+                             int N, int d, int causal, float scale, attn_dtype dtype,
+                             void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -25,7 +25,8 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
-                                  "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd",
+                                  "attn_bwd_preprocess", "attn_bwd_strided",
+                                  "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
                                   "attn_fwd_splitkv_workspace_bytes", "attn_fwd_strided",
@@ -363,3 +364,25 @@ def test_strided_validation():
     assert strided(BNHD, B=0, q=None, k=None, v=None, o=None, lse=None) == ea.ATTN_OK
     assert ea.lib().attn_fwd_strided(Q, K, V, O, L, None, 2, 4, 2, 100, 64, 1, 0.125, 1,
                                      None) == ea.ATTN_ERR_INVALID_ARG  # no strides
+
+
+def test_strided_backward_validation():
+    ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+
+    def sb(strides, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, B=2, Hq=4, Hkv=2,
+                 N=100, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16)
+        a.update(kw)
+        return ea.attn_bwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                                   a["dk"], a["dv"], a["ws"], strides, a["B"], a["Hq"], a["Hkv"],
+                                   a["N"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+    assert sb(BNHD) not in ok
+    bad = list(BNHD)
+    bad[5] = 63
+    assert sb(bad) == ea.ATTN_ERR_INVALID_ARG
+    assert sb(BNHD, dq=Q) == ea.ATTN_ERR_INVALID_ARG  # a gradient over an input
+    assert sb(BNHD, dk=DQ + 128) not in ok  # interleaved gradient slices are allowed
+    assert sb(BNHD, dk=WS + 64) == ea.ATTN_ERR_INVALID_ARG  # a gradient over the workspace
+    assert sb(BNHD, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert sb(BNHD, d=256) == ea.ATTN_ERR_UNSUPPORTED

@@ -91,3 +91,64 @@ def test_output_into_a_strided_view(oracle_mod):
     o = big[:, :, 4:].transpose(1, 2).float().cpu().numpy()
     err = np.abs(o - ro)
     assert not (err > 2e-2 + 1e-2 * np.abs(ro)).any(), err.max()
+
+
+# ---------------------------------------------------------------- backward
+def grads_ok(name, g, r):
+    g = g.float().cpu().numpy()
+    e, m = np.abs(g - r).max(), np.abs(r).max()
+    assert np.all(np.isfinite(g)) and e <= 5e-2 * m, f"{name}: {e} vs {m}"
+    assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 2e-2, f"{name} Frobenius"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_dense_strides_are_bwd_bitwise(d, causal):
+    dev = gpu()
+    q, k, v, do = (t.to(dev) for t in attn_inputs.make(2, 4, 2, 300, d, "bf16", seed=21,
+                                                       with_dout=True))
+    o, lse = ea.fwd(q, k, v, causal=causal)
+    g1 = ea.bwd_strided(q, k, v, o, lse, do, causal=causal)
+    g2 = ea.bwd(q, k, v, o, lse, do, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_token_major(oracle_mod, d, causal):
+    dev = gpu()
+    q, k, v, do = attn_inputs.make(2, 8, 2, 333, d, "bf16", seed=d + 3, with_dout=True)
+    qt, kt, vt, dot = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+                       for t in (q, k, v, do))
+    o, lse = ea.fwd_strided(qt, kt, vt, causal=causal)  # o is token-major too
+    dq, dk, dv = ea.bwd_strided(qt, kt, vt, o, lse, dot, causal=causal)
+    torch.cuda.synchronize()
+    assert dq.transpose(1, 2).is_contiguous() and dk.transpose(1, 2).is_contiguous()
+    rdq, rdk, rdv = oracle_mod.bwd(q, k, v, do, causal=causal)
+    for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        grads_ok(name, g, r)
+
+
+def test_backward_packed_qkv(oracle_mod):
+    # Q, K, V slices of one [B, N, Hq + 2 Hkv, d] buffer; dQ, dK, dV into
+    # slices of one packed gradient buffer; O and dO token-major
+    dev = gpu()
+    B, Hq, Hkv, N, d = 2, 8, 2, 260, 128
+    q, k, v, do = attn_inputs.make(B, Hq, Hkv, N, d, "fp16", seed=31, with_dout=True)
+    packed = torch.cat([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous().to(dev)
+    qv = packed[:, :, :Hq].transpose(1, 2)
+    kv = packed[:, :, Hq:Hq + Hkv].transpose(1, 2)
+    vv = packed[:, :, Hq + Hkv:].transpose(1, 2)
+    o, lse = ea.fwd_strided(qv, kv, vv, causal=True)
+    dob = do.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+    gpack = torch.full_like(packed, 9.0)
+    dq = gpack[:, :, :Hq].transpose(1, 2)
+    dk = gpack[:, :, Hq:Hq + Hkv].transpose(1, 2)
+    dv = gpack[:, :, Hq + Hkv:].transpose(1, 2)
+    ea.bwd_strided(qv, kv, vv, o, lse, dob, causal=True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle_mod.bwd(q, k, v, do, causal=True)
+    for name, g, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        grads_ok(name, g, r)
