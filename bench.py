@@ -532,10 +532,10 @@ def main():
         for cw in cases:
             cq, ck, cv = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=False))
             co, cl = ea.fwd(cq, ck, cv, causal=cw.causal)
-            for _ in range(3):
+            for _ in range(5):
                 ea.fwd(cq, ck, cv, causal=cw.causal, out=co, lse=cl)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 10
+            reps = 25
             e0.record(stream)
             for _ in range(reps):
                 ea.fwd(cq, ck, cv, causal=cw.causal, out=co, lse=cl)
