@@ -81,6 +81,8 @@ def lib():
         L.attn_fwd_strided.restype = ci
         L.attn_bwd_strided.argtypes = [vp] * 11 + [ci] * 6 + [cf, ci, vp]
         L.attn_bwd_strided.restype = ci
+        L.attn_bwd_varlen.argtypes = [vp] * 11 + [ci] * 7 + [cf, ci, vp]
+        L.attn_bwd_varlen.restype = ci
         _lib = L
     return _lib
 
@@ -178,6 +180,13 @@ def attn_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, strides, B, H
     arr = (ctypes.c_longlong * 9)(*[int(x) for x in strides])
     return int(lib().attn_bwd_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, arr, B, Hq,
                                       Hkv, N, d, int(causal), float(scale), int(dtype), stream))
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, nseq, max_seqlen,
+                    Hq, Hkv, T, d, causal, scale, dtype, stream) -> int:
+    return int(lib().attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens,
+                                     nseq, max_seqlen, Hq, Hkv, T, d, int(causal), float(scale),
+                                     int(dtype), stream))
 
 
 # ------------------------------------------------------------ torch conveniences
@@ -405,6 +414,35 @@ def bwd_strided(q, k, v, o, lse, dout, causal: bool = False, scale: float | None
                           _stream_ptr(q))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_strided")
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool = False,
+               scale: float | None = None, workspace=None):
+    """dQ [Hq,T,d], dK, dV [Hkv,T,d] of packed sequences (the forward's fwd_varlen
+    tensors and offsets, upstream dO [Hq,T,d])."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor [H, T, d]")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = attn_bwd_workspace_bytes(1, Hq, Hkv, T, d, code)
+    if nbytes < 0:
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_bwd_workspace_bytes")
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
+    st = attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         workspace.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                         int(max_seqlen), Hq, Hkv, T, d, causal, scale, code, _stream_ptr(q))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_varlen")
     return dq, dk, dv
 
 

@@ -483,4 +483,42 @@ attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const 
   return ATTN_OK;
 }
 
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            void* workspace, const int* cu_seqlens, int nseq, int max_seqlen,
+                            int Hq, int Hkv, int T, int d, int causal, float scale,
+                            attn_dtype dtype, void* stream) {
+  if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
+  attn::BwdArgs a;
+  // the packed tokens as one [1, H, T, d] problem: shapes, statistics, workspace
+  attn_status st = bwd_common(1, Hq, Hkv, T, d, causal, scale, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  if (a.N == 0 || nseq == 0 || max_seqlen == 0) return ATTN_OK;  // no rows
+  const size_t wbytes = attn_bwd_workspace_bytes(1, Hq, Hkv, T, d, dtype);
+  const Sizes z = sizes(1, Hq, Hkv, T, d);
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {lse, z.l}, {dout, z.q}},
+                     {{dq, z.q}, {dk, z.kv}, {dv, z.kv}, {workspace, wbytes}});
+  if (st != ATTN_OK) return st;
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return ATTN_ERR_INVALID_ARG;
+  const Range rc{(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + ((size_t)nseq + 1) * 4};
+  const Range outs[] = {{(uintptr_t)dq, (uintptr_t)dq + z.q},
+                        {(uintptr_t)dk, (uintptr_t)dk + z.kv},
+                        {(uintptr_t)dv, (uintptr_t)dv + z.kv},
+                        {(uintptr_t)workspace, (uintptr_t)workspace + wbytes}};
+  for (const Range& r : outs)
+    if (overlaps(rc, r)) return ATTN_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
+  a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
+  // row statistics of all T packed tokens, then the two gradient stages per
+  // (sequence, head) with B = sequences and N = the longest sequence
+  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
+  a.B = nseq, a.N = max_seqlen, a.cu_seqlens = cu_seqlens, a.T = T;
+  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
 }  // extern "C"

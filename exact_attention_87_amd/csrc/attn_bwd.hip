@@ -99,13 +99,14 @@ struct DkdvCfg {
   static constexpr size_t LDS = (size_t)NBUF * STAGEB;
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D>::WPE, DkdvCfg<D>::WPE)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                      const T* __restrict__ V, const T* __restrict__ dO,
                      const float* __restrict__ stats, T* __restrict__ dK,
-                     T* __restrict__ dV, int Hq, int Hkv, int N, int nkb, Layout lay, float c,
-                     float dk_scale, uint32_t qsign) {
+                     T* __restrict__ dV, int Hq, int Hkv, int Nmax, int nkb, Layout lay, float c,
+                     float dk_scale, uint32_t qsign, const int* __restrict__ cu_seqlens,
+                     int ntok) {
   using Cfg = DkdvCfg<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
@@ -125,13 +126,36 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int BG = gridDim.x / nkb;
   const int kblk = blockIdx.x / BG;  // causal: low key blocks carry the most work
   const int bg = blockIdx.x % BG;
-  const int b = bg / Hkv;
-  const int g = bg - b * Hkv;
   const int group = Hq / Hkv;
-  const int Np = stat_rows(N);
-  // K, V, dK, dV share one stride set; Q; O and dO share another
-  const int64_t kvoff = b * lay.kv.b + g * lay.kv.h;
-  const int krs = lay.kv.r, qrs = lay.q.r, ors = lay.o.r;
+  // This workgroup's problem: one (batch, kv head) slice of Nmax rows, or for
+  // packed variable-length sequences one (sequence, kv head).  Query head hq
+  // reads Q at qb0 + hq*qhs, dO at ob0 + hq*ohs and its statistics at
+  // sb0 + hq*2*Np; K, V, dK, dV share one stride set, O and dO another.
+  int N = Nmax, g, Np, krs, qrs, ors, start = 0;
+  int64_t kvoff, qb0, qhs, ob0, ohs, sb0;
+  if constexpr (VARLEN) {
+    const int seq = bg / Hkv;
+    g = bg - seq * Hkv;
+    start = min(max(cu_seqlens[seq], 0), ntok);
+    const int end = min(max(cu_seqlens[seq + 1], start), ntok);
+    N = end - start;
+    if (kblk * BKV >= N) return;  // the whole workgroup: past this sequence's end
+    Np = stat_rows(ntok);  // statistics of the packed tokens, [Hq][2][Np]
+    krs = qrs = ors = D;
+    kvoff = ((int64_t)g * ntok + start) * D;
+    qb0 = ob0 = (int64_t)start * D;
+    qhs = ohs = (int64_t)ntok * D;
+    sb0 = start;
+  } else {
+    const int b = bg / Hkv;
+    g = bg - b * Hkv;
+    Np = stat_rows(N);
+    krs = lay.kv.r, qrs = lay.q.r, ors = lay.o.r;
+    kvoff = b * lay.kv.b + g * lay.kv.h;
+    qb0 = b * lay.q.b, qhs = lay.q.h;
+    ob0 = b * lay.o.b, ohs = lay.o.h;
+    sb0 = (int64_t)b * Hq * 2 * Np;
+  }
   const int key0 = kblk * BKV + w * 32;  // first key of this wave
   const int krow = key0 + l32;           // key owned by this lane
 
@@ -174,12 +198,9 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   auto issue = [&](int it) {
     const int hq = g * group + it / per_head;
     const int qt = qt0 + it % per_head;
-    const int64_t bh = (int64_t)b * Hq + hq;
     char* base = smem + (it % NBUF) * STAGEB;
-    const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc(Q + b * lay.q.b + hq * lay.q.h, slice_bytes(N, qrs, D));
-    const __amdgpu_buffer_rsrc_t rdo =
-        make_rsrc(dO + b * lay.o.b + hq * lay.o.h, slice_bytes(N, ors, D));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qb0 + hq * qhs, slice_bytes(N, qrs, D));
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + ob0 + hq * ohs, slice_bytes(N, ors, D));
     const uint32_t tq = (uint32_t)(qt * BQ * qrs * 2), to = (uint32_t)(qt * BQ * ors * 2);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
@@ -187,7 +208,10 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, goffo[i] + to);
     }
     if (w == 0 && lane < 32) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(stats + bh * 2 * Np, (uint32_t)(2 * Np * 4));
+      // this head's two statistics rows from the sequence's first token on
+      // (rows past the sequence meet zero Q and dO and add nothing)
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(stats + sb0 + (int64_t)hq * 2 * Np, (uint32_t)((2 * Np - start) * 4));
       buf_load16_lds(rs, base + 2 * TILEB, soff + (uint32_t)qt * BQ * 4);
     }
   };
@@ -365,12 +389,13 @@ struct DqCfg {
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<D>::WPE, DqCfg<D>::WPE)))
 void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                    const T* __restrict__ V, const T* __restrict__ dO,
                    const float* __restrict__ stats, T* __restrict__ dQ, int Hq, int Hkv,
-                   int N, int nqb, Layout lay, float c, float qscale, uint32_t qsign) {
+                   int Nmax, int nqb, Layout lay, float c, float qscale, uint32_t qsign,
+                   const int* __restrict__ cu_seqlens, int ntok) {
   using Cfg = DqCfg<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
@@ -390,14 +415,36 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int id = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
   const int bh = id % BH;
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
-  const int g = h / (Hq / Hkv);
-  const int Np = stat_rows(N);
-  // Q and dQ share one stride set; K and V another; dO has O's
-  const int64_t qoff = b * lay.q.b + h * lay.q.h;
-  const int64_t kvoff = b * lay.kv.b + g * lay.kv.h;
-  const int qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
+  // One (batch, head) slice of Nmax rows, or one (sequence, head) of packed
+  // variable-length sequences.  Q and dQ share one stride set, K and V
+  // another, dO has O's.
+  int N = Nmax, h, Np, qrs, krs, ors;
+  int64_t qoff, kvoff, ooff;
+  const float* st;  // this head's statistics rows, from the slice's first row on
+  if constexpr (VARLEN) {
+    const int seq = bh / Hq;
+    h = bh - seq * Hq;
+    const int start = min(max(cu_seqlens[seq], 0), ntok);
+    const int end = min(max(cu_seqlens[seq + 1], start), ntok);
+    N = end - start;
+    if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
+    const int g = h / (Hq / Hkv);
+    Np = stat_rows(ntok);
+    qrs = krs = ors = D;
+    qoff = ooff = ((int64_t)h * ntok + start) * D;
+    kvoff = ((int64_t)g * ntok + start) * D;
+    st = stats + (int64_t)h * 2 * Np + start;
+  } else {
+    const int b = bh / Hq;
+    h = bh - b * Hq;
+    const int g = h / (Hq / Hkv);
+    Np = stat_rows(N);
+    qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
+    qoff = b * lay.q.b + h * lay.q.h;
+    kvoff = b * lay.kv.b + g * lay.kv.h;
+    ooff = b * lay.o.b + h * lay.o.h;
+    st = stats + (int64_t)bh * 2 * Np;
+  }
   const int q0 = qb * BR + w * 32;
   const int qrow = q0 + l32;
 
@@ -405,15 +452,13 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   V8 qreg[NQC], doreg[NQC];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes(N, qrs, D));
-    const __amdgpu_buffer_rsrc_t rdo =
-        make_rsrc(dO + b * lay.o.b + h * lay.o.h, slice_bytes(N, ors, D));
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + ooff, slice_bytes(N, ors, D));
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc) {
       qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)((qrow * qrs + cc * 16 + hf * 8) * 2)) ^ qsign);
       doreg[cc] = bitcast<V8>(buf_load16(rdo, (uint32_t)((qrow * ors + cc * 16 + hf * 8) * 2)));
     }
   }
-  const float* st = stats + (int64_t)bh * 2 * Np;
   const bool qok = qrow < N;
   const float ndsum = qok ? st[qrow] : 0.f;  // -D of this lane's row
   const float lse2 = qok ? st[Np + qrow] : 0.f;
@@ -592,32 +637,35 @@ static hipError_t pre_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL>
+// For packed variable-length sequences B is the number of sequences and N the
+// longest one (they size the grid); the statistics cover the T packed tokens.
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t dkdv_t(const BwdArgs& a) {
   using Cfg = DkdvCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
   const int nkb = (a.N + Cfg::BKV - 1) / Cfg::BKV;
   const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
-  const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL>, Cfg::LDS);
+  const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                     a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv, a.N, nkb, layout_of(a), k.c, a.scale,
-                     k.qsign);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(256),
+                     Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     (const T*)a.dout, a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv, a.N, nkb,
+                     layout_of(a), k.c, a.scale, k.qsign, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool VARLEN>
 static hipError_t dq_t(const BwdArgs& a) {
   using Cfg = DqCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
   const int nqb = (a.N + Cfg::BR - 1) / Cfg::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const hipError_t e = allow_lds(bwd_dq_kernel<T, D, CAUSAL>, Cfg::LDS);
+  const hipError_t e = allow_lds(bwd_dq_kernel<T, D, CAUSAL, VARLEN>, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256), Cfg::LDS,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                     a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N, nqb, layout_of(a), k.c, a.scale, k.qsign);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(256),
+                     Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     (const T*)a.dout, a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N, nqb, layout_of(a),
+                     k.c, a.scale, k.qsign, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 
@@ -627,13 +675,23 @@ static hipError_t bwd_pre_for(const BwdArgs& a) {
 }
 template <typename T>
 static hipError_t bwd_dkdv_for(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? dkdv_t<T, 64, true>(a) : dkdv_t<T, 64, false>(a);
-  return a.causal ? dkdv_t<T, 128, true>(a) : dkdv_t<T, 128, false>(a);
+  const bool vl = a.cu_seqlens != nullptr;
+  if (a.d == 64) {
+    if (vl) return a.causal ? dkdv_t<T, 64, true, true>(a) : dkdv_t<T, 64, false, true>(a);
+    return a.causal ? dkdv_t<T, 64, true, false>(a) : dkdv_t<T, 64, false, false>(a);
+  }
+  if (vl) return a.causal ? dkdv_t<T, 128, true, true>(a) : dkdv_t<T, 128, false, true>(a);
+  return a.causal ? dkdv_t<T, 128, true, false>(a) : dkdv_t<T, 128, false, false>(a);
 }
 template <typename T>
 static hipError_t bwd_dq_for(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? dq_t<T, 64, true>(a) : dq_t<T, 64, false>(a);
-  return a.causal ? dq_t<T, 128, true>(a) : dq_t<T, 128, false>(a);
+  const bool vl = a.cu_seqlens != nullptr;
+  if (a.d == 64) {
+    if (vl) return a.causal ? dq_t<T, 64, true, true>(a) : dq_t<T, 64, false, true>(a);
+    return a.causal ? dq_t<T, 64, true, false>(a) : dq_t<T, 64, false, false>(a);
+  }
+  if (vl) return a.causal ? dq_t<T, 128, true, true>(a) : dq_t<T, 128, false, true>(a);
+  return a.causal ? dq_t<T, 128, true, false>(a) : dq_t<T, 128, false, false>(a);
 }
 
 hipError_t launch_bwd_pre(const BwdArgs& a) {

@@ -74,6 +74,11 @@ struct BwdArgs {
   hipStream_t stream;
   // Q and dQ; K, V, dK and dV; O and dO.  Zero = dense [B, H, N, d].
   Layout lay{};
+  // Packed variable-length sequences (dK/dV and dQ stages): as in FwdArgs,
+  // B sequences of at most N tokens out of T; the statistics then cover the
+  // T packed tokens ([Hq][2][T rounded up to 64]).
+  const int* cu_seqlens = nullptr;
+  int T = 0;
 };
 
 // Split-K/V forward (16-bit types): queries [B,Hq,Nq,d], keys/values [B,Hkv,Nk,d],

@@ -286,6 +286,22 @@ attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const 
                              int N, int d, int causal, float scale, attn_dtype dtype,
                              void* stream);
 
+/*
+ * Backward of attn_fwd_varlen: packed sequences as there (q, o, dout, dq
+ * [Hq, T, d]; k, v, dk, dv [Hkv, T, d]; lse [Hq, T]; the same cu_seqlens,
+ * nseq and max_seqlen), every sequence's gradients computed within that
+ * sequence only.  workspace: attn_bwd_workspace_bytes(1, Hq, Hkv, T, d,
+ * dtype) bytes (the row statistics of the T packed tokens), caller owned.
+ * Offsets are clamped on the device as in attn_fwd_varlen.  Deterministic.
+ * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}, T <= 2^22,
+ * nseq * Hq <= 2^24; nseq == 0, T == 0 or max_seqlen == 0 launches nothing.
+ */
+attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            void* workspace, const int* cu_seqlens, int nseq, int max_seqlen,
+                            int Hq, int Hkv, int T, int d, int causal, float scale,
+                            attn_dtype dtype, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
-                                  "attn_bwd_preprocess", "attn_bwd_strided",
+                                  "attn_bwd_preprocess", "attn_bwd_strided", "attn_bwd_varlen",
                                   "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
@@ -386,3 +386,26 @@ def test_strided_backward_validation():
     assert sb(BNHD, dk=WS + 64) == ea.ATTN_ERR_INVALID_ARG  # a gradient over the workspace
     assert sb(BNHD, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
     assert sb(BNHD, d=256) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_varlen_backward_validation():
+    ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+
+    def vb(**kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, cu=CU, nseq=3,
+                 maxlen=500, Hq=4, Hkv=2, T=1000, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16)
+        a.update(kw)
+        return ea.attn_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                                  a["dk"], a["dv"], a["ws"], a["cu"], a["nseq"], a["maxlen"],
+                                  a["Hq"], a["Hkv"], a["T"], a["d"], a["causal"], a["scale"],
+                                  a["dtype"], None)
+
+    assert vb() not in ok
+    for kw in (dict(cu=None), dict(cu=CU + 2), dict(maxlen=1001), dict(nseq=-1), dict(dq=Q),
+               dict(ws=None), dict(cu=DQ + 16), dict(Hq=6, Hkv=4)):
+        assert vb(**kw) == ea.ATTN_ERR_INVALID_ARG, kw
+    assert vb(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert vb(d=256) == ea.ATTN_ERR_UNSUPPORTED
+    none = dict(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None,
+                ws=None, cu=None)
+    assert vb(nseq=0, **none) == ea.ATTN_OK

@@ -118,3 +118,101 @@ def test_full_size_documents_sampled_heads(oracle_mod):
         ro, rl = oracle_mod.fwd_varlen(q[h:h + 1], k[g:g + 1], v[g:g + 1], cu.numpy(),
                                        causal=w.causal)
         check(o[h:h + 1], lse[h:h + 1], ro, rl, f"{w.name} head {h}")
+
+
+# ---------------------------------------------------------------- backward
+def varlen_bwd_reference(oracle_mod, q, k, v, do, cu, causal):
+    """The oracle's dense backward on each sequence's slices, put back in place."""
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for a, b in zip(cu[:-1].tolist(), cu[1:].tolist()):
+        if b == a:
+            continue
+        sl = slice(a, b)
+        g = oracle_mod.bwd(q[None, :, sl].contiguous(), k[None, :, sl].contiguous(),
+                           v[None, :, sl].contiguous(), do[None, :, sl].contiguous(), causal=causal)
+        dq[:, sl], dk[:, sl], dv[:, sl] = g[0][0], g[1][0], g[2][0]
+    return dq, dk, dv
+
+
+def grad_ok(name, g, r):
+    g = g.float().cpu().numpy()
+    e, m = np.abs(g - r).max(), np.abs(r).max()
+    assert np.all(np.isfinite(g)), f"{name}: non-finite"
+    assert e <= 5e-2 * m, f"{name}: max err {e} vs max ref {m}"
+    assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 2e-2, f"{name}: Frobenius"
+
+
+BWD_LENGTHS = [[5, 7, 130, 1, 64], [0, 300, 0, 3], [129, 257]]
+
+
+@pytest.mark.parametrize("lengths", BWD_LENGTHS, ids=[str(x) for x in BWD_LENGTHS])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_packed_sequences(oracle_mod, lengths, d, causal):
+    # starts that are not multiples of 4 or 64 exercise the statistics reads
+    dev = gpu()
+    q, k, v, cu = attn_inputs.make_varlen(4, 2, lengths, d, seed=sum(lengths) + 7)
+    g = torch.Generator().manual_seed(5)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    mx = max(lengths)
+    qg, kg, vg, dog, cug = (t.to(dev) for t in (q, k, v, do, cu))
+    o, lse = ea.fwd_varlen(qg, kg, vg, cug, mx, causal=causal)
+    dq, dk, dv = ea.bwd_varlen(qg, kg, vg, o, lse, dog, cug, mx, causal=causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q, k, v, do, cu, causal)
+    for name, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        grad_ok(f"{name} {lengths} d={d}", gg, r)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_one_sequence_is_attn_bwd_bitwise(d):
+    dev = gpu()
+    q, k, v, cu = (t.to(dev) for t in attn_inputs.make_varlen(4, 2, [777], d, seed=9))
+    do = torch.randn_like(q)
+    o, lse = ea.fwd_varlen(q, k, v, cu, 777, causal=True)
+    g1 = ea.bwd_varlen(q, k, v, o, lse, do, cu, 777, causal=True)
+    g2 = ea.bwd(q[None], k[None], v[None], o[None], lse[None], do[None], causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b[0])
+
+
+def test_backward_deterministic_and_fp16(oracle_mod):
+    dev = gpu()
+    lengths = [300, 1, 45, 512]
+    q, k, v, cu = attn_inputs.make_varlen(8, 2, lengths, 64, seed=17, dtype="fp16")
+    g = torch.Generator().manual_seed(6)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    qg, kg, vg, dog, cug = (t.to(dev) for t in (q, k, v, do, cu))
+    o, lse = ea.fwd_varlen(qg, kg, vg, cug, 512, causal=True)
+    ref = ea.bwd_varlen(qg, kg, vg, o, lse, dog, cug, 512, causal=True)
+    for _ in range(3):
+        again = ea.bwd_varlen(qg, kg, vg, o, lse, dog, cug, 512, causal=True)
+        for a, b in zip(ref, again):
+            assert torch.equal(a, b)
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q, k, v, do, cu, True)
+    for name, gg, r in (("dQ", ref[0], rdq), ("dK", ref[1], rdk), ("dV", ref[2], rdv)):
+        grad_ok(name, gg, r)
+
+
+def test_backward_full_size_documents_sampled_heads(oracle_mod):
+    w = attn_inputs.VARLEN_WORKLOADS["docs"]
+    lengths = attn_inputs.varlen_lengths(w)
+    q, k, v, cu = attn_inputs.make_varlen(w.Hq, w.Hkv, lengths, w.d, seed=w.seed)
+    g = torch.Generator().manual_seed(w.seed + 100)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    dev = gpu()
+    mx = max(lengths)
+    qg, kg, vg, dog, cug = (t.to(dev) for t in (q, k, v, do, cu))
+    o, lse = ea.fwd_varlen(qg, kg, vg, cug, mx, causal=w.causal)
+    dq, dk, dv = ea.bwd_varlen(qg, kg, vg, o, lse, dog, cug, mx, causal=w.causal)
+    torch.cuda.synchronize()
+    group = w.Hq // w.Hkv
+    # kv head 0 and its query heads: dK/dV sum over the group's query heads
+    hs = slice(0, group)
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q[hs], k[0:1], v[0:1], do[hs], cu, w.causal)
+    grad_ok("dQ", dq[hs], rdq)
+    grad_ok("dK", dk[0:1], rdk)
+    grad_ok("dV", dv[0:1], rdv)
