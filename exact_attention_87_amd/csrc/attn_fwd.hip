@@ -59,7 +59,18 @@ namespace attn {
 #define ATTN_FWD_NW128 4
 #endif
 
-// Per head dim: a value for d = 64, 128 and 256.
+// Work map of the forward grids (nqb query blocks x BH (batch, head) slices):
+// the heaviest query blocks first under the causal mask; the heads of one
+// kv group are adjacent.  (Keeping a kv group's blocks on one XCD's L2 was
+// measured slower: it breaks the heaviest-first order.)
+template <bool CAUSAL>
+__device__ __forceinline__ void work_item(int nqb, int BH, int& qb, int& bh) {
+  const int id = blockIdx.x;
+  qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
+  bh = id % BH;
+}
+
+// Per head dim: a value for d = 64, 128 and 256.// Per head dim: a value for d = 64, 128 and 256.
 template <int D>
 constexpr int by_dim(int v64, int v128, int v256) {
   return D == 64 ? v64 : D == 128 ? v128 : v256;
@@ -106,9 +117,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   // Work map: heaviest query blocks first for the causal case; the heads of
   // one key/value group are adjacent so they share K/V in cache.
   const int BH = gridDim.x / nqb;
-  const int id = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-  const int bh = id % BH;
+  int qb, bh;
+  work_item<CAUSAL>(nqb, BH, qb, bh);
   // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
@@ -436,9 +446,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #define ATTN_PIPE_VPM256 6
 #endif
 
+#ifndef ATTN_PIPE_NW
+#define ATTN_PIPE_NW 4
+#endif
+
 template <int D>
 struct PipeCfg {
-  static constexpr int NW = 4;
+  static constexpr int NW = ATTN_PIPE_NW;  // waves per workgroup (32 query rows each)
   static constexpr int BR = 32 * NW;
   static constexpr int BC = 64;
   static constexpr int WPE = by_dim<D>(ATTN_PIPE_WPE64, ATTN_PIPE_WPE128, 1);
@@ -472,9 +486,8 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   const int hf = lane >> 5;
 
   const int BH = gridDim.x / nqb;
-  const int id = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-  const int bh = id % BH;
+  int qb, bh;
+  work_item<CAUSAL>(nqb, BH, qb, bh);
   // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
@@ -622,8 +635,10 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
           }
       }
       uint32_t pk[2][8];
+      const char* vt = vstage(BUF);
+      const bool ahead = j + 1 < ntiles && wave_active(j + 1);
       float tsum;
-      if (j + 1 < ntiles && wave_active(j + 1)) {
+      if (ahead) {
         __builtin_amdgcn_sched_barrier(0);
         scores(kstage(BUF ^ 1), sn);
         tsum = softmax_exp(sc, ms, pk);
@@ -663,7 +678,6 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
         }
       }
       lsum += tsum;
-      const char* vt = vstage(BUF);
       if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
