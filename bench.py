@@ -2,8 +2,9 @@
 """Attention throughput on one MI355X: forward + recompute backward.
 
 One step is the whole hot path once over one batch of seeded synthetic input:
-attn_fwd, then the backward's three stages (attn_bwd_preprocess,
-attn_bwd_dkdv, attn_bwd_dq), all through the C ABI on one stream.  The
+attn_fwd, then the backward's two stages (attn_bwd_dq_stats, the dQ stage
+that also writes the row statistics, then attn_bwd_dkdv: exactly what
+attn_bwd launches), all through the C ABI on one stream.  The
 workload is the causal forward + backward problem B=8, H=16, N=2048, d=64
 (bf16 I/O, fp32 accumulation).  Inputs are resident in device memory before
 the timed region starts.
@@ -439,26 +440,24 @@ def main():
         ("fwd", lambda: check(ea.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                           lse.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF,
                                           sp), "attn_fwd")),
-        ("bwd_preprocess", lambda: check(ea.attn_bwd_preprocess(
-            o.data_ptr(), do.data_ptr(), lse.data_ptr(), stats.data_ptr(), B, Hq, N, d, BF, sp),
-            "attn_bwd_preprocess")),
+        ("bwd_dq", lambda: check(ea.attn_bwd_dq_stats(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            stats.data_ptr(), dq.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF, sp),
+            "attn_bwd_dq_stats")),
         ("bwd_dkdv", lambda: check(ea.attn_bwd_dkdv(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), stats.data_ptr(),
             dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF, sp),
             "attn_bwd_dkdv")),
-        ("bwd_dq", lambda: check(ea.attn_bwd_dq(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), stats.data_ptr(),
-            dq.data_ptr(), B, Hq, Hkv, N, d, causal, scale, BF, sp), "attn_bwd_dq")),
     ]
     f1 = fwd_flops(B, Hq, N, d, w.causal)  # = 4*B*H*N^2*d/2
     unit = f1 / 4.0  # B*H*N^2*d/2
     algo = {  # algorithmic FLOPs and HBM bytes per launch
         "fwd": {"flops": 4 * unit, "bytes": (2 * B * Hq + 2 * B * Hkv) * N * d * 2 + B * Hq * N * 4},
-        "bwd_preprocess": {"flops": 0.0, "bytes": 2 * B * Hq * N * d * 2 + 3 * B * Hq * N * 4},
+        # dQ stage: Q, dO, O read, dQ written, K, V read; LSE read, statistics written
+        "bwd_dq": {"flops": 2 * unit,
+                   "bytes": (4 * B * Hq + 2 * B * Hkv) * N * d * 2 + 3 * B * Hq * N * 4},
         "bwd_dkdv": {"flops": 8 * unit,
                      "bytes": (2 * B * Hq + 4 * B * Hkv) * N * d * 2 + 2 * B * Hq * N * 4},
-        "bwd_dq": {"flops": 2 * unit,
-                   "bytes": (3 * B * Hq + 2 * B * Hkv) * N * d * 2 + 2 * B * Hq * N * 4},
     }
     step_flops = 14 * unit
 
@@ -586,7 +585,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d,
                    "causal": bool(causal), "scale": scale, "seed": w.seed,
-                   "step": "attn_fwd + attn_bwd_preprocess + attn_bwd_dkdv + attn_bwd_dq"},
+                   "step": "attn_fwd + attn_bwd_dq_stats + attn_bwd_dkdv"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "peak_tflops_bf16": round(PEAK_BF16_TFLOPS, 1),
         "gpu_ms_per_step": round(gpu_ms, 5),

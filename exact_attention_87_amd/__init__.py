@@ -65,6 +65,8 @@ def lib():
         L.attn_bwd_dkdv.restype = ci
         L.attn_bwd_dq.argtypes = [vp] * 6 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd_dq.restype = ci
+        L.attn_bwd_dq_stats.argtypes = [vp] * 8 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
+        L.attn_bwd_dq_stats.restype = ci
         L.attn_fwd_splitkv.argtypes = [vp] * 6 + [ci] * 7 + [cf, ci, ci, vp]
         L.attn_fwd_splitkv.restype = ci
         L.attn_fwd_splitkv_num_splits.argtypes = [ci] * 7
@@ -126,6 +128,12 @@ def attn_bwd_dq(q, k, v, dout, stats, dq, B, Hq, Hkv, N, d, causal, scale, dtype
                 stream) -> int:
     return int(lib().attn_bwd_dq(q, k, v, dout, stats, dq, B, Hq, Hkv, N, d, int(causal),
                                  float(scale), int(dtype), stream))
+
+
+def attn_bwd_dq_stats(q, k, v, o, lse, dout, stats, dq, B, Hq, Hkv, N, d, causal, scale, dtype,
+                      stream) -> int:
+    return int(lib().attn_bwd_dq_stats(q, k, v, o, lse, dout, stats, dq, B, Hq, Hkv, N, d,
+                                       int(causal), float(scale), int(dtype), stream))
 
 
 def attn_fwd_splitkv(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, causal, scale,

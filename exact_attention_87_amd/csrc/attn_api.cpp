@@ -177,10 +177,29 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   if (st != ATTN_OK) return st;
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
   a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
-  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
+  // dQ first: it also writes the row statistics the dK/dV stage reads
+  if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
+}
+
+attn_status attn_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, float* stats, void* dq, int B,
+                              int Hq, int Hkv, int N, int d, int causal, float scale,
+                              attn_dtype dtype, void* stream) {
+  attn::BwdArgs a;
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if (a.N == 0) return ATTN_OK;  // empty problem
+  const Sizes z = sizes(B, Hq, Hkv, N, d);
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {lse, z.l}, {dout, z.q}},
+                     {{stats, z.st}, {dq, z.q}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
+  a.stats = stats, a.dq = dq;
+  return attn::launch_bwd_dq_stats(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, float* stats,
@@ -477,9 +496,9 @@ attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const 
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
   a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
   a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
-  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
+  // dQ first: it also writes the row statistics the dK/dV stage reads
+  if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 

@@ -22,7 +22,9 @@
 //         (Q, dO and the statistics) stream through LDS.
 //   dq:   one workgroup per (batch, query head, block of 128 queries); the
 //         forward's tiling, with dQ^T accumulated over key tiles that stream
-//         through LDS.
+//         through LDS.  The full backward of a dense problem runs dq first,
+//         in a variant that computes its rows' statistics itself (it already
+//         holds dO) and stores them for dkdv, so pre is not launched there.
 // Probabilities use base 2: P = 2^(s*c - LSE*log2 e), c = |scale| log2 e.  A
 // negative scale is folded into the sign bit of the register-resident operand
 // (Q in the dq kernel, K in the dkdv kernel) as it is loaded.  Query rows
@@ -389,13 +391,19 @@ struct DqCfg {
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+// With STATS the kernel also computes the row statistics the preprocess kernel
+// would (the same sums in the same order, so bit-identical) from O, dO and LSE,
+// and stores them, padding rows included, for the dK/dV kernel launched after
+// it: the workgroups of one head cover every padded row of its statistics.
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool STATS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<D>::WPE, DqCfg<D>::WPE)))
 void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                    const T* __restrict__ V, const T* __restrict__ dO,
-                   const float* __restrict__ stats, T* __restrict__ dQ, int Hq, int Hkv,
+                   const T* __restrict__ O, const float* __restrict__ LSE,
+                   float* __restrict__ stats, T* __restrict__ dQ, int Hq, int Hkv,
                    int Nmax, int nqb, Layout lay, float c, float qscale, uint32_t qsign,
                    const int* __restrict__ cu_seqlens, int ntok) {
+  static_assert(!(STATS && VARLEN), "packed sequences take their statistics from the preprocess");
   using Cfg = DqCfg<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
@@ -420,7 +428,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // another, dO has O's.
   int N = Nmax, h, Np, qrs, krs, ors;
   int64_t qoff, kvoff, ooff;
-  const float* st;  // this head's statistics rows, from the slice's first row on
+  float* st;  // this head's statistics rows, from the slice's first row on
   if constexpr (VARLEN) {
     const int seq = bh / Hq;
     h = bh - seq * Hq;
@@ -448,24 +456,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int q0 = qb * BR + w * 32;
   const int qrow = q0 + l32;
 
-  // Q^T and dO^T operands and this lane's row statistics, resident.
-  V8 qreg[NQC], doreg[NQC];
-  {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes(N, qrs, D));
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + ooff, slice_bytes(N, ors, D));
-#pragma unroll
-    for (int cc = 0; cc < NQC; ++cc) {
-      qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)((qrow * qrs + cc * 16 + hf * 8) * 2)) ^ qsign);
-      doreg[cc] = bitcast<V8>(buf_load16(rdo, (uint32_t)((qrow * ors + cc * 16 + hf * 8) * 2)));
-    }
-  }
-  const bool qok = qrow < N;
-  const float ndsum = qok ? st[qrow] : 0.f;  // -D of this lane's row
-  const float lse2 = qok ? st[Np + qrow] : 0.f;
-  f32x16 pinit;  // seeds dP^T - D
-#pragma unroll
-  for (int r = 0; r < 16; ++r) pinit[r] = ndsum;
-
   const int ntiles_all = (N + BC - 1) / BC;
   int ntiles = ntiles_all, wtiles = ntiles_all;
   if (CAUSAL) {
@@ -492,6 +482,65 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       buf_load16_lds(rv, kt + TILEB + (w * PW + i) * 1024, goff[i] + tbase);
     }
   };
+
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < ntiles) issue(j);
+
+  // Q^T and dO^T operands resident; loaded after the first K/V tiles are
+  // requested, so the two latencies overlap.
+  V8 qreg[NQC], doreg[NQC];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qoff, slice_bytes(N, qrs, D));
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + ooff, slice_bytes(N, ors, D));
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)((qrow * qrs + cc * 16 + hf * 8) * 2)) ^ qsign);
+      doreg[cc] = bitcast<V8>(buf_load16(rdo, (uint32_t)((qrow * ors + cc * 16 + hf * 8) * 2)));
+    }
+  }
+  V8 oreg[STATS ? NQC : 1];  // O, for D = dO . O
+  float lse_row = 0.f;
+  if constexpr (STATS) {
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + ooff, slice_bytes(N, ors, D));
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc)
+      oreg[cc] = bitcast<V8>(buf_load16(ro, (uint32_t)((qrow * ors + cc * 16 + hf * 8) * 2)));
+    if (qrow < N) lse_row = LSE[(int64_t)bh * N + qrow];
+  }
+  const bool qok = qrow < N;
+  float ndsum, lse2;  // -D and LSE log2(e) of this lane's row
+  if constexpr (STATS) {
+    // D = dO . O: per 8-column chunk an fma chain, then a pairwise tree over
+    // the chunks in column order (lane l and l^32 hold alternate chunks)
+    float part[NQC];
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaf((float)oreg[cc][e], (float)doreg[cc][e], a);
+      part[cc] = a;
+    }
+#pragma unroll
+    for (int cc = 0; cc < NQC; ++cc) part[cc] += __shfl_xor(part[cc], 32);
+#pragma unroll
+    for (int m = 1; m < NQC; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < NQC; i += 2 * m) part[i] += part[i + m];
+    ndsum = -part[0];  // rows past N read zeros: -0
+    lse2 = qok ? lse_row * kLog2e : 0.f;
+    if (hf == 0 && qrow < Np) {
+      st[qrow] = ndsum;
+      st[Np + qrow] = lse2;
+    }
+  } else {
+    ndsum = qok ? st[qrow] : 0.f;
+    lse2 = qok ? st[Np + qrow] : 0.f;
+  }
+  f32x16 pinit;  // seeds dP^T - D
+#pragma unroll
+  for (int r = 0; r < 16; ++r) pinit[r] = ndsum;
+
 
   int koff[NQC], troff[2][NMB];
 #pragma unroll
@@ -575,9 +624,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     }
   };
 
-#pragma unroll
-  for (int j = 0; j < NBUF - 1; ++j)
-    if (j < ntiles) issue(j);
   if (NBUF == 3 && ntiles > 1)
     wait_vm_barrier<2 * PW>();
   else
@@ -654,18 +700,18 @@ static hipError_t dkdv_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool STATS = false>
 static hipError_t dq_t(const BwdArgs& a) {
   using Cfg = DqCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
   const int nqb = (a.N + Cfg::BR - 1) / Cfg::BR;
   const int64_t grid = (int64_t)nqb * a.B * a.Hq;
-  const hipError_t e = allow_lds(bwd_dq_kernel<T, D, CAUSAL, VARLEN>, Cfg::LDS);
+  const hipError_t e = allow_lds(bwd_dq_kernel<T, D, CAUSAL, VARLEN, STATS>, Cfg::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(256),
-                     Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (const T*)a.dout, a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N, nqb, layout_of(a),
-                     k.c, a.scale, k.qsign, a.cu_seqlens, a.T);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, VARLEN, STATS>), dim3((unsigned)grid),
+                     dim3(256), Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     (const T*)a.dout, (const T*)a.o, a.lse, a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N,
+                     nqb, layout_of(a), k.c, a.scale, k.qsign, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 
@@ -694,6 +740,12 @@ static hipError_t bwd_dq_for(const BwdArgs& a) {
   return a.causal ? dq_t<T, 128, true, false>(a) : dq_t<T, 128, false, false>(a);
 }
 
+template <typename T>
+static hipError_t bwd_dq_stats_for(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dq_t<T, 64, true, false, true>(a) : dq_t<T, 64, false, false, true>(a);
+  return a.causal ? dq_t<T, 128, true, false, true>(a) : dq_t<T, 128, false, false, true>(a);
+}
+
 hipError_t launch_bwd_pre(const BwdArgs& a) {
   if (a.dtype == kBF16) return bwd_pre_for<__bf16>(a);
   if (a.dtype == kF16) return bwd_pre_for<_Float16>(a);
@@ -709,6 +761,13 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a) {
 hipError_t launch_bwd_dq(const BwdArgs& a) {
   if (a.dtype == kBF16) return bwd_dq_for<__bf16>(a);
   if (a.dtype == kF16) return bwd_dq_for<_Float16>(a);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_bwd_dq_stats(const BwdArgs& a) {
+  if (a.cu_seqlens) return hipErrorNotSupported;
+  if (a.dtype == kBF16) return bwd_dq_stats_for<__bf16>(a);
+  if (a.dtype == kF16) return bwd_dq_stats_for<_Float16>(a);
   return hipErrorNotSupported;
 }
 

@@ -120,5 +120,8 @@ size_t bwd_stats_bytes(int B, int Hq, int N);
 hipError_t launch_bwd_pre(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
+// dQ that also computes and stores the row statistics (dense problems only),
+// so the dK/dV stage can follow it with no preprocess launch.
+hipError_t launch_bwd_dq_stats(const BwdArgs& a);
 
 }  // namespace attn

@@ -112,9 +112,11 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      float scale, attn_dtype dtype, void* stream);
 
 /*
- * The three stages attn_bwd runs, in order, on one stream.  Exposed so a
- * caller can schedule or time them separately; calling them in this order
- * with the same arguments gives exactly attn_bwd's results.
+ * The backward as three separate stages on one stream, exposed so a caller
+ * can schedule or time them separately; calling them in this order with the
+ * same arguments gives exactly attn_bwd's results (bit for bit).  attn_bwd
+ * itself launches two kernels: the dQ stage in a variant that also computes
+ * and stores the statistics below, then the dK/dV stage.
  *
  * `stats` is the backward workspace (attn_bwd_workspace_bytes bytes, caller
  * owned): per (batch, query head) two fp32 rows of Np = N rounded up to 64
@@ -136,6 +138,19 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const voi
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                         const float* stats, void* dq, int B, int Hq, int Hkv, int N, int d,
                         int causal, float scale, attn_dtype dtype, void* stream);
+
+/*
+ * The dQ stage fused with the preprocess: dQ as attn_bwd_dq computes it, and
+ * the statistics attn_bwd_preprocess would write (bit for bit), computed by
+ * the same workgroups from o, dout and lse and written to `stats` (which is
+ * an output here; its prior contents are ignored).  attn_bwd is this call
+ * followed by attn_bwd_dkdv.  Arguments, validation, ownership and error
+ * behaviour are attn_bwd's, with `stats` in place of its workspace.
+ */
+attn_status attn_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, float* stats, void* dq, int B,
+                              int Hq, int Hkv, int N, int d, int causal, float scale,
+                              attn_dtype dtype, void* stream);
 
 /*
  * Split-K/V forward, for few queries against many keys (decoding one token,

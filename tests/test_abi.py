@@ -25,7 +25,7 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
-                                  "attn_bwd_preprocess", "attn_bwd_strided", "attn_bwd_varlen",
+                                  "attn_bwd_dq_stats", "attn_bwd_preprocess", "attn_bwd_strided", "attn_bwd_varlen",
                                   "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
@@ -172,6 +172,14 @@ def test_staged_backward_validation():
     f32 = list(args)
     f32[7] = ea.ATTN_F32
     assert ea.attn_bwd_dkdv(Q, K, V, DO, WS, DK, DV, *f32) == ea.ATTN_ERR_UNSUPPORTED
+    # the fused dQ + statistics stage: stats is an output here
+    assert ea.attn_bwd_dq_stats(*([None] * 8), 2, 4, 2, 0, 64, 1, 0.1, ea.ATTN_BF16,
+                                None) == ea.ATTN_OK
+    assert ea.attn_bwd_dq_stats(Q, K, V, O, L, DO, WS, DQ, *bad) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq_stats(Q, K, V, O, L, DO, None, DQ, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq_stats(Q, K, V, O, L, DO, WS, WS + 256, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq_stats(Q, K, V, O, L, DO, O + 64, DQ, *args) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.attn_bwd_dq_stats(Q, K, V, O, L, DO, WS, DQ, *f32) == ea.ATTN_ERR_UNSUPPORTED
 
 
 # ---------------------------------------------------------------- split K/V

@@ -143,6 +143,37 @@ def test_bwd_constant_values_give_zero_dq_dk():
     assert dk.float().abs().max() <= 1e-2 * dv.float().abs().max()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fused_dq_statistics_equal_the_preprocess(d, causal):
+    """attn_bwd_dq_stats writes the preprocess kernel's statistics bit for bit
+    (padding rows included, over a buffer that starts as NaN), and its dQ is
+    attn_bwd_dq's."""
+    dev = gpu()
+    B, Hq, Hkv, N = 2, 4, 2, 200  # Np = 256: 56 padding rows; the last block holds 72 rows
+    q, k, v, do = (t.to(dev) for t in attn_inputs.make(B, Hq, Hkv, N, d, "bf16", seed=16,
+                                                       with_dout=True))
+    o, lse = ea.fwd(q, k, v, causal=causal)
+    Np = (N + 63) // 64 * 64
+    s = torch.cuda.current_stream().cuda_stream
+    sc = d ** -0.5
+    st_pre = torch.full((B * Hq, 2, Np), float("nan"), device=dev, dtype=torch.float32)
+    st_fused = torch.full_like(st_pre, float("nan"))
+    dq_pre, dq_fused = torch.empty_like(q), torch.empty_like(q)
+    assert ea.attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), st_pre.data_ptr(),
+                                  B, Hq, N, d, ea.ATTN_BF16, s) == ea.ATTN_OK
+    assert ea.attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                          st_pre.data_ptr(), dq_pre.data_ptr(), B, Hq, Hkv, N, d, causal, sc,
+                          ea.ATTN_BF16, s) == ea.ATTN_OK
+    assert ea.attn_bwd_dq_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), do.data_ptr(), st_fused.data_ptr(),
+                                dq_fused.data_ptr(), B, Hq, Hkv, N, d, causal, sc, ea.ATTN_BF16,
+                                s) == ea.ATTN_OK
+    torch.cuda.synchronize()
+    assert torch.equal(st_pre.view(torch.int32), st_fused.view(torch.int32))
+    assert torch.equal(dq_pre, dq_fused)
+
+
 def test_staged_backward_equals_attn_bwd():
     dev = gpu()
     B, Hq, Hkv, N, d = 2, 8, 2, 333, 128
@@ -174,6 +205,18 @@ def test_staged_backward_equals_attn_bwd():
     ref_l = lse.reshape(B * Hq, N) * 1.4426950408889634
     assert (stats[:, 1, :N] - ref_l).abs().max() <= 1e-5 * ref_l.abs().max()
     assert bool((stats[:, :, N:] == 0).all())
+    # the two-launch order attn_bwd uses: dQ with the statistics, then dK/dV
+    stats.fill_(float("nan"))
+    dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    assert ea.attn_bwd_dq_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), do.data_ptr(), stats.data_ptr(), dq2.data_ptr(),
+                                B, Hq, Hkv, N, d, 1, sc, ea.ATTN_BF16, s) == ea.ATTN_OK
+    assert ea.attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                            stats.data_ptr(), dk2.data_ptr(), dv2.data_ptr(),
+                            B, Hq, Hkv, N, d, 1, sc, ea.ATTN_BF16, s) == ea.ATTN_OK
+    torch.cuda.synchronize()
+    for a, b in zip(ref, (dq2, dk2, dv2)):
+        assert torch.equal(a, b)
 
 
 def test_bwd_empty():
