@@ -49,7 +49,7 @@ attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float 
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F16) return ATTN_ERR_INVALID_ARG;
-  // d = 256: 16-bit forward paths only (the callers below say which)
+  // d = 256: 16-bit paths only (the callers below say which)
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   // Limits of the kernels' 32-bit grid, row and byte offsets: one (batch,
   // head) slice stays below 1 GiB.
@@ -97,7 +97,7 @@ attn_status bwd_common(int B, int Hq, int Hkv, int N, int d, int causal, float s
   bool empty = false;
   attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
-  if (dtype == ATTN_F32 || d == 256) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (empty) return ATTN_OK;  // a->N stays 0
   a->B = B, a->Hq = Hq, a->Hkv = Hkv, a->N = N, a->d = d;
   a->causal = causal == 1, a->scale = scale, a->dtype = (attn::Dtype)dtype;
@@ -154,7 +154,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype) {
   bool empty = false;
   if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
-  if (dtype == ATTN_F32 || d == 256) return (size_t)-1;
+  if (dtype == ATTN_F32) return (size_t)-1;
   if (empty) return 0;
   const size_t bytes = attn::bwd_stats_bytes(B, Hq, N);
   return (bytes + 255) & ~(size_t)255;

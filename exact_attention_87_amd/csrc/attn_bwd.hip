@@ -187,14 +187,19 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
   // Direct loads of a query tile: Q and dO pieces as in the forward, plus
   // the 512 bytes of statistics (wave 0, lanes 0..31).
-  uint32_t goffq[PW], goffo[PW];
-#pragma unroll
-  for (int i = 0; i < PW; ++i) {
+  // (kept in registers up to d = 128; recomputed per load at d = 256)
+  auto gpiece = [&](int i, int rs) {
     const int o = (w * PW + i) * 1024 + lane * 16;
     const int row = o / ROWB;
     const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
-    goffq[i] = (uint32_t)((row * qrs + ch * 8) * 2);
-    goffo[i] = (uint32_t)((row * ors + ch * 8) * 2);
+    return (uint32_t)((row * rs + ch * 8) * 2);
+  };
+  constexpr int PWK = D > 128 ? 1 : PW;
+  uint32_t goffq[PWK], goffo[PWK];
+#pragma unroll
+  for (int i = 0; i < PWK; ++i) {
+    goffq[i] = gpiece(i, qrs);
+    goffo[i] = gpiece(i, ors);
   }
   const uint32_t soff = (uint32_t)((lane >> 4) * Np * 4 + (lane & 15) * 16);
   auto issue = [&](int it) {
@@ -206,8 +211,10 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     const uint32_t tq = (uint32_t)(qt * BQ * qrs * 2), to = (uint32_t)(qt * BQ * ors * 2);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      buf_load16_lds(rq, base + (w * PW + i) * 1024, goffq[i] + tq);
-      buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, goffo[i] + to);
+      const uint32_t gq = PWK == PW ? goffq[i % PWK] : gpiece(i, qrs);
+      const uint32_t go = PWK == PW ? goffo[i % PWK] : gpiece(i, ors);
+      buf_load16_lds(rq, base + (w * PW + i) * 1024, gq + tq);
+      buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, go + to);
     }
     if (w == 0 && lane < 32) {
       // this head's two statistics rows from the sequence's first token on
@@ -231,27 +238,31 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       wait_vm_barrier<LOADS>();
   };
 
-  // Per-lane LDS offsets inside a stage (fixed for the whole loop).
-  int qoff_[NQC], troff[2][NMB];
+  // Per-lane LDS offsets inside a stage (fixed for the whole loop).  The
+  // swizzle only permutes chunks within aligned groups of 16, so at d = 256
+  // the second half of a row's offsets are the first half's plus 256 bytes
+  // (an immediate of the LDS read) and are not kept in registers.
+  constexpr int NQO = D > 128 ? NQC / 2 : NQC, NMO = D > 128 ? NMB / 2 : NMB;
+  int qoff_[NQO], troff[2][NMO];
 #pragma unroll
-  for (int cc = 0; cc < NQC; ++cc) qoff_[cc] = tile_off<D>(l32, 2 * cc + hf);
+  for (int cc = 0; cc < NQO; ++cc) qoff_[cc] = tile_off<D>(l32, 2 * cc + hf);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) troff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
+    for (int mb = 0; mb < NMO; ++mb) troff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
+  auto qo = [&](int cc) { return qoff_[cc % NQO] + (cc / NQO) * 256; };
+  auto tro = [&](int t, int mb) { return troff[t][mb % NMO] + (mb / NMO) * 256; };
 
   // The three phases of one 32-query sub-block (rows qbase.. of the tile):
   //   A: S = Q K^T and dP - D = dO V^T - D on the matrix cores;
   //   V: P = 2^(S c - LSE), dS = P (dP - D), both packed to bf16 (vector ALU);
   //   C: dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.
+  // Operand chunks read per group: all at once up to d = 128; at d = 256,
+  // where K, V, dK and dV already hold 384 registers, four at a time, each
+  // group fenced off from the scheduler so the reads are not all hoisted.
+  constexpr int CG = D > 128 ? 2 : NQC;
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
                     f32x16& sacc, f32x16& pacc) {
-    u32x4 qa[NQC], da[NQC];
-#pragma unroll
-    for (int cc = 0; cc < NQC; ++cc) {
-      qa[cc] = lds_read16(qtile + qbase * ROWB + qoff_[cc]);
-      da[cc] = lds_read16(dotile + qbase * ROWB + qoff_[cc]);
-    }
     // the dP accumulator starts at -D of each row (element 4*rg+e is row
     // qbase + 8*rg + 4*hf + e)
 #pragma unroll
@@ -262,9 +273,19 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     }
     sacc = f32x16{};
 #pragma unroll
-    for (int cc = 0; cc < NQC; ++cc) {
-      sacc = mfma32(bitcast<V8>(qa[cc]), kreg[cc], sacc);
-      pacc = mfma32(bitcast<V8>(da[cc]), vreg[cc], pacc);
+    for (int c0 = 0; c0 < NQC; c0 += CG) {
+      u32x4 qa[CG], da[CG];
+#pragma unroll
+      for (int cc = 0; cc < CG; ++cc) {
+        qa[cc] = lds_read16(qtile + qbase * ROWB + qo(c0 + cc));
+        da[cc] = lds_read16(dotile + qbase * ROWB + qo(c0 + cc));
+      }
+#pragma unroll
+      for (int cc = 0; cc < CG; ++cc) {
+        sacc = mfma32(bitcast<V8>(qa[cc]), kreg[c0 + cc], sacc);
+        pacc = mfma32(bitcast<V8>(da[cc]), vreg[c0 + cc], pacc);
+      }
+      if constexpr (CG < NQC) __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto phaseV = [&](const float* lse2, int qbase, int qfirst, bool diag, const f32x16& sacc,
@@ -303,12 +324,14 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       const int rows = (qbase + 16 * cp) * ROWB;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        const u32x2 a0 = lds_read_tr(dotile + rows + troff[0][mb]);
-        const u32x2 a1 = lds_read_tr(dotile + rows + troff[1][mb]);
+        const u32x2 a0 = lds_read_tr(dotile + rows + tro(0, mb));
+        const u32x2 a1 = lds_read_tr(dotile + rows + tro(1, mb));
         dvacc[mb] = mfma32(bitcast<V8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, dvacc[mb]);
-        const u32x2 b0 = lds_read_tr(qtile + rows + troff[0][mb]);
-        const u32x2 b1 = lds_read_tr(qtile + rows + troff[1][mb]);
+        const u32x2 b0 = lds_read_tr(qtile + rows + tro(0, mb));
+        const u32x2 b1 = lds_read_tr(qtile + rows + tro(1, mb));
         dkacc[mb] = mfma32(bitcast<V8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
+        if constexpr (CG < NQC)
+          __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -717,33 +740,38 @@ static hipError_t dq_t(const BwdArgs& a) {
 
 template <typename T>
 static hipError_t bwd_pre_for(const BwdArgs& a) {
-  return a.d == 64 ? pre_t<T, 64>(a) : pre_t<T, 128>(a);
+  if (a.d == 64) return pre_t<T, 64>(a);
+  return a.d == 128 ? pre_t<T, 128>(a) : pre_t<T, 256>(a);
+}
+template <typename T, int D>
+static hipError_t dkdv_d(const BwdArgs& a) {
+  if (a.cu_seqlens)
+    return a.causal ? dkdv_t<T, D, true, true>(a) : dkdv_t<T, D, false, true>(a);
+  return a.causal ? dkdv_t<T, D, true, false>(a) : dkdv_t<T, D, false, false>(a);
 }
 template <typename T>
 static hipError_t bwd_dkdv_for(const BwdArgs& a) {
-  const bool vl = a.cu_seqlens != nullptr;
-  if (a.d == 64) {
-    if (vl) return a.causal ? dkdv_t<T, 64, true, true>(a) : dkdv_t<T, 64, false, true>(a);
-    return a.causal ? dkdv_t<T, 64, true, false>(a) : dkdv_t<T, 64, false, false>(a);
-  }
-  if (vl) return a.causal ? dkdv_t<T, 128, true, true>(a) : dkdv_t<T, 128, false, true>(a);
-  return a.causal ? dkdv_t<T, 128, true, false>(a) : dkdv_t<T, 128, false, false>(a);
+  if (a.d == 64) return dkdv_d<T, 64>(a);
+  return a.d == 128 ? dkdv_d<T, 128>(a) : dkdv_d<T, 256>(a);
+}
+template <typename T, int D>
+static hipError_t dq_d(const BwdArgs& a) {
+  if (a.cu_seqlens) return a.causal ? dq_t<T, D, true, true>(a) : dq_t<T, D, false, true>(a);
+  return a.causal ? dq_t<T, D, true, false>(a) : dq_t<T, D, false, false>(a);
 }
 template <typename T>
 static hipError_t bwd_dq_for(const BwdArgs& a) {
-  const bool vl = a.cu_seqlens != nullptr;
-  if (a.d == 64) {
-    if (vl) return a.causal ? dq_t<T, 64, true, true>(a) : dq_t<T, 64, false, true>(a);
-    return a.causal ? dq_t<T, 64, true, false>(a) : dq_t<T, 64, false, false>(a);
-  }
-  if (vl) return a.causal ? dq_t<T, 128, true, true>(a) : dq_t<T, 128, false, true>(a);
-  return a.causal ? dq_t<T, 128, true, false>(a) : dq_t<T, 128, false, false>(a);
+  if (a.d == 64) return dq_d<T, 64>(a);
+  return a.d == 128 ? dq_d<T, 128>(a) : dq_d<T, 256>(a);
 }
-
+template <typename T, int D>
+static hipError_t dq_stats_d(const BwdArgs& a) {
+  return a.causal ? dq_t<T, D, true, false, true>(a) : dq_t<T, D, false, false, true>(a);
+}
 template <typename T>
 static hipError_t bwd_dq_stats_for(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? dq_t<T, 64, true, false, true>(a) : dq_t<T, 64, false, false, true>(a);
-  return a.causal ? dq_t<T, 128, true, false, true>(a) : dq_t<T, 128, false, false, true>(a);
+  if (a.d == 64) return dq_stats_d<T, 64>(a);
+  return a.d == 128 ? dq_stats_d<T, 128>(a) : dq_stats_d<T, 256>(a);
 }
 
 hipError_t launch_bwd_pre(const BwdArgs& a) {

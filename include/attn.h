@@ -44,8 +44,7 @@
  *
  * Supported: dtype ATTN_BF16 or ATTN_F16 (16-bit inputs/outputs, fp32
  * accumulation on the matrix cores, probabilities rounded to the same 16-bit
- * type for the P V product) with d in {64, 128, 256} for the forward entry
- * points and d in {64, 128} for the backward; dtype ATTN_F32 (fp32
+ * type for the P V product) with d in {64, 128, 256}; dtype ATTN_F32 (fp32
  * throughout, vector ALUs, forward only) with d in {64, 128}.
  */
 #ifndef EXACT_ATTENTION_ATTN_H
@@ -292,8 +291,8 @@ attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* 
  * and dv may be interleaved slices of one packed gradient buffer, so they are
  * only required to address disjoint elements (not checked), while each must
  * stay clear of every input and of the workspace (checked on extents).
- * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}; with the dense strides the
- * result is attn_bwd's bit for bit.
+ * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128, 256}; with the dense
+ * strides the result is attn_bwd's bit for bit.
  */
 attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -308,7 +307,7 @@ attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const 
  * sequence only.  workspace: attn_bwd_workspace_bytes(1, Hq, Hkv, T, d,
  * dtype) bytes (the row statistics of the T packed tokens), caller owned.
  * Offsets are clamped on the device as in attn_fwd_varlen.  Deterministic.
- * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128}, T <= 2^22,
+ * Supported: ATTN_BF16 or ATTN_F16, d in {64, 128, 256}, T <= 2^22,
  * nseq * Hq <= 2^24; nseq == 0, T == 0 or max_seqlen == 0 launches nothing.
  */
 attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,

@@ -88,16 +88,18 @@ def test_fwd_unsupported_head_dim(d):
     assert fwd(d=d) == ea.ATTN_ERR_UNSUPPORTED
 
 
-def test_d256_is_forward_only_and_16_bit():
-    # accepted by the 16-bit forward paths (validation passes; no GPU here)
+def test_d256_is_16_bit_only():
+    # accepted by the 16-bit paths (validation passes; no GPU here)
     for dt in (ea.ATTN_BF16, ea.ATTN_F16):
         assert fwd(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
         assert split(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
         assert sparse(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
         assert varlen(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
     assert fwd(d=256, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
-    assert bwd(d=256) == ea.ATTN_ERR_UNSUPPORTED
-    assert ea.attn_bwd_workspace_bytes(1, 1, 1, 64, 256, ea.ATTN_BF16) == -1
+    for dt in (ea.ATTN_BF16, ea.ATTN_F16):
+        assert bwd(d=256, dtype=dt) not in (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    assert bwd(d=256, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert ea.attn_bwd_workspace_bytes(1, 1, 1, 64, 256, ea.ATTN_BF16) == 512
     assert sparse(d=256, N=(1 << 20) + 1) == ea.ATTN_ERR_UNSUPPORTED
 
 
@@ -393,7 +395,9 @@ def test_strided_backward_validation():
     assert sb(BNHD, dk=DQ + 128) not in ok  # interleaved gradient slices are allowed
     assert sb(BNHD, dk=WS + 64) == ea.ATTN_ERR_INVALID_ARG  # a gradient over the workspace
     assert sb(BNHD, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
-    assert sb(BNHD, d=256) == ea.ATTN_ERR_UNSUPPORTED
+    # token-major strides at d = 256: [B, N, H, 256]
+    b256 = [100 * 4 * 256, 256, 4 * 256, 100 * 2 * 256, 256, 2 * 256, 100 * 4 * 256, 256, 4 * 256]
+    assert sb(b256, d=256) not in ok
 
 
 def test_varlen_backward_validation():
@@ -413,7 +417,7 @@ def test_varlen_backward_validation():
                dict(ws=None), dict(cu=DQ + 16), dict(Hq=6, Hkv=4)):
         assert vb(**kw) == ea.ATTN_ERR_INVALID_ARG, kw
     assert vb(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
-    assert vb(d=256) == ea.ATTN_ERR_UNSUPPORTED
+    assert vb(d=256) not in ok
     none = dict(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None,
                 ws=None, cu=None)
     assert vb(nseq=0, **none) == ea.ATTN_OK
