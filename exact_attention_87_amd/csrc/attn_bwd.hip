@@ -39,17 +39,20 @@ namespace attn {
 
 constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 
+// Waves per SIMD of the backward kernels at d = 64 and 128 (d = 256: 1).
+// d = 64 fits three (168 registers) with operand reads in pairs and fenced
+// phases; the dQ kernel at d = 128 fits two.
 #ifndef ATTN_BWD_WPE64
-#define ATTN_BWD_WPE64 2
+#define ATTN_BWD_WPE64 3
 #endif
 #ifndef ATTN_BWD_WPE128
 #define ATTN_BWD_WPE128 1
 #endif
 #ifndef ATTN_DQ_WPE64
-#define ATTN_DQ_WPE64 2
+#define ATTN_DQ_WPE64 3
 #endif
 #ifndef ATTN_DQ_WPE128
-#define ATTN_DQ_WPE128 1
+#define ATTN_DQ_WPE128 2
 #endif
 
 __host__ __device__ constexpr int stat_rows(int N) { return (N + 63) / 64 * 64; }
@@ -95,7 +98,7 @@ struct DkdvCfg {
   static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 64;    // queries per tile (two 32-query sub-blocks)
   static constexpr int NBUF = D == 64 ? 3 : 2;
-  static constexpr int WPE = D == 64 ? ATTN_BWD_WPE64 : ATTN_BWD_WPE128;
+  static constexpr int WPE = D == 64 ? ATTN_BWD_WPE64 : D == 128 ? ATTN_BWD_WPE128 : 1;
   static constexpr int TILEB = BQ * D * 2;
   static constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q | dO | D | LSE*log2e
   static constexpr size_t LDS = (size_t)NBUF * STAGEB;
@@ -257,10 +260,11 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   //   A: S = Q K^T and dP - D = dO V^T - D on the matrix cores;
   //   V: P = 2^(S c - LSE), dS = P (dP - D), both packed to bf16 (vector ALU);
   //   C: dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.
-  // Operand chunks read per group: all at once up to d = 128; at d = 256,
-  // where K, V, dK and dV already hold 384 registers, four at a time, each
-  // group fenced off from the scheduler so the reads are not all hoisted.
-  constexpr int CG = D > 128 ? 2 : NQC;
+  // Operand chunks read per group: all at once at d = 128; two at a time,
+  // each group fenced off from the scheduler so the reads are not all
+  // hoisted, where registers are tight: d = 256 (K, V, dK and dV already
+  // hold 384) and d = 64 at three waves per SIMD (168 each).
+  constexpr int CG = D > 128 ? 2 : (Cfg::WPE >= 3 ? 2 : NQC);
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
                     f32x16& sacc, f32x16& pacc) {
     // the dP accumulator starts at -D of each row (element 4*rg+e is row
@@ -409,7 +413,7 @@ struct DqCfg {
   static constexpr int BR = 128;  // queries per workgroup (4 waves x 32)
   static constexpr int BC = 64;   // keys per tile
   static constexpr int NBUF = D == 64 ? 3 : 2;
-  static constexpr int WPE = D == 64 ? ATTN_DQ_WPE64 : ATTN_DQ_WPE128;
+  static constexpr int WPE = D == 64 ? ATTN_DQ_WPE64 : D == 128 ? ATTN_DQ_WPE128 : 1;
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
@@ -577,67 +581,70 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
 
+  // Under tight register budgets (three waves per SIMD at d = 64, two at
+  // d = 128) the two key blocks of a tile are kept apart by a scheduling
+  // fence and their operands read two chunks at a time; otherwise the
+  // scheduler may overlap them freely.
+  constexpr bool SEQ = D == 64 ? Cfg::WPE >= 3 : Cfg::WPE >= 2;
+  constexpr int CG = SEQ ? 2 : NQC;
+
   auto tile = [&](auto bufc, int j) {
     constexpr int BUF = decltype(bufc)::value;
     const char* kt = smem + BUF * 2 * TILEB;
     const char* vt = kt + TILEB;
     if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (j < wtiles && q0 < N) {
-      // S^T = K Q^T and dP^T = V dO^T for the tile's two 32-key blocks
-      f32x16 sacc[2], pacc[2];
+      const int k0 = j * BC;
+      const bool edge = (k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0));  // diagonal, tail
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
-        u32x4 ka[NQC], va[NQC];
+        // S^T = K Q^T and dP^T - D = V dO^T - D for the tile's 32-key block kbk
+        f32x16 sacc = f32x16{}, pacc = pinit;
 #pragma unroll
-        for (int cc = 0; cc < NQC; ++cc) {
-          ka[cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
-          va[cc] = lds_read16(vt + kbk * 32 * ROWB + koff[cc]);
+        for (int c0 = 0; c0 < NQC; c0 += CG) {
+          u32x4 ka[CG], va[CG];
+#pragma unroll
+          for (int cc = 0; cc < CG; ++cc) {
+            ka[cc] = lds_read16(kt + kbk * 32 * ROWB + koff[c0 + cc]);
+            va[cc] = lds_read16(vt + kbk * 32 * ROWB + koff[c0 + cc]);
+          }
+#pragma unroll
+          for (int cc = 0; cc < CG; ++cc) {
+            sacc = mfma32(bitcast<V8>(ka[cc]), qreg[c0 + cc], sacc);
+            pacc = mfma32(bitcast<V8>(va[cc]), doreg[c0 + cc], pacc);
+          }
         }
-        sacc[kbk] = f32x16{};
-        pacc[kbk] = pinit;
+        float pv[16];
 #pragma unroll
-        for (int cc = 0; cc < NQC; ++cc) {
-          sacc[kbk] = mfma32(bitcast<V8>(ka[cc]), qreg[cc], sacc[kbk]);
-          pacc[kbk] = mfma32(bitcast<V8>(va[cc]), doreg[cc], pacc[kbk]);
-        }
-      }
-      float pv[2][16];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pv[kbk][r] = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -lse2));
-      const int k0 = j * BC;
-      if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {  // diagonal and tail tiles
-        __asm__ volatile("");
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
+        for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(sacc[r], c, -lse2));
+        if (edge) {
+          __asm__ volatile("");
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kbk * 32 + acc_row(r, hf);
-            if (key >= N || (CAUSAL && key > qrow)) pv[kbk][r] = 0.f;
+            if (key >= N || (CAUSAL && key > qrow)) pv[r] = 0.f;
           }
-      }
-      uint32_t dsk[2][8];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
+        }
+        uint32_t dsk[8];
 #pragma unroll
         for (int r = 0; r < 16; r += 2)
-          dsk[kbk][r >> 1] = pack2<T>(pv[kbk][r] * pacc[kbk][r], pv[kbk][r + 1] * pacc[kbk][r + 1]);
-      // dQ^T += K^T dS^T
+          dsk[r >> 1] = pack2<T>(pv[r] * pacc[r], pv[r + 1] * pacc[r + 1]);
+        // dQ^T += K^T dS^T (per mb the same accumulation order as key block
+        // by key block)
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
+        for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
           for (int cp = 0; cp < 2; ++cp) {
             const int rows = (kbk * 32 + cp * 16) * ROWB;
             const u32x2 lo = lds_read_tr(kt + rows + troff[0][mb]);
             const u32x2 hi = lds_read_tr(kt + rows + troff[1][mb]);
             const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            const V8 sb = bitcast<V8>(u32x4{dsk[kbk][4 * cp], dsk[kbk][4 * cp + 1],
-                                                    dsk[kbk][4 * cp + 2], dsk[kbk][4 * cp + 3]});
+            const V8 sb = bitcast<V8>(
+                u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
             dqacc[mb] = mfma32(a, sb, dqacc[mb]);
           }
+        if constexpr (SEQ) __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (j + 1 < ntiles) {
       if (NBUF == 3 && j + 2 < ntiles)
