@@ -30,8 +30,11 @@ namespace attn {
 
 
 // Tuning knobs (compile-time; the defaults are the shipped configuration).
+// d = 64 runs four waves per SIMD (121 registers) with two LDS stages (32 KiB
+// per workgroup, four workgroups per CU); three waves with three stages was
+// 3-8% slower.
 #ifndef ATTN_FWD_WPE64
-#define ATTN_FWD_WPE64 3
+#define ATTN_FWD_WPE64 4
 #endif
 #ifndef ATTN_FWD_WPE128
 #define ATTN_FWD_WPE128 2
@@ -40,7 +43,7 @@ namespace attn {
 #define ATTN_FWD_SETPRIO 1
 #endif
 #ifndef ATTN_FWD_NBUF64
-#define ATTN_FWD_NBUF64 3
+#define ATTN_FWD_NBUF64 2
 #endif
 #ifndef ATTN_FWD_NBUF128
 #define ATTN_FWD_NBUF128 2
