@@ -25,18 +25,36 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Online softmax: the running maximum only moves when a tile's maximum
-// exceeds it by more than kTau (base-2 units), so probabilities stay below
-// 2^kTau = kSumMax; a lane whose tile sum passes kSumMax takes the max path.
-// Any kTau keeps the result: O and LSE use the same maximum, P keeps bf16's
-// relative precision at any magnitude, and the fp32 accumulators stay far
-// from overflow (at most 2^15 x N x |v|).  A large kTau makes the max path
-// rare for extreme logits; 15 keeps p within fp16's range as well.
-#ifndef ATTN_TAU
-#define ATTN_TAU 15
+// exceeds it by more than tau (base-2 units), so probabilities stay below
+// 2^tau; a lane whose tile sum passes 2^tau takes the max path.  Any tau
+// keeps the result: O and LSE use the same maximum, and P keeps the 16-bit
+// type's relative precision at any magnitude.  A large tau makes the max
+// path rare for extreme logits.  The bound is the P type's range: fp16 P
+// must stay below 65504 (tau = 15); bf16 has fp32's exponent range, and at
+// tau = 30 the fp32 accumulators (at most 2^30 x N x |v|) stay far from
+// overflow.
+#ifndef ATTN_TAU_BF16
+#define ATTN_TAU_BF16 30
 #endif
-static_assert(ATTN_TAU >= 1 && ATTN_TAU <= 30, "rescale threshold");
-constexpr float kTau = (float)ATTN_TAU;
-constexpr float kSumMax = (float)(1u << ATTN_TAU);
+#ifndef ATTN_TAU_F16
+#define ATTN_TAU_F16 15
+#endif
+static_assert(ATTN_TAU_BF16 >= 1 && ATTN_TAU_BF16 <= 30, "rescale threshold");
+static_assert(ATTN_TAU_F16 >= 1 && ATTN_TAU_F16 <= 15, "rescale threshold (fp16 range)");
+template <typename T>
+struct Tau;
+template <>
+struct Tau<__bf16> {
+  static constexpr int v = ATTN_TAU_BF16;
+};
+template <>
+struct Tau<_Float16> {
+  static constexpr int v = ATTN_TAU_F16;
+};
+template <typename T>
+constexpr float kTau = (float)Tau<T>::v;
+template <typename T>
+constexpr float kSumMax = (float)(1u << Tau<T>::v);
 
 template <typename To, typename From>
 __device__ __forceinline__ To bitcast(const From& x) {

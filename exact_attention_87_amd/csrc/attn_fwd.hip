@@ -316,7 +316,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         tsum[nb] = softmax_exp(sacc[nb], ms[nb], pk[nb]);
-        redo |= !(tsum[nb] <= kSumMax);
+        redo |= !(tsum[nb] <= kSumMax<T>);
       }
       if (__builtin_amdgcn_ballot_w64(redo) != 0) {
         __asm__ volatile("");
@@ -329,7 +329,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
             for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[nb][kbk][r]);
           mloc = __builtin_fmaxf(mloc, xor32(mloc));
           const float tmax = mloc * c;
-          if (__builtin_amdgcn_ballot_w64(tmax > ms[nb] + kTau) != 0) {
+          if (__builtin_amdgcn_ballot_w64(tmax > ms[nb] + kTau<T>) != 0) {
             const float mnew = __builtin_fmaxf(ms[nb], tmax);
             const float alpha = fast_exp2(ms[nb] - mnew);
             ms[nb] = mnew;
@@ -661,7 +661,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
       } else {
         tsum = softmax_exp(sc, ms, pk);
       }
-      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax)) != 0) {
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax<T>)) != 0) {
         __asm__ volatile("");
         float mloc = sc[0][0];
 #pragma unroll
@@ -670,7 +670,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
           for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sc[kbk][r]);
         mloc = __builtin_fmaxf(mloc, xor32(mloc));
         const float tmax = mloc * c;
-        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
+        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau<T>) != 0) {
           const float mnew = __builtin_fmaxf(ms, tmax);
           const float alpha = fast_exp2(ms - mnew);
           ms = mnew;

@@ -210,7 +210,7 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
       }
       uint32_t pk[2][8];
       float tsum = softmax_exp(sacc, pk);
-      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax)) != 0) {
+      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax<T>)) != 0) {
         __asm__ volatile("");
         float mloc = sacc[0][0];
 #pragma unroll
@@ -219,7 +219,7 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
           for (int rr = 0; rr < 16; ++rr) mloc = __builtin_fmaxf(mloc, sacc[kbk][rr]);
         mloc = __builtin_fmaxf(mloc, xor32(mloc));
         const float tmax = mloc * c;
-        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau) != 0) {
+        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau<T>) != 0) {
           const float mnew = __builtin_fmaxf(ms, tmax);
           const float alpha = fast_exp2(ms - mnew);
           ms = mnew;

@@ -99,6 +99,28 @@ def test_bf16_extreme_logits(oracle_mod, mult, causal):
     check_bf16(o, lse, ro, rl, f"q x{mult}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_force_rescales(oracle_mod, dtype, d, causal):
+    """Scores that grow by about 20 (base 2) per 64-key tile: the running
+    maximum is overtaken by more than the rescale threshold again and again
+    (every tile at fp16's 15, every other tile at bf16's 30)."""
+    g = torch.Generator().manual_seed(d + int(causal))
+    N, H = 700, 2
+    q = 1.0 + 0.3 * torch.randn(1, H, N, d, generator=g)
+    step = 20.0 / 64 / 1.4426950408889634 / d ** 0.5  # per key, in units of q.k
+    ramp = torch.arange(N, dtype=torch.float32)[None, None, :, None] * step
+    k = ramp + 0.3 * torch.randn(1, H, N, d, generator=g)
+    v = torch.randn(1, H, N, d, generator=g)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float16
+    q, k, v = (t.to(td) for t in (q, k, v))
+    o, lse = run(q, k, v, causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    assert rl.max() > 100  # the logits really span many thresholds
+    check_bf16(o, lse, ro, rl, f"rising {dtype} d={d}")
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5, 1e-3])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_scales(oracle_mod, scale, causal):
