@@ -67,6 +67,10 @@ def lib():
         L.attn_bwd_dq.restype = ci
         L.attn_bwd_dq_stats.argtypes = [vp] * 8 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd_dq_stats.restype = ci
+        L.attn_fwd_varlen_strided.argtypes = [vp] * 7 + [ci] * 7 + [cf, ci, vp]
+        L.attn_fwd_varlen_strided.restype = ci
+        L.attn_bwd_varlen_strided.argtypes = [vp] * 12 + [ci] * 7 + [cf, ci, vp]
+        L.attn_bwd_varlen_strided.restype = ci
         L.attn_fwd_splitkv.argtypes = [vp] * 6 + [ci] * 7 + [cf, ci, ci, vp]
         L.attn_fwd_splitkv.restype = ci
         L.attn_fwd_splitkv_num_splits.argtypes = [ci] * 7
@@ -197,6 +201,24 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, ns
                                      int(dtype), stream))
 
 
+def attn_fwd_varlen_strided(q, k, v, o, lse, cu_seqlens, strides, nseq, max_seqlen, Hq, Hkv, T, d,
+                            causal, scale, dtype, stream) -> int:
+    """strides: 6 element strides (q_h, q_t, kv_h, kv_t, o_h, o_t)."""
+    arr = (ctypes.c_longlong * 6)(*[int(x) for x in strides])
+    return int(lib().attn_fwd_varlen_strided(q, k, v, o, lse, cu_seqlens, arr, nseq, max_seqlen,
+                                             Hq, Hkv, T, d, int(causal), float(scale), int(dtype),
+                                             stream))
+
+
+def attn_bwd_varlen_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, strides, nseq,
+                            max_seqlen, Hq, Hkv, T, d, causal, scale, dtype, stream) -> int:
+    """strides: 6 element strides (q/dq, k/v/dk/dv, o/dout; head, token each)."""
+    arr = (ctypes.c_longlong * 6)(*[int(x) for x in strides])
+    return int(lib().attn_bwd_varlen_strided(q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                                             cu_seqlens, arr, nseq, max_seqlen, Hq, Hkv, T, d,
+                                             int(causal), float(scale), int(dtype), stream))
+
+
 # ------------------------------------------------------------ torch conveniences
 def _dtype_code(t) -> int:
     import torch
@@ -318,32 +340,61 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
     return out, lse
 
 
+def _ht_strides(t):
+    """(head, token) element strides of an [H, T, d] view with a unit stride in d."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("tensors must be 3-D [H, T, d] views with contiguous d")
+    return [t.stride(0), t.stride(1)]
+
+
+def _check_cu(cu_seqlens):
+    import torch
+
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a device int32 vector")
+
+
 def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
                scale: float | None = None, out=None, lse=None):
-    """O [Hq,T,d], LSE [Hq,T] of packed sequences: q [Hq,T,d], k/v [Hkv,T,d] (bf16),
-    cu_seqlens a device int32 tensor of nseq+1 token offsets."""
+    """O [Hq,T,d], LSE [Hq,T] of packed sequences: q [Hq,T,d], k/v [Hkv,T,d] (16-bit),
+    cu_seqlens a device int32 tensor of nseq+1 token offsets.  q, k, v (and out)
+    may be [H, T, d] views of any (head, token) strides, e.g. [T, H, d] tensors
+    transposed; then out defaults to a [T, Hq, d] tensor viewed as [Hq, T, d]."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor [H, T, d]")
+        if t.dim() != 3 or not t.is_cuda or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a device tensor [H, T, d] with contiguous d")
     Hq, T, d = q.shape
     Hkv = k.shape[0]
     if k.shape != v.shape or k.shape[1:] != (T, d):
         raise ValueError("k and v must be [Hkv, T, d] matching q")
-    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
-        raise ValueError("cu_seqlens must be a device int32 vector")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    _check_cu(cu_seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    dense = all(t.is_contiguous() for t in (q, k, v)) and (out is None or out.is_contiguous())
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q) if dense else \
+            torch.empty((T, Hq, d), device=q.device, dtype=q.dtype).transpose(0, 1)
     if lse is None:
         lse = torch.empty((Hq, T), device=q.device, dtype=torch.float32)
-    st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                         cu_seqlens.data_ptr(), cu_seqlens.numel() - 1, int(max_seqlen), Hq, Hkv, T,
-                         d, causal, scale, _dtype_code(q), _stream_ptr(q))
+    nseq = cu_seqlens.numel() - 1
+    if dense:
+        st = attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), cu_seqlens.data_ptr(), nseq, int(max_seqlen), Hq, Hkv,
+                             T, d, causal, scale, _dtype_code(q), _stream_ptr(q))
+        what = "attn_fwd_varlen"
+    else:
+        strides = _ht_strides(q) + _ht_strides(k) + _ht_strides(out)
+        st = attn_fwd_varlen_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), cu_seqlens.data_ptr(), strides, nseq,
+                                     int(max_seqlen), Hq, Hkv, T, d, causal, scale,
+                                     _dtype_code(q), _stream_ptr(q))
+        what = "attn_fwd_varlen_strided"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_varlen")
+        raise AttnError(st, what)
     return out, lse
 
 
@@ -426,31 +477,52 @@ def bwd_strided(q, k, v, o, lse, dout, causal: bool = False, scale: float | None
 
 
 def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool = False,
-               scale: float | None = None, workspace=None):
+               scale: float | None = None, workspace=None, dq=None, dk=None, dv=None):
     """dQ [Hq,T,d], dK, dV [Hkv,T,d] of packed sequences (the forward's fwd_varlen
-    tensors and offsets, upstream dO [Hq,T,d])."""
+    tensors and offsets, upstream dO [Hq,T,d]).  Any (head, token) strides as in
+    fwd_varlen (q/dq, k/v/dk/dv and o/dout each share strides); gradients
+    default to new tensors with their input's strides."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor [H, T, d]")
+        if t.dim() != 3 or not t.is_cuda or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a device tensor [H, T, d] with contiguous d")
+    if k.stride() != v.stride() or o.stride() != dout.stride():
+        raise ValueError("k/v and o/dout must share strides")
+    _check_cu(cu_seqlens)
     Hq, T, d = q.shape
     Hkv = k.shape[0]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     code = _dtype_code(q)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def like(t, grad):
+        if grad is not None:
+            if grad.stride() != t.stride() or grad.shape != t.shape:
+                raise ValueError("gradients must have their input's shape and strides")
+            return grad
+        return torch.empty_strided(t.shape, t.stride(), device=t.device, dtype=t.dtype)
+
+    dq, dk, dv = like(q, dq), like(k, dk), like(v, dv)
     nbytes = attn_bwd_workspace_bytes(1, Hq, Hkv, T, d, code)
     if nbytes < 0:
         raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_bwd_workspace_bytes")
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
-    st = attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                         workspace.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
-                         int(max_seqlen), Hq, Hkv, T, d, causal, scale, code, _stream_ptr(q))
+    nseq = cu_seqlens.numel() - 1
+    ptrs = [t.data_ptr() for t in (q, k, v, o)] + [lse.data_ptr(), dout.data_ptr()] + \
+        [t.data_ptr() for t in (dq, dk, dv, workspace)]
+    if all(t.is_contiguous() for t in (q, k, v, o, dout)):
+        st = attn_bwd_varlen(*ptrs, cu_seqlens.data_ptr(), nseq, int(max_seqlen), Hq, Hkv, T, d,
+                             causal, scale, code, _stream_ptr(q))
+        what = "attn_bwd_varlen"
+    else:
+        strides = _ht_strides(q) + _ht_strides(k) + _ht_strides(o)
+        st = attn_bwd_varlen_strided(*ptrs, cu_seqlens.data_ptr(), strides, nseq, int(max_seqlen),
+                                     Hq, Hkv, T, d, causal, scale, code, _stream_ptr(q))
+        what = "attn_bwd_varlen_strided"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd_varlen")
+        raise AttnError(st, what)
     return dq, dk, dv
 
 

@@ -374,41 +374,7 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
 
 }  // extern "C"
 
-// ------------------------------------------------------------ packed variable length
-extern "C" {
-
-attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
-                            const int* cu_seqlens, int nseq, int max_seqlen, int Hq, int Hkv,
-                            int T, int d, int causal, float scale, attn_dtype dtype,
-                            void* stream) {
-  if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
-  bool empty = false;
-  attn_status st = check_shape(1, Hq, Hkv, T, d, causal, scale, dtype, &empty);
-  if (st != ATTN_OK) return st;
-  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
-  if (nseq == 0 || T == 0 || max_seqlen == 0) return ATTN_OK;  // no rows to compute
-  const Sizes z = sizes(1, Hq, Hkv, T, d);
-  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}}, {{o, z.q}, {lse, z.l}});
-  if (st != ATTN_OK) return st;
-  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return ATTN_ERR_INVALID_ARG;
-  const Range rc{(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + ((size_t)nseq + 1) * 4};
-  if (overlaps(rc, Range{(uintptr_t)o, (uintptr_t)o + z.q}) ||
-      overlaps(rc, Range{(uintptr_t)lse, (uintptr_t)lse + z.l}))
-    return ATTN_ERR_INVALID_ARG;
-  st = check_device();
-  if (st != ATTN_OK) return st;
-  // B = sequences and N = the longest sequence size the grid
-  attn::FwdArgs a{q, k, v, o, lse, nseq, Hq, Hkv, max_seqlen, d, causal == 1, scale,
-                  (attn::Dtype)dtype, (hipStream_t)stream};
-  a.cu_seqlens = cu_seqlens;
-  a.T = T;
-  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-}  // extern "C"
-
-// ------------------------------------------------------------ strided tensors
+// ------------------------------------------------------------ stride checks
 namespace {
 
 // One tensor family's strides from the caller's array (batch, head, row).
@@ -433,6 +399,160 @@ size_t extent(const long long* s, int i, int B, int H, int N, int d) {
 
 }  // namespace
 
+// ------------------------------------------------------------ packed variable length
+
+namespace {
+
+// Strides of packed-sequence tensors: (head, token) pairs for q, for k and v,
+// and for o, in elements; the checks of strides_ok on one [1, H, T, d] slice.
+bool varlen_strides_ok(const long long* s, int T, int d) {
+  for (int i = 0; i < 3; ++i) {
+    const long long full[3] = {0, s[2 * i], s[2 * i + 1]};
+    if (!strides_ok(full, 0, T, d)) return false;
+  }
+  return true;
+}
+size_t varlen_extent(const long long* s, int i, int H, int T, int d) {
+  return (size_t)(((long long)(H - 1) * s[2 * i] + (long long)(T - 1) * s[2 * i + 1] + d) * 2);
+}
+attn::Layout varlen_layout(const long long* s) {
+  auto st = [&](int i) { return attn::Strides3{0, (int64_t)s[2 * i], (int)s[2 * i + 1]}; };
+  return attn::Layout{st(0), st(1), st(2)};
+}
+
+// The packed variable-length forward, dense [H, T, d] (strides == nullptr)
+// or with the caller's (head, token) strides.
+attn_status fwd_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens, const long long* strides, int nseq,
+                            int max_seqlen, int Hq, int Hkv, int T, int d, int causal, float scale,
+                            attn_dtype dtype, void* stream) {
+  if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
+  bool empty = false;
+  attn_status st = check_shape(1, Hq, Hkv, T, d, causal, scale, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  if (nseq == 0 || T == 0 || max_seqlen == 0) return ATTN_OK;  // no rows to compute
+  const Sizes z = sizes(1, Hq, Hkv, T, d);
+  size_t eq = z.q, ek = z.kv, eo = z.q;
+  if (strides) {
+    if (!varlen_strides_ok(strides, T, d)) return ATTN_ERR_INVALID_ARG;
+    eq = varlen_extent(strides, 0, Hq, T, d);
+    ek = varlen_extent(strides, 1, Hkv, T, d);
+    eo = varlen_extent(strides, 2, Hq, T, d);
+  }
+  st = check_buffers({{q, eq}, {k, ek}, {v, ek}}, {{o, eo}, {lse, z.l}});
+  if (st != ATTN_OK) return st;
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return ATTN_ERR_INVALID_ARG;
+  const Range rc{(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + ((size_t)nseq + 1) * 4};
+  if (overlaps(rc, Range{(uintptr_t)o, (uintptr_t)o + eo}) ||
+      overlaps(rc, Range{(uintptr_t)lse, (uintptr_t)lse + z.l}))
+    return ATTN_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  // B = sequences and N = the longest sequence size the grid
+  attn::FwdArgs a{q, k, v, o, lse, nseq, Hq, Hkv, max_seqlen, d, causal == 1, scale,
+                  (attn::Dtype)dtype, (hipStream_t)stream};
+  a.cu_seqlens = cu_seqlens;
+  a.T = T;
+  if (strides) a.lay = varlen_layout(strides);
+  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+
+// The packed variable-length backward, dense [H, T, d] (strides == nullptr)
+// or with the caller's (head, token) strides.  Strided gradients may be
+// interleaved slices of one packed buffer, so they are checked only against
+// the inputs, the workspace and the offsets.
+attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            void* workspace, const int* cu_seqlens, const long long* strides,
+                            int nseq, int max_seqlen, int Hq, int Hkv, int T, int d, int causal,
+                            float scale, attn_dtype dtype, void* stream) {
+  if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
+  attn::BwdArgs a;
+  // the packed tokens as one [1, H, T, d] problem: shapes, statistics, workspace
+  attn_status st = bwd_common(1, Hq, Hkv, T, d, causal, scale, dtype, stream, &a);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  if (a.N == 0 || nseq == 0 || max_seqlen == 0) return ATTN_OK;  // no rows
+  const size_t wbytes = attn_bwd_workspace_bytes(1, Hq, Hkv, T, d, dtype);
+  const Sizes z = sizes(1, Hq, Hkv, T, d);
+  size_t eq = z.q, ek = z.kv, eo = z.q;
+  if (strides) {
+    if (!varlen_strides_ok(strides, T, d)) return ATTN_ERR_INVALID_ARG;
+    eq = varlen_extent(strides, 0, Hq, T, d);
+    ek = varlen_extent(strides, 1, Hkv, T, d);
+    eo = varlen_extent(strides, 2, Hq, T, d);
+  }
+  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return ATTN_ERR_INVALID_ARG;
+  const Range rc{(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + ((size_t)nseq + 1) * 4};
+  if (!strides) {
+    st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {lse, z.l}, {dout, z.q}},
+                       {{dq, z.q}, {dk, z.kv}, {dv, z.kv}, {workspace, wbytes}});
+    if (st != ATTN_OK) return st;
+  } else {
+    const Buf ins[] = {{q, eq}, {k, ek}, {v, ek}, {o, eo}, {lse, z.l}, {dout, eo}};
+    for (const Buf& b : ins)
+      if (!b.p || !aligned16(b.p)) return ATTN_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+    const Range rw{(uintptr_t)workspace, (uintptr_t)workspace + wbytes};
+    const Buf grads[] = {{dq, eq}, {dk, ek}, {dv, ek}};
+    for (const Buf& g : grads) {
+      if (!g.p || !aligned16(g.p)) return ATTN_ERR_INVALID_ARG;
+      const Range rg{(uintptr_t)g.p, (uintptr_t)g.p + g.bytes};
+      if (overlaps(rg, rw)) return ATTN_ERR_INVALID_ARG;
+      for (const Buf& b : ins)
+        if (overlaps(rg, Range{(uintptr_t)b.p, (uintptr_t)b.p + b.bytes})) return ATTN_ERR_INVALID_ARG;
+    }
+    for (const Buf& b : ins)
+      if (overlaps(rw, Range{(uintptr_t)b.p, (uintptr_t)b.p + b.bytes})) return ATTN_ERR_INVALID_ARG;
+  }
+  const Range outs[] = {{(uintptr_t)dq, (uintptr_t)dq + eq},
+                        {(uintptr_t)dk, (uintptr_t)dk + ek},
+                        {(uintptr_t)dv, (uintptr_t)dv + ek},
+                        {(uintptr_t)workspace, (uintptr_t)workspace + wbytes}};
+  for (const Range& r : outs)
+    if (overlaps(rc, r)) return ATTN_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
+  a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
+  if (strides) a.lay = varlen_layout(strides);
+  // row statistics of all T packed tokens, then the two gradient stages per
+  // (sequence, head) with B = sequences and N = the longest sequence
+  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
+  a.B = nseq, a.N = max_seqlen, a.cu_seqlens = cu_seqlens, a.T = T;
+  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int* cu_seqlens, int nseq, int max_seqlen, int Hq, int Hkv,
+                            int T, int d, int causal, float scale, attn_dtype dtype,
+                            void* stream) {
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens, nullptr, nseq, max_seqlen, Hq, Hkv, T, d,
+                         causal, scale, dtype, stream);
+}
+
+attn_status attn_fwd_varlen_strided(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, const int* cu_seqlens, const long long* strides,
+                                    int nseq, int max_seqlen, int Hq, int Hkv, int T, int d,
+                                    int causal, float scale, attn_dtype dtype, void* stream) {
+  if (!strides) return ATTN_ERR_INVALID_ARG;
+  return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens, strides, nseq, max_seqlen, Hq, Hkv, T, d,
+                         causal, scale, dtype, stream);
+}
+
+}  // extern "C"
+
+
+// ------------------------------------------------------------ strided tensors
 extern "C" {
 
 attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -507,37 +627,19 @@ attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const v
                             void* workspace, const int* cu_seqlens, int nseq, int max_seqlen,
                             int Hq, int Hkv, int T, int d, int causal, float scale,
                             attn_dtype dtype, void* stream) {
-  if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
-  attn::BwdArgs a;
-  // the packed tokens as one [1, H, T, d] problem: shapes, statistics, workspace
-  attn_status st = bwd_common(1, Hq, Hkv, T, d, causal, scale, dtype, stream, &a);
-  if (st != ATTN_OK) return st;
-  if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
-  if (a.N == 0 || nseq == 0 || max_seqlen == 0) return ATTN_OK;  // no rows
-  const size_t wbytes = attn_bwd_workspace_bytes(1, Hq, Hkv, T, d, dtype);
-  const Sizes z = sizes(1, Hq, Hkv, T, d);
-  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {lse, z.l}, {dout, z.q}},
-                     {{dq, z.q}, {dk, z.kv}, {dv, z.kv}, {workspace, wbytes}});
-  if (st != ATTN_OK) return st;
-  if (!cu_seqlens || ((uintptr_t)cu_seqlens & 3u)) return ATTN_ERR_INVALID_ARG;
-  const Range rc{(uintptr_t)cu_seqlens, (uintptr_t)cu_seqlens + ((size_t)nseq + 1) * 4};
-  const Range outs[] = {{(uintptr_t)dq, (uintptr_t)dq + z.q},
-                        {(uintptr_t)dk, (uintptr_t)dk + z.kv},
-                        {(uintptr_t)dv, (uintptr_t)dv + z.kv},
-                        {(uintptr_t)workspace, (uintptr_t)workspace + wbytes}};
-  for (const Range& r : outs)
-    if (overlaps(rc, r)) return ATTN_ERR_INVALID_ARG;
-  st = check_device();
-  if (st != ATTN_OK) return st;
-  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
-  a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
-  // row statistics of all T packed tokens, then the two gradient stages per
-  // (sequence, head) with B = sequences and N = the longest sequence
-  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
-  a.B = nseq, a.N = max_seqlen, a.cu_seqlens = cu_seqlens, a.T = T;
-  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, nullptr, nseq,
+                         max_seqlen, Hq, Hkv, T, d, causal, scale, dtype, stream);
+}
+
+attn_status attn_bwd_varlen_strided(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout, void* dq, void* dk,
+                                    void* dv, void* workspace, const int* cu_seqlens,
+                                    const long long* strides, int nseq, int max_seqlen, int Hq,
+                                    int Hkv, int T, int d, int causal, float scale,
+                                    attn_dtype dtype, void* stream) {
+  if (!strides) return ATTN_ERR_INVALID_ARG;
+  return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, strides, nseq,
+                         max_seqlen, Hq, Hkv, T, d, causal, scale, dtype, stream);
 }
 
 }  // extern "C"

@@ -146,10 +146,11 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     N = end - start;
     if (kblk * BKV >= N) return;  // the whole workgroup: past this sequence's end
     Np = stat_rows(ntok);  // statistics of the packed tokens, [Hq][2][Np]
-    krs = qrs = ors = D;
-    kvoff = ((int64_t)g * ntok + start) * D;
-    qb0 = ob0 = (int64_t)start * D;
-    qhs = ohs = (int64_t)ntok * D;
+    // (head, token) strides; the batch strides are unused
+    krs = lay.kv.r, qrs = lay.q.r, ors = lay.o.r;
+    kvoff = g * lay.kv.h + (int64_t)start * lay.kv.r;
+    qb0 = (int64_t)start * lay.q.r, qhs = lay.q.h;
+    ob0 = (int64_t)start * lay.o.r, ohs = lay.o.h;
     sb0 = start;
   } else {
     const int b = bg / Hkv;
@@ -465,9 +466,10 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
     const int g = h / (Hq / Hkv);
     Np = stat_rows(ntok);
-    qrs = krs = ors = D;
-    qoff = ooff = ((int64_t)h * ntok + start) * D;
-    kvoff = ((int64_t)g * ntok + start) * D;
+    qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
+    qoff = h * lay.q.h + (int64_t)start * lay.q.r;
+    kvoff = g * lay.kv.h + (int64_t)start * lay.kv.r;
+    ooff = h * lay.o.h + (int64_t)start * lay.o.r;
     st = stats + (int64_t)h * 2 * Np + start;
   } else {
     const int b = bh / Hq;
@@ -681,9 +683,11 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 }
 
 // ---------------------------------------------------------------- launchers
-// The strides a launch uses: the caller's, or the dense [B, H, N, d] ones.
+// The strides a launch uses: the caller's, or the dense ones ([B, H, N, d],
+// or [H, T, d] for packed sequences).
 static Layout layout_of(const BwdArgs& a) {
-  return a.lay.q.r ? a.lay : dense_layout(a.Hq, a.Hkv, a.N, a.d);
+  if (a.lay.q.r) return a.lay;
+  return a.cu_seqlens ? dense_layout(a.Hq, a.Hkv, a.T, a.d) : dense_layout(a.Hq, a.Hkv, a.N, a.d);
 }
 
 size_t bwd_stats_bytes(int B, int Hq, int N) {

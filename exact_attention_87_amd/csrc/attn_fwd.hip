@@ -136,8 +136,11 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     N = end - start;
     if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
     const int g = h / (Hq / Hkv);
-    qoff = ooff = ((int64_t)h * ntok + start) * D;
-    kvoff = ((int64_t)g * ntok + start) * D;
+    // (head, token) strides; the batch strides are unused
+    qoff = h * lay.q.h + (int64_t)start * lay.q.r;
+    kvoff = g * lay.kv.h + (int64_t)start * lay.kv.r;
+    ooff = h * lay.o.h + (int64_t)start * lay.o.r;
+    qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
     lbase = (int64_t)h * ntok + start;
   } else {
     const int b = bh / Hq;
@@ -505,8 +508,11 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     N = end - start;
     if (qb * BR >= N) return;  // the whole workgroup: past this sequence's end
     const int g = h / (Hq / Hkv);
-    qoff = ooff = ((int64_t)h * ntok + start) * D;
-    kvoff = ((int64_t)g * ntok + start) * D;
+    // (head, token) strides; the batch strides are unused
+    qoff = h * lay.q.h + (int64_t)start * lay.q.r;
+    kvoff = g * lay.kv.h + (int64_t)start * lay.kv.r;
+    ooff = h * lay.o.h + (int64_t)start * lay.o.r;
+    qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
     lbase = (int64_t)h * ntok + start;
   } else {
     const int b = bh / Hq;
@@ -822,7 +828,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
 // ---------------------------------------------------------------- launchers
 // The strides a launch uses: the caller's, or the dense [B, H, N, d] ones.
 static Layout layout_of(const FwdArgs& a) {
-  return a.lay.q.r ? a.lay : dense_layout(a.Hq, a.Hkv, a.N, a.d);
+  if (a.lay.q.r) return a.lay;
+  // dense [B, H, N, d], or [H, T, d] for packed sequences
+  return a.cu_seqlens ? dense_layout(a.Hq, a.Hkv, a.T, a.d) : dense_layout(a.Hq, a.Hkv, a.N, a.d);
 }
 
 // Dynamic LDS of a forward launch: the kernel's stages, plus the 16-bit tile

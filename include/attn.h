@@ -316,6 +316,36 @@ attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const v
                             int Hq, int Hkv, int T, int d, int causal, float scale,
                             attn_dtype dtype, void* stream);
 
+/*
+ * attn_fwd_varlen / attn_bwd_varlen on packed-sequence tensors of any (head,
+ * token) element strides, such as the token-major [T, H, d] layout or slices
+ * of a packed [T, 3, H, d] QKV projection.
+ *   strides[0..1]  (head, token) strides of q (and dq)
+ *   strides[2..3]  (head, token) strides of k and v (and dk, dv)
+ *   strides[4..5]  (head, token) strides of o (and dout)
+ * lse stays dense [Hq, T]; the workspace is as for attn_bwd_varlen.  Every
+ * stride must be a non-negative multiple of 8, token strides at least d, and
+ * ((T + 127) * token_stride + d) * 2 < 2^31 (else ATTN_ERR_INVALID_ARG);
+ * distinct (head, token) pairs must address distinct rows of every output
+ * (not checked).  Inputs may share memory.  The forward's outputs must not
+ * overlap the inputs or each other; the backward's gradients may be
+ * interleaved slices of one packed buffer and are only checked against the
+ * inputs, the workspace and cu_seqlens (on the extents from base to last
+ * element).  Every other convention, including the supported types and head
+ * dimensions, is that of the dense entry point, and with the dense [H, T, d]
+ * strides (T*d, d for every tensor) the results are its results bit for bit.
+ */
+attn_status attn_fwd_varlen_strided(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, const int* cu_seqlens, const long long* strides,
+                                    int nseq, int max_seqlen, int Hq, int Hkv, int T, int d,
+                                    int causal, float scale, attn_dtype dtype, void* stream);
+attn_status attn_bwd_varlen_strided(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout, void* dq, void* dk,
+                                    void* dv, void* workspace, const int* cu_seqlens,
+                                    const long long* strides, int nseq, int max_seqlen, int Hq,
+                                    int Hkv, int T, int d, int causal, float scale,
+                                    attn_dtype dtype, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -26,11 +26,12 @@ def header_functions():
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
                                   "attn_bwd_dq_stats", "attn_bwd_preprocess", "attn_bwd_strided", "attn_bwd_varlen",
+                                  "attn_bwd_varlen_strided",
                                   "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
                                   "attn_fwd_splitkv_workspace_bytes", "attn_fwd_strided",
-                                  "attn_fwd_varlen",
+                                  "attn_fwd_varlen", "attn_fwd_varlen_strided",
                                   "attn_status_str"]
 
 
@@ -421,3 +422,45 @@ def test_varlen_backward_validation():
     none = dict(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None,
                 ws=None, cu=None)
     assert vb(nseq=0, **none) == ea.ATTN_OK
+
+
+def test_varlen_strided_validation():
+    ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    T, H, Hkv, d = 1000, 4, 2, 64
+    tm = [d, H * d, d, Hkv * d, d, H * d]  # token-major [T, H, d] for every tensor
+
+    def fs(strides, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, cu=CU, nseq=3, maxlen=500, Hq=H, Hkv=Hkv, T=T, d=d,
+                 causal=1, scale=0.125, dtype=ea.ATTN_BF16)
+        a.update(kw)
+        return ea.attn_fwd_varlen_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"],
+                                          strides, a["nseq"], a["maxlen"], a["Hq"], a["Hkv"],
+                                          a["T"], a["d"], a["causal"], a["scale"], a["dtype"],
+                                          None)
+
+    def bs(strides, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, cu=CU, nseq=3,
+                 maxlen=500, Hq=H, Hkv=Hkv, T=T, d=d, causal=1, scale=0.125, dtype=ea.ATTN_BF16)
+        a.update(kw)
+        return ea.attn_bwd_varlen_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"],
+                                          a["dq"], a["dk"], a["dv"], a["ws"], a["cu"], strides,
+                                          a["nseq"], a["maxlen"], a["Hq"], a["Hkv"], a["T"],
+                                          a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+    assert fs(tm) not in ok and bs(tm) not in ok
+    for bad in ([d, 32, d, Hkv * d, d, H * d],      # token stride below d
+                [d, H * d + 4, d, Hkv * d, d, H * d],  # not a multiple of 8
+                [-8, H * d, d, Hkv * d, d, H * d],   # negative
+                [d, 1 << 22, d, Hkv * d, d, H * d]):  # rows past 2^31 bytes
+        assert fs(bad) == ea.ATTN_ERR_INVALID_ARG, bad
+        assert bs(bad) == ea.ATTN_ERR_INVALID_ARG, bad
+    assert ea.lib().attn_fwd_varlen_strided(Q, K, V, O, L, CU, None, 3, 500, H, Hkv, T, d, 1,
+                                            0.125, 1, None) == ea.ATTN_ERR_INVALID_ARG
+    assert fs(tm, o=Q + 128) == ea.ATTN_ERR_INVALID_ARG  # output over an input
+    assert fs(tm, q=Q, k=Q + 128, v=Q + 256) not in ok  # inputs may share memory
+    assert bs(tm, dk=DQ + 128) not in ok  # interleaved gradient slices are allowed
+    assert bs(tm, dk=WS + 64) == ea.ATTN_ERR_INVALID_ARG  # a gradient over the workspace
+    assert bs(tm, dq=Q) == ea.ATTN_ERR_INVALID_ARG  # a gradient over an input
+    assert bs(tm, cu=DQ + 16) == ea.ATTN_ERR_INVALID_ARG  # offsets inside a gradient
+    assert fs(tm, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert fs(tm, nseq=0, q=None, k=None, v=None, o=None, lse=None, cu=None) == ea.ATTN_OK

@@ -6,7 +6,12 @@ Tolerances are the bf16 forward's: |O - O_ref| <= 2e-2 + 1e-2 |O_ref|
 element-wise and |LSE - LSE_ref| <= 1e-3.  Cases cover sequences of length
 0, 1, tile multiples and tails, many short sequences, head maps, both head
 dims and causal modes; one sequence must reproduce attn_fwd bit for bit; the
-full-size document workload is checked on whole heads.
+full-size document workload is checked on whole heads.  The backward is
+checked against the oracle's backward on each sequence's slices (gradient
+tolerances: max |g - g_ref| <= 5e-2 max |g_ref|, relative Frobenius <= 2e-2).
+Strided tensors: token-major [T, H, d] and slices of a packed QKV projection,
+forward and backward, and the dense strides bit for bit against the dense
+entry points.
 """
 import numpy as np
 import pytest
@@ -216,3 +221,88 @@ def test_backward_full_size_documents_sampled_heads(oracle_mod):
     grad_ok("dQ", dq[hs], rdq)
     grad_ok("dK", dk[0:1], rdk)
     grad_ok("dV", dv[0:1], rdv)
+
+
+# ---------------------------------------------------------------- strided
+def token_major(t, dev):
+    """[H, T, d] -> the same values in a token-major [T, H, d] buffer, viewed as [H, T, d]."""
+    return t.transpose(0, 1).contiguous().to(dev).transpose(0, 1)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_token_major_forward_and_backward(oracle_mod, d, causal):
+    dev = gpu()
+    lengths = [5, 130, 0, 64, 201]
+    q, k, v, cu = attn_inputs.make_varlen(4, 2, lengths, d, seed=d + 40)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(8)).to(q.dtype)
+    qt, kt, vt, dot = (token_major(t, dev) for t in (q, k, v, do))
+    cug = cu.to(dev)
+    o, lse = ea.fwd_varlen(qt, kt, vt, cug, 201, causal=causal)
+    assert o.transpose(0, 1).is_contiguous()  # token-major output by default
+    dq, dk, dv = ea.bwd_varlen(qt, kt, vt, o, lse, dot, cug, 201, causal=causal)
+    torch.cuda.synchronize()
+    assert dq.stride() == qt.stride() and dk.stride() == kt.stride()
+    ro, rl = oracle_mod.fwd_varlen(q, k, v, cu.numpy(), causal=causal)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"token-major d={d}")
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q, k, v, do, cu, causal)
+    for name, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        grad_ok(f"{name} token-major d={d}", gg, r)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_strides_are_the_dense_entry_points_bitwise(d):
+    dev = gpu()
+    lengths = [100, 1, 300]
+    q, k, v, cu = (t.to(dev) for t in attn_inputs.make_varlen(4, 2, lengths, d, seed=3))
+    do = torch.randn_like(q)
+    T = q.shape[1]
+    o1, l1 = ea.fwd_varlen(q, k, v, cu, 300, causal=True)
+    o2 = torch.empty_like(q)
+    l2 = torch.empty_like(l1)
+    dense = [T * d, d] * 3
+    s = torch.cuda.current_stream().cuda_stream
+    assert ea.attn_fwd_varlen_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(),
+                                      l2.data_ptr(), cu.data_ptr(), dense, 3, 300, 4, 2, T, d, 1,
+                                      d ** -0.5, ea.ATTN_BF16, s) == ea.ATTN_OK
+    g1 = ea.bwd_varlen(q, k, v, o1, l1, do, cu, 300, causal=True)
+    g2 = [torch.empty_like(t) for t in (q, k, v)]
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(1, 4, 2, T, d, ea.ATTN_BF16), device=dev,
+                     dtype=torch.uint8)
+    assert ea.attn_bwd_varlen_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o1.data_ptr(),
+                                      l1.data_ptr(), do.data_ptr(), g2[0].data_ptr(),
+                                      g2[1].data_ptr(), g2[2].data_ptr(), ws.data_ptr(),
+                                      cu.data_ptr(), dense, 3, 300, 4, 2, T, d, 1, d ** -0.5,
+                                      ea.ATTN_BF16, s) == ea.ATTN_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_packed_qkv_projection(oracle_mod):
+    # q, k, v slices of one [T, Hq + 2 Hkv, d] projection; gradients into
+    # slices of one packed gradient buffer; fp16
+    dev = gpu()
+    Hq, Hkv, d = 8, 2, 128
+    lengths = [70, 257, 3]
+    q, k, v, cu = attn_inputs.make_varlen(Hq, Hkv, lengths, d, seed=12, dtype="fp16")
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(2)).to(q.dtype)
+    packed = torch.cat([q, k, v], dim=0).transpose(0, 1).contiguous().to(dev)  # [T, H, d]
+    qv = packed[:, :Hq].transpose(0, 1)
+    kv = packed[:, Hq:Hq + Hkv].transpose(0, 1)
+    vv = packed[:, Hq + Hkv:].transpose(0, 1)
+    cug = cu.to(dev)
+    o, lse = ea.fwd_varlen(qv, kv, vv, cug, 257, causal=True)
+    gpack = torch.full_like(packed, 7.0)
+    dq = gpack[:, :Hq].transpose(0, 1)
+    dk = gpack[:, Hq:Hq + Hkv].transpose(0, 1)
+    dv = gpack[:, Hq + Hkv:].transpose(0, 1)
+    ea.bwd_varlen(qv, kv, vv, o, lse, token_major(do, dev), cug, 257, causal=True,
+                  dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.fwd_varlen(q, k, v, cu.numpy(), causal=True)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "packed qkv")
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q, k, v, do, cu, True)
+    for name, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        grad_ok(f"{name} packed qkv", gg, r)
