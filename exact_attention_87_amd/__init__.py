@@ -71,6 +71,8 @@ def lib():
         L.attn_fwd_varlen_strided.restype = ci
         L.attn_bwd_varlen_strided.argtypes = [vp] * 12 + [ci] * 7 + [cf, ci, vp]
         L.attn_bwd_varlen_strided.restype = ci
+        L.attn_fwd_splitkv_strided.argtypes = [vp] * 7 + [ci] * 7 + [cf, ci, ci, vp]
+        L.attn_fwd_splitkv_strided.restype = ci
         L.attn_fwd_splitkv.argtypes = [vp] * 6 + [ci] * 7 + [cf, ci, ci, vp]
         L.attn_fwd_splitkv.restype = ci
         L.attn_fwd_splitkv_num_splits.argtypes = [ci] * 7
@@ -145,6 +147,15 @@ def attn_fwd_splitkv(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, causal, 
     return int(lib().attn_fwd_splitkv(q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d,
                                       int(causal), float(scale), int(num_splits), int(dtype),
                                       stream))
+
+
+def attn_fwd_splitkv_strided(q, k, v, o, lse, workspace, strides, B, Hq, Hkv, Nq, Nk, d, causal,
+                             scale, num_splits, dtype, stream) -> int:
+    """strides: 9 element strides (q_b, q_h, q_row, kv_b, kv_h, kv_row, o_b, o_h, o_row)."""
+    arr = (ctypes.c_longlong * 9)(*[int(x) for x in strides])
+    return int(lib().attn_fwd_splitkv_strided(q, k, v, o, lse, workspace, arr, B, Hq, Hkv, Nq, Nk,
+                                              d, int(causal), float(scale), int(num_splits),
+                                              int(dtype), stream))
 
 
 def attn_fwd_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
@@ -273,16 +284,21 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
 
 def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
                 num_splits: int = 0, out=None, lse=None, workspace=None):
-    """O, LSE for q [B,Hq,Nq,d] against a key/value cache k/v [B,Hkv,Nk,d] (bf16),
+    """O, LSE for q [B,Hq,Nq,d] against a key/value cache k/v [B,Hkv,Nk,d] (16-bit),
     with the keys cut into num_splits ranges (0: chosen from the shape) and the
-    causal mask aligned to the last query."""
+    causal mask aligned to the last query.  q, k, v (and out) may be
+    [B, H, N, d] views of any (batch, head, row) strides, e.g. a token-major
+    [B, Nk, Hkv, d] cache transposed; out defaults to q's layout when q is
+    contiguous, else to a [B, Nq, Hq, d] tensor viewed as [B, Hq, Nq, d]."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4:
             raise ValueError(f"{name} must be [B, H, N, d]")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+        if not t.is_cuda or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a device tensor with contiguous d")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     B, Hq, Nq, d = q.shape
@@ -293,7 +309,8 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
         scale = 1.0 / math.sqrt(d)
     code = _dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q) if q.is_contiguous() else \
+            torch.empty((B, Nq, Hq, d), device=q.device, dtype=q.dtype).transpose(1, 2)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32)
     nbytes = attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
@@ -301,11 +318,19 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
         raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_fwd_splitkv_workspace_bytes")
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
-    st = attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          lse.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, Nq, Nk, d, causal,
-                          scale, num_splits, code, _stream_ptr(q))
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        st = attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), workspace.data_ptr(), B, Hq, Hkv, Nq, Nk, d, causal,
+                              scale, num_splits, code, _stream_ptr(q))
+        what = "attn_fwd_splitkv"
+    else:
+        strides = _bhnd_strides(q) + _bhnd_strides(k) + _bhnd_strides(out)
+        st = attn_fwd_splitkv_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), workspace.data_ptr(), strides, B, Hq, Hkv,
+                                      Nq, Nk, d, causal, scale, num_splits, code, _stream_ptr(q))
+        what = "attn_fwd_splitkv_strided"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_splitkv")
+        raise AttnError(st, what)
     return out, lse
 
 

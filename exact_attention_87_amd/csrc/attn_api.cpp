@@ -555,6 +555,38 @@ attn_status attn_fwd_varlen_strided(const void* q, const void* k, const void* v,
 // ------------------------------------------------------------ strided tensors
 extern "C" {
 
+attn_status attn_fwd_splitkv_strided(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, void* workspace, const long long* strides, int B,
+                                     int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                                     float scale, int num_splits, attn_dtype dtype, void* stream) {
+  bool empty = false;
+  attn_status st = split_shape(B, Hq, Hkv, Nq, Nk, d, causal, scale, num_splits, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (empty) return ATTN_OK;
+  if (!strides) return ATTN_ERR_INVALID_ARG;
+  if (!strides_ok(strides, 0, Nq, d) || !strides_ok(strides, 1, Nk, d) ||
+      !strides_ok(strides, 2, Nq, d))
+    return ATTN_ERR_INVALID_ARG;
+  // a head group's query rows are addressed from the group's first head
+  const long long group_rows = ((long long)(Hq / Hkv - 1) * strides[1] +
+                                (long long)(Nq - 1) * strides[2] + d) * 2;
+  if (group_rows >= (1ll << 31)) return ATTN_ERR_INVALID_ARG;
+  const size_t eq = extent(strides, 0, B, Hq, Nq, d), ek = extent(strides, 1, B, Hkv, Nk, d),
+               eo = extent(strides, 2, B, Hq, Nq, d);
+  const size_t lb = (size_t)B * Hq * Nq * sizeof(float);
+  const size_t wb = attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  const size_t ekv = Nk == 0 ? 0 : ek;  // no keys: K and V are never read
+  st = check_buffers({{q, eq}, {k, ekv}, {v, ekv}}, {{o, eo}, {lse, lb}, {workspace, wb}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::SplitArgs a{q,  k,  v, o,           lse,   workspace,  B,
+                    Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dtype,
+                    (hipStream_t)stream};
+  a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
+  return attn::launch_fwd_split(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                              const long long* strides, int B, int Hq, int Hkv, int N, int d,
                              int causal, float scale, attn_dtype dtype, void* stream) {

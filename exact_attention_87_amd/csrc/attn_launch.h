@@ -96,6 +96,7 @@ struct SplitArgs {
   int num_splits;  // requested; <= 0 picks one from the shape
   Dtype dtype;     // kBF16 or kF16
   hipStream_t stream;
+  Layout lay{};    // element strides; all zero: dense [B, H, Nq|Nk, d]
 };
 
 struct SplitPlan {

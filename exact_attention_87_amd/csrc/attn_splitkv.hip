@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fwd_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     float* __restrict__ Opart, float* __restrict__ Lpart, int Hq, int Hkv, int Nq, int Nk,
-    int nrb, int nsplit, int split_len, int64_t rows_total, float c, uint32_t qsign) {
+    int nrb, int nsplit, int split_len, int64_t rows_total, float c, uint32_t qsign, Layout lay) {
   using Cfg = SplitCfg<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, TILEB = Cfg::TILEB, NW = Cfg::NW, NBUF = Cfg::NBUF;
@@ -88,20 +88,30 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
   const int group = Hq / Hkv;
   const int R = group * Nq;                         // packed rows of the group
   const int64_t row0 = ((int64_t)b * Hq + (int64_t)g * group) * Nq;  // [B,Hq,Nq] index of row 0
-  const int64_t kvoff = (int64_t)bg * Nk * D;
+  const int krs = lay.kv.r;  // key/value row stride (elements)
+  const int64_t kvoff = b * lay.kv.b + g * lay.kv.h;
   const int r0 = rb * BR + w * 32;  // first packed row of this wave
   const int r = r0 + l32;           // packed row of this lane
   const int qi = r % Nq;            // its query index
   const int off = Nk - Nq;          // bottom-right diagonal offset
 
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + row0 * D, (uint32_t)R * ROWB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, (uint32_t)Nk * ROWB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, (uint32_t)Nk * ROWB);
+  // The group's query rows: head g*group + r/Nq, query r%Nq.  A padding row
+  // (r >= R) reads row R-1 and is never stored.
+  const int64_t qbase = b * lay.q.b + (int64_t)g * group * lay.q.h;
+  const uint32_t qbytes =
+      (uint32_t)(((int64_t)(group - 1) * lay.q.h + (int64_t)(Nq - 1) * lay.q.r + D) * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qbase, qbytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes(Nk, krs, D));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes(Nk, krs, D));
 
   V8 qreg[NQC];
+  {
+    const int rr = min(r, R - 1), hg = rr / Nq;
+    const uint32_t qrow = (uint32_t)(hg * lay.q.h + (int64_t)(rr - hg * Nq) * lay.q.r);
 #pragma unroll
-  for (int cc = 0; cc < NQC; ++cc)
-    qreg[cc] = bitcast<V8>(buf_load16(rq, (uint32_t)(r * D + cc * 16 + hf * 8) * 2) ^ qsign);
+    for (int cc = 0; cc < NQC; ++cc)
+      qreg[cc] = bitcast<V8>(buf_load16(rq, (qrow + cc * 16 + hf * 8) * 2) ^ qsign);
+  }
 
   // Key range of the split.  With the causal mask the workgroup stops after
   // the last key any of its rows sees, and each wave after its own last key;
@@ -124,11 +134,11 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
     const int o = (w * PW + i) * 1024 + lane * 16;
     const int row = o / ROWB;
     const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
-    goff[i] = (uint32_t)(row * D + ch * 8) * 2;
+    goff[i] = (uint32_t)(row * krs + ch * 8) * 2;
   }
   auto issue = [&](int j) {
     char* kt = smem + (j % NBUF) * 2 * TILEB;
-    const uint32_t tbase = (uint32_t)(kbeg + j * BC) * ROWB;
+    const uint32_t tbase = (uint32_t)(kbeg + j * BC) * krs * 2;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       buf_load16_lds(rk, kt + (w * PW + i) * 1024, goff[i] + tbase);
@@ -298,7 +308,8 @@ __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restri
                                                            const float* __restrict__ Lpart,
                                                            T* __restrict__ O,
                                                            float* __restrict__ LSE, int nsplit,
-                                                           int64_t rows) {
+                                                           int64_t rows, int Hq, int Nq,
+                                                           Strides3 os) {
   constexpr int TPR = D / 4;   // lanes per row
   constexpr int RPW = 64 / TPR;  // rows per wave
   constexpr int SG = 8;        // splits whose loads are in flight together
@@ -336,7 +347,15 @@ __global__ __launch_bounds__(64) void split_combine_kernel(const float* __restri
   u32x2 outv;
   outv[0] = pack2<T>(acc[0] * inv, acc[1] * inv);
   outv[1] = pack2<T>(acc[2] * inv, acc[3] * inv);
-  *(u32x2*)(O + row * D + part * 4) = outv;
+  // row = (b*Hq + h)*Nq + i of the [B, Hq, Nq] rows; O at the caller's
+  // strides (os.r == 0 marks the dense layout, where the row is the offset)
+  T* dst = O + row * D;
+  if (os.r != 0) {
+    const int64_t bh = row / Nq;
+    const int64_t b = bh / Hq;
+    dst = O + b * os.b + (bh - b * Hq) * os.h + (row - bh * Nq) * os.r;
+  }
+  *(u32x2*)(dst + part * 4) = outv;
   if (part == 0) LSE[row] = wsum > 0.f ? m + logf(wsum) : ninf;
 }
 
@@ -389,15 +408,24 @@ static hipError_t split_t(const SplitArgs& a) {
   const int64_t grid = (int64_t)p.nrb * p.nsplit * a.B * a.Hkv;
   hipError_t e = allow_lds(fwd_split_kernel<T, D, CAUSAL>, SplitCfg<D>::LDS);
   if (e != hipSuccess) return e;
+  // the caller's strides, or dense [B, H, N, d] ones (Nq rows for Q and O,
+  // Nk for K and V)
+  Layout lay = a.lay;
+  if (!lay.q.r) {
+    const Strides3 q{(int64_t)a.Hq * a.Nq * D, (int64_t)a.Nq * D, D};
+    const Strides3 kv{(int64_t)a.Hkv * a.Nk * D, (int64_t)a.Nk * D, D};
+    lay = Layout{q, kv, q};
+  }
   hipLaunchKernelGGL((fwd_split_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(256),
                      SplitCfg<D>::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      opart, lpart, a.Hq, a.Hkv, a.Nq, a.Nk, p.nrb, p.nsplit,
-                     p.split_len, rows, c, (a.scale < 0.f) ? 0x80008000u : 0u);
+                     p.split_len, rows, c, (a.scale < 0.f) ? 0x80008000u : 0u, lay);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPW = 64 / (D / 4);
   hipLaunchKernelGGL((split_combine_kernel<T, D>), dim3((unsigned)((rows + RPW - 1) / RPW)),
-                     dim3(64), 0, a.stream, opart, lpart, (T*)a.o, a.lse, p.nsplit, rows);
+                     dim3(64), 0, a.stream, opart, lpart, (T*)a.o, a.lse, p.nsplit, rows, a.Hq,
+                     a.Nq, a.lay.q.r ? lay.o : Strides3{0, 0, 0});
   return hipGetLastError();
 }
 

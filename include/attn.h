@@ -191,6 +191,22 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* 
  * for an empty problem, -1 for arguments it would reject. */
 int attn_fwd_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 
+/*
+ * attn_fwd_splitkv on tensors of any (batch, head, row) element strides, such
+ * as a token-major [B, Nk, Hkv, d] key/value cache.  strides[0..2] address q,
+ * strides[3..5] k and v, strides[6..8] o; lse and the workspace stay dense
+ * (the workspace is attn_fwd_splitkv_workspace_bytes(...) bytes).  Stride
+ * rules as for attn_fwd_strided (with Nq rows for q and o, Nk for k and v),
+ * and one head group's query rows must lie within 2^31 bytes of the group's
+ * first row: ((Hq/Hkv - 1) * q_h + (Nq - 1) * q_row + d) * 2 < 2^31.  Every
+ * other convention is attn_fwd_splitkv's, and with the dense strides the
+ * result is attn_fwd_splitkv's bit for bit.
+ */
+attn_status attn_fwd_splitkv_strided(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, void* workspace, const long long* strides, int B,
+                                     int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                                     float scale, int num_splits, attn_dtype dtype, void* stream);
+
 /* Bytes of workspace attn_fwd_splitkv needs (a multiple of 256: fp32 partial
  * outputs and logsumexps of every split); 0 for an empty problem,
  * (size_t)-1 for arguments it would reject. */

@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
                                   "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
+                                  "attn_fwd_splitkv_strided",
                                   "attn_fwd_splitkv_workspace_bytes", "attn_fwd_strided",
                                   "attn_fwd_varlen", "attn_fwd_varlen_strided",
                                   "attn_status_str"]
@@ -464,3 +465,32 @@ def test_varlen_strided_validation():
     assert bs(tm, cu=DQ + 16) == ea.ATTN_ERR_INVALID_ARG  # offsets inside a gradient
     assert fs(tm, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
     assert fs(tm, nseq=0, q=None, k=None, v=None, o=None, lse=None, cu=None) == ea.ATTN_OK
+
+
+def test_splitkv_strided_validation():
+    ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    B, Hq, Hkv, Nq, Nk, d = 2, 8, 2, 3, 1000, 128
+    # q, o token-major [B, Nq, Hq, d]; cache token-major [B, Nk, Hkv, d]
+    tm = [Nq * Hq * d, d, Hq * d, Nk * Hkv * d, d, Hkv * d, Nq * Hq * d, d, Hq * d]
+
+    def ss(strides, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, ws=WS, B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d,
+                 causal=1, scale=0.125, ns=0, dtype=ea.ATTN_BF16)
+        a.update(kw)
+        return ea.attn_fwd_splitkv_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"],
+                                           strides, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                                           a["d"], a["causal"], a["scale"], a["ns"], a["dtype"],
+                                           None)
+
+    assert ss(tm) not in ok
+    for i, val in ((2, 64), (5, 100), (4, -8), (1, 1 << 30)):  # row < d, not x8, negative, group
+        bad = list(tm)
+        bad[i] = val
+        assert ss(bad) == ea.ATTN_ERR_INVALID_ARG, (i, val)
+    assert ea.lib().attn_fwd_splitkv_strided(Q, K, V, O, L, WS, None, B, Hq, Hkv, Nq, Nk, d, 1,
+                                             0.125, 0, 1, None) == ea.ATTN_ERR_INVALID_ARG
+    assert ss(tm, o=Q + 64) == ea.ATTN_ERR_INVALID_ARG  # output over an input
+    assert ss(tm, ws=O + 64) == ea.ATTN_ERR_INVALID_ARG  # workspace over the output
+    assert ss(tm, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert ss(tm, Nk=0) not in ok  # no keys: K and V are not read
+    assert ss(tm, B=0, q=None, k=None, v=None, o=None, lse=None, ws=None) == ea.ATTN_OK

@@ -7,7 +7,10 @@ back exactly O = 0, LSE = -inf.  Small shapes are compared in full (every
 split count, tails inside a split and at Nk, rows of several heads inside one
 wave); the full-size decode and append workloads are compared on whole
 batches that the oracle computes from the same inputs, in the launch
-configuration the benchmark times.
+configuration the benchmark times.  Strided tensors: token-major q, cache
+and output at d = 64, 128, 256, a cache that is a prefix of a longer
+preallocated buffer, and the dense strides bit for bit against the dense
+entry point.
 """
 import numpy as np
 import pytest
@@ -192,3 +195,60 @@ def test_full_size_sampled_batches(oracle_mod, name):
     for b in (0, w.B - 1):
         ro, rl = oracle_mod.fwd_bottom_right(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=w.causal)
         check(o[b:b + 1], lse[b:b + 1], ro, rl, f"{w.name} batch {b}")
+
+
+# ---------------------------------------------------------------- strided
+def token_major(t, dev):
+    """[B, H, N, d] -> the same values in a [B, N, H, d] buffer, viewed as [B, H, N, d]."""
+    return t.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+
+
+@pytest.mark.parametrize("Nq", [1, 5, 70])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_token_major_cache(oracle_mod, Nq, d, causal):
+    # q and the key/value cache token-major ([B, N, H, d]); the output too
+    dev = gpu()
+    q, k, v = attn_inputs.make_cache(2, 8, 2, Nq, 1500, d, seed=Nq + d)
+    qt, kt, vt = (token_major(t, dev) for t in (q, k, v))
+    o, lse = ea.fwd_splitkv(qt, kt, vt, causal=causal, num_splits=3)
+    torch.cuda.synchronize()
+    assert o.transpose(1, 2).is_contiguous()
+    ro, rl = oracle_mod.fwd_bottom_right(q, k, v, causal=causal)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"token-major Nq={Nq} d={d}")
+
+
+def test_cache_slices_of_a_larger_buffer(oracle_mod):
+    # k, v: the first Nk tokens of a longer preallocated [B, Nmax, Hkv, d] cache
+    dev = gpu()
+    B, Hq, Hkv, Nq, Nk, Nmax, d = 2, 8, 2, 4, 1000, 2048, 128
+    q, k, v = attn_inputs.make_cache(B, Hq, Hkv, Nq, Nk, d, seed=44)
+    kc = torch.zeros(B, Nmax, Hkv, d, dtype=k.dtype)
+    vc = torch.zeros(B, Nmax, Hkv, d, dtype=v.dtype)
+    kc[:, :Nk] = k.transpose(1, 2)
+    vc[:, :Nk] = v.transpose(1, 2)
+    kg = kc.to(dev)[:, :Nk].transpose(1, 2)
+    vg = vc.to(dev)[:, :Nk].transpose(1, 2)
+    o, lse = ea.fwd_splitkv(q.to(dev), kg, vg, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.fwd_bottom_right(q, k, v, causal=True)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "cache slice")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dense_strides_are_the_dense_entry_point_bitwise(d):
+    dev = gpu()
+    B, Hq, Hkv, Nq, Nk = 2, 8, 2, 3, 3000
+    q, k, v = (t.to(dev) for t in attn_inputs.make_cache(B, Hq, Hkv, Nq, Nk, d, seed=8))
+    o1, l1 = ea.fwd_splitkv(q, k, v, causal=True, num_splits=4)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    ws = torch.empty(ea.attn_fwd_splitkv_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, 4), device=dev,
+                     dtype=torch.uint8)
+    dense = [Hq * Nq * d, Nq * d, d, Hkv * Nk * d, Nk * d, d, Hq * Nq * d, Nq * d, d]
+    st = ea.attn_fwd_splitkv_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(),
+                                     l2.data_ptr(), ws.data_ptr(), dense, B, Hq, Hkv, Nq, Nk, d,
+                                     1, d ** -0.5, 4, ea.ATTN_BF16,
+                                     torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == ea.ATTN_OK
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
