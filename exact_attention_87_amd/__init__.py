@@ -80,6 +80,8 @@ def lib():
         L.attn_fwd_splitkv_workspace_bytes.argtypes = [ci] * 7
         L.attn_fwd_splitkv_workspace_bytes.restype = sz
         L.attn_fwd_blocksparse.argtypes = [vp] * 6 + [ci, vp] + [ci] * 6 + [cf, ci, vp]
+        L.attn_fwd_blocksparse_strided.argtypes = [vp] * 6 + [ci, vp, vp] + [ci] * 6 + [cf, ci, vp]
+        L.attn_fwd_blocksparse_strided.restype = ci
         L.attn_fwd_blocksparse.restype = ci
         L.attn_fwd_blocksparse_workspace_bytes.argtypes = [ci, ci, ci]
         L.attn_fwd_blocksparse_workspace_bytes.restype = sz
@@ -176,6 +178,15 @@ def attn_fwd_blocksparse(q, k, v, o, lse, block_mask, mask_heads, workspace, B, 
     return int(lib().attn_fwd_blocksparse(q, k, v, o, lse, block_mask, int(mask_heads), workspace,
                                           B, Hq, Hkv, N, d, int(causal), float(scale), int(dtype),
                                           stream))
+
+
+def attn_fwd_blocksparse_strided(q, k, v, o, lse, block_mask, mask_heads, workspace, strides, B, Hq,
+                                 Hkv, N, d, causal, scale, dtype, stream) -> int:
+    """strides: 9 element strides (q_b, q_h, q_row, kv_b, kv_h, kv_row, o_b, o_h, o_row)."""
+    arr = (ctypes.c_longlong * 9)(*[int(x) for x in strides])
+    return int(lib().attn_fwd_blocksparse_strided(q, k, v, o, lse, block_mask, mask_heads,
+                                                  workspace, arr, B, Hq, Hkv, N, d, int(causal),
+                                                  float(scale), int(dtype), stream))
 
 
 def attn_fwd_blocksparse_workspace_bytes(Hq, N, mask_heads) -> int:
@@ -337,10 +348,22 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
 def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None,
                     out=None, lse=None, workspace=None):
     """O, LSE of the block-sparse forward: block_mask is a device uint8 tensor
-    [1 or Hq, ceil(N/128), ceil(N/64)] over tiles of 128 queries x 64 keys."""
+    [1 or Hq, ceil(N/128), ceil(N/64)] over tiles of 128 queries x 64 keys.
+    q, k, v (and out) may be [B, H, N, d] views of any strides, as for
+    fwd_strided (out then defaults to a [B, N, Hq, d] tensor)."""
     import torch
 
-    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
+    dense = all(t.is_contiguous() for t in (q, k, v)) and (out is None or out.is_contiguous())
+    if dense:
+        B, Hq, Hkv, N, d = _check_qkv(q, k, v)
+    else:
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if t.dim() != 4 or not t.is_cuda:
+                raise ValueError(f"{name} must be a 4-D device tensor [B, H, N, d]")
+        if k.stride() != v.stride() or k.shape != v.shape:
+            raise ValueError("k and v must share shape and strides")
+        B, Hq, N, d = q.shape
+        Hkv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     nqb, nkt = -(-N // SPARSE_BLOCK_Q), -(-N // SPARSE_BLOCK_K)
@@ -349,7 +372,8 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
         raise ValueError(f"block_mask must be a contiguous device uint8 [1 or Hq, {nqb}, {nkt}]")
     mh = block_mask.shape[0]
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q) if dense else \
+            torch.empty((B, N, Hq, d), device=q.device, dtype=q.dtype).transpose(1, 2)
     if lse is None:
         lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
     nbytes = attn_fwd_blocksparse_workspace_bytes(Hq, N, mh)
@@ -357,11 +381,20 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
         raise AttnError(ATTN_ERR_INVALID_ARG, "attn_fwd_blocksparse_workspace_bytes")
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(max(nbytes, 256), device=q.device, dtype=torch.uint8)
-    st = attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              lse.data_ptr(), block_mask.data_ptr(), mh, workspace.data_ptr(), B,
-                              Hq, Hkv, N, d, causal, scale, _dtype_code(q), _stream_ptr(q))
+    if dense:
+        st = attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), block_mask.data_ptr(), mh, workspace.data_ptr(),
+                                  B, Hq, Hkv, N, d, causal, scale, _dtype_code(q), _stream_ptr(q))
+        what = "attn_fwd_blocksparse"
+    else:
+        strides = _bhnd_strides(q) + _bhnd_strides(k) + _bhnd_strides(out)
+        st = attn_fwd_blocksparse_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), lse.data_ptr(), block_mask.data_ptr(),
+                                          mh, workspace.data_ptr(), strides, B, Hq, Hkv, N, d,
+                                          causal, scale, _dtype_code(q), _stream_ptr(q))
+        what = "attn_fwd_blocksparse_strided"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fwd_blocksparse")
+        raise AttnError(st, what)
     return out, lse
 
 

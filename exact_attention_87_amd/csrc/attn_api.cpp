@@ -323,57 +323,6 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* 
 
 }  // extern "C"
 
-// ------------------------------------------------------------ block-sparse
-static_assert(ATTN_SPARSE_BLOCK_Q == attn::kSparseBlockQ && ATTN_SPARSE_BLOCK_K == attn::kSparseBlockK,
-              "header block sizes are the kernels' tiles");
-
-extern "C" {
-
-size_t attn_fwd_blocksparse_workspace_bytes(int Hq, int N, int mask_heads) {
-  if (Hq < 1 || N < 0 || N > (1 << 21) || !(mask_heads == 1 || mask_heads == Hq))
-    return (size_t)-1;
-  if (N == 0) return 0;
-  return attn::sparse_workspace_bytes(Hq, N, mask_heads);
-}
-
-attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
-                                 const unsigned char* block_mask, int mask_heads, void* workspace,
-                                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                                 attn_dtype dtype, void* stream) {
-  bool empty = false;
-  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
-  if (st != ATTN_OK) return st;
-  if (!(mask_heads == 1 || mask_heads == Hq)) return ATTN_ERR_INVALID_ARG;
-  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  // the tile list lives in LDS beside the stages (128 KiB of them at d = 256)
-  if (N > (d == 256 ? (1 << 20) : (1 << 21))) return ATTN_ERR_UNSUPPORTED;
-  if (empty) return ATTN_OK;
-  const size_t nqb = ((size_t)N + ATTN_SPARSE_BLOCK_Q - 1) / ATTN_SPARSE_BLOCK_Q;
-  const size_t nkt = ((size_t)N + ATTN_SPARSE_BLOCK_K - 1) / ATTN_SPARSE_BLOCK_K;
-  const Sizes z = sizes(B, Hq, Hkv, N, d);
-  const size_t mb = (size_t)mask_heads * nqb * nkt;
-  const size_t wb = attn_fwd_blocksparse_workspace_bytes(Hq, N, mask_heads);
-  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}},
-                     {{o, z.q}, {lse, z.l}, {workspace, wb}});
-  if (st != ATTN_OK) return st;
-  // the mask is an input too (any alignment: it is read byte by byte)
-  if (!block_mask) return ATTN_ERR_INVALID_ARG;
-  const Range rm{(uintptr_t)block_mask, (uintptr_t)block_mask + mb};
-  const Range outs[] = {{(uintptr_t)o, (uintptr_t)o + z.q},
-                        {(uintptr_t)lse, (uintptr_t)lse + z.l},
-                        {(uintptr_t)workspace, (uintptr_t)workspace + wb}};
-  for (const Range& r : outs)
-    if (overlaps(rm, r)) return ATTN_ERR_INVALID_ARG;
-  st = check_device();
-  if (st != ATTN_OK) return st;
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dtype,
-                  (hipStream_t)stream};
-  a.mask_heads = mask_heads;
-  return attn::launch_fwd_sparse(a, block_mask, workspace) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-}  // extern "C"
-
 // ------------------------------------------------------------ stride checks
 namespace {
 
@@ -398,6 +347,91 @@ size_t extent(const long long* s, int i, int B, int H, int N, int d) {
 }
 
 }  // namespace
+
+namespace {
+
+// The block-sparse forward on dense tensors (strides == nullptr) or with
+// the caller's 9 strides.
+attn_status fwd_blocksparse_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const unsigned char* block_mask, int mask_heads, void* workspace,
+                                 const long long* strides, int B, int Hq, int Hkv, int N, int d,
+                                 int causal, float scale, attn_dtype dtype, void* stream) {
+  bool empty = false;
+  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
+  if (st != ATTN_OK) return st;
+  if (!(mask_heads == 1 || mask_heads == Hq)) return ATTN_ERR_INVALID_ARG;
+  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  // the tile list lives in LDS beside the stages (128 KiB of them at d = 256)
+  if (N > (d == 256 ? (1 << 20) : (1 << 21))) return ATTN_ERR_UNSUPPORTED;
+  if (empty) return ATTN_OK;
+  const size_t nqb = ((size_t)N + ATTN_SPARSE_BLOCK_Q - 1) / ATTN_SPARSE_BLOCK_Q;
+  const size_t nkt = ((size_t)N + ATTN_SPARSE_BLOCK_K - 1) / ATTN_SPARSE_BLOCK_K;
+  const Sizes z = sizes(B, Hq, Hkv, N, d);
+  size_t eq = z.q, ek = z.kv, eo = z.q;
+  if (strides) {
+    for (int i = 0; i < 3; ++i)
+      if (!strides_ok(strides, i, N, d)) return ATTN_ERR_INVALID_ARG;
+    eq = extent(strides, 0, B, Hq, N, d);
+    ek = extent(strides, 1, B, Hkv, N, d);
+    eo = extent(strides, 2, B, Hq, N, d);
+  }
+  const size_t mb = (size_t)mask_heads * nqb * nkt;
+  const size_t wb = attn_fwd_blocksparse_workspace_bytes(Hq, N, mask_heads);
+  st = check_buffers({{q, eq}, {k, ek}, {v, ek}}, {{o, eo}, {lse, z.l}, {workspace, wb}});
+  if (st != ATTN_OK) return st;
+  // the mask is an input too (any alignment: it is read byte by byte)
+  if (!block_mask) return ATTN_ERR_INVALID_ARG;
+  const Range rm{(uintptr_t)block_mask, (uintptr_t)block_mask + mb};
+  const Range outs[] = {{(uintptr_t)o, (uintptr_t)o + eo},
+                        {(uintptr_t)lse, (uintptr_t)lse + z.l},
+                        {(uintptr_t)workspace, (uintptr_t)workspace + wb}};
+  for (const Range& r : outs)
+    if (overlaps(rm, r)) return ATTN_ERR_INVALID_ARG;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dtype,
+                  (hipStream_t)stream};
+  a.mask_heads = mask_heads;
+  if (strides)
+    a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
+  return attn::launch_fwd_sparse(a, block_mask, workspace) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ block-sparse
+static_assert(ATTN_SPARSE_BLOCK_Q == attn::kSparseBlockQ && ATTN_SPARSE_BLOCK_K == attn::kSparseBlockK,
+              "header block sizes are the kernels' tiles");
+
+extern "C" {
+
+size_t attn_fwd_blocksparse_workspace_bytes(int Hq, int N, int mask_heads) {
+  if (Hq < 1 || N < 0 || N > (1 << 21) || !(mask_heads == 1 || mask_heads == Hq))
+    return (size_t)-1;
+  if (N == 0) return 0;
+  return attn::sparse_workspace_bytes(Hq, N, mask_heads);
+}
+
+attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const unsigned char* block_mask, int mask_heads, void* workspace,
+                                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                 attn_dtype dtype, void* stream) {
+  return fwd_blocksparse_impl(q, k, v, o, lse, block_mask, mask_heads, workspace, nullptr, B, Hq,
+                              Hkv, N, d, causal, scale, dtype, stream);
+}
+
+attn_status attn_fwd_blocksparse_strided(const void* q, const void* k, const void* v, void* o,
+                                         float* lse, const unsigned char* block_mask,
+                                         int mask_heads, void* workspace,
+                                         const long long* strides, int B, int Hq, int Hkv, int N,
+                                         int d, int causal, float scale, attn_dtype dtype,
+                                         void* stream) {
+  if (!strides) return ATTN_ERR_INVALID_ARG;
+  return fwd_blocksparse_impl(q, k, v, o, lse, block_mask, mask_heads, workspace, strides, B, Hq,
+                              Hkv, N, d, causal, scale, dtype, stream);
+}
+
+}  // extern "C"
 
 // ------------------------------------------------------------ packed variable length
 

@@ -241,6 +241,19 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
                                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                                  attn_dtype dtype, void* stream);
 
+/*
+ * attn_fwd_blocksparse on tensors of any (batch, head, row) element strides:
+ * strides[0..8] and their rules as for attn_fwd_strided (the mask, lse and
+ * workspace stay dense).  With the dense strides the result is
+ * attn_fwd_blocksparse's bit for bit.
+ */
+attn_status attn_fwd_blocksparse_strided(const void* q, const void* k, const void* v, void* o,
+                                         float* lse, const unsigned char* block_mask,
+                                         int mask_heads, void* workspace,
+                                         const long long* strides, int B, int Hq, int Hkv, int N,
+                                         int d, int causal, float scale, attn_dtype dtype,
+                                         void* stream);
+
 /* Bytes of workspace attn_fwd_blocksparse needs (a multiple of 256); 0 for
  * N == 0; (size_t)-1 for Hq < 1, N outside [0, 2^21] or mask_heads other
  * than 1 or Hq. */

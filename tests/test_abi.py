@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
                                   "attn_bwd_dq_stats", "attn_bwd_preprocess", "attn_bwd_strided", "attn_bwd_varlen",
                                   "attn_bwd_varlen_strided",
                                   "attn_bwd_workspace_bytes", "attn_fwd",
-                                  "attn_fwd_blocksparse", "attn_fwd_blocksparse_workspace_bytes",
+                                  "attn_fwd_blocksparse", "attn_fwd_blocksparse_strided",
+                                  "attn_fwd_blocksparse_workspace_bytes",
                                   "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
                                   "attn_fwd_splitkv_strided",
                                   "attn_fwd_splitkv_workspace_bytes", "attn_fwd_strided",
@@ -494,3 +495,30 @@ def test_splitkv_strided_validation():
     assert ss(tm, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
     assert ss(tm, Nk=0) not in ok  # no keys: K and V are not read
     assert ss(tm, B=0, q=None, k=None, v=None, o=None, lse=None, ws=None) == ea.ATTN_OK
+
+
+def test_blocksparse_strided_validation():
+    ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
+    B, Hq, Hkv, N, d = 2, 4, 2, 300, 64
+    tm = [N * Hq * d, d, Hq * d, N * Hkv * d, d, Hkv * d, N * Hq * d, d, Hq * d]
+    M = 0x10000000 * 13  # the mask
+
+    def bs(strides, **kw):
+        a = dict(q=Q, k=K, v=V, o=O, lse=L, m=M, mh=1, ws=WS, B=B, Hq=Hq, Hkv=Hkv, N=N, d=d,
+                 causal=1, scale=0.125, dtype=ea.ATTN_BF16)
+        a.update(kw)
+        return ea.attn_fwd_blocksparse_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["m"],
+                                               a["mh"], a["ws"], strides, a["B"], a["Hq"],
+                                               a["Hkv"], a["N"], a["d"], a["causal"], a["scale"],
+                                               a["dtype"], None)
+
+    assert bs(tm) not in ok
+    bad = list(tm)
+    bad[2] = 32  # row stride below d
+    assert bs(bad) == ea.ATTN_ERR_INVALID_ARG
+    assert ea.lib().attn_fwd_blocksparse_strided(Q, K, V, O, L, M, 1, WS, None, B, Hq, Hkv, N, d,
+                                                 1, 0.125, 1, None) == ea.ATTN_ERR_INVALID_ARG
+    assert bs(tm, o=Q + 64) == ea.ATTN_ERR_INVALID_ARG
+    assert bs(tm, m=O + 16) == ea.ATTN_ERR_INVALID_ARG  # mask inside the output
+    assert bs(tm, mh=3) == ea.ATTN_ERR_INVALID_ARG
+    assert bs(tm, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED

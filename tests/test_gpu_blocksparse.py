@@ -6,7 +6,8 @@ element-wise and |LSE - LSE_ref| <= 1e-3; a row that sees no key must be
 exactly O = 0, LSE = -inf.  A full mask must reproduce attn_fwd bit for bit
 (same tiles, same order, same arithmetic), an empty mask must leave every row
 empty.  The full-size case is checked on whole heads that the oracle
-computes from the same inputs.
+computes from the same inputs.  Strided tensors: token-major q, k, v and
+output, and the dense strides bit for bit against the dense entry point.
 """
 import numpy as np
 import pytest
@@ -159,3 +160,37 @@ def test_full_size_sampled_heads(oracle_mod):
                                           v[:, g:g + 1].contiguous(), mask[h:h + 1], BQ, BK,
                                           causal=w.causal)
         check(o[:, h:h + 1], lse[:, h:h + 1], ro, rl, f"{w.name} head {h}")
+
+
+# ---------------------------------------------------------------- strided
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_token_major_layout(oracle_mod, d, causal):
+    dev = gpu()
+    q, k, v = attn_inputs.make(2, 8, 2, 700, d, "bf16", seed=d + 60)
+    mask = rand_mask(8, 700, 0.4, seed=d)
+    qt, kt, vt = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2) for t in (q, k, v))
+    o, lse = ea.fwd_blocksparse(qt, kt, vt, torch.from_numpy(mask).to(dev), causal=causal)
+    torch.cuda.synchronize()
+    assert o.transpose(1, 2).is_contiguous()
+    ro, rl = oracle_mod.fwd_blockmask(q, k, v, mask, BQ, BK, causal=causal)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"token-major d={d}")
+
+
+def test_dense_strides_are_the_dense_entry_point_bitwise():
+    dev = gpu()
+    B, Hq, Hkv, N, d = 2, 4, 2, 500, 128
+    q, k, v = (t.to(dev) for t in attn_inputs.make(B, Hq, Hkv, N, d, "bf16", seed=61))
+    mask = torch.from_numpy(rand_mask(1, N, 0.5, seed=4)).to(dev)
+    o1, l1 = ea.fwd_blocksparse(q, k, v, mask, causal=True)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    ws = torch.empty(ea.attn_fwd_blocksparse_workspace_bytes(Hq, N, 1), device=dev,
+                     dtype=torch.uint8)
+    dense = [Hq * N * d, N * d, d, Hkv * N * d, N * d, d, Hq * N * d, N * d, d]
+    st = ea.attn_fwd_blocksparse_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(),
+                                         l2.data_ptr(), mask.data_ptr(), 1, ws.data_ptr(), dense,
+                                         B, Hq, Hkv, N, d, 1, d ** -0.5, ea.ATTN_BF16,
+                                         torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == ea.ATTN_OK
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
