@@ -452,6 +452,17 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #define ATTN_PIPE_VPM256 6
 #endif
 
+#ifndef ATTN_PIPE_LA
+#define ATTN_PIPE_LA 4  // K-fragment LDS reads issued ahead of their MFMA
+#endif
+// Wave priorities (s_setprio) of the pipelined kernel: during the P V
+// products, and during the look-ahead scores interleaved with the softmax.
+#ifndef ATTN_PIPE_PRIO_PV
+#define ATTN_PIPE_PRIO_PV 1
+#endif
+#ifndef ATTN_PIPE_PRIO_S
+#define ATTN_PIPE_PRIO_S 0
+#endif
 #ifndef ATTN_PIPE_NW
 #define ATTN_PIPE_NW 4
 #endif
@@ -649,12 +660,13 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
       float tsum;
       if (ahead) {
         __builtin_amdgcn_sched_barrier(0);
+        if (ATTN_PIPE_PRIO_S) __builtin_amdgcn_s_setprio(ATTN_PIPE_PRIO_S);
         scores(kstage(BUF ^ 1), sn);
         tsum = softmax_exp(sc, ms, pk);
         if (ATTN_PIPE_SCHED) {
           // K fragments stream a few MFMAs ahead of their use; the softmax
           // of tile j fills the matrix-core issue gaps.
-          constexpr int LA = 4;  // LDS reads ahead
+          constexpr int LA = ATTN_PIPE_LA;  // LDS reads ahead
           __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
           for (int i = 0; i < 2 * NQC; ++i) {
@@ -664,6 +676,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (ATTN_PIPE_PRIO_S) __builtin_amdgcn_s_setprio(0);
       } else {
         tsum = softmax_exp(sc, ms, pk);
       }
@@ -687,7 +700,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
         }
       }
       lsum += tsum;
-      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_PIPE_PRIO_PV);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
