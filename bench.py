@@ -22,7 +22,8 @@ block-sparse forward on a local + global + random block mask (TFLOP/s over
 the visible pairs, and the dense forward of the same shape beside it), the
 packed variable-length forward on a document batch (and the same documents
 padded to the longest), and the fp64 CPU oracle timed on a bounded sample of
-the same workload.
+the same workload.  A backward sweep times attn_bwd alone (algorithmic
+10*B*H*N^2*d, halved for causal) on d = 128 and 256 shapes.
 """
 from __future__ import annotations
 
@@ -474,22 +475,29 @@ def main():
     calibration_copy(args.copy_mib, dev)
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in launches] for _ in range(K)]
-    start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    # HIP events recorded between the launches of every other timed step give
+    # each kernel's duration; the steps in between run without them, which
+    # halves the wall time the instrumentation adds to the timed region.
+    probed = list(range(0, K, 2))
+    evs = {s: [torch.cuda.Event(enable_timing=True) for _ in launches] for s in probed}
+    start = {s: torch.cuda.Event(enable_timing=True) for s in probed}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        start[s].record(stream)
-        step(evs[s])
+        if s in start:
+            start[s].record(stream)
+            step(evs[s])
+        else:
+            step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
 
     kern_ms = {name: 0.0 for name, _ in launches}
-    for s in range(K):
+    for s in probed:
         prev = start[s]
         for i, (name, _) in enumerate(launches):
-            kern_ms[name] += prev.elapsed_time(evs[s][i]) / K
+            kern_ms[name] += prev.elapsed_time(evs[s][i]) / len(probed)
             prev = evs[s][i]
     gpu_ms = sum(kern_ms.values())
 
@@ -547,6 +555,50 @@ def main():
             del cq, ck, cv, co, cl
         torch.cuda.synchronize()
 
+    # backward sweep (attn_bwd alone, back-to-back calls; parity-tested separately)
+    bwd_sweep = {}
+    if not args.no_sweep:
+        bcases = [
+            attn_inputs.Workload("causal_gqa_bf16_B1_Hq32_Hkv8_N16384_d128", 1, 32, 8, 16384, 128,
+                                 True, "bf16", seed=4),
+            attn_inputs.Workload("noncausal_bf16_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, False,
+                                 "bf16", seed=6),
+            attn_inputs.Workload("causal_bf16_B4_H32_N4000_d128", 4, 32, 32, 4000, 128, True,
+                                 "bf16", seed=3),
+            attn_inputs.Workload("noncausal_bf16_B1_H16_N8192_d256", 1, 16, 16, 8192, 256, False,
+                                 "bf16", seed=9),
+        ]
+        for cw in bcases:
+            cq, ck, cv, cdo = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=True))
+            co, cl = ea.fwd(cq, ck, cv, causal=cw.causal)
+            cws = torch.empty(ea.attn_bwd_workspace_bytes(cw.B, cw.Hq, cw.Hkv, cw.N, cw.d,
+                                                          ea.ATTN_BF16), device=dev,
+                              dtype=torch.uint8)
+            grads = [torch.empty_like(t) for t in (cq, ck, cv)]
+
+            def bwd_call():
+                check(ea.attn_bwd(cq.data_ptr(), ck.data_ptr(), cv.data_ptr(), co.data_ptr(),
+                                  cl.data_ptr(), cdo.data_ptr(), grads[0].data_ptr(),
+                                  grads[1].data_ptr(), grads[2].data_ptr(), cws.data_ptr(), cw.B,
+                                  cw.Hq, cw.Hkv, cw.N, cw.d, int(cw.causal), cw.d ** -0.5,
+                                  ea.ATTN_BF16, sp), "attn_bwd")
+
+            for _ in range(3):
+                bwd_call()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record(stream)
+            for _ in range(reps):
+                bwd_call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            tf = 2.5 * fwd_flops(cw.B, cw.Hq, cw.N, cw.d, cw.causal) / (ms / 1e3) / 1e12
+            bwd_sweep[cw.name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                  "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del cq, ck, cv, cdo, co, cl, cws, grads
+        torch.cuda.synchronize()
+
     # split-K/V forward on the key/value-cache workloads (parity-tested separately)
     splitkv = {}
     if not args.no_sweep:
@@ -592,6 +644,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "forward_sweep": sweep,
+        "backward_sweep": bwd_sweep,
         "splitkv": splitkv,
         "blocksparse": blocksparse,
         "varlen": varlen,
