@@ -48,6 +48,16 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 #ifndef ATTN_BWD_WPE128
 #define ATTN_BWD_WPE128 1
 #endif
+// Scheduling fences between the dV/dK products of the d = 64 dK/dV kernel at
+// three waves per SIMD: 0 none, 1 per feature block, 2 per 16 queries.  None
+// fits 168 registers and was fastest on the causal d = 64 backward (+3%).
+// d = 256 keeps one per feature block.
+#ifndef ATTN_BWD_FENCE_C64
+#define ATTN_BWD_FENCE_C64 0
+#endif
+#ifndef ATTN_DQ_FENCE
+#define ATTN_DQ_FENCE 1  // fence between the two key blocks of a dQ tile when registers are tight
+#endif
 #ifndef ATTN_DQ_WPE64
 #define ATTN_DQ_WPE64 3
 #endif
@@ -266,6 +276,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // hoisted, where registers are tight: d = 256 (K, V, dK and dV already
   // hold 384) and d = 64 at three waves per SIMD (168 each).
   constexpr int CG = D > 128 ? 2 : (Cfg::WPE >= 3 ? 2 : NQC);
+  constexpr int FENCE_C = D > 128 ? 1 : ATTN_BWD_FENCE_C64;
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
                     f32x16& sacc, f32x16& pacc) {
     // the dP accumulator starts at -D of each row (element 4*rg+e is row
@@ -335,9 +346,9 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         const u32x2 b0 = lds_read_tr(qtile + rows + tro(0, mb));
         const u32x2 b1 = lds_read_tr(qtile + rows + tro(1, mb));
         dkacc[mb] = mfma32(bitcast<V8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
-        if constexpr (CG < NQC)
-          __builtin_amdgcn_sched_barrier(0);
+        if constexpr (CG < NQC && FENCE_C == 1) __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (CG < NQC && FENCE_C == 2) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -645,7 +656,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
             dqacc[mb] = mfma32(a, sb, dqacc[mb]);
           }
-        if constexpr (SEQ) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SEQ && ATTN_DQ_FENCE) __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (j + 1 < ntiles) {
