@@ -55,6 +55,10 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 #ifndef ATTN_BWD_FENCE_C64
 #define ATTN_BWD_FENCE_C64 0
 #endif
+#ifndef ATTN_BWD_FENCE_A64
+#define ATTN_BWD_FENCE_A64 1  // fences between the operand groups of the S, dP products
+                              // (without them: 3 spilled registers, -2% causal)
+#endif
 #ifndef ATTN_DQ_FENCE
 #define ATTN_DQ_FENCE 1  // fence between the two key blocks of a dQ tile when registers are tight
 #endif
@@ -277,6 +281,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // hold 384) and d = 64 at three waves per SIMD (168 each).
   constexpr int CG = D > 128 ? 2 : (Cfg::WPE >= 3 ? 2 : NQC);
   constexpr int FENCE_C = D > 128 ? 1 : ATTN_BWD_FENCE_C64;
+  constexpr bool FENCE_A = D > 128 || ATTN_BWD_FENCE_A64;
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
                     f32x16& sacc, f32x16& pacc) {
     // the dP accumulator starts at -D of each row (element 4*rg+e is row
@@ -301,7 +306,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         sacc = mfma32(bitcast<V8>(qa[cc]), kreg[c0 + cc], sacc);
         pacc = mfma32(bitcast<V8>(da[cc]), vreg[c0 + cc], pacc);
       }
-      if constexpr (CG < NQC) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (CG < NQC && FENCE_A) __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto phaseV = [&](const float* lse2, int qbase, int qfirst, bool diag, const f32x16& sacc,
