@@ -55,6 +55,16 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 #ifndef ATTN_BWD_FENCE_C64
 #define ATTN_BWD_FENCE_C64 0
 #endif
+// Raised wave priority (s_setprio 1) in the matrix-core phases of the dK/dV
+// kernel: 0 never, 1 in the S/dP and dV/dK products, 2 in dV/dK only,
+// 3 in S/dP only.  None of them, nor raising it in the dQ kernel's products,
+// helped the d = 64 or d = 128 backward (same-box A/B, 0 to -3%).
+#ifndef ATTN_BWD_PRIO
+#define ATTN_BWD_PRIO 0
+#endif
+#ifndef ATTN_DQ_PRIO
+#define ATTN_DQ_PRIO 0  // 1: raised priority in the dQ kernel's products
+#endif
 #ifndef ATTN_BWD_FENCE_A64
 #define ATTN_BWD_FENCE_A64 1  // fences between the operand groups of the S, dP products
                               // (without them: 3 spilled registers, -2% causal)
@@ -293,6 +303,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
     }
     sacc = f32x16{};
+    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 3) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c0 = 0; c0 < NQC; c0 += CG) {
       u32x4 qa[CG], da[CG];
@@ -308,6 +319,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       }
       if constexpr (CG < NQC && FENCE_A) __builtin_amdgcn_sched_barrier(0);
     }
+    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 3) __builtin_amdgcn_s_setprio(0);
   };
   auto phaseV = [&](const float* lse2, int qbase, int qfirst, bool diag, const f32x16& sacc,
                     const f32x16& pacc, uint32_t (&pk)[8], uint32_t (&dsk)[8]) {
@@ -337,6 +349,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   };
   auto phaseC = [&](const char* qtile, const char* dotile, int qbase, const uint32_t (&pk)[8],
                     const uint32_t (&dsk)[8]) {
+    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int cp = 0; cp < 2; ++cp) {
       const V8 pb = bitcast<V8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
@@ -355,6 +368,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       }
       if constexpr (CG < NQC && FENCE_C == 2) __builtin_amdgcn_sched_barrier(0);
     }
+    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 2) __builtin_amdgcn_s_setprio(0);
   };
 
   auto step = [&](auto bufc, int it) {
@@ -618,6 +632,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int kbk = 0; kbk < 2; ++kbk) {
         // S^T = K Q^T and dP^T - D = V dO^T - D for the tile's 32-key block kbk
         f32x16 sacc = f32x16{}, pacc = pinit;
+        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c0 = 0; c0 < NQC; c0 += CG) {
           u32x4 ka[CG], va[CG];
@@ -632,6 +647,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             pacc = mfma32(bitcast<V8>(va[cc]), doreg[c0 + cc], pacc);
           }
         }
+        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(0);
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(sacc[r], c, -lse2));
@@ -649,6 +665,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
           dsk[r >> 1] = pack2<T>(pv[r] * pacc[r], pv[r + 1] * pacc[r + 1]);
         // dQ^T += K^T dS^T (per mb the same accumulation order as key block
         // by key block)
+        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -661,6 +678,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
             dqacc[mb] = mfma32(a, sb, dqacc[mb]);
           }
+        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(0);
         if constexpr (SEQ && ATTN_DQ_FENCE) __builtin_amdgcn_sched_barrier(0);
       }
     }

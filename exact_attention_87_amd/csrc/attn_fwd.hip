@@ -39,6 +39,12 @@ namespace attn {
 #ifndef ATTN_FWD_WPE128
 #define ATTN_FWD_WPE128 2
 #endif
+// Raised wave priority around the matrix-core products (s_setprio 1): worth
+// 4-6% on the pipelined d = 128 forward; off for the plain kernel at d = 64,
+// where four waves share a SIMD and it cost 1-3%.
+#ifndef ATTN_FWD_PRIO64
+#define ATTN_FWD_PRIO64 0
+#endif
 #ifndef ATTN_FWD_SETPRIO
 #define ATTN_FWD_SETPRIO 1
 #endif
@@ -109,6 +115,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   static_assert(PW * NW * 1024 == TILEB, "tile pieces");
   constexpr int NQC = D / 16;  // k-chunks of the S contraction
   constexpr int NMB = D / 32;  // 32-row blocks of O^T
+  constexpr bool PRIO = D == 64 ? ATTN_FWD_PRIO64 : ATTN_FWD_SETPRIO;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];  // [NBUF][K tile | V tile]
 
@@ -282,7 +289,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #pragma unroll
           for (int cc = 0; cc < NQC; ++cc)
             kfrag[kk][cc] = lds_read16(kt + (k0b + kk) * 32 * ROWB + koff[cc]);
-        if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < KF; ++kk)
 #pragma unroll
@@ -292,7 +299,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
             for (int cc = 0; cc < NQC; ++cc)
               sacc[nb][k0b + kk] = mfma32(bitcast<V8>(kfrag[kk][cc]), qreg[nb][cc], sacc[nb][k0b + kk]);
           }
-        if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
       }
       // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
       // and kept as a branch rather than flattened into selects)
@@ -346,7 +353,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) lsum[nb] += tsum[nb];
       // ---- O^T += V^T P^T (each V^T fragment feeds every query block)
-      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(1);
+      if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -364,7 +371,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
               oacc[nb][mb] = mfma32(a, bp, oacc[nb][mb]);
             }
           }
-      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
+      if (PRIO) __builtin_amdgcn_s_setprio(0);
     }
     if (j + 1 < ntiles) {
       // tile j+1 must have landed; tile j+2 (three stages) may stay in flight
