@@ -17,7 +17,8 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Tensors are dense, contiguous, row-major:
+ *  - Tensors are dense, contiguous, row-major (the *_strided entry points
+ *    take element strides instead):
  *        Q, O, dQ, dO : [B, Hq,  N, d]
  *        K, V, dK, dV : [B, Hkv, N, d]
  *        LSE          : [B, Hq,  N]      (fp32, natural log)
