@@ -389,7 +389,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; use --gpus 1"}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; use --gpus 1"}))
         print("bench.py: only --gpus 1 is supported (single-GPU kernel library)", file=sys.stderr)
         sys.exit(2)
 

@@ -45,8 +45,8 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with exact_attention_87_amd._build.build() "
-                "(or __graft_entry__.build()); there is no fallback implementation")
+                f"{LIB_PATH} is missing: build it with `python -m exact_attention_87_amd._build`; "
+                "there is no fallback implementation")
         L = ctypes.CDLL(LIB_PATH)
         vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.attn_abi_version.argtypes = []

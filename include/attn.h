@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,        /* bad pointer, size, alignment or overlap */
-  ATTN_ERR_UNSUPPORTED = 2,        /* valid request this build does not implement */
+  ATTN_ERR_UNSUPPORTED = 2,        /* valid request the library does not implement */
   ATTN_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 */
   ATTN_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } attn_status;
