@@ -54,6 +54,9 @@ attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float 
   // Limits of the kernels' 32-bit grid, row and byte offsets: one (batch,
   // head) slice stays below 1 GiB.
   if ((int64_t)B * Hq > (1 << 24) || N > (1 << 22)) return ATTN_ERR_UNSUPPORTED;
+  // every one-dimensional grid (at most one workgroup per 32 rows of each
+  // (batch, head) slice) stays below 2^31 workgroups
+  if ((int64_t)B * Hq * ((N + 31) / 32) >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
   *empty = (B == 0 || N == 0);
   return ATTN_OK;
 }

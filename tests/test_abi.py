@@ -522,3 +522,10 @@ def test_blocksparse_strided_validation():
     assert bs(tm, m=O + 16) == ea.ATTN_ERR_INVALID_ARG  # mask inside the output
     assert bs(tm, mh=3) == ea.ATTN_ERR_INVALID_ARG
     assert bs(tm, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_grid_limit_is_rejected():
+    # (1 << 24) slices of 2^12 rows: 2^31 workgroups of 32 rows; valid sizes
+    # individually, too many workgroups together
+    assert fwd(B=1 << 20, Hq=16, Hkv=16, N=1 << 12) == ea.ATTN_ERR_UNSUPPORTED
+    assert fwd(B=1 << 20, Hq=16, Hkv=16, N=(1 << 12) - 32) not in (ea.ATTN_ERR_UNSUPPORTED,)
