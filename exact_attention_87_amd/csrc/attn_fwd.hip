@@ -79,7 +79,7 @@ __device__ __forceinline__ void work_item(int nqb, int BH, int& qb, int& bh) {
   bh = id % BH;
 }
 
-// Per head dim: a value for d = 64, 128 and 256.// Per head dim: a value for d = 64, 128 and 256.
+// Per head dim: a value for d = 64, 128 and 256.
 template <int D>
 constexpr int by_dim(int v64, int v128, int v256) {
   return D == 64 ? v64 : D == 128 ? v128 : v256;
