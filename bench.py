@@ -20,8 +20,8 @@ duration, a forward sweep over the other workloads, the split-K/V forward on
 the key/value-cache workloads (decode, append; GB/s against HBM), the
 block-sparse forward on a local + global + random block mask (TFLOP/s over
 the visible pairs, and the dense forward of the same shape beside it), the
-packed variable-length forward on a document batch (and the same documents
-padded to the longest), and the fp64 CPU oracle timed on a bounded sample of
+packed variable-length forward and backward on a document batch (and the
+same documents padded to the longest), and the fp64 CPU oracle timed on a bounded sample of
 the same workload.  A backward sweep times attn_bwd alone (algorithmic
 10*B*H*N^2*d, halved for causal) on d = 128 and 256 shapes.
 """
@@ -138,6 +138,10 @@ def forward_only(w, args, dev):
         "ms_per_step": round(wall * 1e3 / args.steps, 5), "kernel_ms": round(ms, 5),
         "frac_of_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "higher_is_better": True,
         "dtype": w.dtype, "data": "synthetic",
+        "roofline": {"bound": "mfma", "achieved": round(fl / ms / 1e9, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(f"fwd_workload{args.fwd_only}"), "kernel": "fwd"},
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "q_mult": w.q_mult, "seed": w.seed}}), flush=True)
 
@@ -313,11 +317,21 @@ def varlen_case(vw, dev, steps, warmup):
 
     ms = timed(lambda: ea.fwd_varlen(q, k, v, cu, mx, causal=vw.causal, out=o, lse=lse))
     ms_pad = timed(lambda: ea.fwd(qp, kp, vp_, causal=vw.causal, out=op, lse=lp))
+    # backward of the same packed batch (statistics, dK/dV and dQ launches)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(vw.seed + 1)).to(
+        dev, dtype=q.dtype)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(ea.attn_bwd_workspace_bytes(1, vw.Hq, vw.Hkv, vw.T, vw.d, ea.ATTN_BF16),
+                         256), device=dev, dtype=torch.uint8)
+    ms_bwd = timed(lambda: ea.bwd_varlen(q, k, v, o, lse, do, cu, mx, causal=vw.causal,
+                                         workspace=ws, dq=dq, dk=dk, dv=dv))
     pairs = sum(n * (n + 1) // 2 if vw.causal else n * n for n in lengths) * vw.Hq
     tf = 4.0 * vw.d * pairs / (ms / 1e3) / 1e12
+    tfb = 10.0 * vw.d * pairs / (ms_bwd / 1e3) / 1e12
     return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "sequences": nseq, "longest": mx, "padded_ms": round(ms_pad, 4),
-            "speedup_vs_padded": round(ms_pad / ms, 2)}
+            "speedup_vs_padded": round(ms_pad / ms, 2), "bwd_ms": round(ms_bwd, 4),
+            "bwd_tflops": round(tfb, 1), "bwd_frac_of_peak": round(tfb / PEAK_BF16_TFLOPS, 4)}
 
 
 def varlen_only(name, args, dev):
@@ -329,7 +343,12 @@ def varlen_only(name, args, dev):
         "metric": "packed variable-length attention forward TFLOP/s on 1 MI355X",
         "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "dtype": "bf16",
-        "data": "synthetic", "detail": r,
+        "data": "synthetic",
+        "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": r["frac_of_peak"],
+                     "traffic": load_traffic("varlen_" + name),
+                     "kernel": "fwd_mfma_pipe (one launch; 4*d FLOP per visible pair)"},
+        "detail": r,
         "config": {"workload": vw.name, "Hq": vw.Hq, "Hkv": vw.Hkv, "T": vw.T, "d": vw.d,
                    "causal": vw.causal, "seed": vw.seed}}), flush=True)
 
@@ -343,7 +362,12 @@ def sparse_only(name, args, dev):
         "metric": "block-sparse attention forward TFLOP/s (visible pairs) on 1 MI355X",
         "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": r["ms"], "higher_is_better": True, "dtype": "bf16",
-        "data": "synthetic", "detail": r,
+        "data": "synthetic",
+        "roofline": {"bound": "mfma", "achieved": r["tflops"], "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": r["frac_of_peak"],
+                     "traffic": load_traffic("blocksparse_" + name),
+                     "kernel": "sparse_compact + fwd_mfma_pipe (one call; 4*d FLOP per visible pair)"},
+        "detail": r,
         "config": {"workload": sw.name, "B": sw.B, "Hq": sw.Hq, "Hkv": sw.Hkv, "N": sw.N,
                    "d": sw.d, "causal": sw.causal, "seed": sw.seed}}), flush=True)
 

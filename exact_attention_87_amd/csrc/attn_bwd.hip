@@ -480,7 +480,9 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int BH = gridDim.x / nqb;
   const int id = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-  const int bh = id % BH;
+  // grouped-query heads of one kv group share one XCD's L2 (as in the
+  // forward; packed variable-length slices keep the plain round-robin deal)
+  const int bh = (!VARLEN && Hq != Hkv) ? xcd_contiguous(id % BH, BH) : id % BH;
   // One (batch, head) slice of Nmax rows, or one (sequence, head) of packed
   // variable-length sequences.  Q and dQ share one stride set, K and V
   // another, dO has O's.

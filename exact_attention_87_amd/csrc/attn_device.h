@@ -170,6 +170,17 @@ __device__ __forceinline__ int tr_off(int lane, int kbase, int dbase, int t) {
   return tile_off<D>(row, d >> 3) + ((d & 7) << 1);
 }
 
+// Workgroup ids are dealt round robin to the 8 XCDs, each with its own L2.
+// Remap the slice index j of a round of n workgroups (one per slice) so that
+// the XCD receiving ids = x (mod 8) gets the contiguous slices x*n/8 ..
+// (x+1)*n/8 - 1: the query heads of one kv group, adjacent in the slice
+// order, then share that XCD's L2 and K/V come from HBM once per group
+// rather than once per head.  A bijection when n is a multiple of 8; the
+// identity otherwise.
+__device__ __forceinline__ int xcd_contiguous(int j, int n) {
+  return (n & 7) ? j : (j & 7) * (n >> 3) + (j >> 3);
+}
+
 // Raw buffer resource over [base, base + bytes): loads beyond the range
 // return zeros, which is how tail rows and keys are padded.  Word 3 is the
 // gfx9-family raw-buffer format.

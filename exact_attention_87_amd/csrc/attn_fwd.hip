@@ -70,13 +70,24 @@ namespace attn {
 
 // Work map of the forward grids (nqb query blocks x BH (batch, head) slices):
 // the heaviest query blocks first under the causal mask; the heads of one
-// kv group are adjacent.  (Keeping a kv group's blocks on one XCD's L2 was
-// measured slower: it breaks the heaviest-first order.)
+// kv group are adjacent.  (A map that kept all of a kv group's query blocks on
+// one XCD was measured slower: it breaks the heaviest-first order.  The
+// per-round deal below keeps that order.)
+#ifndef ATTN_FWD_XCD
+#define ATTN_FWD_XCD 1
+#endif
 template <bool CAUSAL>
-__device__ __forceinline__ void work_item(int nqb, int BH, int& qb, int& bh) {
+__device__ __forceinline__ void work_item(int nqb, int BH, bool grouped, int& qb, int& bh) {
   const int id = blockIdx.x;
   qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
   bh = id % BH;
+  // Grouped-query problems: within each round of BH workgroups (one query
+  // block of every slice) the heads of one kv group go to one XCD and share
+  // its L2 (xcd_contiguous).  The round order, and with it the heaviest-first
+  // order, is unchanged.  With one query head per kv head there is nothing to
+  // share; packed variable-length slices differ in work, and contiguous runs
+  // of them would load the XCDs unevenly, so that mode keeps the plain deal.
+  if (ATTN_FWD_XCD && grouped) bh = xcd_contiguous(bh, BH);
 }
 
 // Per head dim: a value for d = 64, 128 and 256.
@@ -128,7 +139,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   // one key/value group are adjacent so they share K/V in cache.
   const int BH = gridDim.x / nqb;
   int qb, bh;
-  work_item<CAUSAL>(nqb, BH, qb, bh);
+  work_item<CAUSAL>(nqb, BH, MODE != kFwdVarlen && Hq != Hkv, qb, bh);
   // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
@@ -511,7 +522,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
 
   const int BH = gridDim.x / nqb;
   int qb, bh;
-  work_item<CAUSAL>(nqb, BH, qb, bh);
+  work_item<CAUSAL>(nqb, BH, MODE != kFwdVarlen && Hq != Hkv, qb, bh);
   // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
