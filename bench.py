@@ -23,7 +23,8 @@ the visible pairs, and the dense forward of the same shape beside it), the
 packed variable-length forward and backward on a document batch (and the
 same documents padded to the longest), and the fp64 CPU oracle timed on a bounded sample of
 the same workload.  A backward sweep times attn_bwd alone (algorithmic
-10*B*H*N^2*d, halved for causal) on d = 128 and 256 shapes.
+10*B*H*N^2*d, halved for causal) on d = 128 and 256 shapes, one of them a
+grouped-query shape short enough that the dK/dV stage splits its query heads.
 """
 from __future__ import annotations
 
@@ -591,6 +592,10 @@ def main():
                                  "bf16", seed=3),
             attn_inputs.Workload("noncausal_bf16_B1_H16_N8192_d256", 1, 16, 16, 8192, 256, False,
                                  "bf16", seed=9),
+            # grouped-query heads at a short length: 128 key blocks x kv heads, so the
+            # dK/dV stage splits each group's query heads over 4 workgroups
+            attn_inputs.Workload("causal_gqa_bf16_B1_Hq32_Hkv8_N2048_d128", 1, 32, 8, 2048, 128,
+                                 True, "bf16", seed=12),
         ]
         for cw in bcases:
             cq, ck, cv, cdo = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=True))

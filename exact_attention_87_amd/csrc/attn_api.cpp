@@ -1,6 +1,7 @@
 // C ABI of the exact-attention library (declared in include/attn.h):
 // argument validation, the per-device architecture check and dispatch to the
 // gfx950 kernels.  Nothing here allocates device memory or synchronises.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -112,7 +113,7 @@ attn_status bwd_common(int B, int Hq, int Hkv, int N, int d, int causal, float s
 
 extern "C" {
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 const char* attn_status_str(attn_status s) {
   switch (s) {
@@ -159,9 +160,20 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype
   if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
   if (dtype == ATTN_F32) return (size_t)-1;
   if (empty) return 0;
-  const size_t bytes = attn::bwd_stats_bytes(B, Hq, N);
-  return (bytes + 255) & ~(size_t)255;
+  const size_t stats = (attn::bwd_stats_bytes(B, Hq, N) + 255) & ~(size_t)255;
+  const size_t part = attn::bwd_partial_bytes(B, Hkv, N, d, attn::bwd_dkdv_splits(B, Hq, Hkv, N, d));
+  return stats + ((part + 255) & ~(size_t)255);
 }
+
+namespace {
+// The dK/dV stage's query-head split for a dense problem and its fp32
+// partial sums, which live in the workspace after the statistics.
+void set_split(attn::BwdArgs* a, void* workspace) {
+  a->nsplit = attn::bwd_dkdv_splits(a->B, a->Hq, a->Hkv, a->N, a->d);
+  const size_t stats = (attn::bwd_stats_bytes(a->B, a->Hq, a->N) + 255) & ~(size_t)255;
+  a->part = a->nsplit > 1 ? (float*)((char*)workspace + stats) : nullptr;
+}
+}  // namespace
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -180,6 +192,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   if (st != ATTN_OK) return st;
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
   a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
+  set_split(&a, workspace);
   // dQ first: it also writes the row statistics the dK/dV stage reads
   if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
@@ -221,19 +234,25 @@ attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* ls
 }
 
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                          const float* stats, void* dk, void* dv, int B, int Hq, int Hkv, int N,
-                          int d, int causal, float scale, attn_dtype dtype, void* stream) {
+                          float* stats, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                          int causal, float scale, attn_dtype dtype, void* stream) {
   attn::BwdArgs a;
+  const size_t wbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype);
   attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hkv, N, d);
-  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {stats, z.st}},
-                     {{dk, z.kv}, {dv, z.kv}});
+  set_split(&a, stats);
+  if (a.nsplit > 1)  // the partial sums are written after the statistics
+    st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}},
+                       {{stats, wbytes}, {dk, z.kv}, {dv, z.kv}});
+  else
+    st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {dout, z.q}, {stats, z.st}},
+                       {{dk, z.kv}, {dv, z.kv}});
   if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  a.q = q, a.k = k, a.v = v, a.dout = dout, a.stats = (float*)stats;
+  a.q = q, a.k = k, a.v = v, a.dout = dout, a.stats = stats;
   a.dk = dk, a.dv = dv;
   return attn::launch_bwd_dkdv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -560,6 +579,17 @@ attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, const v
   // (sequence, head) with B = sequences and N = the longest sequence
   if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
   a.B = nseq, a.N = max_seqlen, a.cu_seqlens = cu_seqlens, a.T = T;
+  // Query-head split of the dK/dV stage, chosen on the grid it launches
+  // (sequences x longest sequence) like a batched problem, and capped by the
+  // split the workspace was sized for ([1, H, T, d]): the partial sums are
+  // kept per (kv head, token), which that size covers for any count up to it.
+  {
+    const int s = std::min(attn::bwd_dkdv_splits(nseq, Hq, Hkv, max_seqlen, d),
+                           attn::bwd_dkdv_splits(1, Hq, Hkv, T, d));
+    const size_t stats = (attn::bwd_stats_bytes(1, Hq, T) + 255) & ~(size_t)255;
+    a.nsplit = s;
+    a.part = s > 1 ? (float*)((char*)workspace + stats) : nullptr;
+  }
   if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
@@ -685,6 +715,7 @@ attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const 
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
   a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
   a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
+  set_split(&a, workspace);
   // dQ first: it also writes the row statistics the dK/dV stage reads
   if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;

@@ -128,15 +128,16 @@ struct DkdvCfg {
   static constexpr size_t LDS = (size_t)NBUF * STAGEB;
 };
 
-template <typename T, int D, bool CAUSAL, bool VARLEN>
+template <typename T, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D>::WPE, DkdvCfg<D>::WPE)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                      const T* __restrict__ V, const T* __restrict__ dO,
                      const float* __restrict__ stats, T* __restrict__ dK,
                      T* __restrict__ dV, int Hq, int Hkv, int Nmax, int nkb, Layout lay, float c,
                      float dk_scale, uint32_t qsign, const int* __restrict__ cu_seqlens,
-                     int ntok) {
+                     int ntok, int nsplit_arg, float* __restrict__ part) {
   using Cfg = DkdvCfg<D>;
+  const int nsplit = SPLIT ? nsplit_arg : 1;
   using V8 = typename Elem<T>::v8;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
   constexpr int STAGEB = Cfg::STAGEB;
@@ -152,10 +153,16 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int BG = gridDim.x / nkb;
-  const int kblk = blockIdx.x / BG;  // causal: low key blocks carry the most work
+  // blockIdx = (key block, split, slice): key block major, so that under the
+  // causal mask the low key blocks, which carry the most work, start first
+  const int BGS = gridDim.x / nkb;
+  const int BG = BGS / nsplit;
+  const int kblk = blockIdx.x / BGS;
+  const int split = (blockIdx.x % BGS) / BG;
   const int bg = blockIdx.x % BG;
   const int group = Hq / Hkv;
+  // query heads g*group + hs0 .. g*group + hs1 - 1 of the kv group
+  const int hs0 = split * group / nsplit, hs1 = (split + 1) * group / nsplit;
   // This workgroup's problem: one (batch, kv head) slice of Nmax rows, or for
   // packed variable-length sequences one (sequence, kv head).  Query head hq
   // reads Q at qb0 + hq*qhs, dO at ob0 + hq*ohs and its statistics at
@@ -211,7 +218,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kblk * BKV) / BQ : 0;
   const int per_head = nqt - qt0;
-  const int iters = group * per_head;
+  const int iters = (hs1 - hs0) * per_head;
 
   // Direct loads of a query tile: Q and dO pieces as in the forward, plus
   // the 512 bytes of statistics (wave 0, lanes 0..31).
@@ -231,7 +238,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   }
   const uint32_t soff = (uint32_t)((lane >> 4) * Np * 4 + (lane & 15) * 16);
   auto issue = [&](int it) {
-    const int hq = g * group + it / per_head;
+    const int hq = g * group + hs0 + it / per_head;
     const int qt = qt0 + it % per_head;
     char* base = smem + (it % NBUF) * STAGEB;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qb0 + hq * qhs, slice_bytes(N, qrs, D));
@@ -417,6 +424,29 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       if (it + 2 < iters) step(std::integral_constant<int, 2 % NBUF>{}, it + 2);
   }
 
+  // ---- split query heads: fp32 partial sums (dK unscaled, then dV), added
+  // by the merge kernel in split order.  Rows are (slice, key) [BG][N] for a
+  // batched problem and (kv head, token) [Hkv][T] for packed sequences, so a
+  // plane holds `prows` rows per split: [2][nsplit][prows][D].
+  if constexpr (SPLIT) {
+    if (krow < N) {
+      const int64_t prows = VARLEN ? (int64_t)Hkv * ntok : (int64_t)BG * N;
+      const int64_t prow = VARLEN ? (int64_t)g * ntok + start + krow : (int64_t)bg * N + krow;
+      const int64_t plane = (int64_t)nsplit * prows * D;
+      float* pk = part + ((int64_t)split * prows + prow) * D;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = mb * 32 + rg * 8 + hf * 4;
+          *(f32x4*)(pk + d0) = f32x4{dkacc[mb][4 * rg], dkacc[mb][4 * rg + 1],
+                                     dkacc[mb][4 * rg + 2], dkacc[mb][4 * rg + 3]};
+          *(f32x4*)(pk + plane + d0) = f32x4{dvacc[mb][4 * rg], dvacc[mb][4 * rg + 1],
+                                             dvacc[mb][4 * rg + 2], dvacc[mb][4 * rg + 3]};
+        }
+    }
+    return;
+  }
   // ---- store dK = scale * (dK^T)^T (Q was not sign-flipped), dV
   // (lane: key krow; element r: feature)
   if (krow < N) {
@@ -436,6 +466,59 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         *(u32x2*)(dvp + d0) = vv;
       }
   }
+}
+
+// ---------------------------------------------------------------- split merge
+// dK = scale * sum_s dK_s and dV = sum_s dV_s over the query-head splits, in
+// split order (deterministic); one thread per 8 features of one key row.
+// Rows are (slice bg = b * Hkv + g, key) of a batched problem; packed
+// sequences pass BG = Hkv, N = T (rows (kv head, token)) and their offsets,
+// and tokens outside [cu_seqlens[0], cu_seqlens[nseq]) are left untouched,
+// as the unsplit stage leaves them.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_merge_kernel(const float* __restrict__ part,
+                                                             T* __restrict__ dK, T* __restrict__ dV,
+                                                             int nsplit, int BG, int Hkv, int N,
+                                                             float dk_scale, Strides3 ks,
+                                                             const int* __restrict__ cu_seqlens,
+                                                             int nseq) {
+  constexpr int TPR = D / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)BG * N;
+  if (t >= rows * TPR) return;
+  const int64_t row = t / TPR;  // bg * N + key
+  const int f = (int)(t - row * TPR) * 8;
+  if (cu_seqlens) {  // packed sequences: the tokens the sequences cover
+    const int key = (int)(row % N);
+    const int lo = min(max(cu_seqlens[0], 0), N);
+    const int hi = min(max(cu_seqlens[nseq], lo), N);
+    if (key < lo || key >= hi) return;
+  }
+  const int64_t plane = (int64_t)nsplit * rows * D;
+  const float* pk = part + row * D + f;
+  f32x4 k0 = *(const f32x4*)pk, k1 = *(const f32x4*)(pk + 4);
+  f32x4 v0 = *(const f32x4*)(pk + plane), v1 = *(const f32x4*)(pk + plane + 4);
+  for (int sp = 1; sp < nsplit; ++sp) {
+    const float* q = pk + (int64_t)sp * rows * D;
+    k0 += *(const f32x4*)q;
+    k1 += *(const f32x4*)(q + 4);
+    v0 += *(const f32x4*)(q + plane);
+    v1 += *(const f32x4*)(q + plane + 4);
+  }
+  const int bg = (int)(row / N), key = (int)(row - (int64_t)bg * N);
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int64_t off = b * ks.b + g * ks.h + (int64_t)key * ks.r + f;
+  u32x4 ko, vo;
+  ko[0] = pack2<T>(k0[0] * dk_scale, k0[1] * dk_scale);
+  ko[1] = pack2<T>(k0[2] * dk_scale, k0[3] * dk_scale);
+  ko[2] = pack2<T>(k1[0] * dk_scale, k1[1] * dk_scale);
+  ko[3] = pack2<T>(k1[2] * dk_scale, k1[3] * dk_scale);
+  vo[0] = pack2<T>(v0[0], v0[1]);
+  vo[1] = pack2<T>(v0[2], v0[3]);
+  vo[2] = pack2<T>(v1[0], v1[1]);
+  vo[3] = pack2<T>(v1[2], v1[3]);
+  *(u32x4*)(dK + off) = ko;
+  *(u32x4*)(dV + off) = vo;
 }
 
 // ---------------------------------------------------------------- dQ
@@ -760,14 +843,60 @@ static hipError_t dkdv_t(const BwdArgs& a) {
   using Cfg = DkdvCfg<D>;
   const BwdConsts k = bwd_consts(a.scale);
   const int nkb = (a.N + Cfg::BKV - 1) / Cfg::BKV;
-  const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
-  const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>, Cfg::LDS);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(256),
-                     Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (const T*)a.dout, a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv, a.N, nkb,
-                     layout_of(a), k.c, a.scale, k.qsign, a.cu_seqlens, a.T);
+  const int nsplit = a.nsplit;
+  if (nsplit > 1 && a.part == nullptr) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)nkb * a.B * a.Hkv * nsplit;
+  const Layout lay = layout_of(a);
+  if (nsplit > 1) {
+    const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, true>, Cfg::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, true>), dim3((unsigned)grid),
+                       dim3(256), Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.dout, a.stats, (T*)a.dk, (T*)a.dv, a.Hq,
+                       a.Hkv, a.N, nkb, lay, k.c, a.scale, k.qsign, a.cu_seqlens, a.T, nsplit,
+                       a.part);
+  } else {
+    const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, false>, Cfg::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, false>), dim3((unsigned)grid),
+                       dim3(256), Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k,
+                       (const T*)a.v, (const T*)a.dout, a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv,
+                       a.N, nkb, lay, k.c, a.scale, k.qsign, a.cu_seqlens, a.T, 1, a.part);
+  }
+  if (nsplit > 1) {
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    // packed sequences: rows (kv head, token) over all T tokens
+    const int BG = VARLEN ? a.Hkv : a.B * a.Hkv, Nr = VARLEN ? a.T : a.N;
+    const int64_t threads = (int64_t)BG * Nr * (D / 8);
+    hipLaunchKernelGGL((bwd_dkdv_merge_kernel<T, D>), dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, a.stream, (const float*)a.part, (T*)a.dk, (T*)a.dv, nsplit,
+                       BG, a.Hkv, Nr, a.scale, lay.kv, VARLEN ? a.cu_seqlens : nullptr, a.B);
+  }
   return hipGetLastError();
+}
+
+// Query-head splits of the dK/dV stage.  Its grid is key blocks x (batch, kv
+// head); for grouped-query problems with few kv heads or short sequences it
+// can leave most of the device idle, since every workgroup walks all query
+// heads of its group.  Then the heads are split over more workgroups: the
+// smallest divisor of the group that gives at least two rounds of resident
+// workgroups (256 CUs x workgroups per CU), or one split per head.
+int bwd_dkdv_splits(int B, int Hq, int Hkv, int N, int d) {
+  const int group = Hq / Hkv;
+  if (group <= 1) return 1;
+  const int per_cu = d == 64 ? DkdvCfg<64>::WPE : 1;
+  const int64_t target = 2LL * 256 * per_cu;
+  const int64_t grid = (int64_t)((N + DkdvCfg<64>::BKV - 1) / DkdvCfg<64>::BKV) * B * Hkv;
+  if (grid >= target) return 1;
+  const int64_t need = (target + grid - 1) / grid;
+  for (int s = 2; s < group; ++s)
+    if (group % s == 0 && s >= need) return s;
+  return group;
+}
+
+size_t bwd_partial_bytes(int B, int Hkv, int N, int d, int nsplit) {
+  return nsplit > 1 ? (size_t)2 * nsplit * B * Hkv * N * d * sizeof(float) : 0;
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool STATS = false>

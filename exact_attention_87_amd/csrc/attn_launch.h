@@ -79,6 +79,11 @@ struct BwdArgs {
   // T packed tokens ([Hq][2][T rounded up to 64]).
   const int* cu_seqlens = nullptr;
   int T = 0;
+  // dK/dV stage: a kv group's query heads split over this many workgroups
+  // per key block, each writing fp32 partial sums to `part` (workspace after
+  // the statistics) that a merge kernel adds in split order.  1 = no split.
+  int nsplit = 1;
+  float* part = nullptr;
 };
 
 // Split-K/V forward (16-bit types): queries [B,Hq,Nq,d], keys/values [B,Hkv,Nk,d],
@@ -117,6 +122,11 @@ size_t sparse_workspace_bytes(int Hq, int N, int mask_heads);
 hipError_t launch_fwd_sparse(const FwdArgs& a, const unsigned char* mask, void* workspace);
 // Bytes of the backward row-statistics workspace.
 size_t bwd_stats_bytes(int B, int Hq, int N);
+// Query-head splits of the dK/dV stage for a dense problem (1 when the grid
+// of key blocks x kv heads already fills the device), and the bytes of fp32
+// partial sums they need (0 for one split).
+int bwd_dkdv_splits(int B, int Hq, int Hkv, int N, int d);
+size_t bwd_partial_bytes(int B, int Hkv, int N, int d, int nsplit);
 // Backward stages; each launches one kernel on a.stream.
 hipError_t launch_bwd_pre(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);

@@ -87,8 +87,14 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Bytes of device workspace attn_bwd needs for this problem (a multiple of
- * 256; 8 * B * Hq * (N rounded up to 64)).  0 for an empty problem.  Returns
- * (size_t)-1 for arguments attn_bwd would reject.
+ * 256).  0 for an empty problem.  Returns (size_t)-1 for arguments attn_bwd
+ * would reject.  The workspace holds the row statistics (8 * B * Hq * (N
+ * rounded up to 64) bytes, rounded up to 256) and, for grouped-query problems
+ * whose grid of key blocks x (batch, kv head) would leave the device mostly
+ * idle, fp32 partial sums of dK and dV after them: the dK/dV stage then
+ * splits each group's query heads over S workgroups per key block and merges
+ * their sums in a fixed order (2 * S * B * Hkv * N * d * 4 bytes, rounded up
+ * to 256; S is chosen from the shape, at most Hq / Hkv).
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype);
 
@@ -119,9 +125,13 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * and stores the statistics below, then the dK/dV stage.
  *
  * `stats` is the backward workspace (attn_bwd_workspace_bytes bytes, caller
- * owned): per (batch, query head) two fp32 rows of Np = N rounded up to 64
- * entries, [B*Hq][2][Np]: -D_i = -(dO_i . O_i) and LSE_i * log2(e), zero in
- * the padding.  attn_bwd_preprocess writes it; the other two stages read it.
+ * owned).  It starts with per (batch, query head) two fp32 rows of Np = N
+ * rounded up to 64 entries, [B*Hq][2][Np]: -D_i = -(dO_i . O_i) and
+ * LSE_i * log2(e), zero in the padding.  attn_bwd_preprocess writes them; the
+ * other two stages read them.  attn_bwd_dkdv also writes the workspace's
+ * partial-sum region after them when it splits query heads (see
+ * attn_bwd_workspace_bytes), so it takes `stats` as writable and needs the
+ * whole workspace; the other stages need only the statistics.
  *
  *   attn_bwd_preprocess: the row statistics from O, dO and LSE.
  *   attn_bwd_dkdv:       dK, dV, recomputing P and dP tile by tile from q, k
@@ -133,8 +143,8 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
 attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, float* stats,
                                 int B, int Hq, int N, int d, attn_dtype dtype, void* stream);
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                          const float* stats, void* dk, void* dv, int B, int Hq, int Hkv, int N,
-                          int d, int causal, float scale, attn_dtype dtype, void* stream);
+                          float* stats, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                          int causal, float scale, attn_dtype dtype, void* stream);
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                         const float* stats, void* dq, int B, int Hq, int Hkv, int N, int d,
                         int causal, float scale, attn_dtype dtype, void* stream);

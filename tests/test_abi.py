@@ -45,7 +45,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in header_functions():
         assert name in exported, name
         assert hasattr(lib, name)
-    assert ea.attn_abi_version() == 1
+    assert ea.attn_abi_version() == 2
 
 
 def test_status_strings():
@@ -135,10 +135,31 @@ def test_bwd_fp32_is_unsupported():
 
 
 def test_workspace_bytes():
-    # [B*Hq][2][N rounded up to 64] fp32, rounded up to 256 bytes
-    assert ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_BF16) == 2 * 4 * 2 * 128 * 4
+    # statistics: [B*Hq][2][N rounded up to 64] fp32, rounded up to 256 bytes
     assert ea.attn_bwd_workspace_bytes(1, 1, 1, 1, 64, ea.ATTN_BF16) == 512
     assert ea.attn_bwd_workspace_bytes(8, 16, 16, 2048, 64, ea.ATTN_BF16) == 8 * 16 * 2 * 2048 * 4
+    # grouped-query problem whose 128-key blocks x kv heads fill the device
+    # (1024 workgroups at d = 128, one per CU): statistics only
+    assert ea.attn_bwd_workspace_bytes(1, 32, 8, 16384, 128, ea.ATTN_BF16) == 32 * 2 * 16384 * 4
+    # small grids: the dK/dV stage splits each group's query heads over S
+    # workgroups and keeps 2 * S * B * Hkv * N * d fp32 partial sums after the
+    # statistics.  S is the smallest divisor of the group reaching two rounds
+    # of resident workgroups (512 at d = 128, 1536 at d = 64), else the group.
+    #   B=1 Hq=32 Hkv=8 N=2048 d=128: 128 workgroups, S = 4 (the group)
+    assert ea.attn_bwd_workspace_bytes(1, 32, 8, 2048, 128, ea.ATTN_BF16) == \
+        32 * 2 * 2048 * 4 + 2 * 4 * 8 * 2048 * 128 * 4
+    #   B=8 Hq=16 Hkv=2 N=2048 d=64: 256 workgroups, need 6, divisors of 8 -> S = 8
+    assert ea.attn_bwd_workspace_bytes(8, 16, 2, 2048, 64, ea.ATTN_BF16) == \
+        8 * 16 * 2 * 2048 * 4 + 2 * 8 * 8 * 2 * 2048 * 64 * 4
+    #   B=2 Hq=4 Hkv=2 N=100 d=64: 4 workgroups, S = 2 (the group)
+    assert ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_BF16) == \
+        2 * 4 * 2 * 128 * 4 + 2 * 2 * 2 * 2 * 100 * 64 * 4
+    #   B=4 Hq=24 Hkv=2 N=1024 d=64: 64 workgroups, need 24, group 12 -> S = 12
+    assert ea.attn_bwd_workspace_bytes(4, 24, 2, 1024, 64, ea.ATTN_BF16) == \
+        4 * 24 * 2 * 1024 * 4 + 2 * 12 * 4 * 2 * 1024 * 64 * 4
+    #   B=16 Hq=32 Hkv=4 N=1024 d=64: 512 workgroups, need 3, group 8 -> S = 4
+    assert ea.attn_bwd_workspace_bytes(16, 32, 4, 1024, 64, ea.ATTN_BF16) == \
+        16 * 32 * 2 * 1024 * 4 + 2 * 4 * 16 * 4 * 1024 * 64 * 4
     assert ea.attn_bwd_workspace_bytes(0, 4, 2, 100, 64, ea.ATTN_BF16) == 0
     assert ea.attn_bwd_workspace_bytes(1, 3, 2, 100, 64, ea.ATTN_BF16) == -1
     assert ea.attn_bwd_workspace_bytes(1, 4, 2, 100, 80, ea.ATTN_BF16) == -1

@@ -131,6 +131,29 @@ def test_bwd_gqa_equals_summed_mha():
     assert (dv.float() - dv_sum).abs().max() <= 2e-2 * dv_sum.abs().max()
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_gqa_split_query_heads(oracle_mod, d, causal):
+    """Few kv heads and a short sequence: the dK/dV stage splits each group's
+    query heads over several workgroups (fp32 partial sums in the workspace,
+    merged in a fixed order).  Parity with the oracle, and bitwise repeatable."""
+    B, Hq, Hkv, N = 1, 12, 2, 300
+    stats = B * Hq * 2 * 320 * 4
+    assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, ea.ATTN_BF16) > stats  # split taken
+    q, k, v, do = attn_inputs.make(B, Hq, Hkv, N, d, "bf16", seed=70 + d, with_dout=True)
+    dev = gpu()
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o, lse = ea.fwd(qg, kg, vg, causal=causal)
+    g1 = ea.bwd(qg, kg, vg, o, lse, dog, causal=causal)
+    g2 = ea.bwd(qg, kg, vg, o, lse, dog, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    rq, rk, rv = oracle_mod.bwd(q, k, v, do, causal=causal)
+    for name, g, r in zip(("dQ", "dK", "dV"), g1, (rq, rk, rv)):
+        check_grad(f"{name} d={d} causal={causal} (split heads)", g.float().cpu().numpy(), r)
+
+
 def test_bwd_constant_values_give_zero_dq_dk():
     dev = gpu()
     q, k, v, do = attn_inputs.make(1, 2, 2, 200, 64, "bf16", seed=14, with_dout=True)
@@ -183,8 +206,11 @@ def test_staged_backward_equals_attn_bwd():
     ref = ea.bwd(q, k, v, o, lse, do, causal=True)
     nbytes = ea.attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, ea.ATTN_BF16)
     Np = (N + 63) // 64 * 64
-    assert nbytes == B * Hq * 2 * Np * 4
-    stats = torch.full((B * Hq, 2, Np), float("nan"), device=dev, dtype=torch.float32)
+    # this grouped-query shape splits its query heads in the dK/dV stage, which
+    # keeps partial sums in the workspace after the statistics
+    assert nbytes > B * Hq * 2 * Np * 4
+    ws = torch.full((nbytes // 4,), float("nan"), device=dev, dtype=torch.float32)
+    stats = ws[:B * Hq * 2 * Np].view(B * Hq, 2, Np)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     s = torch.cuda.current_stream().cuda_stream
     sc = d ** -0.5

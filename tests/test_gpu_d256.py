@@ -154,7 +154,12 @@ def test_backward_staged_and_deterministic():
         again = ea.bwd(q, k, v, o, lse, do, causal=True)
         assert all(torch.equal(a, b) for a, b in zip(ref, again))
     Np = (N + 63) // 64 * 64
-    stats = torch.full((B * Hq, 2, Np), float("nan"), device=dev)
+    # the whole workspace: the dK/dV stage keeps the partial sums of its
+    # query-head split after the statistics
+    nbytes = ea.attn_bwd_workspace_bytes(B, Hq, Hkv, N, D, ea.ATTN_BF16)
+    assert nbytes > B * Hq * 2 * Np * 4
+    ws = torch.full((nbytes // 4,), float("nan"), device=dev)
+    stats = ws[:B * Hq * 2 * Np].view(B * Hq, 2, Np)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     s = torch.cuda.current_stream().cuda_stream
     sc = D ** -0.5
