@@ -70,24 +70,31 @@ namespace attn {
 
 // Work map of the forward grids (nqb query blocks x BH (batch, head) slices):
 // the heaviest query blocks first under the causal mask; the heads of one
-// kv group are adjacent.  (A map that kept all of a kv group's query blocks on
-// one XCD was measured slower: it breaks the heaviest-first order.  The
-// per-round deal below keeps that order.)
-#ifndef ATTN_FWD_XCD
-#define ATTN_FWD_XCD 1
-#endif
+// kv group are adjacent.
+// xg > 0: XCD-aware order.  Workgroup ids are dealt round robin to the 8
+// XCDs, each with its own L2.  XCD x (ids = x mod 8) takes the contiguous
+// slices x*BH/8 .. (x+1)*BH/8 - 1 (the query heads of a kv group are
+// adjacent, so they share one L2) in groups of xg slices, each group query
+// block major, heaviest first under the causal mask.  Small groups keep the
+// workgroups that read one slice's K/V running together, so its tiles are
+// fetched from HBM about once per group instead of once per workgroup.
+// xg = BH/8 is a single group: the plain order restricted to the XCD's
+// slices.  xg = 0: the plain order (the host passes 0 when BH % 8 != 0 and
+// for packed variable-length slices, whose work differs from slice to slice).
 template <bool CAUSAL>
-__device__ __forceinline__ void work_item(int nqb, int BH, bool grouped, int& qb, int& bh) {
+__device__ __forceinline__ void work_item(int nqb, int BH, int xg, int& qb, int& bh) {
   const int id = blockIdx.x;
+  if (xg > 0) {
+    const int x = id & 7, l = id >> 3;
+    const int per_group = xg * nqb;
+    const int p = l / per_group, r = l - p * per_group;
+    const int qi = r / xg;
+    bh = x * (BH >> 3) + p * xg + (r - qi * xg);
+    qb = CAUSAL ? nqb - 1 - qi : qi;
+    return;
+  }
   qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
   bh = id % BH;
-  // Grouped-query problems: within each round of BH workgroups (one query
-  // block of every slice) the heads of one kv group go to one XCD and share
-  // its L2 (xcd_contiguous).  The round order, and with it the heaviest-first
-  // order, is unchanged.  With one query head per kv head there is nothing to
-  // share; packed variable-length slices differ in work, and contiguous runs
-  // of them would load the XCDs unevenly, so that mode keeps the plain deal.
-  if (ATTN_FWD_XCD && grouped) bh = xcd_contiguous(bh, BH);
 }
 
 // Per head dim: a value for d = 64, 128 and 256.
@@ -112,7 +119,7 @@ template <typename T, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64 * FwdCfg<D>::NW)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mfma_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
+    T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, int xg, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
     int mask_heads, const int* __restrict__ cu_seqlens, int ntok, Layout lay) {
   constexpr bool SPARSE = MODE == kFwdSparse;
@@ -139,7 +146,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   // one key/value group are adjacent so they share K/V in cache.
   const int BH = gridDim.x / nqb;
   int qb, bh;
-  work_item<CAUSAL>(nqb, BH, MODE != kFwdVarlen && Hq != Hkv, qb, bh);
+  work_item<CAUSAL>(nqb, BH, xg, qb, bh);
   // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
@@ -500,7 +507,7 @@ template <typename T, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(64 * PipeCfg<D>::NW)
 __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_mfma_pipe_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, float c,
+    T* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nmax, int nqb, int xg, float c,
     uint32_t qsign, const int* __restrict__ tlist, const int* __restrict__ tcount,
     int mask_heads, const int* __restrict__ cu_seqlens, int ntok, Layout lay) {
   constexpr bool SPARSE = MODE == kFwdSparse;
@@ -522,7 +529,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
 
   const int BH = gridDim.x / nqb;
   int qb, bh;
-  work_item<CAUSAL>(nqb, BH, MODE != kFwdVarlen && Hq != Hkv, qb, bh);
+  work_item<CAUSAL>(nqb, BH, xg, qb, bh);
   // This workgroup's problem: one (batch, head) slice of Nmax rows, or, for a
   // packed variable-length batch, one (sequence, head) of the packed tokens;
   // offsets are in elements of Q/O, of K/V and in entries of LSE.
@@ -870,6 +877,38 @@ static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
   return a.tlist ? ((size_t)((a.N + BC - 1) / BC) * 2 + 15) & ~(size_t)15 : 0;
 }
 
+// Slice group xg of the XCD-aware work order (work_item): the largest divisor
+// of the XCD's BH/8 slices whose K/V fit an L2 budget (the query heads of a
+// kv group share theirs), at least 1; 0 for the plain order.  Measured
+// (same-box A/B against the plain order): non-causal with 2 MiB, +19% at
+// B=8 H=32 N=1024 d=128 and +5% at d=64; causal grids need their heaviest
+// query blocks of many slices in flight at once, and took a loss with 2 MiB
+// groups (-9% causal B=8 H=16 N=2048 d=64) but gain 2% with 8 MiB ones.
+#ifndef ATTN_FWD_XG_BUDGET
+#define ATTN_FWD_XG_BUDGET (2 << 20)
+#endif
+#ifndef ATTN_FWD_XG_BUDGET_CAUSAL
+#define ATTN_FWD_XG_BUDGET_CAUSAL (8 << 20)
+#endif
+static int fwd_xcd_group(const FwdArgs& a, int D) {
+  const int BH = a.B * a.Hq;
+  if (a.cu_seqlens || (BH & 7)) return 0;
+  const int S8 = BH >> 3, group = a.Hq / a.Hkv;
+  const int64_t budget = a.causal ? ATTN_FWD_XG_BUDGET_CAUSAL : ATTN_FWD_XG_BUDGET;
+  // One group for the whole XCD (everything fits), or not even one slice
+  // fitting: the plain order, or for grouped-query heads its restriction to
+  // whole kv groups per XCD (xg = BH/8).
+  const int whole = group > 1 ? S8 : 0;
+  if ((int64_t)a.N * D * 4 > budget) return whole;
+  int best = 1;
+  for (int G = 1; G <= S8; ++G) {
+    const int64_t kv = (int64_t)((G + group - 1) / group) * a.N * D * 4;
+    if (kv > budget) break;
+    if (S8 % G == 0) best = G;
+  }
+  return best == S8 ? whole : best;
+}
+
 template <typename T, int D, bool CAUSAL, int MODE>
 static hipError_t launch_pipe(const FwdArgs& a) {
   constexpr bool SPARSE = MODE == kFwdSparse;
@@ -885,7 +924,7 @@ static hipError_t launch_pipe(const FwdArgs& a) {
   const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
   hipLaunchKernelGGL((fwd_mfma_pipe_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
                      dim3(64 * PipeCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
+                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, fwd_xcd_group(a, D), c, qsign, a.tlist,
                      a.tcount, a.mask_heads, a.cu_seqlens, a.T, layout_of(a));
   return hipGetLastError();
 }
@@ -909,7 +948,7 @@ static hipError_t launch_mfma(const FwdArgs& a) {
     const uint32_t qsign = (a.scale < 0.f) ? 0x80008000u : 0u;
     hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, MODE>), dim3((unsigned)grid),
                        dim3(64 * FwdCfg<D>::NW), lds, a.stream, (const T*)a.q, (const T*)a.k,
-                       (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, c, qsign, a.tlist,
+                       (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, fwd_xcd_group(a, D), c, qsign, a.tlist,
                        a.tcount, a.mask_heads, a.cu_seqlens, a.T, layout_of(a));
     return hipGetLastError();
   }
