@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D>:
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                      const T* __restrict__ V, const T* __restrict__ dO,
                      const float* __restrict__ stats, T* __restrict__ dK,
-                     T* __restrict__ dV, int Hq, int Hkv, int Nmax, int nkb, Layout lay, float c,
+                     T* __restrict__ dV, int Hq, int Hkv, int Nmax, int nkb, int xg, Layout lay, float c,
                      float dk_scale, uint32_t qsign, const int* __restrict__ cu_seqlens,
                      int ntok, int nsplit_arg, float* __restrict__ part) {
   using Cfg = DkdvCfg<D>;
@@ -155,11 +155,19 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
   // blockIdx = (key block, split, slice): key block major, so that under the
   // causal mask the low key blocks, which carry the most work, start first
+  // (xg > 0, one split only: the XCD-aware order of xcd_item, key blocks
+  // ascending within each slice group)
   const int BGS = gridDim.x / nkb;
   const int BG = BGS / nsplit;
-  const int kblk = blockIdx.x / BGS;
-  const int split = (blockIdx.x % BGS) / BG;
-  const int bg = blockIdx.x % BG;
+  int kblk, split, bg;
+  if (xg > 0) {
+    xcd_item(nkb, BG, xg, kblk, bg);
+    split = 0;
+  } else {
+    kblk = blockIdx.x / BGS;
+    split = (blockIdx.x % BGS) / BG;
+    bg = blockIdx.x % BG;
+  }
   const int group = Hq / Hkv;
   // query heads g*group + hs0 .. g*group + hs1 - 1 of the kv group
   const int hs0 = split * group / nsplit, hs1 = (split + 1) * group / nsplit;
@@ -542,7 +550,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                    const T* __restrict__ V, const T* __restrict__ dO,
                    const T* __restrict__ O, const float* __restrict__ LSE,
                    float* __restrict__ stats, T* __restrict__ dQ, int Hq, int Hkv,
-                   int Nmax, int nqb, Layout lay, float c, float qscale, uint32_t qsign,
+                   int Nmax, int nqb, int xg, Layout lay, float c, float qscale, uint32_t qsign,
                    const int* __restrict__ cu_seqlens, int ntok) {
   static_assert(!(STATS && VARLEN), "packed sequences take their statistics from the preprocess");
   using Cfg = DqCfg<D>;
@@ -560,12 +568,12 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
+  // XCD-aware order of (query block, slice), heaviest query blocks first
+  // under the causal mask (xcd_item; xg from the host)
   const int BH = gridDim.x / nqb;
-  const int id = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-  // grouped-query heads of one kv group share one XCD's L2 (as in the
-  // forward; packed variable-length slices keep the plain round-robin deal)
-  const int bh = (!VARLEN && Hq != Hkv) ? xcd_contiguous(id % BH, BH) : id % BH;
+  int qi, bh;
+  xcd_item(nqb, BH, xg, qi, bh);
+  const int qb = CAUSAL ? nqb - 1 - qi : qi;
   // One (batch, head) slice of Nmax rows, or one (sequence, head) of packed
   // variable-length sequences.  Q and dQ share one stride set, K and V
   // another, dO has O's.
@@ -836,6 +844,33 @@ static hipError_t pre_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+// Slice groups of the XCD-aware orders (xcd_group).  dQ: K/V of a slice,
+// shared by the query heads of a kv group, as in the forward.  dK/dV: the Q
+// and dO tiles of a kv group's query heads, per (batch, kv head) slice,
+// non-causal only: under the causal mask its slice groups cost the
+// heaviest-first order more than they saved (same-box A/B of attn_bwd: dQ
+// groups +3% at causal B=4 H=32 N=4000 d=128 and +4% non-causal N=1024;
+// dK/dV groups +2% non-causal, but -3% causal N=2048 and -2% causal
+// grouped-query N=4096).  Packed variable-length slices differ in work and
+// keep the plain order.
+#ifndef ATTN_DQ_XG
+#define ATTN_DQ_XG 1
+#endif
+#ifndef ATTN_DKDV_XG
+#define ATTN_DKDV_XG 1
+#endif
+static int dq_xcd_group(const BwdArgs& a, int D, bool varlen) {
+  if (varlen) return 0;
+  const int64_t nsl = (int64_t)a.B * a.Hq;
+  const int group = a.Hq / a.Hkv;
+  if (!ATTN_DQ_XG) return (group > 1 && nsl % 8 == 0) ? (int)(nsl / 8) : 0;
+  return xcd_group(nsl, group, (int64_t)a.N * D * 4, a.causal ? kXgBudgetCausal : kXgBudget);
+}
+static int dkdv_xcd_group(const BwdArgs& a, int D, bool varlen) {
+  if (varlen || a.causal || !ATTN_DKDV_XG) return 0;
+  return xcd_group((int64_t)a.B * a.Hkv, 1, (int64_t)(a.Hq / a.Hkv) * a.N * D * 4, kXgBudget);
+}
+
 // For packed variable-length sequences B is the number of sequences and N the
 // longest one (they size the grid); the statistics cover the T packed tokens.
 template <typename T, int D, bool CAUSAL, bool VARLEN>
@@ -853,7 +888,7 @@ static hipError_t dkdv_t(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, true>), dim3((unsigned)grid),
                        dim3(256), Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.dout, a.stats, (T*)a.dk, (T*)a.dv, a.Hq,
-                       a.Hkv, a.N, nkb, lay, k.c, a.scale, k.qsign, a.cu_seqlens, a.T, nsplit,
+                       a.Hkv, a.N, nkb, 0, lay, k.c, a.scale, k.qsign, a.cu_seqlens, a.T, nsplit,
                        a.part);
   } else {
     const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, false>, Cfg::LDS);
@@ -861,7 +896,8 @@ static hipError_t dkdv_t(const BwdArgs& a) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, false>), dim3((unsigned)grid),
                        dim3(256), Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.dout, a.stats, (T*)a.dk, (T*)a.dv, a.Hq, a.Hkv,
-                       a.N, nkb, lay, k.c, a.scale, k.qsign, a.cu_seqlens, a.T, 1, a.part);
+                       a.N, nkb, dkdv_xcd_group(a, D, VARLEN), lay, k.c, a.scale, k.qsign,
+                       a.cu_seqlens, a.T, 1, a.part);
   }
   if (nsplit > 1) {
     const hipError_t e2 = hipGetLastError();
@@ -910,7 +946,8 @@ static hipError_t dq_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, VARLEN, STATS>), dim3((unsigned)grid),
                      dim3(256), Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.dout, (const T*)a.o, a.lse, a.stats, (T*)a.dq, a.Hq, a.Hkv, a.N,
-                     nqb, layout_of(a), k.c, a.scale, k.qsign, a.cu_seqlens, a.T);
+                     nqb, dq_xcd_group(a, D, VARLEN), layout_of(a), k.c, a.scale, k.qsign,
+                     a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 

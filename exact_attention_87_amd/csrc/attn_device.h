@@ -170,15 +170,26 @@ __device__ __forceinline__ int tr_off(int lane, int kbase, int dbase, int t) {
   return tile_off<D>(row, d >> 3) + ((d & 7) << 1);
 }
 
-// Workgroup ids are dealt round robin to the 8 XCDs, each with its own L2.
-// Remap the slice index j of a round of n workgroups (one per slice) so that
-// the XCD receiving ids = x (mod 8) gets the contiguous slices x*n/8 ..
-// (x+1)*n/8 - 1: the query heads of one kv group, adjacent in the slice
-// order, then share that XCD's L2 and K/V come from HBM once per group
-// rather than once per head.  A bijection when n is a multiple of 8; the
-// identity otherwise.
-__device__ __forceinline__ int xcd_contiguous(int j, int n) {
-  return (n & 7) ? j : (j & 7) * (n >> 3) + (j >> 3);
+// XCD-aware work order over a grid of nmaj x nsl workgroups (nmaj major
+// blocks, e.g. query blocks, of nsl slices).  Workgroup ids are dealt round
+// robin to the 8 XCDs, each with its own L2.  With xg > 0, XCD x (ids = x
+// mod 8) takes the contiguous slices x*nsl/8 .. (x+1)*nsl/8 - 1 in groups of
+// xg slices, each group major-block-major: the workgroups reading one slice's
+// tiles run together on one L2, and adjacent slices that share their data
+// (the query heads of a kv group) do too.  xg = 0: the plain order, major
+// index id / nsl.  A bijection when nsl % 8 == 0 and xg divides nsl / 8.
+__device__ __forceinline__ void xcd_item(int nmaj, int nsl, int xg, int& maj, int& sl) {
+  const int id = blockIdx.x;
+  if (xg > 0) {
+    const int x = id & 7, l = id >> 3;
+    const int per = xg * nmaj;
+    const int p = l / per, r = l - p * per;
+    maj = r / xg;
+    sl = x * (nsl >> 3) + p * xg + (r - maj * xg);
+  } else {
+    maj = id / nsl;
+    sl = id % nsl;
+  }
 }
 
 // Raw buffer resource over [base, base + bytes): loads beyond the range

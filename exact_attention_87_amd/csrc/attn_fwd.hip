@@ -71,30 +71,13 @@ namespace attn {
 // Work map of the forward grids (nqb query blocks x BH (batch, head) slices):
 // the heaviest query blocks first under the causal mask; the heads of one
 // kv group are adjacent.
-// xg > 0: XCD-aware order.  Workgroup ids are dealt round robin to the 8
-// XCDs, each with its own L2.  XCD x (ids = x mod 8) takes the contiguous
-// slices x*BH/8 .. (x+1)*BH/8 - 1 (the query heads of a kv group are
-// adjacent, so they share one L2) in groups of xg slices, each group query
-// block major, heaviest first under the causal mask.  Small groups keep the
-// workgroups that read one slice's K/V running together, so its tiles are
-// fetched from HBM about once per group instead of once per workgroup.
-// xg = BH/8 is a single group: the plain order restricted to the XCD's
-// slices.  xg = 0: the plain order (the host passes 0 when BH % 8 != 0 and
-// for packed variable-length slices, whose work differs from slice to slice).
+// Work map: (query block, slice) from the XCD-aware order (xcd_item); the
+// heaviest query blocks first under the causal mask.
 template <bool CAUSAL>
 __device__ __forceinline__ void work_item(int nqb, int BH, int xg, int& qb, int& bh) {
-  const int id = blockIdx.x;
-  if (xg > 0) {
-    const int x = id & 7, l = id >> 3;
-    const int per_group = xg * nqb;
-    const int p = l / per_group, r = l - p * per_group;
-    const int qi = r / xg;
-    bh = x * (BH >> 3) + p * xg + (r - qi * xg);
-    qb = CAUSAL ? nqb - 1 - qi : qi;
-    return;
-  }
-  qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-  bh = id % BH;
+  int qi;
+  xcd_item(nqb, BH, xg, qi, bh);
+  qb = CAUSAL ? nqb - 1 - qi : qi;
 }
 
 // Per head dim: a value for d = 64, 128 and 256.
@@ -877,36 +860,16 @@ static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
   return a.tlist ? ((size_t)((a.N + BC - 1) / BC) * 2 + 15) & ~(size_t)15 : 0;
 }
 
-// Slice group xg of the XCD-aware work order (work_item): the largest divisor
-// of the XCD's BH/8 slices whose K/V fit an L2 budget (the query heads of a
-// kv group share theirs), at least 1; 0 for the plain order.  Measured
-// (same-box A/B against the plain order): non-causal with 2 MiB, +19% at
-// B=8 H=32 N=1024 d=128 and +5% at d=64; causal grids need their heaviest
-// query blocks of many slices in flight at once, and took a loss with 2 MiB
-// groups (-9% causal B=8 H=16 N=2048 d=64) but gain 2% with 8 MiB ones.
-#ifndef ATTN_FWD_XG_BUDGET
-#define ATTN_FWD_XG_BUDGET (2 << 20)
-#endif
-#ifndef ATTN_FWD_XG_BUDGET_CAUSAL
-#define ATTN_FWD_XG_BUDGET_CAUSAL (8 << 20)
-#endif
+// Slice group of the XCD-aware work order: K/V of a slice, shared by the
+// query heads of a kv group.  Measured (same-box A/B against the plain
+// order): non-causal with 2 MiB groups, +18% at B=8 H=32 N=1024 d=128 and
+// +2-5% at d=64; causal grids lost 9% with 2 MiB groups (B=8 H=16 N=2048
+// d=64) but gain 1-3% with 8 MiB ones.  Packed variable-length slices differ
+// in work and keep the plain order.
 static int fwd_xcd_group(const FwdArgs& a, int D) {
-  const int BH = a.B * a.Hq;
-  if (a.cu_seqlens || (BH & 7)) return 0;
-  const int S8 = BH >> 3, group = a.Hq / a.Hkv;
-  const int64_t budget = a.causal ? ATTN_FWD_XG_BUDGET_CAUSAL : ATTN_FWD_XG_BUDGET;
-  // One group for the whole XCD (everything fits), or not even one slice
-  // fitting: the plain order, or for grouped-query heads its restriction to
-  // whole kv groups per XCD (xg = BH/8).
-  const int whole = group > 1 ? S8 : 0;
-  if ((int64_t)a.N * D * 4 > budget) return whole;
-  int best = 1;
-  for (int G = 1; G <= S8; ++G) {
-    const int64_t kv = (int64_t)((G + group - 1) / group) * a.N * D * 4;
-    if (kv > budget) break;
-    if (S8 % G == 0) best = G;
-  }
-  return best == S8 ? whole : best;
+  if (a.cu_seqlens) return 0;
+  return xcd_group((int64_t)a.B * a.Hq, a.Hq / a.Hkv, (int64_t)a.N * D * 4,
+                   a.causal ? kXgBudgetCausal : kXgBudget);
 }
 
 template <typename T, int D, bool CAUSAL, int MODE>

@@ -121,6 +121,27 @@ constexpr int kSparseBlockQ = 128, kSparseBlockK = 64;
 size_t sparse_workspace_bytes(int Hq, int N, int mask_heads);
 hipError_t launch_fwd_sparse(const FwdArgs& a, const unsigned char* mask, void* workspace);
 // Bytes of the backward row-statistics workspace.
+// Slice group xg of the XCD-aware work order (xcd_item) for nsl slices that
+// each stream `bytes` of data through L2, shared by `share` adjacent slices:
+// the largest divisor of nsl/8 whose data fit `budget`.  When one group
+// would cover all of an XCD's slices, or not even one slice fits: the plain
+// order (0), or for shared data its restriction to whole sharing groups per
+// XCD (nsl/8).  0 when nsl % 8 != 0.
+inline int xcd_group(int64_t nsl, int share, int64_t bytes, int64_t budget) {
+  if (nsl <= 0 || (nsl & 7) || nsl > (1LL << 30)) return 0;
+  const int S8 = (int)(nsl >> 3), whole = share > 1 ? S8 : 0;
+  if (bytes > budget) return whole;
+  int best = 1;
+  for (int G = 1; G <= S8; ++G) {
+    if ((int64_t)((G + share - 1) / share) * bytes > budget) break;
+    if (S8 % G == 0) best = G;
+  }
+  return best == S8 ? whole : best;
+}
+// L2 budgets of the slice groups: causal grids also need their heaviest
+// blocks of many slices in flight at once, so they take larger groups.
+constexpr int64_t kXgBudget = 2 << 20, kXgBudgetCausal = 8 << 20;
+
 size_t bwd_stats_bytes(int B, int Hq, int N);
 // Query-head splits of the dK/dV stage for a dense problem (1 when the grid
 // of key blocks x kv heads already fills the device), and the bytes of fp32
