@@ -282,3 +282,15 @@ def test_gqa_backward_reduced_length(oracle_mod):
     """Workload 4's heads (Hq=32, Hkv=8, d=128, Q x 8, causal) at N=2048."""
     w = attn_inputs.WORKLOADS[4].scaled(N=2048, backward=True, seed=41)
     full_size_slices(oracle_mod, w, [0, 5, 7])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_xcd_slice_groups_sampled(oracle_mod, causal):
+    """Shapes whose dQ (and, non-causal, dK/dV) workgroups run in XCD slice
+    groups smaller than an XCD's share of slices: B=4, H=16 is 64 slices, 8 per
+    XCD; non-causal N=1024 has 512 KiB of K/V per slice (groups of 4 under a
+    2 MiB budget), causal N=4096 has 2 MiB (groups of 4 under 8 MiB)."""
+    N = 4096 if causal else 1024
+    w = attn_inputs.Workload(f"xcd_groups_B4_H16_N{N}_d128", 4, 16, 16, N, 128, causal, "bf16",
+                             backward=True, seed=43)
+    full_size_slices(oracle_mod, w, [0, 21, 63])
