@@ -294,3 +294,15 @@ def test_bwd_xcd_slice_groups_sampled(oracle_mod, causal):
     w = attn_inputs.Workload(f"xcd_groups_B4_H16_N{N}_d128", 4, 16, 16, N, 128, causal, "bf16",
                              backward=True, seed=43)
     full_size_slices(oracle_mod, w, [0, 21, 63])
+
+
+def test_gqa_backward_unsplit_sampled(oracle_mod):
+    """A grouped-query backward whose 128-key blocks x kv heads already fill the
+    device (B=4, Hkv=4, N=4096: 512 workgroups at d = 128), so the dK/dV stage
+    keeps each group's query heads in one workgroup: no partial sums in the
+    workspace."""
+    w = attn_inputs.Workload("gqa_unsplit_B4_Hq8_Hkv4_N4096_d128", 4, 8, 4, 4096, 128, True,
+                             "bf16", backward=True, seed=44)
+    assert ea.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, ea.ATTN_BF16) == \
+        w.B * w.Hq * 2 * w.N * 4
+    full_size_slices(oracle_mod, w, [0, 15])
