@@ -48,6 +48,18 @@ namespace attn {
 #ifndef ATTN_FWD_SETPRIO
 #define ATTN_FWD_SETPRIO 1
 #endif
+// Fair wave priority for the plain kernel where it runs without the
+// matrix-core phase priority (d = 64), non-causal grids only: each wave's
+// priority falls with its remaining key tiles (one level per ATTN_FWD_FAIR
+// tiles, 0 = off).  Four waves of four workgroups share a SIMD; with equal
+// priority the oldest wins, so they finish staggered and the SIMD ends the
+// grid with fewer and fewer waves to hide latency.  Measured (same-box A/B):
+// non-causal B=8 H=16 N=1024 d=64 +4.7%, B=4 H=32 N=2048 +2.5%; causal grids
+// lost 1-4% (heaviest-first already orders them), so they keep equal
+// priority.
+#ifndef ATTN_FWD_FAIR
+#define ATTN_FWD_FAIR 4
+#endif
 #ifndef ATTN_FWD_NBUF64
 #define ATTN_FWD_NBUF64 2
 #endif
@@ -275,6 +287,17 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     constexpr int BUF = decltype(bufc)::value;
     const char* kt = smem + BUF * 2 * TILEB;
     const char* vt = kt + TILEB;
+    if constexpr (!PRIO && !CAUSAL && ATTN_FWD_FAIR > 0) {
+      const int rem = ntiles - j;  // wave-uniform
+      if (rem > 3 * ATTN_FWD_FAIR)
+        __builtin_amdgcn_s_setprio(3);
+      else if (rem > 2 * ATTN_FWD_FAIR)
+        __builtin_amdgcn_s_setprio(2);
+      else if (rem > ATTN_FWD_FAIR)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
     if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (wave_active(j)) {
       // ---- S^T = K Q^T for the tile's two 32-key blocks and every query block
