@@ -128,15 +128,19 @@ hipError_t launch_fwd_sparse(const FwdArgs& a, const unsigned char* mask, void* 
 // order (0), or for shared data its restriction to whole sharing groups per
 // XCD (nsl/8).  0 when nsl % 8 != 0.
 inline int xcd_group(int64_t nsl, int share, int64_t bytes, int64_t budget) {
-  if (nsl <= 0 || (nsl & 7) || nsl > (1LL << 30)) return 0;
-  const int S8 = (int)(nsl >> 3), whole = share > 1 ? S8 : 0;
+  if (nsl <= 0 || (nsl & 7) || nsl > (1LL << 30) || bytes <= 0) return 0;
+  const int64_t S8 = nsl >> 3;
+  const int whole = share > 1 ? (int)S8 : 0;
   if (bytes > budget) return whole;
-  int best = 1;
-  for (int G = 1; G <= S8; ++G) {
-    if ((int64_t)((G + share - 1) / share) * bytes > budget) break;
-    if (S8 % G == 0) best = G;
+  // ceil(G / share) * bytes <= budget  <=>  G <= floor(budget / bytes) * share
+  const int64_t gmax = (budget / bytes) * share;
+  int64_t best = 1;
+  for (int64_t f = 1; f * f <= S8; ++f) {  // divisors of S8 in pairs (f, S8 / f)
+    if (S8 % f) continue;
+    if (f <= gmax && f > best) best = f;
+    if (S8 / f <= gmax && S8 / f > best) best = S8 / f;
   }
-  return best == S8 ? whole : best;
+  return best == S8 ? whole : (int)best;
 }
 // L2 budgets of the slice groups: causal grids also need their heaviest
 // blocks of many slices in flight at once, so they take larger groups.
