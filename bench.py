@@ -51,6 +51,24 @@ def fwd_flops(B, H, N, d, causal):
     return f / 2 if causal else f
 
 
+def warm_up(fn, min_calls: int, min_ms: float = 60.0):
+    """Untimed calls of fn: at least min_calls, and until the GPU has been kept
+    busy for min_ms.  Its clocks ramp up from idle over tens of milliseconds
+    (measured: the B=8 H=16 N=2048 d=64 step takes 0.40 ms after 5 warm-up
+    steps and a steady 0.34 ms after 50-200), and host work between the sweep
+    cases lets them fall again."""
+    import torch
+
+    t0 = time.perf_counter()
+    for _ in range(min_calls):
+        fn()
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def kernel_source_hash() -> str:
     """Hash of the kernel sources with comments and blank lines removed, so a
     comment edit does not invalidate counters taken on the same code."""
@@ -119,8 +137,7 @@ def forward_only(w, args, dev):
 
     q, k, v = (t.to(dev) for t in attn_inputs.make_workload(w, with_dout=False))
     o, lse = ea.fwd(q, k, v, causal=w.causal)
-    for _ in range(args.warmup):
-        ea.fwd(q, k, v, causal=w.causal, out=o, lse=lse)
+    warm_up(lambda: ea.fwd(q, k, v, causal=w.causal, out=o, lse=lse), args.warmup)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -195,8 +212,7 @@ def splitkv_case(cw, dev, steps, warmup, num_splits=0):
         if st != ea.ATTN_OK:
             raise ea.AttnError(st, "attn_fwd_splitkv")
 
-    for _ in range(warmup):
-        call()
+    warm_up(call, warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -256,8 +272,7 @@ def sparse_case(sw, dev, steps, warmup):
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
+        warm_up(fn, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -305,8 +320,7 @@ def varlen_case(vw, dev, steps, warmup):
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
+        warm_up(fn, warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
@@ -395,7 +409,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before the timed ones (the GPU's clocks ramp up from idle "
+                         "over tens of milliseconds)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep")
@@ -566,8 +582,7 @@ def main():
         for cw in cases:
             cq, ck, cv = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=False))
             co, cl = ea.fwd(cq, ck, cv, causal=cw.causal)
-            for _ in range(5):
-                ea.fwd(cq, ck, cv, causal=cw.causal, out=co, lse=cl)
+            warm_up(lambda: ea.fwd(cq, ck, cv, causal=cw.causal, out=co, lse=cl), 5)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 25
             e0.record(stream)
@@ -614,8 +629,7 @@ def main():
                                   cw.Hq, cw.Hkv, cw.N, cw.d, int(cw.causal), cw.d ** -0.5,
                                   ea.ATTN_BF16, sp), "attn_bwd")
 
-            for _ in range(3):
-                bwd_call()
+            warm_up(bwd_call, 3)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 10
             e0.record(stream)
