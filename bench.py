@@ -164,6 +164,58 @@ def forward_only(w, args, dev):
                    "causal": w.causal, "q_mult": w.q_mult, "seed": w.seed}}), flush=True)
 
 
+def backward_only(w, args, dev):
+    """attn_bwd alone on workload w (the forward's O and LSE precomputed): K timed
+    calls, HIP events on the stream.  Algorithmic FLOPs 10*B*Hq*N^2*d, halved
+    for causal (the dQ stage's recomputed S and dP are executed, not counted)."""
+    import torch
+
+    import attn_inputs
+    import exact_attention_87_amd as ea
+
+    q, k, v, do = (t.to(dev) for t in attn_inputs.make_workload(w, with_dout=True))
+    o, lse = ea.fwd(q, k, v, causal=w.causal)
+    ws = torch.empty(max(ea.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, ea.ATTN_BF16),
+                         256), device=dev, dtype=torch.uint8)
+    grads = [torch.empty_like(t) for t in (q, k, v)]
+    sp = torch.cuda.current_stream(dev).cuda_stream
+
+    def call():
+        st = ea.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         do.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                         grads[2].data_ptr(), ws.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+                         int(w.causal), w.d ** -0.5, ea.ATTN_BF16, sp)
+        if st != ea.ATTN_OK:
+            raise ea.AttnError(st, "attn_bwd")
+
+    warm_up(call, args.warmup)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    fl = 2.5 * fwd_flops(w.B, w.Hq, w.N, w.d, w.causal)
+    tf = fl / ms / 1e9
+    print(json.dumps({
+        "metric": "attention backward TFLOP/s on 1 MI355X", "value": round(tf, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "kernel_ms": round(ms, 5),
+        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "higher_is_better": True,
+        "dtype": w.dtype, "data": "synthetic",
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(f"bwd_workload{args.bwd_only}"),
+                     "kernel": "attn_bwd (dQ stage with statistics + dK/dV stage)"},
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "q_mult": w.q_mult, "seed": w.seed}}), flush=True)
+
+
 def calibration_copy(mib, dev):
     """One plain device copy of `mib` MiB: a transfer of known size that
     scales the HBM byte counters of a profiling run."""
@@ -419,6 +471,8 @@ def main():
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--fwd-only", type=int, default=0, metavar="ID",
                     help="time only the forward of workload ID (1-5) and print its JSON line")
+    ap.add_argument("--bwd-only", type=int, default=0, metavar="ID",
+                    help="time only attn_bwd on workload ID (1-5; fp32 workload 1 has none)")
     ap.add_argument("--sparse-only", default="", metavar="NAME",
                     help="time only the block-sparse forward of workload NAME (local_global)")
     ap.add_argument("--varlen-only", default="", metavar="NAME",
@@ -445,10 +499,17 @@ def main():
     dev = torch.device("cuda:0")
     ea.lib()  # fail loudly if the HIP library is missing
 
-    if args.fwd_only or args.splitkv_only or args.sparse_only or args.varlen_only:
+    if args.fwd_only or args.bwd_only or args.splitkv_only or args.sparse_only or args.varlen_only:
         calibration_copy(args.copy_mib, dev)
     if args.fwd_only:
         forward_only(attn_inputs.WORKLOADS[args.fwd_only], args, dev)
+        return
+    if args.bwd_only:
+        if args.bwd_only == 1:
+            print("bench.py: workload 1 is the fp32 forward parity case; it has no backward",
+                  file=sys.stderr)
+            sys.exit(2)
+        backward_only(attn_inputs.WORKLOADS[args.bwd_only], args, dev)
         return
     if args.splitkv_only:
         splitkv_only(args.splitkv_only, args, dev)
