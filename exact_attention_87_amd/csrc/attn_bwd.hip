@@ -19,7 +19,10 @@
 //         keeps its 32 keys' K and V as matrix-core operands in registers and
 //         accumulates dK^T, dV^T over every query tile of every query head of
 //         the group (so grouped-query heads are summed on chip).  Query tiles
-//         (Q, dO and the statistics) stream through LDS.
+//         (Q, dO and the statistics) stream through LDS.  When that grid is
+//         too small to fill the device, a group's query heads are split over
+//         several workgroups per key block, each writing fp32 partial sums to
+//         the workspace, and a merge kernel adds them in split order.
 //   dq:   one workgroup per (batch, query head, block of 128 queries); the
 //         forward's tiling, with dQ^T accumulated over key tiles that stream
 //         through LDS.  The full backward of a dense problem runs dq first,
