@@ -196,6 +196,10 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
     wtiles = min(ntiles, (q0 + 32 * NB - 1) / BC + 1);
   }
+  // A wave whose rows all lie past the slice's end (the last, partial query
+  // block) computes nothing; it still shares the workgroup's loads and
+  // barriers.
+  if (q0 >= N) wtiles = 0;
   // Block-sparse: the key tiles of this query block's mask row (ascending,
   // already cut at the causal diagonal), copied to LDS after the stages as
   // 16-bit indices; loop position j then loads tile tiles[j].
@@ -216,7 +220,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   // does this wave have visible keys in loop position j (< ntiles)?
   auto wave_active = [&](int j) -> bool {
     if constexpr (SPARSE)
-      return !CAUSAL || tile_of(j) * BC <= q0 + 32 * NB - 1;
+      return q0 < N && (!CAUSAL || tile_of(j) * BC <= q0 + 32 * NB - 1);
     else
       return j < wtiles;
   };
@@ -586,6 +590,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
     wtiles = min(ntiles, (q0 + 31) / BC + 1);
   }
+  if (q0 >= N) wtiles = 0;  // every row of this wave lies past the slice's end
   // Block-sparse tile list, as in fwd_mfma_kernel (LDS after the stages).
   unsigned short* tl = (unsigned short*)(smem + 4 * TILEB);
   if constexpr (SPARSE) {
@@ -603,7 +608,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   };
   auto wave_active = [&](int j) -> bool {  // j < ntiles
     if constexpr (SPARSE)
-      return !CAUSAL || tile_of(j) * BC <= q0 + 31;
+      return q0 < N && (!CAUSAL || tile_of(j) * BC <= q0 + 31);
     else
       return j < wtiles;
   };
