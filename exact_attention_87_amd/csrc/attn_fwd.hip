@@ -196,10 +196,11 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
     wtiles = min(ntiles, (q0 + 32 * NB - 1) / BC + 1);
   }
-  // A wave whose rows all lie past the slice's end (the last, partial query
-  // block) computes nothing; it still shares the workgroup's loads and
-  // barriers.
-  if (q0 >= N) wtiles = 0;
+  // Causal: a wave whose rows all lie past the slice's end (the last, partial
+  // query block) computes nothing; it still shares the workgroup's loads and
+  // barriers.  (Not under a non-causal mask: there every wave is active on
+  // every tile, and the compiler drops the activity test altogether.)
+  if (CAUSAL && q0 >= N) wtiles = 0;
   // Block-sparse: the key tiles of this query block's mask row (ascending,
   // already cut at the causal diagonal), copied to LDS after the stages as
   // 16-bit indices; loop position j then loads tile tiles[j].
@@ -220,7 +221,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   // does this wave have visible keys in loop position j (< ntiles)?
   auto wave_active = [&](int j) -> bool {
     if constexpr (SPARSE)
-      return q0 < N && (!CAUSAL || tile_of(j) * BC <= q0 + 32 * NB - 1);
+      return !CAUSAL || (q0 < N && tile_of(j) * BC <= q0 + 32 * NB - 1);
     else
       return j < wtiles;
   };
@@ -590,7 +591,10 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
     ntiles = min(ntiles_all, (qb * BR + BR - 1) / BC + 1);
     wtiles = min(ntiles, (q0 + 31) / BC + 1);
   }
-  if (q0 >= N) wtiles = 0;  // every row of this wave lies past the slice's end
+  // causal: every row of this wave may lie past the slice's end.  Not under a
+  // non-causal mask, where the activity test compiles away: there a runtime
+  // test made the scheduled tile body spill 303 registers.
+  if (CAUSAL && q0 >= N) wtiles = 0;
   // Block-sparse tile list, as in fwd_mfma_kernel (LDS after the stages).
   unsigned short* tl = (unsigned short*)(smem + 4 * TILEB);
   if constexpr (SPARSE) {
@@ -608,7 +612,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   };
   auto wave_active = [&](int j) -> bool {  // j < ntiles
     if constexpr (SPARSE)
-      return q0 < N && (!CAUSAL || tile_of(j) * BC <= q0 + 31);
+      return !CAUSAL || (q0 < N && tile_of(j) * BC <= q0 + 31);
     else
       return j < wtiles;
   };
