@@ -464,6 +464,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps before the timed ones (the GPU's clocks ramp up from idle "
                          "over tens of milliseconds)")
+    ap.add_argument("--prewarm-ms", type=float, default=60.0,
+                    help="before the warm-up steps, run untimed steps until the GPU has been busy "
+                         "this long (reported as prewarm_ms; 0 disables)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep")
@@ -570,6 +573,17 @@ def main():
             if events is not None:
                 events[i].record(stream)
 
+    # Pre-warm, reported separately: untimed steps until the GPU has been busy
+    # for --prewarm-ms, so the clocks have left idle whatever W is; then
+    # exactly W untimed warm-up steps, then the K timed ones.
+    t_pw = time.perf_counter()
+    prewarm_steps = 0
+    while (time.perf_counter() - t_pw) * 1e3 < args.prewarm_ms:
+        for _ in range(8):
+            step()
+        prewarm_steps += 8
+        torch.cuda.synchronize()
+    prewarm_ms = (time.perf_counter() - t_pw) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -734,7 +748,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": args.warmup, "prewarm_ms": round(prewarm_ms, 1), "prewarm_steps": prewarm_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
