@@ -100,6 +100,120 @@ def load_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def roofline_mfma(tflops: float, traffic_key: str | None):
+    """A sweep entry's roofline: algorithmic TFLOP/s against the dense bf16
+    peak, with the HBM bytes per call from the counters when they were taken
+    on the current sources."""
+    return {"bound": "mfma", "achieved": round(tflops, 1), "peak": round(PEAK_BF16_TFLOPS, 1),
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(traffic_key) if traffic_key else None}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz) from the SMI library's metrics
+    table in a background thread, e.g. over the timed region.  Under sustained
+    matrix-core load the board runs at its power cap below the 2.4 GHz the
+    published peak assumes, so the clock explains part of any gap to it.
+    Disabled (source None) where the SMI library is unavailable."""
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+
+        self.period = period_s
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                clks = m.get("current_gfxclks")
+                if isinstance(clks, (list, tuple)):
+                    vals = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000]
+                    if vals:  # one per XCD
+                        return sum(vals) / len(vals)
+                for key in ("current_gfxclk", "average_gfxclk_frequency"):
+                    c = m.get(key)
+                    if isinstance(c, (int, float)) and 0 < c < 10000:
+                        return float(c)
+                return None
+
+            if read() is not None:
+                self._read = read
+                self.source = "amdsmi gpu_metrics current graphics clock (mean over XCDs)"
+        except Exception as e:  # no SMI library, no permission, no device
+            self.source = None
+            self.error = f"{type(e).__name__}: {e}"[:200]
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                c = self._read()
+                if c is not None:
+                    self.samples.append(c)
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self._read is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": self.source, "samples": 0, "error": getattr(self, "error", None)}
+        v = self.samples
+        return {"mean_mhz": round(sum(v) / len(v), 1), "min_mhz": round(min(v), 1),
+                "max_mhz": round(max(v), 1), "samples": len(v), "source": self.source}
+
+
+def environment(dev):
+    """Where the numbers were taken: device, software versions, host."""
+    import subprocess
+
+    import torch
+
+    props = torch.cuda.get_device_properties(dev)
+    env = {"gpu": torch.cuda.get_device_name(dev), "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count,
+           "device_memory_bytes": props.total_memory, "torch": torch.__version__,
+           "torch_hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
+                             timeout=30).stdout
+        env["hipcc"] = next((l.strip() for l in out.splitlines() if "HIP version" in l), None)
+    except Exception:
+        env["hipcc"] = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            env["host_cpu"] = next((l.split(":", 1)[1].strip() for l in f if
+                                    l.startswith("model name")), None)
+    except OSError:
+        env["host_cpu"] = None
+    env["host_cpus"] = os.cpu_count()
+    return env
+
+
 def cpu_baseline(w, budget_s: float):
     """The fp64 oracle (forward + backward) on whole (batch, head) slices of
     the workload, one after another until the time budget is spent."""
@@ -524,6 +638,8 @@ def main():
         varlen_only(args.varlen_only, args, dev)
         return
 
+    env = environment(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
     w = attn_inputs.WORKLOADS[5]
     B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
     scale = 1.0 / math.sqrt(d)
@@ -599,17 +715,22 @@ def main():
     probed = list(range(0, K, 5))
     evs = {s: [torch.cuda.Event(enable_timing=True) for _ in launches] for s in probed}
     start = {s: torch.cuda.Event(enable_timing=True) for s in probed}
+    clock = ClockSampler()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        if s in start:
-            start[s].record(stream)
-            step(evs[s])
-        else:
-            step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with clock:
+        t0 = time.perf_counter()
+        for s in range(K):
+            if s in start:
+                start[s].record(stream)
+                step(evs[s])
+            else:
+                step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
+    # device memory the step holds (the library allocates none itself: inputs,
+    # outputs, statistics workspace)
+    peak_mem = torch.cuda.max_memory_allocated(dev)
 
     kern_ms = {name: 0.0 for name, _ in launches}
     for s in probed:
@@ -655,6 +776,8 @@ def main():
                                  "bf16", seed=9),
         ]
         for cw in cases:
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats(dev)
             cq, ck, cv = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=False))
             co, cl = ea.fwd(cq, ck, cv, causal=cw.causal)
             warm_up(lambda: ea.fwd(cq, ck, cv, causal=cw.causal, out=co, lse=cl), 5)
@@ -667,8 +790,11 @@ def main():
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
             tf = fwd_flops(cw.B, cw.Hq, cw.N, cw.d, cw.causal) / (ms / 1e3) / 1e12
+            wid = next((i for i, x in attn_inputs.WORKLOADS.items() if x.name == cw.name), None)
             sweep[cw.name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
-                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                              "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "roofline": roofline_mfma(tf, f"fwd_workload{wid}" if wid else None),
+                              "peak_mem_bytes": torch.cuda.max_memory_allocated(dev)}
             del cq, ck, cv, co, cl
         torch.cuda.synchronize()
 
@@ -690,6 +816,8 @@ def main():
                                  True, "bf16", seed=12),
         ]
         for cw in bcases:
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats(dev)
             cq, ck, cv, cdo = (t.to(dev) for t in attn_inputs.make_workload(cw, with_dout=True))
             co, cl = ea.fwd(cq, ck, cv, causal=cw.causal)
             cws = torch.empty(ea.attn_bwd_workspace_bytes(cw.B, cw.Hq, cw.Hkv, cw.N, cw.d,
@@ -714,8 +842,11 @@ def main():
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
             tf = 2.5 * fwd_flops(cw.B, cw.Hq, cw.N, cw.d, cw.causal) / (ms / 1e3) / 1e12
+            key = "bwd_workload4" if cw.name == "causal_gqa_bf16_B1_Hq32_Hkv8_N16384_d128" else None
             bwd_sweep[cw.name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
-                                  "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+                                  "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                  "roofline": roofline_mfma(tf, key),
+                                  "peak_mem_bytes": torch.cuda.max_memory_allocated(dev)}
             del cq, ck, cv, cdo, co, cl, cws, grads
         torch.cuda.synchronize()
 
@@ -723,21 +854,29 @@ def main():
     splitkv = {}
     if not args.no_sweep:
         for name, cw in attn_inputs.CACHE_WORKLOADS.items():
-            splitkv[cw.name] = splitkv_case(cw, dev, steps=20, warmup=3)
+            r = splitkv_case(cw, dev, steps=20, warmup=3)
+            r["roofline"] = {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": r["frac_of_hbm"],
+                             "traffic": load_traffic("splitkv_" + name)}
+            splitkv[cw.name] = r
         torch.cuda.synchronize()
 
     # block-sparse forward (parity-tested separately)
     blocksparse = {}
     if not args.no_sweep:
         for name, sw in attn_inputs.SPARSE_WORKLOADS.items():
-            blocksparse[sw.name] = sparse_case(sw, dev, steps=10, warmup=3)
+            r = sparse_case(sw, dev, steps=10, warmup=3)
+            r["roofline"] = roofline_mfma(r["tflops"], "blocksparse_" + name)
+            blocksparse[sw.name] = r
         torch.cuda.synchronize()
 
     # packed variable-length forward (parity-tested separately)
     varlen = {}
     if not args.no_sweep:
         for name, vw in attn_inputs.VARLEN_WORKLOADS.items():
-            varlen[vw.name] = varlen_case(vw, dev, steps=10, warmup=3)
+            r = varlen_case(vw, dev, steps=10, warmup=3)
+            r["roofline"] = roofline_mfma(r["tflops"], "varlen_" + name)
+            varlen[vw.name] = r
         torch.cuda.synchronize()
 
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
@@ -769,7 +908,10 @@ def main():
         "blocksparse": blocksparse,
         "varlen": varlen,
         "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_name(dev),
+        "peak_mem_bytes": peak_mem,
+        "sclk_timed_region": clock.summary(),
+        "env": env,
+        "device": env["gpu"],
         "torch": torch.__version__,
     }
     print(json.dumps(out), flush=True)

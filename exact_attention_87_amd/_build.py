@@ -34,21 +34,36 @@ def _run(cmd):
     return out
 
 
+# Object files of the last build (not tracked): a host-sanitized build of the
+# argument-validation code links against the kernel objects kept here.
+OBJDIR = os.path.join(HERE, "_build")
+
+
+def object_path(source: str) -> str:
+    return os.path.join(OBJDIR, os.path.splitext(source)[0] + ".o")
+
+
 def build(verbose: bool = False) -> str:
     """Always recompiles (one hipcc per source, in parallel, then a link);
     returns the path of the library."""
-    import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
-    with tempfile.TemporaryDirectory(prefix="attn_build_") as tmpdir:
-        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o]
-                for s, o in zip(SOURCES, objs)]
-        jobs = min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+    os.makedirs(OBJDIR, exist_ok=True)
+    pid = os.getpid()
+    objs = [object_path(s) + ".tmp%d" % pid for s in SOURCES]
+    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    jobs = min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+    try:
         with ThreadPoolExecutor(max_workers=jobs) as pool:
             outs = list(pool.map(_run, cmds))
-        tmp = LIB + ".tmp%d" % os.getpid()
+        tmp = LIB + ".tmp%d" % pid
         outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
+        for s, o in zip(SOURCES, objs):
+            os.replace(o, object_path(s))
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     out = "\n".join(o for o in outs if o.strip())
     if verbose and out.strip():
         print(out)

@@ -15,6 +15,17 @@
 
 namespace {
 
+// The ABI's enum arguments may carry any int a C caller passed; they are read
+// as int before any comparison (loading an out-of-range value through the C++
+// enum type would be undefined behaviour).
+template <typename E>
+int as_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950, 2 = other architecture.
 std::atomic<int> g_arch_state[kMaxDevices];
@@ -41,10 +52,19 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// A dispatch's grid size is a 32-bit count of work-items: `units` work units
+// of `per_unit` threads each must stay below 2^32 (a larger grid would be
+// truncated, leaving most of the problem uncomputed).
+bool dispatch_fits(int64_t units, int64_t per_unit) {
+  return units >= 0 && per_unit > 0 && units < ((int64_t)1 << 32) / per_unit;
+}
+
 // Shape checks common to both passes.  Returns ATTN_OK and sets *empty when
 // the problem has no rows.
 attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                        attn_dtype dtype, bool* empty) {
+                        int dtype, bool* empty) {
   if (B < 0 || N < 0 || Hq < 1 || Hkv < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
@@ -55,9 +75,12 @@ attn_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float 
   // Limits of the kernels' 32-bit grid, row and byte offsets: one (batch,
   // head) slice stays below 1 GiB.
   if ((int64_t)B * Hq > (1 << 24) || N > (1 << 22)) return ATTN_ERR_UNSUPPORTED;
-  // every one-dimensional grid (at most one workgroup per 32 rows of each
-  // (batch, head) slice) stays below 2^31 workgroups
-  if ((int64_t)B * Hq * ((N + 31) / 32) >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  // Every launch over the query rows fits one dispatch: its work-items
+  // (workgroups x threads) stay below 2^32.  The most per row are the
+  // statistics kernel's d/8 lanes (at least 8: the fp32 forward), over rows
+  // padded to the 128-row blocks of the matrix-core grids.
+  if (!dispatch_fits((int64_t)B * Hq * round_up(N, 128), std::max(8, d / 8)))
+    return ATTN_ERR_UNSUPPORTED;
   *empty = (B == 0 || N == 0);
   return ATTN_OK;
 }
@@ -96,7 +119,7 @@ Sizes sizes(int B, int Hq, int Hkv, int N, int d) {
 // Checks shared by the backward entry points.  On success fills *a's shape
 // fields; a->N == 0 marks an empty problem (nothing to launch).
 attn_status bwd_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                       attn_dtype dtype, void* stream, attn::BwdArgs* a) {
+                       int dtype, void* stream, attn::BwdArgs* a) {
   *a = attn::BwdArgs{};
   bool empty = false;
   attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
@@ -109,6 +132,17 @@ attn_status bwd_common(int B, int Hq, int Hkv, int N, int d, int causal, float s
   return ATTN_OK;
 }
 
+// attn_bwd_workspace_bytes on an int dtype.
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int dtype) {
+  bool empty = false;
+  if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
+  if (dtype == ATTN_F32) return (size_t)-1;
+  if (empty) return 0;
+  const size_t stats = (attn::bwd_stats_bytes(B, Hq, N) + 255) & ~(size_t)255;
+  const size_t part = attn::bwd_partial_bytes(B, Hkv, N, d, attn::bwd_dkdv_splits(B, Hq, Hkv, N, d));
+  return stats + ((part + 255) & ~(size_t)255);
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,7 +150,7 @@ extern "C" {
 int attn_abi_version(void) { return 2; }
 
 const char* attn_status_str(attn_status s) {
-  switch (s) {
+  switch (as_int(s)) {  // any int a C caller passed
     case ATTN_OK: return "ATTN_OK";
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
@@ -129,15 +163,16 @@ const char* attn_status_str(attn_status s) {
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int Hq, int Hkv, int N, int d, int causal, float scale, attn_dtype dtype,
                      void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   bool empty = false;
-  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
+  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dt, &empty);
   if (st != ATTN_OK) return st;
-  if (dtype == ATTN_F32 && d == 256) return ATTN_ERR_UNSUPPORTED;
+  if (dt == ATTN_F32 && d == 256) return ATTN_ERR_UNSUPPORTED;
   if (empty) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_INVALID_ARG;
-  const size_t es = dtype == ATTN_F32 ? 4 : 2;
+  const size_t es = dt == ATTN_F32 ? 4 : 2;
   const size_t qbytes = (size_t)B * Hq * N * d * es;
   const size_t kvbytes = (size_t)B * Hkv * N * d * es;
   const size_t lbytes = (size_t)B * Hq * N * sizeof(float);
@@ -150,19 +185,13 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
   st = check_device();
   if (st != ATTN_OK) return st;
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dtype,
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dt,
                   (hipStream_t)stream};
   return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype) {
-  bool empty = false;
-  if (check_shape(B, Hq, Hkv, N, d, 0, 1.0f, dtype, &empty) != ATTN_OK) return (size_t)-1;
-  if (dtype == ATTN_F32) return (size_t)-1;
-  if (empty) return 0;
-  const size_t stats = (attn::bwd_stats_bytes(B, Hq, N) + 255) & ~(size_t)255;
-  const size_t part = attn::bwd_partial_bytes(B, Hkv, N, d, attn::bwd_dkdv_splits(B, Hq, Hkv, N, d));
-  return stats + ((part + 255) & ~(size_t)255);
+  return bwd_workspace_bytes(B, Hq, Hkv, N, d, as_int(dtype));
 }
 
 namespace {
@@ -173,15 +202,32 @@ void set_split(attn::BwdArgs* a, void* workspace) {
   const size_t stats = (attn::bwd_stats_bytes(a->B, a->Hq, a->N) + 255) & ~(size_t)255;
   a->part = a->nsplit > 1 ? (float*)((char*)workspace + stats) : nullptr;
 }
+
+// attn_bwd's launches on validated arguments: the dQ stage, which also writes
+// the row statistics, then the dK/dV stage (and its merge when it splits).
+// Every workspace byte either kernel reads is written earlier in the same
+// call, so the workspace needs no initialisation.
+attn_status bwd_launch(attn::BwdArgs* a, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                       void* dv, void* workspace) {
+  a->q = q, a->k = k, a->v = v, a->o = o, a->lse = lse, a->dout = dout;
+  a->dq = dq, a->dk = dk, a->dv = dv, a->stats = (float*)workspace;
+  set_split(a, workspace);
+  if (attn::launch_bwd_dq_stats(*a) != hipSuccess) return ATTN_ERR_HIP;
+  if (attn::launch_bwd_dkdv(*a) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
 }  // namespace
+
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
                      void* workspace, int B, int Hq, int Hkv, int N, int d, int causal,
                      float scale, attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   attn::BwdArgs a;
-  const size_t wbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype);
-  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  const size_t wbytes = bwd_workspace_bytes(B, Hq, Hkv, N, d, dt);
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dt, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hkv, N, d);
@@ -190,21 +236,17 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
-  a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
-  set_split(&a, workspace);
-  // dQ first: it also writes the row statistics the dK/dV stage reads
-  if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return bwd_launch(&a, q, k, v, o, lse, dout, dq, dk, dv, workspace);
 }
+
 
 attn_status attn_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o,
                               const float* lse, const void* dout, float* stats, void* dq, int B,
                               int Hq, int Hkv, int N, int d, int causal, float scale,
                               attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   attn::BwdArgs a;
-  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dt, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hkv, N, d);
@@ -220,8 +262,9 @@ attn_status attn_bwd_dq_stats(const void* q, const void* k, const void* v, const
 
 attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, float* stats,
                                 int B, int Hq, int N, int d, attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   attn::BwdArgs a;
-  attn_status st = bwd_common(B, Hq, Hq, N, d, 0, 1.0f, dtype, stream, &a);
+  attn_status st = bwd_common(B, Hq, Hq, N, d, 0, 1.0f, dt, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hq, N, d);
@@ -236,9 +279,10 @@ attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* ls
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                           float* stats, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
                           int causal, float scale, attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   attn::BwdArgs a;
-  const size_t wbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype);
-  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  const size_t wbytes = bwd_workspace_bytes(B, Hq, Hkv, N, d, dt);
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dt, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hkv, N, d);
@@ -260,8 +304,9 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const voi
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                         const float* stats, void* dq, int B, int Hq, int Hkv, int N, int d,
                         int causal, float scale, attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   attn::BwdArgs a;
-  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dt, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   const Sizes z = sizes(B, Hq, Hkv, N, d);
@@ -282,7 +327,7 @@ namespace {
 // query rows (Nk == 0 with query rows is a real problem: every row sees no
 // key).
 attn_status split_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                        int num_splits, attn_dtype dtype, bool* empty) {
+                        int num_splits, int dtype, bool* empty) {
   if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
@@ -298,7 +343,11 @@ attn_status split_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causa
   *empty = (B == 0 || Nq == 0);
   if (*empty) return ATTN_OK;
   const attn::SplitPlan p = attn::split_plan(B, Hq, Hkv, Nq, Nk, d, num_splits);
-  if ((int64_t)p.nrb * p.nsplit * B * Hkv >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  // one dispatch each: 256-thread workgroups per (range, slice, row block),
+  // and the merge's (at most) 64 threads per output row
+  if (!dispatch_fits((int64_t)p.nrb * p.nsplit * B * Hkv, 256) ||
+      !dispatch_fits((int64_t)B * Hq * Nq, 64))
+    return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -326,8 +375,9 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* 
                              void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                              int causal, float scale, int num_splits, attn_dtype dtype,
                              void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   bool empty = false;
-  attn_status st = split_shape(B, Hq, Hkv, Nq, Nk, d, causal, scale, num_splits, dtype, &empty);
+  attn_status st = split_shape(B, Hq, Hkv, Nq, Nk, d, causal, scale, num_splits, dt, &empty);
   if (st != ATTN_OK) return st;
   if (empty) return ATTN_OK;
   const size_t qb = (size_t)B * Hq * Nq * d * 2, kvb = (size_t)B * Hkv * Nk * d * 2;
@@ -338,7 +388,7 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   st = check_device();
   if (st != ATTN_OK) return st;
   attn::SplitArgs a{q,  k,  v, o,           lse,   workspace,  B,
-                    Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dtype,
+                    Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dt,
                     (hipStream_t)stream};
   return attn::launch_fwd_split(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -377,7 +427,7 @@ namespace {
 attn_status fwd_blocksparse_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                                  const unsigned char* block_mask, int mask_heads, void* workspace,
                                  const long long* strides, int B, int Hq, int Hkv, int N, int d,
-                                 int causal, float scale, attn_dtype dtype, void* stream) {
+                                 int causal, float scale, int dtype, void* stream) {
   bool empty = false;
   attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
@@ -438,8 +488,9 @@ attn_status attn_fwd_blocksparse(const void* q, const void* k, const void* v, vo
                                  const unsigned char* block_mask, int mask_heads, void* workspace,
                                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                                  attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   return fwd_blocksparse_impl(q, k, v, o, lse, block_mask, mask_heads, workspace, nullptr, B, Hq,
-                              Hkv, N, d, causal, scale, dtype, stream);
+                              Hkv, N, d, causal, scale, dt, stream);
 }
 
 attn_status attn_fwd_blocksparse_strided(const void* q, const void* k, const void* v, void* o,
@@ -448,9 +499,10 @@ attn_status attn_fwd_blocksparse_strided(const void* q, const void* k, const voi
                                          const long long* strides, int B, int Hq, int Hkv, int N,
                                          int d, int causal, float scale, attn_dtype dtype,
                                          void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   if (!strides) return ATTN_ERR_INVALID_ARG;
   return fwd_blocksparse_impl(q, k, v, o, lse, block_mask, mask_heads, workspace, strides, B, Hq,
-                              Hkv, N, d, causal, scale, dtype, stream);
+                              Hkv, N, d, causal, scale, dt, stream);
 }
 
 }  // extern "C"
@@ -481,13 +533,15 @@ attn::Layout varlen_layout(const long long* s) {
 attn_status fwd_varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
                             const int* cu_seqlens, const long long* strides, int nseq,
                             int max_seqlen, int Hq, int Hkv, int T, int d, int causal, float scale,
-                            attn_dtype dtype, void* stream) {
+                            int dtype, void* stream) {
   if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
   bool empty = false;
   attn_status st = check_shape(1, Hq, Hkv, T, d, causal, scale, dtype, &empty);
   if (st != ATTN_OK) return st;
   if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  // the grid is (sequence, head, 128-row block of the longest sequence)
+  if (!dispatch_fits((int64_t)nseq * Hq * round_up(max_seqlen, 128), 2)) return ATTN_ERR_UNSUPPORTED;
   if (nseq == 0 || T == 0 || max_seqlen == 0) return ATTN_OK;  // no rows to compute
   const Sizes z = sizes(1, Hq, Hkv, T, d);
   size_t eq = z.q, ek = z.kv, eo = z.q;
@@ -524,15 +578,18 @@ attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, const v
                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
                             void* workspace, const int* cu_seqlens, const long long* strides,
                             int nseq, int max_seqlen, int Hq, int Hkv, int T, int d, int causal,
-                            float scale, attn_dtype dtype, void* stream) {
+                            float scale, int dtype, void* stream) {
   if (nseq < 0 || max_seqlen < 0 || T < 0 || max_seqlen > T) return ATTN_ERR_INVALID_ARG;
   attn::BwdArgs a;
   // the packed tokens as one [1, H, T, d] problem: shapes, statistics, workspace
   attn_status st = bwd_common(1, Hq, Hkv, T, d, causal, scale, dtype, stream, &a);
   if (st != ATTN_OK) return st;
   if ((int64_t)nseq * Hq > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
+  // the dK/dV and dQ grids are (sequence, head, 128-row block of the longest
+  // sequence), at most two threads per padded row
+  if (!dispatch_fits((int64_t)nseq * Hq * round_up(max_seqlen, 128), 2)) return ATTN_ERR_UNSUPPORTED;
   if (a.N == 0 || nseq == 0 || max_seqlen == 0) return ATTN_OK;  // no rows
-  const size_t wbytes = attn_bwd_workspace_bytes(1, Hq, Hkv, T, d, dtype);
+  const size_t wbytes = bwd_workspace_bytes(1, Hq, Hkv, T, d, dtype);
   const Sizes z = sizes(1, Hq, Hkv, T, d);
   size_t eq = z.q, ek = z.kv, eo = z.q;
   if (strides) {
@@ -603,17 +660,19 @@ attn_status attn_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             const int* cu_seqlens, int nseq, int max_seqlen, int Hq, int Hkv,
                             int T, int d, int causal, float scale, attn_dtype dtype,
                             void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens, nullptr, nseq, max_seqlen, Hq, Hkv, T, d,
-                         causal, scale, dtype, stream);
+                         causal, scale, dt, stream);
 }
 
 attn_status attn_fwd_varlen_strided(const void* q, const void* k, const void* v, void* o,
                                     float* lse, const int* cu_seqlens, const long long* strides,
                                     int nseq, int max_seqlen, int Hq, int Hkv, int T, int d,
                                     int causal, float scale, attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   if (!strides) return ATTN_ERR_INVALID_ARG;
   return fwd_varlen_impl(q, k, v, o, lse, cu_seqlens, strides, nseq, max_seqlen, Hq, Hkv, T, d,
-                         causal, scale, dtype, stream);
+                         causal, scale, dt, stream);
 }
 
 }  // extern "C"
@@ -626,8 +685,9 @@ attn_status attn_fwd_splitkv_strided(const void* q, const void* k, const void* v
                                      float* lse, void* workspace, const long long* strides, int B,
                                      int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                                      float scale, int num_splits, attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   bool empty = false;
-  attn_status st = split_shape(B, Hq, Hkv, Nq, Nk, d, causal, scale, num_splits, dtype, &empty);
+  attn_status st = split_shape(B, Hq, Hkv, Nq, Nk, d, causal, scale, num_splits, dt, &empty);
   if (st != ATTN_OK) return st;
   if (empty) return ATTN_OK;
   if (!strides) return ATTN_ERR_INVALID_ARG;
@@ -648,7 +708,7 @@ attn_status attn_fwd_splitkv_strided(const void* q, const void* k, const void* v
   st = check_device();
   if (st != ATTN_OK) return st;
   attn::SplitArgs a{q,  k,  v, o,           lse,   workspace,  B,
-                    Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dtype,
+                    Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dt,
                     (hipStream_t)stream};
   a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
   return attn::launch_fwd_split(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -657,10 +717,11 @@ attn_status attn_fwd_splitkv_strided(const void* q, const void* k, const void* v
 attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
                              const long long* strides, int B, int Hq, int Hkv, int N, int d,
                              int causal, float scale, attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   bool empty = false;
-  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dtype, &empty);
+  attn_status st = check_shape(B, Hq, Hkv, N, d, causal, scale, dt, &empty);
   if (st != ATTN_OK) return st;
-  if (dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (dt == ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (empty) return ATTN_OK;
   if (!strides) return ATTN_ERR_INVALID_ARG;
   for (int i = 0; i < 3; ++i)
@@ -671,7 +732,7 @@ attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* 
   if (st != ATTN_OK) return st;
   st = check_device();
   if (st != ATTN_OK) return st;
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dtype,
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dt,
                   (hipStream_t)stream};
   a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
   return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -682,9 +743,10 @@ attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const 
                              void* workspace, const long long* strides, int B, int Hq, int Hkv,
                              int N, int d, int causal, float scale, attn_dtype dtype,
                              void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   attn::BwdArgs a;
-  const size_t wbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, N, d, dtype);
-  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dtype, stream, &a);
+  const size_t wbytes = bwd_workspace_bytes(B, Hq, Hkv, N, d, dt);
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dt, stream, &a);
   if (st != ATTN_OK) return st;
   if (a.N == 0) return ATTN_OK;  // empty problem
   if (!strides) return ATTN_ERR_INVALID_ARG;
@@ -727,8 +789,9 @@ attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const v
                             void* workspace, const int* cu_seqlens, int nseq, int max_seqlen,
                             int Hq, int Hkv, int T, int d, int causal, float scale,
                             attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, nullptr, nseq,
-                         max_seqlen, Hq, Hkv, T, d, causal, scale, dtype, stream);
+                         max_seqlen, Hq, Hkv, T, d, causal, scale, dt, stream);
 }
 
 attn_status attn_bwd_varlen_strided(const void* q, const void* k, const void* v, const void* o,
@@ -737,9 +800,10 @@ attn_status attn_bwd_varlen_strided(const void* q, const void* k, const void* v,
                                     const long long* strides, int nseq, int max_seqlen, int Hq,
                                     int Hkv, int T, int d, int causal, float scale,
                                     attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
   if (!strides) return ATTN_ERR_INVALID_ARG;
   return bwd_varlen_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, strides, nseq,
-                         max_seqlen, Hq, Hkv, T, d, causal, scale, dtype, stream);
+                         max_seqlen, Hq, Hkv, T, d, causal, scale, dt, stream);
 }
 
 }  // extern "C"

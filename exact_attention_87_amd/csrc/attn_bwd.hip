@@ -42,45 +42,18 @@ namespace attn {
 
 constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 
-// Waves per SIMD of the backward kernels at d = 64 and 128 (d = 256: 1).
-// d = 64 fits three (168 registers) with operand reads in pairs and fenced
-// phases; the dQ kernel at d = 128 fits two.
-#ifndef ATTN_BWD_WPE64
-#define ATTN_BWD_WPE64 3
-#endif
-#ifndef ATTN_BWD_WPE128
-#define ATTN_BWD_WPE128 1
-#endif
-// Scheduling fences between the dV/dK products of the d = 64 dK/dV kernel at
-// three waves per SIMD: 0 none, 1 per feature block, 2 per 16 queries.  None
-// fits 168 registers and was fastest on the causal d = 64 backward (+3%).
-// d = 256 keeps one per feature block.
-#ifndef ATTN_BWD_FENCE_C64
-#define ATTN_BWD_FENCE_C64 0
-#endif
-// Raised wave priority (s_setprio 1) in the matrix-core phases of the dK/dV
-// kernel: 0 never, 1 in the S/dP and dV/dK products, 2 in dV/dK only,
-// 3 in S/dP only.  None of them, nor raising it in the dQ kernel's products,
-// helped the d = 64 or d = 128 backward (same-box A/B, 0 to -3%).
-#ifndef ATTN_BWD_PRIO
-#define ATTN_BWD_PRIO 0
-#endif
-#ifndef ATTN_DQ_PRIO
-#define ATTN_DQ_PRIO 0  // 1: raised priority in the dQ kernel's products
-#endif
-#ifndef ATTN_BWD_FENCE_A64
-#define ATTN_BWD_FENCE_A64 1  // fences between the operand groups of the S, dP products
-                              // (without them: 3 spilled registers, -2% causal)
-#endif
-#ifndef ATTN_DQ_FENCE
-#define ATTN_DQ_FENCE 1  // fence between the two key blocks of a dQ tile when registers are tight
-#endif
-#ifndef ATTN_DQ_WPE64
-#define ATTN_DQ_WPE64 3
-#endif
-#ifndef ATTN_DQ_WPE128
-#define ATTN_DQ_WPE128 2
-#endif
+// Measured choices (same-box A/B each; the alternatives are not kept):
+//  - Waves per SIMD: the dK/dV kernel runs 3 at d = 64 (168 registers, with
+//    operand reads in pairs and fenced phases) and 1 at d = 128 and 256 (the
+//    dK, dV accumulators and resident K, V take 336-354 registers); the dQ
+//    kernel runs 3 at d = 64 and 2 at d = 128.  Against 2/2/1: +5% on the
+//    causal B=8 H=16 N=2048 d=64 backward, +7-9% on the d = 128 cases.
+//  - Raised wave priority (s_setprio 1) in any matrix-core phase of the dK/dV
+//    or dQ kernel, or a priority falling with the remaining tiles: 0 to -3%
+//    on the d = 64 and d = 128 backward, so neither kernel raises it.
+//  - d = 64 dK/dV at three waves: fences between the operand groups of the
+//    S and dP products (without them 3 registers spill, -2% causal), none
+//    between the dV/dK products (+3% causal against one per feature block).
 
 __host__ __device__ constexpr int stat_rows(int N) { return (N + 63) / 64 * 64; }
 
@@ -125,7 +98,7 @@ struct DkdvCfg {
   static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 64;    // queries per tile (two 32-query sub-blocks)
   static constexpr int NBUF = D == 64 ? 3 : 2;
-  static constexpr int WPE = D == 64 ? ATTN_BWD_WPE64 : D == 128 ? ATTN_BWD_WPE128 : 1;
+  static constexpr int WPE = D == 64 ? 3 : 1;  // waves per SIMD
   static constexpr int TILEB = BQ * D * 2;
   static constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q | dO | D | LSE*log2e
   static constexpr size_t LDS = (size_t)NBUF * STAGEB;
@@ -279,10 +252,16 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, go + to);
     }
     if (w == 0 && lane < 32) {
-      // this head's two statistics rows from the sequence's first token on
-      // (rows past the sequence meet zero Q and dO and add nothing)
+      // this head's two statistics rows (lanes 0-15: -D, 16-31: LSE log2 e)
+      // from the slice's (or packed sequence's) first row on.  The buffer
+      // ends right after the LSE row's last row of the slice, so rows past
+      // it read LSE = 0: batched slices have zero padding there anyway, and a
+      // packed sequence must not read the next sequence's LSE, which could
+      // make P = 2^(-LSE log2 e) overflow (fp16 once LSE < -11) and 0 * inf
+      // poison dK and dV.  Their -D (the padding, or the next sequence's) is
+      // finite and meets zero Q and dO rows, so those rows add nothing.
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(stats + sb0 + (int64_t)hq * 2 * Np, (uint32_t)((2 * Np - start) * 4));
+          make_rsrc(stats + sb0 + (int64_t)hq * 2 * Np, (uint32_t)((Np + N) * 4));
       buf_load16_lds(rs, base + 2 * TILEB, soff + (uint32_t)qt * BQ * 4);
     }
   };
@@ -291,11 +270,12 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // must wait with its own count: allowing wave 0's count on the others
   // would let one load of the stage about to be read still be in flight.
   constexpr int LOADS = 2 * PW;
+  constexpr int SLOADS = 1;
   // Wait until only the newest stage's loads may be outstanding, then
   // synchronise the workgroup (w is wave-uniform).
   auto wait_stage = [&]() {
     if (w == 0)
-      wait_vm_barrier<LOADS + 1>();
+      wait_vm_barrier<LOADS + SLOADS>();
     else
       wait_vm_barrier<LOADS>();
   };
@@ -324,8 +304,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // hoisted, where registers are tight: d = 256 (K, V, dK and dV already
   // hold 384) and d = 64 at three waves per SIMD (168 each).
   constexpr int CG = D > 128 ? 2 : (Cfg::WPE >= 3 ? 2 : NQC);
-  constexpr int FENCE_C = D > 128 ? 1 : ATTN_BWD_FENCE_C64;
-  constexpr bool FENCE_A = D > 128 || ATTN_BWD_FENCE_A64;
+  constexpr bool FENCE_C = D > 128;  // a fence per feature block of the dV/dK products
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
                     f32x16& sacc, f32x16& pacc) {
     // the dP accumulator starts at -D of each row (element 4*rg+e is row
@@ -337,7 +316,6 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
     }
     sacc = f32x16{};
-    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 3) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c0 = 0; c0 < NQC; c0 += CG) {
       u32x4 qa[CG], da[CG];
@@ -351,9 +329,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         sacc = mfma32(bitcast<V8>(qa[cc]), kreg[c0 + cc], sacc);
         pacc = mfma32(bitcast<V8>(da[cc]), vreg[c0 + cc], pacc);
       }
-      if constexpr (CG < NQC && FENCE_A) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (CG < NQC) __builtin_amdgcn_sched_barrier(0);
     }
-    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 3) __builtin_amdgcn_s_setprio(0);
   };
   auto phaseV = [&](const float* lse2, int qbase, int qfirst, bool diag, const f32x16& sacc,
                     const f32x16& pacc, uint32_t (&pk)[8], uint32_t (&dsk)[8]) {
@@ -383,7 +360,6 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   };
   auto phaseC = [&](const char* qtile, const char* dotile, int qbase, const uint32_t (&pk)[8],
                     const uint32_t (&dsk)[8]) {
-    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 2) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int cp = 0; cp < 2; ++cp) {
       const V8 pb = bitcast<V8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
@@ -398,11 +374,9 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         const u32x2 b0 = lds_read_tr(qtile + rows + tro(0, mb));
         const u32x2 b1 = lds_read_tr(qtile + rows + tro(1, mb));
         dkacc[mb] = mfma32(bitcast<V8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
-        if constexpr (CG < NQC && FENCE_C == 1) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (CG < NQC && FENCE_C) __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (CG < NQC && FENCE_C == 2) __builtin_amdgcn_sched_barrier(0);
     }
-    if (ATTN_BWD_PRIO == 1 || ATTN_BWD_PRIO == 2) __builtin_amdgcn_s_setprio(0);
   };
 
   auto step = [&](auto bufc, int it) {
@@ -554,7 +528,7 @@ struct DqCfg {
   static constexpr int BR = 128;  // queries per workgroup (4 waves x 32)
   static constexpr int BC = 64;   // keys per tile
   static constexpr int NBUF = D == 64 ? 3 : 2;
-  static constexpr int WPE = D == 64 ? ATTN_DQ_WPE64 : D == 128 ? ATTN_DQ_WPE128 : 1;
+  static constexpr int WPE = D == 64 ? 3 : D == 128 ? 2 : 1;  // waves per SIMD
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
@@ -744,7 +718,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int kbk = 0; kbk < 2; ++kbk) {
         // S^T = K Q^T and dP^T - D = V dO^T - D for the tile's 32-key block kbk
         f32x16 sacc = f32x16{}, pacc = pinit;
-        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int c0 = 0; c0 < NQC; c0 += CG) {
           u32x4 ka[CG], va[CG];
@@ -759,7 +732,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             pacc = mfma32(bitcast<V8>(va[cc]), doreg[c0 + cc], pacc);
           }
         }
-        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(0);
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(__builtin_fmaf(sacc[r], c, -lse2));
@@ -777,7 +749,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
           dsk[r >> 1] = pack2<T>(pv[r] * pacc[r], pv[r + 1] * pacc[r + 1]);
         // dQ^T += K^T dS^T (per mb the same accumulation order as key block
         // by key block)
-        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -790,8 +761,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
             dqacc[mb] = mfma32(a, sb, dqacc[mb]);
           }
-        if (ATTN_DQ_PRIO) __builtin_amdgcn_s_setprio(0);
-        if constexpr (SEQ && ATTN_DQ_FENCE) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SEQ) __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (j + 1 < ntiles) {
@@ -872,21 +842,14 @@ static hipError_t pre_t(const BwdArgs& a) {
 // dK/dV groups +2% non-causal, but -3% causal N=2048 and -2% causal
 // grouped-query N=4096).  Packed variable-length slices differ in work and
 // keep the plain order.
-#ifndef ATTN_DQ_XG
-#define ATTN_DQ_XG 1
-#endif
-#ifndef ATTN_DKDV_XG
-#define ATTN_DKDV_XG 1
-#endif
 static int dq_xcd_group(const BwdArgs& a, int D, bool varlen) {
   if (varlen) return 0;
   const int64_t nsl = (int64_t)a.B * a.Hq;
   const int group = a.Hq / a.Hkv;
-  if (!ATTN_DQ_XG) return (group > 1 && nsl % 8 == 0) ? (int)(nsl / 8) : 0;
   return xcd_group(nsl, group, (int64_t)a.N * D * 4, a.causal ? kXgBudgetCausal : kXgBudget);
 }
 static int dkdv_xcd_group(const BwdArgs& a, int D, bool varlen) {
-  if (varlen || a.causal || !ATTN_DKDV_XG) return 0;
+  if (varlen || a.causal) return 0;
   return xcd_group((int64_t)a.B * a.Hkv, 1, (int64_t)(a.Hq / a.Hkv) * a.N * D * 4, kXgBudget);
 }
 

@@ -29,56 +29,15 @@
 namespace attn {
 
 
-// Tuning knobs (compile-time; the defaults are the shipped configuration).
-// d = 64 runs four waves per SIMD (121 registers) with two LDS stages (32 KiB
-// per workgroup, four workgroups per CU); three waves with three stages was
-// 3-8% slower.
-#ifndef ATTN_FWD_WPE64
-#define ATTN_FWD_WPE64 4
-#endif
-#ifndef ATTN_FWD_WPE128
-#define ATTN_FWD_WPE128 2
-#endif
-// Raised wave priority around the matrix-core products (s_setprio 1): worth
-// 4-6% on the pipelined d = 128 forward; off for the plain kernel at d = 64,
-// where four waves share a SIMD and it cost 1-3%.
-#ifndef ATTN_FWD_PRIO64
-#define ATTN_FWD_PRIO64 0
-#endif
-#ifndef ATTN_FWD_SETPRIO
-#define ATTN_FWD_SETPRIO 1
-#endif
-// Fair wave priority for the plain kernel where it runs without the
+// Fair wave priority of the plain kernel where it runs without the
 // matrix-core phase priority (d = 64), non-causal grids only: each wave's
-// priority falls with its remaining key tiles (one level per ATTN_FWD_FAIR
-// tiles, 0 = off).  Four waves of four workgroups share a SIMD; with equal
-// priority the oldest wins, so they finish staggered and the SIMD ends the
-// grid with fewer and fewer waves to hide latency.  Measured (same-box A/B):
-// non-causal B=8 H=16 N=1024 d=64 +4.7%, B=4 H=32 N=2048 +2.5%; causal grids
-// lost 1-4% (heaviest-first already orders them), so they keep equal
-// priority.
-#ifndef ATTN_FWD_FAIR
-#define ATTN_FWD_FAIR 4
-#endif
-#ifndef ATTN_FWD_NBUF64
-#define ATTN_FWD_NBUF64 2
-#endif
-#ifndef ATTN_FWD_NBUF128
-#define ATTN_FWD_NBUF128 2
-#endif
-
-#ifndef ATTN_FWD_NB64
-#define ATTN_FWD_NB64 1
-#endif
-#ifndef ATTN_FWD_NB128
-#define ATTN_FWD_NB128 1
-#endif
-#ifndef ATTN_FWD_NW64
-#define ATTN_FWD_NW64 4
-#endif
-#ifndef ATTN_FWD_NW128
-#define ATTN_FWD_NW128 4
-#endif
+// priority falls by one level per kFairTiles of its remaining key tiles.  Four
+// waves of four workgroups share a SIMD; with equal priority the oldest wins,
+// so they finish staggered and the SIMD ends the grid with fewer and fewer
+// waves to hide latency.  Measured (same-box A/B): non-causal B=8 H=16 N=1024
+// d=64 +4.7%, B=4 H=32 N=2048 +2.5%; causal grids lost 1-4% (heaviest-first
+// already orders them), so they keep equal priority.
+constexpr int kFairTiles = 4;
 
 // Work map of the forward grids (nqb query blocks x BH (batch, head) slices):
 // the heaviest query blocks first under the causal mask; the heads of one
@@ -98,14 +57,20 @@ constexpr int by_dim(int v64, int v128, int v256) {
   return D == 64 ? v64 : D == 128 ? v128 : v256;
 }
 
+// Plain (not software-pipelined) kernel, used at d = 64 and d = 256.
+//   d = 64: four waves per SIMD (121 registers) with two LDS stages (32 KiB
+//     per workgroup, four workgroups per CU); three waves with three stages
+//     was 3-8% slower, and two 32-row blocks per wave (two waves per
+//     workgroup) 25-30% slower.
+//   d = 256: one wave per SIMD (256 VGPRs + 256 AGPRs), two stages (128 KiB).
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = by_dim<D>(ATTN_FWD_NW64, ATTN_FWD_NW128, 4);  // waves per workgroup
-  static constexpr int NB = by_dim<D>(ATTN_FWD_NB64, ATTN_FWD_NB128, 1);  // 32-row blocks per wave
+  static constexpr int NW = 4;             // waves per workgroup
+  static constexpr int NB = 1;             // 32-row blocks per wave
   static constexpr int BR = 32 * NB * NW;  // query rows per workgroup
-  static constexpr int BC = 64;   // keys per tile
-  static constexpr int NBUF = by_dim<D>(ATTN_FWD_NBUF64, ATTN_FWD_NBUF128, 2);  // LDS stages
-  static constexpr int WPE = by_dim<D>(ATTN_FWD_WPE64, ATTN_FWD_WPE128, 1);     // waves per SIMD
+  static constexpr int BC = 64;            // keys per tile
+  static constexpr int NBUF = 2;           // LDS stages
+  static constexpr int WPE = by_dim<D>(4, 2, 1);  // waves per SIMD
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;
 };
@@ -128,7 +93,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   static_assert(PW * NW * 1024 == TILEB, "tile pieces");
   constexpr int NQC = D / 16;  // k-chunks of the S contraction
   constexpr int NMB = D / 32;  // 32-row blocks of O^T
-  constexpr bool PRIO = D == 64 ? ATTN_FWD_PRIO64 : ATTN_FWD_SETPRIO;
+  // Raised wave priority around the matrix-core products (s_setprio 1) at
+  // d = 256; not at d = 64, where four waves share a SIMD and it cost 1-3%.
+  constexpr bool PRIO = D != 64;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];  // [NBUF][K tile | V tile]
 
@@ -292,13 +259,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     constexpr int BUF = decltype(bufc)::value;
     const char* kt = smem + BUF * 2 * TILEB;
     const char* vt = kt + TILEB;
-    if constexpr (!PRIO && !CAUSAL && ATTN_FWD_FAIR > 0) {
+    if constexpr (!PRIO && !CAUSAL) {
       const int rem = ntiles - j;  // wave-uniform
-      if (rem > 3 * ATTN_FWD_FAIR)
+      if (rem > 3 * kFairTiles)
         __builtin_amdgcn_s_setprio(3);
-      else if (rem > 2 * ATTN_FWD_FAIR)
+      else if (rem > 2 * kFairTiles)
         __builtin_amdgcn_s_setprio(2);
-      else if (rem > ATTN_FWD_FAIR)
+      else if (rem > kFairTiles)
         __builtin_amdgcn_s_setprio(1);
       else
         __builtin_amdgcn_s_setprio(0);
@@ -460,56 +427,23 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 // LDS stages: K(j+2) and V(j+1) are loaded during tile j (K(j) was consumed
 // one tile earlier, by the look-ahead score product), so one barrier per tile
 // still suffices.  Same arithmetic and results as fwd_mfma_kernel.
-#ifndef ATTN_FWD_PIPE64
-#define ATTN_FWD_PIPE64 0
-#endif
-#ifndef ATTN_FWD_PIPE128
-#define ATTN_FWD_PIPE128 1
-#endif
-#ifndef ATTN_PIPE_WPE64
-#define ATTN_PIPE_WPE64 3
-#endif
-#ifndef ATTN_PIPE_WPE128
-#define ATTN_PIPE_WPE128 2
-#endif
-#ifndef ATTN_PIPE_SCHED
-#define ATTN_PIPE_SCHED 1
-#endif
-#ifndef ATTN_PIPE_VPM64
-#define ATTN_PIPE_VPM64 14  // VALU instructions placed after each look-ahead MFMA
-#endif
-#ifndef ATTN_PIPE_VPM128
-#define ATTN_PIPE_VPM128 12
-#endif
-#ifndef ATTN_FWD_PIPE256
-#define ATTN_FWD_PIPE256 0
-#endif
-#ifndef ATTN_PIPE_VPM256
-#define ATTN_PIPE_VPM256 6
-#endif
-
-#ifndef ATTN_PIPE_LA
-#define ATTN_PIPE_LA 4  // K-fragment LDS reads issued ahead of their MFMA
-#endif
-// Wave priorities (s_setprio) of the pipelined kernel: during the P V
-// products, and during the look-ahead scores interleaved with the softmax.
-#ifndef ATTN_PIPE_PRIO_PV
-#define ATTN_PIPE_PRIO_PV 1
-#endif
-#ifndef ATTN_PIPE_PRIO_S
-#define ATTN_PIPE_PRIO_S 0
-#endif
-#ifndef ATTN_PIPE_NW
-#define ATTN_PIPE_NW 4
-#endif
-
+// The pipelined kernel runs at d = 128 only.  At d = 64 the plain kernel at
+// four waves per SIMD stays ahead (the pipelined one needs more than the 168
+// registers of three waves), and at d = 256 the pipelined one spills more.
+// Scheduling (same-box A/B each): 12 VALU instructions placed after each
+// look-ahead MFMA (10 and 16 measured the same), K-fragment LDS reads 4 MFMAs
+// ahead (2: the same; 6 spills and loses 1-10%), raised priority (1) during
+// the P V products (+4-6%; 2 or 3 the same) and none during the look-ahead
+// scores (raising it there changed nothing); 8 waves per workgroup lost 4%.
 template <int D>
 struct PipeCfg {
-  static constexpr int NW = ATTN_PIPE_NW;  // waves per workgroup (32 query rows each)
+  static_assert(D == 128, "the pipelined forward is tuned for d = 128");
+  static constexpr int NW = 4;   // waves per workgroup (32 query rows each)
   static constexpr int BR = 32 * NW;
   static constexpr int BC = 64;
-  static constexpr int WPE = by_dim<D>(ATTN_PIPE_WPE64, ATTN_PIPE_WPE128, 1);
-  static constexpr int VPM = by_dim<D>(ATTN_PIPE_VPM64, ATTN_PIPE_VPM128, ATTN_PIPE_VPM256);
+  static constexpr int WPE = 2;  // waves per SIMD (244 registers)
+  static constexpr int VPM = 12; // VALU instructions after each look-ahead MFMA
+  static constexpr int LA = 4;   // K-fragment LDS reads issued ahead of their MFMA
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)4 * TILEB;  // K[2] | V[2]
 };
@@ -700,13 +634,13 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
       float tsum;
       if (ahead) {
         __builtin_amdgcn_sched_barrier(0);
-        if (ATTN_PIPE_PRIO_S) __builtin_amdgcn_s_setprio(ATTN_PIPE_PRIO_S);
         scores(kstage(BUF ^ 1), sn);
         tsum = softmax_exp(sc, ms, pk);
-        if (ATTN_PIPE_SCHED) {
+        {
           // K fragments stream a few MFMAs ahead of their use; the softmax
-          // of tile j fills the matrix-core issue gaps.
-          constexpr int LA = ATTN_PIPE_LA;  // LDS reads ahead
+          // of tile j fills the matrix-core issue gaps.  (Without these
+          // scheduling groups the same code is slower than the plain kernel.)
+          constexpr int LA = Cfg::LA;
           __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
 #pragma unroll
           for (int i = 0; i < 2 * NQC; ++i) {
@@ -716,7 +650,6 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (ATTN_PIPE_PRIO_S) __builtin_amdgcn_s_setprio(0);
       } else {
         tsum = softmax_exp(sc, ms, pk);
       }
@@ -740,7 +673,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
         }
       }
       lsum += tsum;
-      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(ATTN_PIPE_PRIO_PV);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -755,7 +688,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
                 u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
             oacc[mb] = mfma32(a, bp, oacc[mb]);
           }
-      if (ATTN_FWD_SETPRIO) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
     }
     // V(j+1) and K(j+2) must have landed, and every wave be done with
     // K(j+1) and V(j), before their stages are refilled.
@@ -927,8 +860,7 @@ static hipError_t launch_pipe(const FwdArgs& a) {
 template <typename T, int D, bool CAUSAL, int MODE>
 static hipError_t launch_mfma(const FwdArgs& a) {
   constexpr bool SPARSE = MODE == kFwdSparse;
-  if constexpr ((D == 64 && ATTN_FWD_PIPE64) || (D == 128 && ATTN_FWD_PIPE128) ||
-                (D == 256 && ATTN_FWD_PIPE256)) {
+  if constexpr (D == 128) {
     return launch_pipe<T, D, CAUSAL, MODE>(a);
   } else {
     static_assert(!SPARSE || (FwdCfg<D>::BR == kSparseBlockQ && FwdCfg<D>::BC == kSparseBlockK),

@@ -120,7 +120,6 @@ hipError_t launch_fwd(const FwdArgs& a);
 constexpr int kSparseBlockQ = 128, kSparseBlockK = 64;
 size_t sparse_workspace_bytes(int Hq, int N, int mask_heads);
 hipError_t launch_fwd_sparse(const FwdArgs& a, const unsigned char* mask, void* workspace);
-// Bytes of the backward row-statistics workspace.
 // Slice group xg of the XCD-aware work order (xcd_item) for nsl slices that
 // each stream `bytes` of data through L2, shared by `share` adjacent slices:
 // the largest divisor of nsl/8 whose data fit `budget`.  When one group
@@ -146,6 +145,7 @@ inline int xcd_group(int64_t nsl, int share, int64_t bytes, int64_t budget) {
 // blocks of many slices in flight at once, so they take larger groups.
 constexpr int64_t kXgBudget = 2 << 20, kXgBudgetCausal = 8 << 20;
 
+// Bytes of the backward row-statistics workspace.
 size_t bwd_stats_bytes(int B, int Hq, int N);
 // Query-head splits of the dK/dV stage for a dense problem (1 when the grid
 // of key blocks x kv heads already fills the device), and the bytes of fp32

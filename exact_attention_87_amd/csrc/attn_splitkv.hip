@@ -30,27 +30,18 @@
 
 namespace attn {
 
-// Tuning knobs (compile-time; the defaults are the shipped configuration).
-#ifndef ATTN_SPLIT_NBUF64
-#define ATTN_SPLIT_NBUF64 2
-#endif
-#ifndef ATTN_SPLIT_NBUF128
-#define ATTN_SPLIT_NBUF128 2
-#endif
-#ifndef ATTN_SPLIT_WPE64
-#define ATTN_SPLIT_WPE64 3
-#endif
-#ifndef ATTN_SPLIT_WPE128
-#define ATTN_SPLIT_WPE128 2
-#endif
-
+// Two LDS stages at the highest occupancy the registers allow (3 waves per
+// SIMD at d = 64, 2 at d = 128, 1 at d = 256): on decode, 2 stages at 2
+// workgroups per CU (d = 128) beat 3 or 4 stages at 1 workgroup per CU by
+// 5-10%; more resident workgroups, not deeper prefetch, keep more K/V bytes
+// in flight.
 template <int D>
 struct SplitCfg {
   static constexpr int NW = 4;
   static constexpr int BR = 128;  // packed query rows per workgroup (32 per wave)
   static constexpr int BC = 64;   // keys per tile
-  static constexpr int NBUF = D == 64 ? ATTN_SPLIT_NBUF64 : D == 128 ? ATTN_SPLIT_NBUF128 : 2;
-  static constexpr int WPE = D == 64 ? ATTN_SPLIT_WPE64 : D == 128 ? ATTN_SPLIT_WPE128 : 1;
+  static constexpr int NBUF = 2;                           // LDS stages
+  static constexpr int WPE = D == 64 ? 3 : D == 128 ? 2 : 1;  // waves per SIMD
   static_assert(NBUF >= 2 && NBUF <= 4, "stages");
   static constexpr int TILEB = BC * D * 2;
   static constexpr size_t LDS = (size_t)NBUF * 2 * TILEB;

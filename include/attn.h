@@ -36,8 +36,16 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the default stream).  The call returns once the kernels are launched;
  *    it never synchronises.
- *  - Sizes: N <= 2^22 and B * Hq <= 2^24 (larger requests return
- *    ATTN_ERR_UNSUPPORTED).
+ *  - Sizes: N <= 2^22 and B * Hq <= 2^24, and every launch must fit one
+ *    dispatch of fewer than 2^32 work-items: B * Hq * (N rounded up to 128)
+ *    * max(8, d / 8) < 2^32 (larger requests return ATTN_ERR_UNSUPPORTED).
+ *  - Value range (16-bit paths): the online softmax moves its running row
+ *    maximum lazily, only once a row's scores exceed it by more than tau
+ *    (base 2; tau = 30 for bf16, 15 for fp16), so probabilities carried in
+ *    the fp32 accumulators are at most 2^tau instead of 1.  bf16 outputs are
+ *    therefore within range as long as (number of visible keys) * max|V| <
+ *    2^98 (about 3e29; a plain online softmax allows up to 3.4e38).  fp16
+ *    inputs cannot reach the limit (2^15 * 65504 * 2^22 < 2^128).
  *  - B == 0 or N == 0 is an empty problem: nothing is launched and ATTN_OK
  *    is returned (pointers may then be NULL).
  *  - Arguments are validated on the host before any HIP call.  On error no

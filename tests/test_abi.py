@@ -1,6 +1,13 @@
 """The C ABI library on the host: it loads, exports every entry point the
-header declares, and rejects bad arguments before touching the GPU (CPU only;
-no call here launches a kernel)."""
+header declares, and rejects bad arguments before touching the GPU.
+
+The arguments are fake device addresses.  Calls that are meant to fail
+validation never reach the device on any host.  Calls that are meant to pass
+validation stop at the device check only where no GPU is visible; on a host
+with a GPU they would launch kernels on unmapped addresses.  Every test that
+makes such a call is marked ``reaches_device`` and is skipped when a device
+node or a torch device is visible, so this module is safe to collect on a GPU
+host as well."""
 import os
 import re
 import subprocess
@@ -11,6 +18,49 @@ import exact_attention_87_amd as ea
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _gpu_visible() -> bool:
+    # /dev/kfd is the ROCm compute device node; counting torch devices does
+    # not initialise the HIP runtime
+    if os.path.exists("/dev/kfd"):
+        return True
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+GPU_VISIBLE = _gpu_visible()
+# A test that makes at least one call expected to pass validation (and, with
+# no GPU, to stop at the device check with ATTN_ERR_HIP).
+reaches_device = pytest.mark.skipif(
+    GPU_VISIBLE, reason="passes fake addresses through validation; with a GPU visible the call "
+                        "would launch kernels on them")
+
+@pytest.fixture(autouse=True)
+def _device_reach_is_marked(request, monkeypatch):
+    """Keeps the marker honest: on a host without a GPU, a test not marked
+    ``reaches_device`` fails if any of its calls got past validation."""
+    if GPU_VISIBLE or request.node.get_closest_marker("skipif") is not None:
+        yield
+        return
+    reached = []
+    for name in [n for n in dir(ea) if n.startswith("attn_") and callable(getattr(ea, n))]:
+        fn = getattr(ea, name)
+
+        def wrap(*a, _fn=fn, _name=name):
+            r = _fn(*a)
+            if isinstance(r, int) and r in (ea.ATTN_ERR_HIP, ea.ATTN_ERR_UNSUPPORTED_DEVICE):
+                reached.append(_name)
+            return r
+
+        monkeypatch.setattr(ea, name, wrap)
+    yield
+    assert not reached, f"unmarked test reached the device check via {sorted(set(reached))}"
+
 
 # Fake, 16-byte aligned, non-overlapping addresses: validation must fail
 # before anything dereferences them.
@@ -25,7 +75,8 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
-                                  "attn_bwd_dq_stats", "attn_bwd_preprocess", "attn_bwd_strided", "attn_bwd_varlen",
+                                  "attn_bwd_dq_stats", "attn_bwd_preprocess",
+                                  "attn_bwd_strided", "attn_bwd_varlen",
                                   "attn_bwd_varlen_strided",
                                   "attn_bwd_workspace_bytes", "attn_fwd",
                                   "attn_fwd_blocksparse", "attn_fwd_blocksparse_strided",
@@ -91,6 +142,7 @@ def test_fwd_unsupported_head_dim(d):
     assert fwd(d=d) == ea.ATTN_ERR_UNSUPPORTED
 
 
+@reaches_device
 def test_d256_is_16_bit_only():
     # accepted by the 16-bit paths (validation passes; no GPU here)
     for dt in (ea.ATTN_BF16, ea.ATTN_F16):
@@ -300,6 +352,7 @@ def test_blocksparse_rejects_bad_arguments(kw):
     assert sparse(**kw) == ea.ATTN_ERR_INVALID_ARG
 
 
+@reaches_device
 def test_blocksparse_unsupported_and_empty():
     assert sparse(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
     assert sparse(d=96) == ea.ATTN_ERR_UNSUPPORTED
@@ -357,6 +410,7 @@ def test_varlen_unsupported_and_empty():
     assert varlen(maxlen=0, **none) == ea.ATTN_OK
 
 
+@reaches_device
 def test_fp16_is_accepted_where_bf16_is():
     assert ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_F16) == \
         ea.attn_bwd_workspace_bytes(2, 4, 2, 100, 64, ea.ATTN_BF16)
@@ -382,6 +436,7 @@ def strided(strides, **kw):
 BNHD = [100 * 4 * 64, 64, 4 * 64, 100 * 2 * 64, 64, 2 * 64, 100 * 4 * 64, 64, 4 * 64]
 
 
+@reaches_device
 def test_strided_validation():
     ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
     assert strided(BNHD) not in ok  # passes validation, stops at the device check
@@ -400,6 +455,7 @@ def test_strided_validation():
                                      None) == ea.ATTN_ERR_INVALID_ARG  # no strides
 
 
+@reaches_device
 def test_strided_backward_validation():
     ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
 
@@ -424,6 +480,7 @@ def test_strided_backward_validation():
     assert sb(b256, d=256) not in ok
 
 
+@reaches_device
 def test_varlen_backward_validation():
     ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
 
@@ -447,6 +504,7 @@ def test_varlen_backward_validation():
     assert vb(nseq=0, **none) == ea.ATTN_OK
 
 
+@reaches_device
 def test_varlen_strided_validation():
     ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
     T, H, Hkv, d = 1000, 4, 2, 64
@@ -489,6 +547,7 @@ def test_varlen_strided_validation():
     assert fs(tm, nseq=0, q=None, k=None, v=None, o=None, lse=None, cu=None) == ea.ATTN_OK
 
 
+@reaches_device
 def test_splitkv_strided_validation():
     ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
     B, Hq, Hkv, Nq, Nk, d = 2, 8, 2, 3, 1000, 128
@@ -518,6 +577,7 @@ def test_splitkv_strided_validation():
     assert ss(tm, B=0, q=None, k=None, v=None, o=None, lse=None, ws=None) == ea.ATTN_OK
 
 
+@reaches_device
 def test_blocksparse_strided_validation():
     ok = (ea.ATTN_ERR_INVALID_ARG, ea.ATTN_ERR_UNSUPPORTED)
     B, Hq, Hkv, N, d = 2, 4, 2, 300, 64
@@ -546,7 +606,45 @@ def test_blocksparse_strided_validation():
 
 
 def test_grid_limit_is_rejected():
-    # (1 << 24) slices of 2^12 rows: 2^31 workgroups of 32 rows; valid sizes
-    # individually, too many workgroups together
+    # A dispatch counts its work-items (workgroups x threads) in 32 bits.  The
+    # batched checks allow up to max(8, d/8) threads per query row padded to
+    # 128 rows: at d = 64, B*Hq*round_up(N, 128) < 2^29.
     assert fwd(B=1 << 20, Hq=16, Hkv=16, N=1 << 12) == ea.ATTN_ERR_UNSUPPORTED
-    assert fwd(B=1 << 20, Hq=16, Hkv=16, N=(1 << 12) - 32) not in (ea.ATTN_ERR_UNSUPPORTED,)
+    assert fwd(B=1 << 12, Hq=16, Hkv=16, N=8192) == ea.ATTN_ERR_UNSUPPORTED
+    assert fwd(B=1 << 12, Hq=16, Hkv=16, N=8192 - 127) == ea.ATTN_ERR_UNSUPPORTED  # pads to 8192
+    # one row block fewer fits: the shape passes, and the fake buffers (each
+    # tens of GB) then overlap, which validation rejects
+    assert fwd(B=1 << 12, Hq=16, Hkv=16, N=8192 - 128) == ea.ATTN_ERR_INVALID_ARG
+    # d = 256: 32 threads per row (the statistics kernel of the backward)
+    assert bwd(B=1 << 10, Hq=16, Hkv=16, N=8192, d=256) == ea.ATTN_ERR_UNSUPPORTED
+    assert bwd(B=1 << 10, Hq=16, Hkv=16, N=8192 - 128, d=256) == ea.ATTN_ERR_INVALID_ARG
+
+
+def vbwd(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, cu=CU, nseq=3,
+             maxlen=500, Hq=4, Hkv=2, T=1000, d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16)
+    a.update(kw)
+    return ea.attn_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                              a["dk"], a["dv"], a["ws"], a["cu"], a["nseq"], a["maxlen"], a["Hq"],
+                              a["Hkv"], a["T"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+def test_varlen_grid_limit_is_rejected():
+    # The packed grids are (sequence, head, 128-row block of the longest
+    # sequence) with two threads per padded row; the header allows any
+    # max_seqlen up to T, so the product can pass 2^32 work-items (and 2^32
+    # workgroups) with every size individually valid.
+    for call in (varlen, vbwd):
+        # 1024 documents, 32 heads, longest 2^18 tokens: 2^26 workgroups, 2^34 work-items
+        assert call(nseq=1024, Hq=32, Hkv=8, maxlen=1 << 18, T=1 << 18) == ea.ATTN_ERR_UNSUPPORTED
+        # 2^14 + 1 documents, 64 heads, longest 2^20: more than 2^32 workgroups
+        assert call(nseq=(1 << 14) + 1, Hq=64, Hkv=8, maxlen=1 << 20,
+                    T=1 << 20) == ea.ATTN_ERR_UNSUPPORTED
+        # 2^23 padded rows x 2 threads fit; the fake buffers then overlap
+        assert call(nseq=512, Hq=16, Hkv=8, maxlen=1024, T=1 << 18) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_splitkv_grid_limit_is_rejected():
+    # the merge runs up to 64 threads per output row: B*Hq*Nq*64 < 2^32
+    assert split(B=1 << 12, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 10, Nk=64) == ea.ATTN_ERR_UNSUPPORTED
+

@@ -202,3 +202,80 @@ def test_full_size_workload_sampled_rows(oracle_mod, wid):
     l_s = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
     ro, rl = oracle_mod.fwd_rows(q, k, v, rows, causal=w.causal)
     check_bf16(o_s, l_s, ro, rl, w.name)
+
+
+def test_workload2_whole_output(oracle_mod):
+    """Workload 2 (B=8 H=16 N=1024 d=64, non-causal) compared element by
+    element over the whole output, in the launch the benchmark times."""
+    w = attn_inputs.WORKLOADS[2]
+    q, k, v = attn_inputs.make_workload(w, with_dout=False)
+    o, lse = run(q, k, v, w.causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=w.causal)
+    check_bf16(o, lse, ro, rl, w.name + " (whole output)")
+
+
+# ---------------------------------------------------------------- non-finite inputs
+def test_non_finite_inputs_reach_only_the_rows_that_use_them(oracle_mod):
+    """A NaN or Inf in an input makes the outputs that use it non-finite, and
+    every output that does not use it matches the oracle run on the same
+    inputs, with one documented exception: the P V product multiplies a
+    masked key's probability, exactly 0, with its value row, so a non-finite
+    V row j also reaches (as 0 x NaN) the rows of its own 64-key tile that the
+    causal mask hides it from, rows [64 floor(j/64), j).
+      Q row (b=0, h=1, i=17) with a NaN: that row's O and LSE.
+      Q row (b=1, h=3, i=250) with +Inf: scores of +-Inf, so the row's max is
+        +Inf and its weights Inf - Inf: that row's O and LSE.
+      K row (b=1, kv head 1, j=50) with a NaN: under the causal mask rows
+        i >= 50 of query heads 2 and 3 of batch 1 (O and LSE); the rows of its
+        tile before it are masked to -inf before the exponential and stay
+        finite.
+      V row (b=1, kv head 0, j=200) with a NaN in feature 3: column 3 of O for
+        rows i >= 200 of query heads 0 and 1 of batch 1 (LSE stays finite);
+        rows 192..199 of column 3 may be NaN too (same key tile)."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 300, 64
+    q, k, v = attn_inputs.make(B, Hq, Hkv, N, d, "bf16", seed=77)
+    q[0, 1, 17, 5] = float("nan")
+    q[1, 3, 250, 0] = float("inf")
+    k[1, 1, 50, 7] = float("nan")
+    v[1, 0, 200, 3] = float("nan")
+    o, lse = run(q, k, v, True)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=True)
+    bad_o = np.zeros(o.shape, dtype=bool)
+    bad_l = np.zeros(lse.shape, dtype=bool)
+    bad_o[0, 1, 17] = bad_l[0, 1, 17] = True
+    bad_o[1, 3, 250] = bad_l[1, 3, 250] = True
+    bad_o[1, 2:4, 50:] = bad_l[1, 2:4, 50:] = True
+    bad_o[1, 0:2, 200:, 3] = True
+    tile_mates = np.zeros(o.shape, dtype=bool)  # may be NaN through 0 x NaN
+    tile_mates[1, 0:2, 192:200, 3] = True
+    assert not np.isfinite(o[bad_o]).any(), "an output that uses a non-finite input is finite"
+    assert not np.isfinite(lse[bad_l]).any(), "an LSE that uses a non-finite input is finite"
+    # the oracle agrees on which outputs use a non-finite input
+    assert np.array_equal(~np.isfinite(ro), bad_o) and np.array_equal(~np.isfinite(rl), bad_l)
+    good_o, good_l = ~(bad_o | tile_mates), ~bad_l
+    assert np.isfinite(o[good_o]).all() and np.isfinite(lse[good_l]).all()
+    err = np.abs(o[good_o] - ro[good_o])
+    assert np.all(err <= 2e-2 + 1e-2 * np.abs(ro[good_o])), err.max()
+    assert np.abs(lse[good_l] - rl[good_l]).max() <= 1e-3
+    # tile-mates that stayed finite are right
+    fin = tile_mates & np.isfinite(o)
+    assert np.all(np.abs(o[fin] - ro[fin]) <= 2e-2 + 1e-2 * np.abs(ro[fin]))
+
+
+# ---------------------------------------------------------------- value range
+@pytest.mark.parametrize("e", [60, 80])
+def test_large_values_scale_exactly(e):
+    """V scaled by 2^e gives O scaled by 2^e bit for bit (every step scales
+    exactly), up to the range the header states for bf16: with the lazy
+    rescale the accumulators carry at most 2^30 * (visible keys) * max|V|,
+    here 2^30 * 2^10 * 2^(e+3) <= 2^123 < 2^128."""
+    dev = gpu()
+    q, k, v = attn_inputs.make(1, 4, 2, 1024, 128, "bf16", seed=78)
+    q = q * 8  # extreme logits as in the grouped-query workload: rescales happen too
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    for causal in (False, True):
+        o1, l1 = ea.fwd(qg, kg, vg, causal=causal)
+        o2, l2 = ea.fwd(qg, kg, vg * 2.0 ** e, causal=causal)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(o2).all())
+        assert torch.equal(o2, o1 * 2.0 ** e) and torch.equal(l1, l2)

@@ -202,6 +202,33 @@ def test_backward_deterministic_and_fp16(oracle_mod):
         grad_ok(name, gg, r)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_fp16_next_sequence_with_very_negative_lse(oracle_mod, d):
+    # The dK/dV stage reads statistics per 64-row query tile; the last tile of
+    # a sequence reaches past its end.  Here the second document's first token
+    # sees only itself with score s_00 = -20, so its LSE is -20: read as the
+    # statistic of a padding row of the first document, P = e^20 would
+    # overflow fp16 and 0 * inf would turn that kv head's dK/dV into NaN.
+    dev = gpu()
+    lengths = [100, 40]
+    q, k, v, cu = attn_inputs.make_varlen(4, 2, lengths, d, seed=23, dtype="fp16")
+    scale = 1.0 / d ** 0.5
+    t0 = lengths[0]
+    for h in range(4):
+        kk = k[h // 2, t0].float()
+        q[h, t0] = (kk * (-20.0 / (scale * float(kk @ kk)))).to(q.dtype)
+    g = torch.Generator().manual_seed(8)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    qg, kg, vg, dog, cug = (t.to(dev) for t in (q, k, v, do, cu))
+    o, lse = ea.fwd_varlen(qg, kg, vg, cug, max(lengths), causal=True)
+    dq, dk, dv = ea.bwd_varlen(qg, kg, vg, o, lse, dog, cug, max(lengths), causal=True)
+    torch.cuda.synchronize()
+    assert float(lse[0, t0]) < -19.0  # the planted statistic is there
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q, k, v, do, cu, True)
+    for name, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        grad_ok(f"{name} d={d}", gg, r)
+
+
 def test_backward_full_size_documents_sampled_heads(oracle_mod):
     w = attn_inputs.VARLEN_WORKLOADS["docs"]
     lengths = attn_inputs.varlen_lengths(w)
