@@ -59,6 +59,8 @@ def lib():
         L.attn_bwd_workspace_bytes.restype = sz
         L.attn_bwd.argtypes = [vp] * 10 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd.restype = ci
+        L.attn_bwd_noalloc.argtypes = [vp] * 9 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
+        L.attn_bwd_noalloc.restype = ci
         L.attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
         L.attn_bwd_preprocess.restype = ci
         L.attn_bwd_dkdv.argtypes = [vp] * 7 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
@@ -120,6 +122,16 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, cau
              dtype, stream) -> int:
     return int(lib().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d,
                               int(causal), float(scale), int(dtype), stream))
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, dtype,
+                     stream) -> int:
+    return int(lib().attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d,
+                                      int(causal), float(scale), int(dtype), stream))
+
+
+# Bytes of the static device scratch attn_bwd_noalloc uses (ATTN_NOALLOC_SCRATCH_BYTES).
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def attn_bwd_preprocess(o, dout, lse, stats, B, Hq, N, d, dtype, stream) -> int:

@@ -219,6 +219,8 @@ attn_status bwd_launch(attn::BwdArgs* a, const void* q, const void* k, const voi
 }
 }  // namespace
 
+static_assert(ATTN_NOALLOC_SCRATCH_BYTES == attn::kNoallocScratchBytes,
+              "header scratch size is the library's");
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -239,6 +241,28 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   return bwd_launch(&a, q, k, v, o, lse, dout, dq, dk, dv, workspace);
 }
 
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                             attn_dtype dtype, void* stream) {
+  const int dt = as_int(dtype);  // any int a C caller passed
+  attn::BwdArgs a;
+  attn_status st = bwd_common(B, Hq, Hkv, N, d, causal, scale, dt, stream, &a);
+  if (st != ATTN_OK) return st;
+  if (a.N == 0) return ATTN_OK;  // empty problem
+  const size_t wbytes = bwd_workspace_bytes(B, Hq, Hkv, N, d, dt);
+  if (wbytes > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_ERR_UNSUPPORTED;
+  const Sizes z = sizes(B, Hq, Hkv, N, d);
+  st = check_buffers({{q, z.q}, {k, z.kv}, {v, z.kv}, {o, z.q}, {lse, z.l}, {dout, z.q}},
+                     {{dq, z.q}, {dk, z.kv}, {dv, z.kv}});
+  if (st != ATTN_OK) return st;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  void* scratch = nullptr;
+  if (attn::noalloc_scratch(&scratch) != hipSuccess) return ATTN_ERR_HIP;
+  // The static scratch is a different allocation from every caller buffer.
+  return bwd_launch(&a, q, k, v, o, lse, dout, dq, dk, dv, scratch);
+}
 
 attn_status attn_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o,
                               const float* lse, const void* dout, float* stats, void* dq, int B,

@@ -147,6 +147,11 @@ constexpr int64_t kXgBudget = 2 << 20, kXgBudgetCausal = 8 << 20;
 
 // Bytes of the backward row-statistics workspace.
 size_t bwd_stats_bytes(int B, int Hq, int N);
+// Scratch of the entry point that allocates nothing: a static device array of
+// this many bytes per device (attn_noalloc.hip), and its device address on the
+// current device (looked up on first use, then cached).
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
 // Query-head splits of the dK/dV stage for a dense problem (1 when the grid
 // of key blocks x kv heads already fills the device), and the bytes of fp32
 // partial sums they need (0 for one split).

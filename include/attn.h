@@ -126,6 +126,31 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      float scale, attn_dtype dtype, void* stream);
 
 /*
+ * attn_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (without `workspace`), validation and results as attn_bwd, bit for
+ * bit: the same kernels with the same launch plan, the workspace placed in a
+ * scratch array of ATTN_NOALLOC_SCRATCH_BYTES that the library keeps in
+ * static device memory on every device it runs on until the process ends
+ * (its address is looked up on the first call on each device).  Nothing is
+ * allocated or freed.
+ *   - Problems whose attn_bwd_workspace_bytes(...) exceeds
+ *     ATTN_NOALLOC_SCRATCH_BYTES return ATTN_ERR_UNSUPPORTED (for example
+ *     B * Hq * (N rounded up to 64) > 4M rows, or a grouped-query split whose
+ *     partial sums do not fit).
+ *   - Every call on a device shares that device's scratch.  Calls whose work
+ *     overlaps in time on one device race on it and give wrong results:
+ *     issue them on one stream, or order them with events.  The scratch keeps
+ *     the last call's contents; no call depends on them (each reads only what
+ *     it wrote first).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                             attn_dtype dtype, void* stream);
+
+/*
  * The backward as three separate stages on one stream, exposed so a caller
  * can schedule or time them separately; calling them in this order with the
  * same arguments gives exactly attn_bwd's results (bit for bit).  attn_bwd

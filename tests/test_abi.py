@@ -75,7 +75,7 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["attn_abi_version", "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq",
-                                  "attn_bwd_dq_stats", "attn_bwd_preprocess",
+                                  "attn_bwd_dq_stats", "attn_bwd_noalloc", "attn_bwd_preprocess",
                                   "attn_bwd_strided", "attn_bwd_varlen",
                                   "attn_bwd_varlen_strided",
                                   "attn_bwd_workspace_bytes", "attn_fwd",
@@ -648,3 +648,50 @@ def test_splitkv_grid_limit_is_rejected():
     # the merge runs up to 64 threads per output row: B*Hq*Nq*64 < 2^32
     assert split(B=1 << 12, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 10, Nk=64) == ea.ATTN_ERR_UNSUPPORTED
 
+
+# ---------------------------------------------------------------- no-allocation backward
+def noalloc(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, B=2, Hq=4, Hkv=2, N=100,
+             d=64, causal=1, scale=0.125, dtype=ea.ATTN_BF16)
+    a.update(kw)
+    return ea.attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                               a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"],
+                               a["causal"], a["scale"], a["dtype"], None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == ea.ATTN_NOALLOC_SCRATCH_BYTES
+
+
+NOALLOC_INVALID = [dict(q=None), dict(dout=None), dict(dq=None), dict(dk=DK + 8), dict(dq=DO),
+                   dict(dk=DV), dict(dv=DK + 1024), dict(Hq=3, Hkv=2), dict(causal=5),
+                   dict(scale=float("nan"))]
+
+
+@pytest.mark.parametrize("kw", NOALLOC_INVALID, ids=[str(k) for k in NOALLOC_INVALID])
+def test_noalloc_rejects_bad_arguments(kw):
+    assert noalloc(**kw) == ea.ATTN_ERR_INVALID_ARG
+
+
+def test_noalloc_sizes():
+    # empty problems need no pointers
+    none = dict(q=None, k=None, v=None, o=None, lse=None, dout=None, dq=None, dk=None, dv=None)
+    assert noalloc(B=0, **none) == ea.ATTN_OK
+    assert noalloc(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    # the workspace attn_bwd would need must fit the static scratch (32 MiB):
+    # statistics of B*Hq*Np rows at 8 bytes each, so 4M rows fit exactly ...
+    cap = ea.ATTN_NOALLOC_SCRATCH_BYTES
+    assert ea.attn_bwd_workspace_bytes(64, 16, 16, 4096, 64, ea.ATTN_BF16) == cap
+    assert noalloc(B=64, Hq=16, Hkv=16, N=4096 + 1) == ea.ATTN_ERR_UNSUPPORTED
+    # ... and a grouped-query split whose partial sums do not fit is refused
+    # (B=1 Hq=32 Hkv=8 N=2048 d=128 splits 4 ways: 64.5 MiB of workspace)
+    assert ea.attn_bwd_workspace_bytes(1, 32, 8, 2048, 128, ea.ATTN_BF16) > cap
+    assert noalloc(B=1, Hq=32, Hkv=8, N=2048, d=128) == ea.ATTN_ERR_UNSUPPORTED
+
+
+@reaches_device
+def test_noalloc_passes_validation():
+    assert noalloc() == ea.ATTN_ERR_HIP  # no GPU here: stops at the device check
+    assert noalloc(B=64, Hq=16, Hkv=16, N=4096) == ea.ATTN_ERR_INVALID_ARG  # fake buffers overlap
