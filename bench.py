@@ -131,22 +131,31 @@ class ClockSampler:
             amdsmi.amdsmi_init()
             h = amdsmi.amdsmi_get_processor_handles()[0]
 
-            def read():
+            def fields():
                 m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                clks = m.get("current_gfxclks")
+                return {k: v for k, v in m.items() if "gfxclk" in k}
+
+            def valid(c):
+                return isinstance(c, (int, float)) and 0 < c < 10000
+
+            def read():
+                f = fields()
+                # the firmware's average over its sampling interval, else the
+                # current clock, else the mean of the per-XCD current clocks
+                for key in ("average_gfxclk_frequency", "current_gfxclk"):
+                    if valid(f.get(key)):
+                        return float(f[key])
+                clks = f.get("current_gfxclks")
                 if isinstance(clks, (list, tuple)):
-                    vals = [c for c in clks if isinstance(c, (int, float)) and 0 < c < 10000]
-                    if vals:  # one per XCD
+                    vals = [c for c in clks if valid(c)]
+                    if vals:
                         return sum(vals) / len(vals)
-                for key in ("current_gfxclk", "average_gfxclk_frequency"):
-                    c = m.get(key)
-                    if isinstance(c, (int, float)) and 0 < c < 10000:
-                        return float(c)
                 return None
 
+            self.raw = fields()  # the fields as read once, for the record
             if read() is not None:
                 self._read = read
-                self.source = "amdsmi gpu_metrics current graphics clock (mean over XCDs)"
+                self.source = "amdsmi gpu_metrics graphics clock (average, else current)"
         except Exception as e:  # no SMI library, no permission, no device
             self.source = None
             self.error = f"{type(e).__name__}: {e}"[:200]
@@ -179,7 +188,9 @@ class ClockSampler:
             return {"source": self.source, "samples": 0, "error": getattr(self, "error", None)}
         v = self.samples
         return {"mean_mhz": round(sum(v) / len(v), 1), "min_mhz": round(min(v), 1),
-                "max_mhz": round(max(v), 1), "samples": len(v), "source": self.source}
+                "max_mhz": round(max(v), 1), "samples": len(v), "source": self.source,
+                "fields_at_start": {k: (x if isinstance(x, (int, float)) else str(x)[:120])
+                                    for k, x in getattr(self, "raw", {}).items()}}
 
 
 def environment(dev):
@@ -581,6 +592,11 @@ def main():
     ap.add_argument("--prewarm-ms", type=float, default=60.0,
                     help="before the warm-up steps, run untimed steps until the GPU has been busy "
                          "this long (reported as prewarm_ms; 0 disables)")
+    ap.add_argument("--clock", choices=("after", "timed", "off"), default="after",
+                    help="sample the graphics clock over the same steps right after the timed "
+                         "region (default), inside it, or not at all")
+    ap.add_argument("--clock-ms", type=float, default=300.0,
+                    help="length of the clock-sampling window after the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep")
@@ -715,9 +731,13 @@ def main():
     probed = list(range(0, K, 5))
     evs = {s: [torch.cuda.Event(enable_timing=True) for _ in launches] for s in probed}
     start = {s: torch.cuda.Event(enable_timing=True) for s in probed}
-    clock = ClockSampler()
+    import contextlib
+
+    # The SMI library is only loaded where asked: with it initialised (and
+    # more so with a thread polling it) the same steps ran 4-5% slower.
+    clock = ClockSampler() if args.clock == "timed" else None
     torch.cuda.synchronize()
-    with clock:
+    with clock if args.clock == "timed" else contextlib.nullcontext():
         t0 = time.perf_counter()
         for s in range(K):
             if s in start:
@@ -731,6 +751,16 @@ def main():
     # device memory the step holds (the library allocates none itself: inputs,
     # outputs, statistics workspace)
     peak_mem = torch.cuda.max_memory_allocated(dev)
+    if args.clock == "after":
+        # the graphics clock over the same steps, run for --clock-ms right
+        # after the timed region (sampling inside it disturbs it)
+        clock = ClockSampler()
+        with clock:
+            t1 = time.perf_counter()
+            while (time.perf_counter() - t1) * 1e3 < args.clock_ms:
+                for _ in range(32):
+                    step()
+                torch.cuda.synchronize()
 
     kern_ms = {name: 0.0 for name, _ in launches}
     for s in probed:
@@ -909,7 +939,10 @@ def main():
         "varlen": varlen,
         "cpu_baseline": cpu,
         "peak_mem_bytes": peak_mem,
-        "sclk_timed_region": clock.summary(),
+        "sclk": dict(clock.summary(), window=(
+            "the timed region" if args.clock == "timed" else
+            f"{args.clock_ms:.0f} ms of the same steps right after the timed region"))
+        if clock is not None else None,
         "env": env,
         "device": env["gpu"],
         "torch": torch.__version__,

@@ -80,6 +80,18 @@ def test_bf16_small_full_compare(oracle_mod, N, d, causal):
     check_bf16(o, lse, ro, rl, f"N={N} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("N", [255, 256, 257, 511, 513, 767, 1000, 1281])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_several_query_blocks(oracle_mod, N, dtype, causal):
+    """d = 128 shapes spanning several 256-row query blocks of the forward,
+    with ragged last blocks and tiles."""
+    q, k, v = attn_inputs.make(1, 4, 2, N, 128, dtype, seed=3000 + N)
+    o, lse = run(q, k, v, causal)
+    ro, rl = oracle_mod.fwd(q, k, v, causal=causal)
+    check_bf16(o, lse, ro, rl, f"N={N} {dtype} causal={causal}")
+
+
 @pytest.mark.parametrize("heads", [(1, 1), (8, 1), (8, 2), (6, 3), (5, 5)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_head_maps(oracle_mod, heads, causal):
