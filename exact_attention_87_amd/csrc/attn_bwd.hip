@@ -202,21 +202,24 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kblk * BKV) / BQ : 0;
   const int per_head = nqt - qt0;
-  const int iters = (hs1 - hs0) * per_head;
-  // Query tile of step `it` (head-major).  Under the causal mask each key
-  // block starts at its own diagonal tile, so with an ascending walk the
-  // workgroups of one kv group read a given Q/dO tile at different times; when
-  // the group's stream is larger than an XCD's L2 every key block fetches it
-  // from HBM again (16x the algorithmic bytes on the causal grouped-query
-  // N=16384 d=128 backward).  With `desc` the tiles are walked from the last
-  // one down, so the workgroups of a group, whatever their key block, read
-  // the same tile at about the same time.  Same-box interleaved A/B: speed
-  // within 1% either way on every shape tried.  The host sets desc for every
-  // causal problem.  It is a runtime argument on purpose: with the direction
-  // fixed at compile time the d = 256 instances spill 20-21 registers instead
-  // of 7-11, and run 14% slower on the causal B=1 H=16 N=8192 backward.
+  const int nh = hs1 - hs0;
+  const int iters = nh * per_head;
+  // Step `it` takes query tile rank it / nh of head hs0 + it % nh: tile-major,
+  // the group's query heads innermost.  Under the causal mask each key block
+  // starts at its own diagonal tile, so with an ascending walk the
+  // workgroups of one kv group would read a given Q/dO tile at different
+  // times, and when the group's stream is larger than an XCD's L2 every key
+  // block would fetch it from HBM again.  With `desc` the tiles are walked
+  // from the last one down, so the workgroups of a group, whatever their key
+  // block, read the same tiles at about the same time; taking all heads of a
+  // tile before the next tile keeps them in step across heads too (walked
+  // head by head, a short walk moves on to the next head while the long
+  // ones are still low in the first).  The host sets desc for every causal
+  // problem.  It is a runtime argument on purpose: with the direction fixed
+  // at compile time the d = 256 instances spill 20-21 registers instead of
+  // 7-11, and run 14% slower on the causal B=1 H=16 N=8192 backward.
   auto qtile_of = [&](int it) {
-    const int r = it % per_head;
+    const int r = it / nh;
     return (CAUSAL && desc) ? nqt - 1 - r : qt0 + r;
   };
 
@@ -238,7 +241,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   }
   const uint32_t soff = (uint32_t)((lane >> 4) * Np * 4 + (lane & 15) * 16);
   auto issue = [&](int it) {
-    const int hq = g * group + hs0 + it / per_head;
+    const int hq = g * group + hs0 + it % nh;
     const int qt = qtile_of(it);
     char* base = smem + (it % NBUF) * STAGEB;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + qb0 + hq * qhs, slice_bytes(N, qrs, D));
@@ -846,7 +849,8 @@ static int dq_xcd_group(const BwdArgs& a, int D, bool varlen) {
   if (varlen) return 0;
   const int64_t nsl = (int64_t)a.B * a.Hq;
   const int group = a.Hq / a.Hkv;
-  return xcd_group(nsl, group, (int64_t)a.N * D * 4, a.causal ? kXgBudgetCausal : kXgBudget);
+  const int64_t bytes = (int64_t)a.N * D * 4;
+  return a.causal ? xcd_group_causal(nsl, group, bytes) : xcd_group(nsl, group, bytes, kXgBudget);
 }
 static int dkdv_xcd_group(const BwdArgs& a, int D, bool varlen) {
   if (varlen || a.causal) return 0;

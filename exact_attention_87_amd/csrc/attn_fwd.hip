@@ -833,8 +833,9 @@ static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
 // in work and keep the plain order.
 static int fwd_xcd_group(const FwdArgs& a, int D) {
   if (a.cu_seqlens) return 0;
-  return xcd_group((int64_t)a.B * a.Hq, a.Hq / a.Hkv, (int64_t)a.N * D * 4,
-                   a.causal ? kXgBudgetCausal : kXgBudget);
+  const int64_t nsl = (int64_t)a.B * a.Hq, bytes = (int64_t)a.N * D * 4;
+  return a.causal ? xcd_group_causal(nsl, a.Hq / a.Hkv, bytes)
+                  : xcd_group(nsl, a.Hq / a.Hkv, bytes, kXgBudget);
 }
 
 template <typename T, int D, bool CAUSAL, int MODE>

@@ -144,6 +144,16 @@ inline int xcd_group(int64_t nsl, int share, int64_t bytes, int64_t budget) {
 // L2 budgets of the slice groups: causal grids also need their heaviest
 // blocks of many slices in flight at once, so they take larger groups.
 constexpr int64_t kXgBudget = 2 << 20, kXgBudgetCausal = 8 << 20;
+// The slice group of a causal grid.  A group of one unshared slice per XCD
+// leaves too few of the heaviest query blocks in flight at a time: there the
+// plain order is the faster one (by 2.5-3% on the forward and dQ stage of
+// the causal B=1 H=16 N=8192 d=256 and B=4 H=32 N=4000 d=128 problems), and
+// smaller budgets than this one, which would group the causal d=64 problems,
+// made them 5-20% slower than the plain order.
+inline int xcd_group_causal(int64_t nsl, int share, int64_t bytes) {
+  const int g = xcd_group(nsl, share, bytes, kXgBudgetCausal);
+  return g == 1 && share == 1 ? 0 : g;
+}
 
 // Bytes of the backward row-statistics workspace.
 size_t bwd_stats_bytes(int B, int Hq, int N);
