@@ -578,7 +578,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   float* st;  // this head's statistics rows, from the slice's first row on
   if constexpr (VARLEN) {
     const int seq = bh / Hq;
-    h = bh - seq * Hq;
+    h = xcd_head(bh - seq * Hq, Hq);  // xg is 0 here: the plain order
     const int start = min(max(cu_seqlens[seq], 0), ntok);
     const int end = min(max(cu_seqlens[seq + 1], start), ntok);
     N = end - start;
@@ -844,7 +844,8 @@ static hipError_t pre_t(const BwdArgs& a) {
 // groups +3% at causal B=4 H=32 N=4000 d=128 and +4% non-causal N=1024;
 // dK/dV groups +2% non-causal, but -3% causal N=2048 and -2% causal
 // grouped-query N=4096).  Packed variable-length slices differ in work and
-// keep the plain order.
+// keep the plain order, with each sequence's heads permuted (xcd_head) so that
+// an XCD takes whole kv groups.
 static int dq_xcd_group(const BwdArgs& a, int D, bool varlen) {
   if (varlen) return 0;
   const int64_t nsl = (int64_t)a.B * a.Hq;

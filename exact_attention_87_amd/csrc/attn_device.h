@@ -190,6 +190,17 @@ __device__ __forceinline__ void xcd_item(int nmaj, int nsl, int xg, int& maj, in
   }
 }
 
+// Head of slice index i (0 <= i < H) of a packed sequence in the plain
+// order.  There slice seq*H + i goes to XCD i % 8 when H % 8 == 0, which
+// would spread the query heads of one kv head over several XCDs, each then
+// fetching that head's K/V.  This bijection gives XCD x the contiguous heads
+// x*H/8 .. (x+1)*H/8 - 1 instead: whole kv groups, or as few XCDs per kv
+// head as the group size allows, while every XCD still gets H/8 heads of
+// every sequence.  Other H: the identity.
+__device__ __forceinline__ int xcd_head(int i, int H) {
+  return (H & 7) ? i : (i & 7) * (H >> 3) + (i >> 3);
+}
+
 // Raw buffer resource over [base, base + bytes): loads beyond the range
 // return zeros, which is how tail rows and keys are padded.  Word 3 is the
 // gfx9-family raw-buffer format.

@@ -117,7 +117,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   int qrs = D, krs = D, ors = D;  // row strides (elements) of Q, K/V and O
   if constexpr (MODE == kFwdVarlen) {
     const int seq = bh / Hq;
-    h = bh - seq * Hq;
+    h = xcd_head(bh - seq * Hq, Hq);  // xg is 0 here: the plain order
     const int start = min(max(cu_seqlens[seq], 0), ntok);
     const int end = min(max(cu_seqlens[seq + 1], start), ntok);
     N = end - start;
@@ -483,7 +483,7 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
   int qrs = D, krs = D, ors = D;  // row strides (elements) of Q, K/V and O
   if constexpr (MODE == kFwdVarlen) {
     const int seq = bh / Hq;
-    h = bh - seq * Hq;
+    h = xcd_head(bh - seq * Hq, Hq);  // xg is 0 here: the plain order
     const int start = min(max(cu_seqlens[seq], 0), ntok);
     const int end = min(max(cu_seqlens[seq + 1], start), ntok);
     N = end - start;
@@ -830,7 +830,8 @@ static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
 // order): non-causal with 2 MiB groups, +18% at B=8 H=32 N=1024 d=128 and
 // +2-5% at d=64; causal grids lost 9% with 2 MiB groups (B=8 H=16 N=2048
 // d=64) but gain 1-3% with 8 MiB ones.  Packed variable-length slices differ
-// in work and keep the plain order.
+// in work and keep the plain order, with each sequence's heads permuted (xcd_head) so that
+// an XCD takes whole kv groups.
 static int fwd_xcd_group(const FwdArgs& a, int D) {
   if (a.cu_seqlens) return 0;
   const int64_t nsl = (int64_t)a.B * a.Hq, bytes = (int64_t)a.N * D * 4;
