@@ -109,88 +109,46 @@ def roofline_mfma(tflops: float, traffic_key: str | None):
             "traffic": load_traffic(traffic_key) if traffic_key else None}
 
 
-class ClockSampler:
-    """Samples the GPU's graphics clock (MHz) from the SMI library's metrics
-    table in a background thread, e.g. over the timed region.  Under sustained
-    matrix-core load the board runs at its power cap below the 2.4 GHz the
-    published peak assumes, so the clock explains part of any gap to it.
-    Disabled (source None) where the SMI library is unavailable."""
+class ClockProbe:
+    """The shader clock of each XCD while the steps run.  attn_probe_clock's
+    one-wave workgroups (8: one per XCD) spin on a second stream for a fixed
+    real-time window beside the steps, each comparing its XCD's shader-clock
+    counter with the 100 MHz real-time counter.  Under sustained matrix-core
+    load the board lowers its clock to hold its power limit and raises it
+    again within microseconds once the load stops, so the probe has to overlap
+    the steps: probes launched between kernels read the idle 2.4 GHz.  (The
+    SMI library's graphics-clock fields read 200-700 MHz during such steps on
+    these boards, and loading it slowed the steps by 4-5%, so it is not
+    used.)"""
 
-    def __init__(self, period_s: float = 0.002):
-        import threading
+    NWG = 8
 
-        self.period = period_s
-        self.samples = []
-        self.source = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._read = None
-        try:
-            import amdsmi
+    def __init__(self, dev, window_ms: float):
+        import torch
 
-            amdsmi.amdsmi_init()
-            h = amdsmi.amdsmi_get_processor_handles()[0]
+        self.buf = torch.zeros(2 * self.NWG, dtype=torch.int64, device=dev)
+        self.stream = torch.cuda.Stream(dev)  # default priority
+        self.window_ms = min(max(window_ms, 0.01), 2000.0)
 
-            def fields():
-                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-                return {k: v for k, v in m.items() if "gfxclk" in k}
+    def start(self):
+        import exact_attention_87_amd as ea
 
-            def valid(c):
-                return isinstance(c, (int, float)) and 0 < c < 10000
-
-            def read():
-                f = fields()
-                # the firmware's average over its sampling interval, else the
-                # current clock, else the mean of the per-XCD current clocks
-                for key in ("average_gfxclk_frequency", "current_gfxclk"):
-                    if valid(f.get(key)):
-                        return float(f[key])
-                clks = f.get("current_gfxclks")
-                if isinstance(clks, (list, tuple)):
-                    vals = [c for c in clks if valid(c)]
-                    if vals:
-                        return sum(vals) / len(vals)
-                return None
-
-            self.raw = fields()  # the fields as read once, for the record
-            if read() is not None:
-                self._read = read
-                self.source = "amdsmi gpu_metrics graphics clock (average, else current)"
-        except Exception as e:  # no SMI library, no permission, no device
-            self.source = None
-            self.error = f"{type(e).__name__}: {e}"[:200]
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                c = self._read()
-                if c is not None:
-                    self.samples.append(c)
-            except Exception:
-                pass
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        import threading
-
-        if self._read is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join()
+        st = ea.attn_probe_clock(self.buf.data_ptr(), self.NWG, int(self.window_ms * 1e5),
+                                 self.stream.cuda_stream)
+        if st != ea.ATTN_OK:
+            raise ea.AttnError(st, "attn_probe_clock")
 
     def summary(self):
-        if not self.samples:
-            return {"source": self.source, "samples": 0, "error": getattr(self, "error", None)}
-        v = self.samples
-        return {"mean_mhz": round(sum(v) / len(v), 1), "min_mhz": round(min(v), 1),
-                "max_mhz": round(max(v), 1), "samples": len(v), "source": self.source,
-                "fields_at_start": {k: (x if isinstance(x, (int, float)) else str(x)[:120])
-                                    for k, x in getattr(self, "raw", {}).items()}}
+        """After the device has been synchronised."""
+        v = self.buf.cpu().tolist()
+        mhz = [v[2 * i] / v[2 * i + 1] * 100.0 for i in range(self.NWG) if v[2 * i + 1] > 0]
+        if not mhz:
+            return {"source": "attn_probe_clock", "samples": 0}
+        return {"mean_mhz": round(sum(mhz) / len(mhz), 1), "min_mhz": round(min(mhz), 1),
+                "max_mhz": round(max(mhz), 1), "per_xcd_mhz": [round(x, 1) for x in mhz],
+                "probe_ms": round(v[1] / 1e5, 2),
+                "source": "attn_probe_clock: shader-clock counter against the 100 MHz real-time "
+                          "counter, one wave per XCD on a second stream beside the steps"}
 
 
 def environment(dev):
@@ -593,10 +551,11 @@ def main():
                     help="before the warm-up steps, run untimed steps until the GPU has been busy "
                          "this long (reported as prewarm_ms; 0 disables)")
     ap.add_argument("--clock", choices=("after", "timed", "off"), default="after",
-                    help="sample the graphics clock over the same steps right after the timed "
-                         "region (default), inside it, or not at all")
+                    help="measure the shader clock (attn_probe_clock on a second stream) beside "
+                         "the same steps right after the timed region (default), beside the timed "
+                         "steps themselves, or not at all")
     ap.add_argument("--clock-ms", type=float, default=300.0,
-                    help="length of the clock-sampling window after the timed region")
+                    help="length of the clock window after the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep")
@@ -731,36 +690,44 @@ def main():
     probed = list(range(0, K, 5))
     evs = {s: [torch.cuda.Event(enable_timing=True) for _ in launches] for s in probed}
     start = {s: torch.cuda.Event(enable_timing=True) for s in probed}
-    import contextlib
-
-    # The SMI library is only loaded where asked: with it initialised (and
-    # more so with a thread polling it) the same steps ran 4-5% slower.
-    clock = ClockSampler() if args.clock == "timed" else None
+    # The clock probe runs beside the same steps for --clock-ms right after the
+    # timed region (the default: steps beside it ran at the timed rate), or
+    # beside the timed steps themselves (--clock timed: its launch on a second
+    # queue made a 30-step timed region 13% slower).
+    clock = None
+    if args.clock == "timed":
+        est_ms = prewarm_ms / max(prewarm_steps, 1) * K  # this box's pre-warm rate
+        clock = ClockProbe(dev, 0.9 * est_ms)
     torch.cuda.synchronize()
-    with clock if args.clock == "timed" else contextlib.nullcontext():
-        t0 = time.perf_counter()
-        for s in range(K):
-            if s in start:
-                start[s].record(stream)
-                step(evs[s])
-            else:
-                step()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    if clock is not None:
+        clock.start()
+    t0 = time.perf_counter()
+    for s in range(K):
+        if s in start:
+            start[s].record(stream)
+            step(evs[s])
+        else:
+            step()
+    stream.synchronize()
+    wall = time.perf_counter() - t0
+    torch.cuda.synchronize()
     ms_per_step = wall * 1e3 / K
     # device memory the step holds (the library allocates none itself: inputs,
     # outputs, statistics workspace)
     peak_mem = torch.cuda.max_memory_allocated(dev)
+    beside_ms = None
     if args.clock == "after":
-        # the graphics clock over the same steps, run for --clock-ms right
-        # after the timed region (sampling inside it disturbs it)
-        clock = ClockSampler()
-        with clock:
-            t1 = time.perf_counter()
-            while (time.perf_counter() - t1) * 1e3 < args.clock_ms:
-                for _ in range(32):
-                    step()
-                torch.cuda.synchronize()
+        clock = ClockProbe(dev, args.clock_ms)
+        clock.start()
+        t1 = time.perf_counter()
+        n1 = 0
+        while (time.perf_counter() - t1) * 1e3 < args.clock_ms:
+            for _ in range(32):
+                step()
+            n1 += 32
+            stream.synchronize()  # the steps' stream only: the probe is still running
+        beside_ms = (time.perf_counter() - t1) * 1e3 / n1
+        torch.cuda.synchronize()  # now the probe too
 
     kern_ms = {name: 0.0 for name, _ in launches}
     for s in probed:
@@ -940,8 +907,9 @@ def main():
         "cpu_baseline": cpu,
         "peak_mem_bytes": peak_mem,
         "sclk": dict(clock.summary(), window=(
-            "the timed region" if args.clock == "timed" else
-            f"{args.clock_ms:.0f} ms of the same steps right after the timed region"))
+            "beside the timed steps" if args.clock == "timed" else
+            f"{args.clock_ms:.0f} ms beside the same steps right after the timed region"),
+            ms_per_step_beside_probe=None if beside_ms is None else round(beside_ms, 5))
         if clock is not None else None,
         "env": env,
         "device": env["gpu"],

@@ -61,6 +61,8 @@ def lib():
         L.attn_bwd.restype = ci
         L.attn_bwd_noalloc.argtypes = [vp] * 9 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
         L.attn_bwd_noalloc.restype = ci
+        L.attn_probe_clock.argtypes = [vp, ci, ctypes.c_uint, vp]
+        L.attn_probe_clock.restype = ci
         L.attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
         L.attn_bwd_preprocess.restype = ci
         L.attn_bwd_dkdv.argtypes = [vp] * 7 + [ci, ci, ci, ci, ci, ci, cf, ci, vp]
@@ -128,6 +130,10 @@ def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal
                      stream) -> int:
     return int(lib().attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d,
                                       int(causal), float(scale), int(dtype), stream))
+
+
+def attn_probe_clock(out, nwg, ticks, stream) -> int:
+    return int(lib().attn_probe_clock(out, int(nwg), int(ticks), stream))
 
 
 # Bytes of the static device scratch attn_bwd_noalloc uses (ATTN_NOALLOC_SCRATCH_BYTES).

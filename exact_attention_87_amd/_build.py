@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_splitkv.hip", "attn_sparse.hip",
-           "attn_noalloc.hip"]
+           "attn_noalloc.hip", "attn_clock.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -241,6 +241,16 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   return bwd_launch(&a, q, k, v, o, lse, dout, dq, dk, dv, workspace);
 }
 
+attn_status attn_probe_clock(unsigned long long* out, int nwg, unsigned ticks, void* stream) {
+  if (out == nullptr || (reinterpret_cast<uintptr_t>(out) & 7u) != 0) return ATTN_ERR_INVALID_ARG;
+  if (nwg < 1 || nwg > 64 || ticks < 1 || ticks > 200000000u) return ATTN_ERR_INVALID_ARG;
+  const attn_status st = check_device();
+  if (st != ATTN_OK) return st;
+  return attn::launch_clock_probe(out, nwg, ticks, (hipStream_t)stream) == hipSuccess
+             ? ATTN_OK
+             : ATTN_ERR_HIP;
+}
+
 attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,

@@ -162,6 +162,10 @@ size_t bwd_stats_bytes(int B, int Hq, int N);
 // current device (looked up on first use, then cached).
 constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
 hipError_t noalloc_scratch(void** ptr);
+// Measurement helper (attn_clock.hip): nwg one-wave workgroups, each storing
+// the shader-clock cycles and 100 MHz real-time ticks elapsed over a spin of
+// at most `ticks` ticks to out[2i], out[2i+1].
+hipError_t launch_clock_probe(unsigned long long* out, int nwg, unsigned ticks, hipStream_t stream);
 // Query-head splits of the dK/dV stage for a dense problem (1 when the grid
 // of key blocks x kv heads already fills the device), and the bytes of fp32
 // partial sums they need (0 for one split).

@@ -419,6 +419,24 @@ attn_status attn_bwd_varlen_strided(const void* q, const void* k, const void* v,
                                     int Hkv, int T, int d, int causal, float scale,
                                     attn_dtype dtype, void* stream);
 
+/*
+ * Measurement helper, not part of the attention path: the device's shader
+ * clock while other work runs.  Launches nwg one-wave workgroups on
+ * `stream`; workgroup i spins (sleeping) for `ticks` ticks of the 100 MHz
+ * real-time counter and stores
+ *   out[2i] = shader-clock cycles elapsed, out[2i+1] = real-time ticks elapsed,
+ * so its mean clock over the spin is out[2i] / out[2i+1] * 100 MHz.
+ * Workgroups are dealt round robin to the 8 XCDs, each with its own clock,
+ * so nwg = 8 samples every XCD once.  Under sustained matrix-core load the
+ * board lowers its clock to hold its power limit, and raises it again within
+ * microseconds once the load stops, so the probe is meant for a second
+ * stream beside the kernels being measured (bench.py does so).  out: device
+ * pointer to 2*nwg unsigned 64-bit values, 8-byte aligned, written when the
+ * kernel ends (asynchronously, like every launch here).  1 <= nwg <= 64 and
+ * 1 <= ticks <= 200000000 (2 s); else ATTN_ERR_INVALID_ARG.
+ */
+attn_status attn_probe_clock(unsigned long long* out, int nwg, unsigned ticks, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -85,7 +85,7 @@ def test_header_declares_the_boundary():
                                   "attn_fwd_splitkv_strided",
                                   "attn_fwd_splitkv_workspace_bytes", "attn_fwd_strided",
                                   "attn_fwd_varlen", "attn_fwd_varlen_strided",
-                                  "attn_status_str"]
+                                  "attn_probe_clock", "attn_status_str"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -647,6 +647,28 @@ def test_varlen_grid_limit_is_rejected():
 def test_splitkv_grid_limit_is_rejected():
     # the merge runs up to 64 threads per output row: B*Hq*Nq*64 < 2^32
     assert split(B=1 << 12, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 10, Nk=64) == ea.ATTN_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- clock probe
+def probe(**kw):
+    a = dict(out=Q, nwg=8, ticks=1000)
+    a.update(kw)
+    return ea.attn_probe_clock(a["out"], a["nwg"], a["ticks"], None)
+
+
+PROBE_INVALID = [dict(out=None), dict(out=Q + 4), dict(nwg=0), dict(nwg=65), dict(ticks=0),
+                 dict(ticks=200000001)]
+
+
+@pytest.mark.parametrize("kw", PROBE_INVALID, ids=[str(k) for k in PROBE_INVALID])
+def test_probe_clock_rejects_bad_arguments(kw):
+    assert probe(**kw) == ea.ATTN_ERR_INVALID_ARG
+
+
+@reaches_device
+def test_probe_clock_passes_validation():
+    assert probe() == ea.ATTN_ERR_HIP  # no GPU here: stops at the device check
+    assert probe(nwg=64, ticks=200000000) == ea.ATTN_ERR_HIP
 
 
 # ---------------------------------------------------------------- no-allocation backward
