@@ -15,10 +15,12 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long* out
   const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
   const unsigned long long c0 = __builtin_amdgcn_s_memtime();
   unsigned long long t = t0;
-  // Ends after `ticks` real-time ticks, or after 2^22 iterations (each at
-  // least one s_sleep) should the real-time counter not advance.
-  for (int i = 0; i < (1 << 22) && t - t0 < ticks; ++i) {
-    __builtin_amdgcn_s_sleep(2);
+  // Ends after `ticks` real-time ticks (at most 2 s), or after 2^23
+  // iterations should the real-time counter not advance.  Each iteration
+  // sleeps 640 shader cycles (0.27 us at 2.4 GHz, so the cap lies beyond 2 s
+  // at any clock up to 2.4 GHz, and within 6 s at any clock above 1 GHz).
+  for (int i = 0; i < (1 << 23) && t - t0 < ticks; ++i) {
+    __builtin_amdgcn_s_sleep(10);
     t = __builtin_amdgcn_s_memrealtime();
   }
   const unsigned long long c1 = __builtin_amdgcn_s_memtime();

@@ -40,3 +40,18 @@ def test_probe_clock_beside_other_work():
     v = buf.cpu().tolist()
     assert all(20000 <= v[2 * i + 1] for i in range(8))
     assert all(300.0 < v[2 * i] / v[2 * i + 1] * 100.0 < 3000.0 for i in range(8))
+
+
+def test_probe_clock_long_window_is_not_cut_short():
+    """A 0.4 s window runs to its end at the idle 2.4 GHz clock (the spin's
+    iteration cap lies beyond the 2 s maximum)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    buf = torch.zeros(2, dtype=torch.int64, device=dev)
+    assert ea.attn_probe_clock(buf.data_ptr(), 1, 40_000_000,
+                               torch.cuda.current_stream(dev).cuda_stream) == ea.ATTN_OK
+    torch.cuda.synchronize()
+    cycles, ticks = buf.cpu().tolist()
+    assert 40_000_000 <= ticks < 40_100_000, ticks
+    assert 300.0 < cycles / ticks * 100.0 < 3000.0
