@@ -262,7 +262,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       // packed sequence must not read the next sequence's LSE, which could
       // make P = 2^(-LSE log2 e) overflow (fp16 once LSE < -11) and 0 * inf
       // poison dK and dV.  Their -D (the padding, or the next sequence's) is
-      // finite and meets zero Q and dO rows, so those rows add nothing.
+      // replaced by 0 where the dP accumulator is seeded (phaseA).
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(stats + sb0 + (int64_t)hq * 2 * Np, (uint32_t)((Np + N) * 4));
       buf_load16_lds(rs, base + 2 * TILEB, soff + (uint32_t)qt * BQ * 4);
@@ -309,12 +309,22 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   constexpr int CG = D > 128 ? 2 : (Cfg::WPE >= 3 ? 2 : NQC);
   constexpr bool FENCE_C = D > 128;  // a fence per feature block of the dV/dK products
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
-                    f32x16& sacc, f32x16& pacc) {
+                    int qfirst, f32x16& sacc, f32x16& pacc) {
     // the dP accumulator starts at -D of each row (element 4*rg+e is row
-    // qbase + 8*rg + 4*hf + e)
+    // qbase + 8*rg + 4*hf + e).  Packed sequences: on a sequence's last
+    // query tile the rows past its end (zero Q and dO) would start at the
+    // next sequence's -D; they start at 0 instead, so that their dS is 0 and
+    // a non-finite value in the next sequence cannot reach this one's dK
+    // through 0 * inf.
+    const int lim = N - qfirst - 4 * hf;  // element 4*rg+e is a row of the sequence iff 8*rg+e < lim
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const f32x4 nd = *(const f32x4*)(dsum + qbase + 8 * rg + 4 * hf);
+      f32x4 nd = *(const f32x4*)(dsum + qbase + 8 * rg + 4 * hf);
+      if (VARLEN && qfirst + 32 > N) {  // wave-uniform
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (8 * rg + e >= lim) nd[e] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
     }
@@ -402,7 +412,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       if (!(qs == 0 ? act0 : act1)) continue;  // wave-uniform
       f32x16 sacc, pacc;
       uint32_t pk[8], dsk[8];
-      phaseA(qtile, dotile, dsum, qs * 32, sacc, pacc);
+      phaseA(qtile, dotile, dsum, qs * 32, qs == 0 ? qf0 : qf1, sacc, pacc);
       phaseV(lse2, qs * 32, qs == 0 ? qf0 : qf1, qs == 0 ? diag0 : diag1, sacc, pacc, pk, dsk);
       phaseC(qtile, dotile, qs * 32, pk, dsk);
     }

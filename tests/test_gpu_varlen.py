@@ -229,6 +229,34 @@ def test_backward_fp16_next_sequence_with_very_negative_lse(oracle_mod, d):
         grad_ok(f"{name} d={d}", gg, r)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_non_finite_sequence_stays_in_its_sequence(oracle_mod, d, causal):
+    # A NaN and an Inf in the upstream gradient of the middle sequence make
+    # that sequence's gradients non-finite; the sequences before and after it
+    # must still match the oracle.  The first sequence's last query tile
+    # reaches past its end into the middle sequence's rows, whose statistics
+    # the dK/dV stage reads there (and must not let through).
+    dev = gpu()
+    lengths = [100, 40, 70]
+    q, k, v, cu = attn_inputs.make_varlen(4, 2, lengths, d, seed=31 + d)
+    g = torch.Generator().manual_seed(9)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    t1 = lengths[0]
+    do[:, t1, 0] = float("nan")
+    do[:, t1 + 1, 3] = float("inf")
+    qg, kg, vg, dog, cug = (t.to(dev) for t in (q, k, v, do, cu))
+    o, lse = ea.fwd_varlen(qg, kg, vg, cug, max(lengths), causal=causal)
+    dq, dk, dv = ea.bwd_varlen(qg, kg, vg, o, lse, dog, cug, max(lengths), causal=causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q, k, v, do, cu, causal)
+    assert not np.all(np.isfinite(dk[:, t1:t1 + 40].float().cpu().numpy()))  # the planted values act
+    for a, b in ((0, t1), (t1 + 40, sum(lengths))):
+        sl = slice(a, b)
+        for name, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+            grad_ok(f"{name}[{a}:{b}] d={d}", gg[:, sl], r[:, sl])
+
+
 def test_backward_full_size_documents_sampled_heads(oracle_mod):
     w = attn_inputs.VARLEN_WORKLOADS["docs"]
     lengths = attn_inputs.varlen_lengths(w)
