@@ -83,6 +83,27 @@ def test_head_maps_and_scales(oracle_mod, heads):
         check(o, lse, ro, rl, f"heads={heads} scale={scale}")
 
 
+@pytest.mark.parametrize("heads", [(16, 4), (24, 3), (32, 8), (16, 16)])
+def test_head_order_over_xcds(oracle_mod, heads):
+    # With Hq a multiple of 8 each sequence's heads are dealt to the XCDs in a
+    # permuted order (whole kv groups per XCD); every head must still land on
+    # its own rows, forward and backward, against the oracle in full.
+    dev = gpu()
+    Hq, Hkv = heads
+    lengths = [150, 70, 300]
+    q, k, v, cu = attn_inputs.make_varlen(Hq, Hkv, lengths, 64, seed=Hq + Hkv)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(Hq)).to(q.dtype)
+    qg, kg, vg, dog, cug = (t.to(dev) for t in (q, k, v, do, cu))
+    o, lse = ea.fwd_varlen(qg, kg, vg, cug, max(lengths), causal=True)
+    dq, dk, dv = ea.bwd_varlen(qg, kg, vg, o, lse, dog, cug, max(lengths), causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mod.fwd_varlen(q, k, v, cu.numpy(), causal=True)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"heads={heads}")
+    rdq, rdk, rdv = varlen_bwd_reference(oracle_mod, q, k, v, do, cu, True)
+    for name, gg, r in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        grad_ok(f"{name} heads={heads}", gg, r)
+
+
 def test_max_seqlen_larger_than_needed(oracle_mod):
     q, k, v, cu = attn_inputs.make_varlen(2, 2, [100, 30], 64, seed=7)
     o, lse = run(q, k, v, cu, True, max_seqlen=130)
@@ -92,9 +113,10 @@ def test_max_seqlen_larger_than_needed(oracle_mod):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_one_sequence_is_the_batched_forward_bitwise(d, causal):
+@pytest.mark.parametrize("heads", [(4, 2), (16, 4)])
+def test_one_sequence_is_the_batched_forward_bitwise(d, causal, heads):
     dev = gpu()
-    q, k, v, cu = attn_inputs.make_varlen(4, 2, [999], d, seed=11)
+    q, k, v, cu = attn_inputs.make_varlen(heads[0], heads[1], [999], d, seed=11)
     q, k, v, cu = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
     o, lse = ea.fwd_varlen(q, k, v, cu, 999, causal=causal)
     fo, fl = ea.fwd(q[None], k[None], v[None], causal=causal)
