@@ -666,9 +666,9 @@ attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, const v
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
   a.dq = dq, a.dk = dk, a.dv = dv, a.stats = (float*)workspace;
   if (strides) a.lay = varlen_layout(strides);
-  // row statistics of all T packed tokens, then the two gradient stages per
-  // (sequence, head) with B = sequences and N = the longest sequence
-  if (attn::launch_bwd_pre(a) != hipSuccess) return ATTN_ERR_HIP;
+  // the two gradient stages per (sequence, head) with B = sequences and N =
+  // the longest sequence: dQ, which also stores the row statistics of every
+  // sequence's tokens, then dK/dV
   a.B = nseq, a.N = max_seqlen, a.cu_seqlens = cu_seqlens, a.T = T;
   // Query-head split of the dK/dV stage, chosen on the grid it launches
   // (sequences x longest sequence) like a batched problem, and capped by the
@@ -681,8 +681,8 @@ attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, const v
     a.nsplit = s;
     a.part = s > 1 ? (float*)((char*)workspace + stats) : nullptr;
   }
+  if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
   if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dq(a) != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 

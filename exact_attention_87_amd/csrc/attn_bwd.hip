@@ -548,8 +548,11 @@ struct DqCfg {
 
 // With STATS the kernel also computes the row statistics the preprocess kernel
 // would (the same sums in the same order, so bit-identical) from O, dO and LSE,
-// and stores them, padding rows included, for the dK/dV kernel launched after
-// it: the workgroups of one head cover every padded row of its statistics.
+// and stores them for the dK/dV kernel launched after it.  Batched: padding
+// rows included, since the workgroups of one head cover every padded row of
+// its statistics.  Packed sequences: each sequence's own rows only; the dK/dV
+// kernel reads no statistic past a sequence's end (its LSE row ends there,
+// and -D past it is replaced by 0).
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool STATS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqCfg<D>::WPE, DqCfg<D>::WPE)))
 void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
@@ -558,7 +561,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                    float* __restrict__ stats, T* __restrict__ dQ, int Hq, int Hkv,
                    int Nmax, int nqb, int xg, Layout lay, float c, float qscale, uint32_t qsign,
                    const int* __restrict__ cu_seqlens, int ntok) {
-  static_assert(!(STATS && VARLEN), "packed sequences take their statistics from the preprocess");
   using Cfg = DqCfg<D>;
   using V8 = typename Elem<T>::v8;
   constexpr int BR = Cfg::BR, BC = Cfg::BC, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
@@ -584,7 +586,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // variable-length sequences.  Q and dQ share one stride set, K and V
   // another, dO has O's.
   int N = Nmax, h, Np, qrs, krs, ors;
-  int64_t qoff, kvoff, ooff;
+  int64_t qoff, kvoff, ooff, lrow0;  // lrow0: LSE entry of the slice's first row
   float* st;  // this head's statistics rows, from the slice's first row on
   if constexpr (VARLEN) {
     const int seq = bh / Hq;
@@ -600,11 +602,13 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     kvoff = g * lay.kv.h + (int64_t)start * lay.kv.r;
     ooff = h * lay.o.h + (int64_t)start * lay.o.r;
     st = stats + (int64_t)h * 2 * Np + start;
+    lrow0 = (int64_t)h * ntok + start;  // LSE is [Hq, T]
   } else {
     const int b = bh / Hq;
     h = bh - b * Hq;
     const int g = h / (Hq / Hkv);
     Np = stat_rows(N);
+    lrow0 = (int64_t)bh * N;
     qrs = lay.q.r, krs = lay.kv.r, ors = lay.o.r;
     qoff = b * lay.q.b + h * lay.q.h;
     kvoff = b * lay.kv.b + g * lay.kv.h;
@@ -664,7 +668,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
     for (int cc = 0; cc < NQC; ++cc)
       oreg[cc] = bitcast<V8>(buf_load16(ro, (uint32_t)((qrow * ors + cc * 16 + hf * 8) * 2)));
-    if (qrow < N) lse_row = LSE[(int64_t)bh * N + qrow];
+    if (qrow < N) lse_row = LSE[lrow0 + qrow];
   }
   const bool qok = qrow < N;
   float ndsum, lse2;  // -D and LSE log2(e) of this lane's row
@@ -687,7 +691,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int i = 0; i < NQC; i += 2 * m) part[i] += part[i + m];
     ndsum = -part[0];  // rows past N read zeros: -0
     lse2 = qok ? lse_row * kLog2e : 0.f;
-    if (hf == 0 && qrow < Np) {
+    if (hf == 0 && qrow < (VARLEN ? N : Np)) {
       st[qrow] = ndsum;
       st[Np + qrow] = lse2;
     }
@@ -977,6 +981,8 @@ static hipError_t bwd_dq_for(const BwdArgs& a) {
 }
 template <typename T, int D>
 static hipError_t dq_stats_d(const BwdArgs& a) {
+  if (a.cu_seqlens)
+    return a.causal ? dq_t<T, D, true, true, true>(a) : dq_t<T, D, false, true, true>(a);
   return a.causal ? dq_t<T, D, true, false, true>(a) : dq_t<T, D, false, false, true>(a);
 }
 template <typename T>
@@ -1004,7 +1010,6 @@ hipError_t launch_bwd_dq(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_dq_stats(const BwdArgs& a) {
-  if (a.cu_seqlens) return hipErrorNotSupported;
   if (a.dtype == kBF16) return bwd_dq_stats_for<__bf16>(a);
   if (a.dtype == kF16) return bwd_dq_stats_for<_Float16>(a);
   return hipErrorNotSupported;

@@ -175,7 +175,8 @@ size_t bwd_partial_bytes(int B, int Hkv, int N, int d, int nsplit);
 hipError_t launch_bwd_pre(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
-// dQ that also computes and stores the row statistics (dense problems only),
+// dQ that also computes and stores the row statistics (batched: padding rows
+// included; packed sequences: the rows of each sequence),
 // so the dK/dV stage can follow it with no preprocess launch.
 hipError_t launch_bwd_dq_stats(const BwdArgs& a);
 
