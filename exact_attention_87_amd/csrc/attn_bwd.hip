@@ -858,8 +858,8 @@ static hipError_t pre_t(const BwdArgs& a) {
 // groups +3% at causal B=4 H=32 N=4000 d=128 and +4% non-causal N=1024;
 // dK/dV groups +2% non-causal, but -3% causal N=2048 and -2% causal
 // grouped-query N=4096).  Packed variable-length slices differ in work and
-// keep the plain order, with each sequence's heads permuted (xcd_head) so that
-// an XCD takes whole kv groups.
+// keep the plain order, with each sequence's heads permuted (xcd_head) so
+// that an XCD takes whole kv groups.
 static int dq_xcd_group(const BwdArgs& a, int D, bool varlen) {
   if (varlen) return 0;
   const int64_t nsl = (int64_t)a.B * a.Hq;

@@ -220,13 +220,23 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   // K operand rows (l32, +32) at chunk 2cc+hf, and the transposing-read
   // addresses of the V^T operand for key block 0 (other key blocks are
   // multiples of 16 rows further, which the swizzle leaves unchanged).
-  int koff[NQC], voff[2][NMB];
+  // At d = 256 only half of them are kept: the swizzle permutes chunks
+  // within aligned groups of 16, so chunk c + 16 lies 256 bytes after chunk
+  // c, an immediate of the LDS read.
+  constexpr int NKO = D > 128 ? NQC / 2 : NQC, NVO = D > 128 ? NMB / 2 : NMB;
+  int koff_[NKO], voff_[2][NVO];
 #pragma unroll
-  for (int cc = 0; cc < NQC; ++cc) koff[cc] = tile_off<D>(l32, 2 * cc + hf);
+  for (int cc = 0; cc < NKO; ++cc) koff_[cc] = tile_off<D>(l32, 2 * cc + hf);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) voff[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
+    for (int mb = 0; mb < NVO; ++mb) voff_[t][mb] = tr_off<D>(lane, 0, mb * 32, t);
+  auto koff = [&](int cc) __attribute__((always_inline)) {
+    return koff_[cc % NKO] + (cc / NKO) * 256;
+  };
+  auto voff = [&](int t, int mb) __attribute__((always_inline)) {
+    return voff_[t][mb % NVO] + (mb / NVO) * 256;
+  };
 
   float ms[NB], lsum[NB];  // running max (scaled base-2 units), this lane's share of l
   f32x16 oacc[NB][NMB];
@@ -284,7 +294,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
         for (int kk = 0; kk < KF; ++kk)
 #pragma unroll
           for (int cc = 0; cc < NQC; ++cc)
-            kfrag[kk][cc] = lds_read16(kt + (k0b + kk) * 32 * ROWB + koff[cc]);
+            kfrag[kk][cc] = lds_read16(kt + (k0b + kk) * 32 * ROWB + koff(cc));
         if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < KF; ++kk)
@@ -357,8 +367,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #pragma unroll
           for (int cp = 0; cp < 2; ++cp) {
             const int rows = (kbk * 32 + cp * 16) * ROWB;
-            const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
-            const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
+            const u32x2 lo = lds_read_tr(vt + rows + voff(0, mb));
+            const u32x2 hi = lds_read_tr(vt + rows + voff(1, mb));
             const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -830,8 +840,8 @@ static size_t sparse_list_bytes(const FwdArgs& a, int BC) {
 // order): non-causal with 2 MiB groups, +18% at B=8 H=32 N=1024 d=128 and
 // +2-5% at d=64; causal grids lost 9% with 2 MiB groups (B=8 H=16 N=2048
 // d=64) but gain 1-3% with 8 MiB ones.  Packed variable-length slices differ
-// in work and keep the plain order, with each sequence's heads permuted (xcd_head) so that
-// an XCD takes whole kv groups.
+// in work and keep the plain order, with each sequence's heads permuted
+// (xcd_head) so that an XCD takes whole kv groups.
 static int fwd_xcd_group(const FwdArgs& a, int D) {
   if (a.cu_seqlens) return 0;
   const int64_t nsl = (int64_t)a.B * a.Hq, bytes = (int64_t)a.N * D * 4;
