@@ -182,6 +182,25 @@ def environment(dev):
     except OSError:
         env["host_cpu"] = None
     env["host_cpus"] = os.cpu_count()
+    # the peak recomputed from this device: CUs x 4096 bf16 FLOP/clk/CU x the
+    # maximum engine clock rocminfo reports for its gfx agent
+    env["max_sclk_mhz"] = env["peak_bf16_tflops_at_max_sclk"] = None
+    try:
+        out = subprocess.run(["/opt/rocm/bin/rocminfo"], capture_output=True, text=True,
+                             timeout=60).stdout
+        agent = None
+        for line in out.splitlines():
+            line = line.strip()
+            if line.startswith("Name:"):
+                agent = line.split(":", 1)[1].strip()
+            elif line.startswith("Max Clock Freq. (MHz):") and agent and agent.startswith("gfx"):
+                mhz = int(line.split(":", 1)[1].strip())
+                env["max_sclk_mhz"] = mhz
+                env["peak_bf16_tflops_at_max_sclk"] = round(
+                    props.multi_processor_count * 4096 * mhz * 1e6 / 1e12, 1)
+                break
+    except Exception:
+        pass
     return env
 
 
