@@ -427,10 +427,13 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
   for (int it = 0; it < NBUF - 1; ++it)
     if (it < iters) issue(it);
-  if (NBUF == 3 && iters > 1)
-    wait_stage();
-  else
-    wait_vm_barrier<0>();
+  // A full wait here, not one that lets the second stage stay in flight: the
+  // compiler's wait analysis does not see the direct-to-LDS loads (inline
+  // assembly), so after a partial count it takes the last loads of K and V
+  // above for still pending and waits for them inside the loop, which at run
+  // time drained each step's own prefetch (vmcnt(1), then vmcnt(0), before
+  // the last S and dP products).  After vmcnt(0) nothing is pending for it.
+  wait_vm_barrier<0>();
   for (int it = 0; it < iters; it += NBUF) {
     step(std::integral_constant<int, 0>{}, it);
     if (it + 1 < iters) step(std::integral_constant<int, 1>{}, it + 1);
