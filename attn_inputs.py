@@ -209,3 +209,24 @@ def make_varlen(Hq: int, Hkv: int, lengths, d: int, seed: int = 0, dtype: str = 
     v = torch.randn((Hkv, T, d), generator=g, dtype=torch.float32).to(td)
     cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
     return q, k, v, cu
+
+
+def make_long_filler(M: int, T: int, d: int, pool: int = 4096, seed: int = 0,
+                     dtype: str = "bf16", with_dout: bool = False):
+    """Pieces of the maximum-length inputs: N = M + T rows of one head, whose
+    first M keys are zero and whose last T keys are drawn; query, value and
+    upstream-gradient rows repeat with a period of `pool` rows.
+
+    Returns (qpool [pool, d], vpool [pool, d], ktail [T, d], dopool [pool, d]
+    or None) rounded to the 16-bit type, on the CPU.  Row i of Q is
+    qpool[i % pool], of V vpool[i % pool], of dO dopool[i % pool]; key i is 0
+    for i < M and ktail[i - M] after.  Draw order: Q pool, key tail, V pool,
+    dO pool.
+    """
+    g = torch.Generator().manual_seed(seed)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    qpool = torch.randn((pool, d), generator=g).to(tdt)
+    ktail = torch.randn((T, d), generator=g).to(tdt)
+    vpool = torch.randn((pool, d), generator=g).to(tdt)
+    dopool = torch.randn((pool, d), generator=g).to(tdt) if with_dout else None
+    return qpool, vpool, ktail, dopool
