@@ -143,3 +143,34 @@ def test_backward_at_the_maximum_length(oracle_mod):
         bound = 2.0 ** -8 * g.abs().sum(0).cpu().numpy() + 1e-2 * np.abs(ref) + 1e-3
         assert np.all(np.abs(s - ref) <= bound), (
             f"sum of {name} over the keys before L: max |diff| {np.abs(s - ref).max()}")
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_splitkv_at_the_maximum_length(oracle_mod, d):
+    # Nq = 3 queries of 2 heads against a cache of N keys (bottom-right
+    # causal): query i sees keys 0 .. N - 3 + i, that is the M zero keys and
+    # the tail up to its own position; the oracle's bottom-right forward on
+    # [one key for the zero keys, the tail keys] is the exact reference.
+    dev = torch.device("cuda:0")
+    Nq, Hq = 3, 2
+    qpool, vpool, ktail, _ = attn_inputs.make_long_filler(M, T, d, pool=P, seed=80 + d)
+    idx = torch.arange(N, device=dev) % P
+    v = vpool.to(dev)[idx]
+    k = torch.zeros((N, d), device=dev, dtype=qpool.dtype)
+    k[M:] = ktail.to(dev)
+    q = qpool[:Hq * Nq].reshape(1, Hq, Nq, d).to(dev)
+    o, lse = ea.fwd_splitkv(q, k[None, None], v[None, None], causal=True)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(d)
+    q64, v64, k64 = qpool.double().numpy(), vpool.double().numpy(), ktail.double().numpy()
+    qa = np.zeros((1, Hq, Nq, d + 1))
+    qa[0, :, :, :d] = q64[:Hq * Nq].reshape(Hq, Nq, d)
+    qa[0, :, :, d] = 1.0
+    ka = np.zeros((1, 1, T + 1, d + 1))
+    ka[0, 0, 0, d] = math.log(M) / scale
+    ka[0, 0, 1:, :d] = k64
+    va = np.zeros((1, 1, T + 1, d))
+    va[0, 0, 0] = pool_sum(v64, M) / M
+    va[0, 0, 1:] = v64[np.arange(M, N) % P]
+    ro, rl = oracle_mod.fwd_bottom_right(qa, ka, va, causal=True, scale=scale)
+    check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"split-K/V d={d}")
