@@ -174,3 +174,45 @@ def test_splitkv_at_the_maximum_length(oracle_mod, d):
     va[0, 0, 1:] = v64[np.arange(M, N) % P]
     ro, rl = oracle_mod.fwd_bottom_right(qa, ka, va, causal=True, scale=scale)
     check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"split-K/V d={d}")
+
+
+def test_varlen_at_the_maximum_length(oracle_mod):
+    # T = N packed tokens in two sequences: the first, of S1 tokens, holds
+    # only zero keys (closed forms as above, and within it the dK sum to 0
+    # and the dV to the sum of its dO); the second starts S1 tokens in, past
+    # 4M, and is short enough for the oracle to run whole.
+    d = 64
+    dev = torch.device("cuda:0")
+    S1 = M - 300
+    host, q, k, v, do = build(d, seed=90, with_dout=True)
+    qpool, vpool, ktail, dopool = host
+    cu = torch.tensor([0, S1, N], dtype=torch.int32, device=dev)
+    o, lse = ea.fwd_varlen(q[0], k[0], v[0], cu, S1, causal=True)
+    dq, dk, dv = ea.bwd_varlen(q[0], k[0], v[0], o, lse, do[0], cu, S1, causal=True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, P - 1, P, 1 << 20, S1 - 1]
+    ro = np.stack([pool_sum(vpool, i + 1) / (i + 1) for i in rows])
+    rl = np.log(np.asarray(rows, dtype=np.float64) + 1.0)
+    check(o[0, rows].float().cpu().numpy(), lse[0, rows].cpu().numpy(), ro, rl,
+          "first sequence")
+    assert not bool(dq[0, :S1].any()), "dQ of the first sequence is not 0"
+    for name, g, ref in (("dK", dk[0, :S1].double(), np.zeros(d)),
+                         ("dV", dv[0, :S1].double(), pool_sum(dopool, S1))):
+        s = g.sum(0).cpu().numpy()
+        bound = 2.0 ** -8 * g.abs().sum(0).cpu().numpy() + 1e-2 * np.abs(ref) + 1e-3
+        assert np.all(np.abs(s - ref) <= bound), (
+            f"sum of {name} over the first sequence: max |diff| {np.abs(s - ref).max()}")
+    # the second sequence alone
+    tok = np.arange(S1, N)
+    q2 = qpool[tok % P][None, None]
+    k2 = np.zeros((N - S1, d))
+    k2[M - S1:] = ktail
+    v2 = vpool[tok % P][None, None]
+    do2 = dopool[tok % P][None, None]
+    r2o, r2l = oracle_mod.fwd(q2, k2[None, None], v2, causal=True)
+    check(o[0, S1:].float().cpu().numpy(), lse[0, S1:].cpu().numpy(), r2o[0, 0], r2l[0, 0],
+          "second sequence")
+    rdq, rdk, rdv = oracle_mod.bwd(q2, k2[None, None], v2, do2, causal=True)
+    grad_ok("dQ second sequence", dq[0, S1:].float().cpu().numpy(), rdq[0, 0])
+    grad_ok("dK second sequence", dk[0, S1:].float().cpu().numpy(), rdk[0, 0])
+    grad_ok("dV second sequence", dv[0, S1:].float().cpu().numpy(), rdv[0, 0])
