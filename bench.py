@@ -102,6 +102,154 @@ def load_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+# Counter runs read by --traffic-from: run name -> this script's arguments.  Each run
+# is profiled three times, all with --copy-mib 512 (the calibration copy):
+#   rocprofv3 --pmc FETCH_SIZE -d DIR/<run>_FETCH_SIZE -o run --output-format csv
+#       -- python3 bench.py <args> --steps 2 --warmup 1 --copy-mib 512
+#   the same with WRITE_SIZE into DIR/<run>_WRITE_SIZE, and
+#   rocprofv3 --kernel-trace --stats -d DIR/<run>_trace -o run --output-format csv
+#       -- python3 bench.py <args> --steps 30
+TRAFFIC_RUNS = {
+    "step": "--no-sweep --cpu-seconds 0",
+    "fwd2": "--fwd-only 2", "fwd3": "--fwd-only 3", "fwd4": "--fwd-only 4",
+    "bwd4": "--bwd-only 4",
+    "decode": "--splitkv-only decode",
+    "sparse": "--sparse-only local_global",
+    "varlen": "--varlen-only docs",
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+CALIBRATION_KIB = 512 * 1024.0  # the copy reads and writes 512 MiB
+
+
+def kernel_label(mangled: str) -> str:
+    """Readable name of one of this library's kernels: the name and its template
+    arguments (element type, head dimension, flags)."""
+    import re
+
+    if mangled.startswith("attn::"):
+        return mangled.split("(")[0][len("attn::"):]
+    m = re.match(r"_ZN4attn\d+(\w+?)I(.*?)EEv", mangled)
+    if m is None:
+        return mangled
+    args = []
+    for t in re.finditer(r"DF16b|DF16_|Li(\d+)E|Lb([01])E", m.group(2)):
+        if t.group(0) == "DF16b":
+            args.append("__bf16")
+        elif t.group(0) == "DF16_":
+            args.append("_Float16")
+        elif t.group(1) is not None:
+            args.append(t.group(1))
+        else:
+            args.append("true" if t.group(2) == "1" else "false")
+    return m.group(1) + "<" + ", ".join(args) + ">"
+
+
+def counter_run(indir: str, run: str, timed: int = 30):
+    """Per-kernel HBM bytes per launch of one profiled run: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, averaged over the dispatches) scaled so the
+    calibration copy reads 512 MiB each, and the average duration of each
+    kernel's last `timed` traced dispatches (the timed launches)."""
+    import collections
+    import csv
+
+    def per_kernel(ctr):
+        agg = collections.defaultdict(list)
+        with open(os.path.join(indir, f"{run}_{ctr}", "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        res = {k: sum(v) / len(v) for k, v in agg.items()}
+        # the calibration copy is the run's largest copy (a run may hold smaller ones)
+        res[COPY_KERNEL] = max(agg[COPY_KERNEL])
+        return res
+
+    spans = collections.defaultdict(list)
+    with open(os.path.join(indir, f"{run}_trace", "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            spans[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    avg_us = {}
+    for k, v in spans.items():
+        last = sorted(v)[-timed:]
+        avg_us[k] = sum(e - b for b, e in last) / len(last) / 1e3
+
+    fetch, write = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
+    fs, ws = CALIBRATION_KIB / fetch[COPY_KERNEL], CALIBRATION_KIB / write[COPY_KERNEL]
+    out = {}
+    for k in fetch:
+        if not (k.startswith("_ZN4attn") or k.startswith("attn::")) or "clock_probe" in k:
+            continue
+        out[kernel_label(k)] = {
+            "kernel": kernel_label(k), "avg_us": avg_us.get(k),
+            "hbm_bytes_per_launch": (fetch[k] * fs + write[k] * ws) * 1024,
+            "fetch_kib_raw": fetch[k], "write_kib_raw": write[k],
+            "fetch_scale": fs, "write_scale": ws}
+    return out
+
+
+def traffic_from(indir: str, path: str = TRAFFIC_FILE):
+    """Write the traffic file from the counter runs under `indir` (the runs of
+    TRAFFIC_RUNS that are there), stamped with the current kernel-source hash."""
+    def has(run):
+        return all(os.path.exists(os.path.join(indir, f"{run}_{p}", f))
+                   for p, f in (("FETCH_SIZE", "run_counter_collection.csv"),
+                                ("WRITE_SIZE", "run_counter_collection.csv"),
+                                ("trace", "run_kernel_trace.csv")))
+
+    def pick(ks, prefix, suffix=""):
+        hits = [v for k, v in ks.items()
+                if (k == prefix or k.startswith(prefix + "<")) and k.endswith(suffix)]
+        if len(hits) != 1:
+            raise SystemExit(f"traffic: {len(hits)} kernels match {prefix}...{suffix}")
+        return hits[0]
+
+    def call(*parts):
+        return {"kernel": " + ".join(p["kernel"] for p in parts),
+                "avg_us": sum(p["avg_us"] for p in parts),
+                "hbm_bytes_per_launch": sum(p["hbm_bytes_per_launch"] for p in parts)}
+
+    rec = {"source_hash": kernel_source_hash(),
+           "note": "HBM bytes per launch (per call where one call launches several kernels), "
+                   "from rocprofv3 FETCH_SIZE and WRITE_SIZE scaled by a 512 MiB copy",
+           "kernels": {}}
+    kern = rec["kernels"]
+    if has("step"):
+        s = counter_run(indir, "step")
+        kern["fwd"] = pick(s, "fwd_mfma_kernel")
+        kern["bwd_dq"] = pick(s, "bwd_dq_kernel")
+        kern["bwd_dkdv"] = pick(s, "bwd_dkdv_kernel")
+    for n in (2, 3, 4):
+        if has(f"fwd{n}"):
+            f = counter_run(indir, f"fwd{n}")
+            kern[f"fwd_workload{n}"] = next(v for k, v in f.items() if k.startswith("fwd_mfma"))
+    if has("bwd4"):
+        b = counter_run(indir, "bwd4")
+        dq, kv = pick(b, "bwd_dq_kernel"), pick(b, "bwd_dkdv_kernel")
+        kern["bwd_workload4"] = call(dq, kv)
+        rec["bwd_workload4_kernels"] = {"bwd_dq": dq, "bwd_dkdv": kv}
+    if has("decode"):
+        c = counter_run(indir, "decode")
+        sp, cb = pick(c, "fwd_split_kernel"), pick(c, "split_combine_kernel")
+        kern["splitkv_decode"] = call(sp, cb)
+        rec["splitkv_decode_kernels"] = {"fwd_split": sp, "split_combine": cb}
+    if has("sparse"):
+        c = counter_run(indir, "sparse")
+        cp = pick(c, "sparse_compact_kernel")
+        fw = next(v for k, v in c.items() if k.startswith("fwd_mfma") and k.endswith(", 1>"))
+        kern["blocksparse_local_global"] = call(cp, fw)
+        rec["blocksparse_kernels"] = {"sparse_compact": cp, "fwd": fw}
+    if has("varlen"):
+        c = counter_run(indir, "varlen")
+        kern["varlen_docs"] = next(v for k, v in c.items()
+                                   if k.startswith("fwd_mfma") and k.endswith(", 2>"))
+        rec["varlen_backward_kernels"] = {k: v for k, v in c.items() if k.startswith("bwd")}
+    if not kern:
+        raise SystemExit(f"traffic: no complete counter run under {indir}")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    for k, v in kern.items():
+        print(f"{k:26s} {v['avg_us']:9.1f} us {v['hbm_bytes_per_launch'] / 1e9:7.3f} GB  {v['kernel']}")
+
+
 def roofline_mfma(tflops: float, traffic_key: str | None):
     """A sweep entry's roofline: algorithmic TFLOP/s against the dense bf16
     peak, with the HBM bytes per call from the counters when they were taken
@@ -593,7 +741,13 @@ def main():
     ap.add_argument("--splitkv-only", default="", metavar="NAME",
                     help="time only the split-K/V forward of cache workload NAME "
                          "(decode, append) and print its JSON line")
+    ap.add_argument("--traffic-from", default="", metavar="DIR",
+                    help="no GPU run: write profiles/traffic.json from the rocprofv3 counter "
+                         "runs under DIR (named as in TRAFFIC_RUNS)")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -1,6 +1,6 @@
-"""Host-side logic of bench.py (no GPU): the single-GPU refusal and the
+"""Host-side logic of bench.py (no GPU): the single-GPU refusal, the
 HBM-traffic record that is only reported for the kernel sources it was
-measured on."""
+measured on, and its derivation from rocprofv3 counter runs."""
 import json
 import os
 import subprocess
@@ -45,3 +45,50 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
     (src / "k.hip").write_text("int f() { return 2; }\n")
     assert bench.kernel_source_hash() != h1
 
+
+def _counter_csv(path, rows):
+    path.mkdir()
+    lines = ["Kernel_Name,Counter_Name,Counter_Value"]
+    lines += [f"{k},C,{v}" for k, v in rows]
+    (path / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+
+
+def test_traffic_from_counter_runs(tmp_path):
+    """The traffic file derived from a synthetic counter run: each counter is
+    scaled so the largest copy reads 512 MiB, averaged over a kernel's
+    dispatches, and durations are the last traced dispatches' mean."""
+    fwd = "_ZN4attn15fwd_mfma_kernelIDF16bLi64ELb1ELi0EEEvPKT_"
+    dq = "_ZN4attn13bwd_dq_kernelIDF16bLi64ELb1ELb0ELb1EEEvPKT_"
+    kv = "_ZN4attn15bwd_dkdv_kernelIDF16bLi64ELb1ELb0ELb0EEEvPKT_"
+    cp = bench.COPY_KERNEL
+    # FETCH reads half of the copy's bytes (scale 2), WRITE all of them (scale 1);
+    # a smaller copy in the same run must not be taken for the calibration.
+    _counter_csv(tmp_path / "step_FETCH_SIZE",
+                 [(cp, 1024.0), (cp, 262144.0), (fwd, 100.0), (fwd, 300.0), (dq, 50.0), (kv, 10.0)])
+    _counter_csv(tmp_path / "step_WRITE_SIZE",
+                 [(cp, 524288.0), (fwd, 40.0), (dq, 20.0), (kv, 30.0)])
+    tr = tmp_path / "step_trace"
+    tr.mkdir()
+    spans = [(fwd, 0, 1000), (fwd, 5000, 7000), (dq, 1000, 4000), (kv, 4000, 4500)]
+    (tr / "run_kernel_trace.csv").write_text(
+        "Kernel_Name,Start_Timestamp,End_Timestamp\n"
+        + "".join(f"{k},{b},{e}\n" for k, b, e in spans))
+    out = tmp_path / "traffic.json"
+    bench.traffic_from(str(tmp_path), str(out))
+    rec = json.loads(out.read_text())
+    assert rec["source_hash"] == bench.kernel_source_hash()
+    k = rec["kernels"]
+    assert k["fwd"]["kernel"] == "fwd_mfma_kernel<__bf16, 64, true, 0>"
+    assert k["bwd_dq"]["kernel"] == "bwd_dq_kernel<__bf16, 64, true, false, true>"
+    assert k["fwd"]["hbm_bytes_per_launch"] == (200.0 * 2 + 40.0) * 1024
+    assert k["bwd_dq"]["hbm_bytes_per_launch"] == (50.0 * 2 + 20.0) * 1024
+    assert k["bwd_dkdv"]["hbm_bytes_per_launch"] == (10.0 * 2 + 30.0) * 1024
+    assert k["fwd"]["avg_us"] == 1.5 and k["bwd_dq"]["avg_us"] == 3.0
+    assert set(k) == {"fwd", "bwd_dq", "bwd_dkdv"}  # only the runs that are there
+
+
+def test_kernel_label_of_plain_and_template_kernels():
+    assert bench.kernel_label("_ZN4attn16split_combine_kernelIDF16_Li256EEEvPKf") == \
+        "split_combine_kernel<_Float16, 256>"
+    assert bench.kernel_label("attn::sparse_compact_kernel(unsigned char const*)") == \
+        "sparse_compact_kernel"
