@@ -16,7 +16,9 @@
 //         are 0.  -D seeds the accumulator of dP = dO V^T, so the matrix
 //         cores return dP - D directly.
 //   dkdv: one workgroup per (batch, kv head, block of 128 keys); each wave
-//         keeps its 32 keys' K and V as matrix-core operands in registers and
+//         keeps its 32 keys' K and V as matrix-core operands in registers
+//         (at d = 128 V stays in LDS, read per product, so that two
+//         workgroups fit on a CU) and
 //         accumulates dK^T, dV^T over every query tile of every query head of
 //         the group (so grouped-query heads are summed on chip).  Query tiles
 //         (Q, dO and the statistics) stream through LDS.  When that grid is
@@ -44,13 +46,20 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 
 // Measured choices (same-box A/B each; the alternatives are not kept):
 //  - Waves per SIMD: the dK/dV kernel runs 3 at d = 64 (168 registers, with
-//    operand reads in pairs and fenced phases) and 1 at d = 128 and 256 (the
-//    dK, dV accumulators and resident K, V take 336-354 registers); the dQ
-//    kernel runs 3 at d = 64 and 2 at d = 128.  Against 2/2/1: +5% on the
-//    causal B=8 H=16 N=2048 d=64 backward, +7-9% on the d = 128 cases.
-//  - Raised wave priority (s_setprio 1) in any matrix-core phase of the dK/dV
-//    or dQ kernel, or a priority falling with the remaining tiles: 0 to -3%
-//    on the d = 64 and d = 128 backward, so neither kernel raises it.
+//    operand reads in pairs and fenced phases), 2 at d = 128 and 1 at d = 256
+//    (the dK, dV accumulators and resident K, V take 336-354 registers); the
+//    dQ kernel runs 3 at d = 64 and 2 at d = 128.  Against 2/2/1: +5% on the
+//    causal B=8 H=16 N=2048 d=64 backward.  d = 128 dK/dV at 2 waves (V in
+//    LDS, 32-query tiles) against 1 wave (V in registers, 64-query tiles):
+//    +4 to +10% on the d = 128 backward, but -7% on the small query-head
+//    split case B=1 Hq=32 Hkv=8 N=2048, where one round of workgroups cannot
+//    hide the shorter prefetch distance.
+//  - Raised wave priority (s_setprio 1) in any matrix-core phase of the dQ
+//    kernel or of the dK/dV kernel at 1 or 3 waves per SIMD, or a priority
+//    falling with the remaining tiles: 0 to -3%, so they do not raise it.
+//    At d = 128 (2 waves per SIMD) the dK/dV kernel raises it for the S and
+//    dP products: +1 to +3.6%; around the dV/dK products instead: +0 to
+//    +2.6%; fences between the dV/dK feature blocks: -1 to +1%.
 //  - d = 64 dK/dV at three waves: fences between the operand groups of the
 //    S and dP products (without them 3 registers spill, -2% causal), none
 //    between the dV/dK products (+3% causal against one per feature block).
@@ -96,12 +105,18 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 template <int D>
 struct DkdvCfg {
   static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
-  static constexpr int BQ = 64;    // queries per tile (two 32-query sub-blocks)
+  // d = 128: V of the workgroup's keys sits in LDS (read as the dP
+  // product's operand) instead of registers, and query tiles hold one
+  // 32-query sub-block, so that registers (256) and LDS (64.5 KiB) allow two
+  // workgroups per CU.
+  static constexpr bool VLDS = D == 128;
+  static constexpr int BQ = VLDS ? 32 : 64;  // queries per tile (32-query sub-blocks)
   static constexpr int NBUF = D == 64 ? 3 : 2;
-  static constexpr int WPE = D == 64 ? 3 : 1;  // waves per SIMD
+  static constexpr int WPE = D == 64 ? 3 : D == 128 ? 2 : 1;  // waves per SIMD
   static constexpr int TILEB = BQ * D * 2;
   static constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q | dO | D | LSE*log2e
-  static constexpr size_t LDS = (size_t)NBUF * STAGEB;
+  static constexpr int VB = VLDS ? BKV * D * 2 : 0;       // V of the key block
+  static constexpr size_t LDS = (size_t)NBUF * STAGEB + VB;
 };
 
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
@@ -180,8 +195,12 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   const int key0 = kblk * BKV + w * 32;  // first key of this wave
   const int krow = key0 + l32;           // key owned by this lane
 
-  // K^T and V^T operands of this wave's 32 keys, resident (zero past N).
-  V8 kreg[NQC], vreg[NQC];
+  // K^T and V^T operands of this wave's 32 keys, resident (zero past N);
+  // with VLDS, V of the workgroup's 128 keys goes to LDS instead (a
+  // swizzled [BKV][D] tile after the query stages, waited for with them).
+  constexpr bool VLDS = Cfg::VLDS;
+  V8 kreg[NQC], vreg[VLDS ? 1 : NQC];
+  char* const vtile = smem + NBUF * STAGEB;
   {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kvoff, slice_bytes(N, krs, D));
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kvoff, slice_bytes(N, krs, D));
@@ -189,7 +208,18 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     for (int cc = 0; cc < NQC; ++cc) {
       const uint32_t off = (uint32_t)((krow * krs + cc * 16 + hf * 8) * 2);
       kreg[cc] = bitcast<V8>(buf_load16(rk, off) ^ qsign);  // scale's sign rides on K here
-      vreg[cc] = bitcast<V8>(buf_load16(rv, off));
+      if constexpr (!VLDS) vreg[cc] = bitcast<V8>(buf_load16(rv, off));
+    }
+    if constexpr (VLDS) {
+      constexpr int VPW = Cfg::VB / 1024 / 4;  // 1 KiB pieces per wave
+#pragma unroll
+      for (int i = 0; i < VPW; ++i) {
+        const int o = (w * VPW + i) * 1024 + lane * 16;
+        const int row = o / ROWB;
+        const int ch = ((o % ROWB) >> 4) ^ swz<D>(row);
+        buf_load16_lds(rv, vtile + (w * VPW + i) * 1024,
+                       (uint32_t)(((kblk * BKV + row) * krs + ch * 8) * 2));
+      }
     }
   }
   f32x16 dkacc[NMB], dvacc[NMB];
@@ -239,7 +269,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     goffq[i] = gpiece(i, qrs);
     goffo[i] = gpiece(i, ors);
   }
-  const uint32_t soff = (uint32_t)((lane >> 4) * Np * 4 + (lane & 15) * 16);
+  constexpr int SLN = BQ / 4;  // lanes per statistics row of a tile (16 bytes each)
+  const uint32_t soff = (uint32_t)((lane / SLN) * Np * 4 + (lane % SLN) * 16);
   auto issue = [&](int it) {
     const int hq = g * group + hs0 + it % nh;
     const int qt = qtile_of(it);
@@ -254,8 +285,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       buf_load16_lds(rq, base + (w * PW + i) * 1024, gq + tq);
       buf_load16_lds(rdo, base + TILEB + (w * PW + i) * 1024, go + to);
     }
-    if (w == 0 && lane < 32) {
-      // this head's two statistics rows (lanes 0-15: -D, 16-31: LSE log2 e)
+    if (w == 0 && lane < 2 * SLN) {
+      // this head's two statistics rows (lanes 0..SLN-1: -D, then LSE log2 e)
       // from the slice's (or packed sequence's) first row on.  The buffer
       // ends right after the LSE row's last row of the slice, so rows past
       // it read LSE = 0: batched slices have zero padding there anyway, and a
@@ -306,7 +337,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // each group fenced off from the scheduler so the reads are not all
   // hoisted, where registers are tight: d = 256 (K, V, dK and dV already
   // hold 384) and d = 64 at three waves per SIMD (168 each).
-  constexpr int CG = D > 128 ? 2 : (Cfg::WPE >= 3 ? 2 : NQC);
+  constexpr int CG = (D > 128 || Cfg::WPE >= 2) ? 2 : NQC;
   constexpr bool FENCE_C = D > 128;  // a fence per feature block of the dV/dK products
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
                     int qfirst, f32x16& sacc, f32x16& pacc) {
@@ -331,16 +362,20 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     sacc = f32x16{};
 #pragma unroll
     for (int c0 = 0; c0 < NQC; c0 += CG) {
-      u32x4 qa[CG], da[CG];
+      u32x4 qa[CG], da[CG], va[VLDS ? CG : 1];
 #pragma unroll
       for (int cc = 0; cc < CG; ++cc) {
         qa[cc] = lds_read16(qtile + qbase * ROWB + qo(c0 + cc));
         da[cc] = lds_read16(dotile + qbase * ROWB + qo(c0 + cc));
+        if constexpr (VLDS) va[cc] = lds_read16(vtile + w * 32 * ROWB + qo(c0 + cc));
       }
 #pragma unroll
       for (int cc = 0; cc < CG; ++cc) {
         sacc = mfma32(bitcast<V8>(qa[cc]), kreg[c0 + cc], sacc);
-        pacc = mfma32(bitcast<V8>(da[cc]), vreg[c0 + cc], pacc);
+        if constexpr (VLDS)
+          pacc = mfma32(bitcast<V8>(da[cc]), bitcast<V8>(va[cc]), pacc);
+        else
+          pacc = mfma32(bitcast<V8>(da[cc]), vreg[c0 + cc], pacc);
       }
       if constexpr (CG < NQC) __builtin_amdgcn_sched_barrier(0);
     }
@@ -412,7 +447,11 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       if (!(qs == 0 ? act0 : act1)) continue;  // wave-uniform
       f32x16 sacc, pacc;
       uint32_t pk[8], dsk[8];
+      // d = 128 (two workgroups per CU): the S and dP products run at raised
+      // wave priority, so one wave's products overlap the other's exp work
+      if constexpr (VLDS) __builtin_amdgcn_s_setprio(1);
       phaseA(qtile, dotile, dsum, qs * 32, qs == 0 ? qf0 : qf1, sacc, pacc);
+      if constexpr (VLDS) __builtin_amdgcn_s_setprio(0);
       phaseV(lse2, qs * 32, qs == 0 ? qf0 : qf1, qs == 0 ? diag0 : diag1, sacc, pacc, pk, dsk);
       phaseC(qtile, dotile, qs * 32, pk, dsk);
     }
