@@ -301,10 +301,45 @@ class ClockProbe:
                           "counter, one wave per XCD on a second stream beside the steps"}
 
 
-def environment(dev):
-    """Where the numbers were taken: device, software versions, host."""
-    import subprocess
+HIP_DEVICE_ATTRIBUTE_CLOCK_RATE = 5  # hipDeviceAttributeClockRate (kHz), hip_runtime_api.h
 
+
+def hip_version_string():
+    """HIP version of the installed toolchain, from its version header."""
+    import re
+
+    try:
+        with open("/opt/rocm/include/hip/hip_version.h") as f:
+            text = f.read()
+    except OSError:
+        return None
+    v = dict(re.findall(r"#define HIP_VERSION_(MAJOR|MINOR|PATCH|GITHASH)\s+\"?([^\s\"]*)", text))
+    if not all(k in v for k in ("MAJOR", "MINOR", "PATCH")):
+        return None
+    return f"HIP version: {v['MAJOR']}.{v['MINOR']}.{v['PATCH']}" + (
+        f"-{v['GITHASH']}" if v.get("GITHASH") else "")
+
+
+def max_sclk_mhz(index: int):
+    """Peak engine clock of device `index` from the HIP runtime torch has
+    loaded (by soname, so no second runtime is opened).  Asked in-process:
+    a child tool (rocminfo) would, under a profiler that preloads its library
+    into every process, initialise the GPU in the child before it execs."""
+    import ctypes
+
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        val = ctypes.c_int(0)
+        rc = hip.hipDeviceGetAttribute(ctypes.byref(val), HIP_DEVICE_ATTRIBUTE_CLOCK_RATE, index)
+    except (OSError, AttributeError):
+        return None
+    return val.value // 1000 if rc == 0 and val.value > 0 else None
+
+
+def environment(dev):
+    """Where the numbers were taken: device, software versions, host.  Read
+    from files and in-process calls only: this process holds the GPU, and no
+    child program is started."""
     import torch
 
     props = torch.cuda.get_device_properties(dev)
@@ -317,12 +352,7 @@ def environment(dev):
             env["rocm"] = f.read().strip()
     except OSError:
         env["rocm"] = None
-    try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
-                             timeout=30).stdout
-        env["hipcc"] = next((l.strip() for l in out.splitlines() if "HIP version" in l), None)
-    except Exception:
-        env["hipcc"] = None
+    env["hipcc"] = hip_version_string()
     try:
         with open("/proc/cpuinfo") as f:
             env["host_cpu"] = next((l.split(":", 1)[1].strip() for l in f if
@@ -330,25 +360,12 @@ def environment(dev):
     except OSError:
         env["host_cpu"] = None
     env["host_cpus"] = os.cpu_count()
-    # the peak recomputed from this device: CUs x 4096 bf16 FLOP/clk/CU x the
-    # maximum engine clock rocminfo reports for its gfx agent
-    env["max_sclk_mhz"] = env["peak_bf16_tflops_at_max_sclk"] = None
-    try:
-        out = subprocess.run(["/opt/rocm/bin/rocminfo"], capture_output=True, text=True,
-                             timeout=60).stdout
-        agent = None
-        for line in out.splitlines():
-            line = line.strip()
-            if line.startswith("Name:"):
-                agent = line.split(":", 1)[1].strip()
-            elif line.startswith("Max Clock Freq. (MHz):") and agent and agent.startswith("gfx"):
-                mhz = int(line.split(":", 1)[1].strip())
-                env["max_sclk_mhz"] = mhz
-                env["peak_bf16_tflops_at_max_sclk"] = round(
-                    props.multi_processor_count * 4096 * mhz * 1e6 / 1e12, 1)
-                break
-    except Exception:
-        pass
+    # the peak recomputed from this device: CUs x 4096 bf16 FLOP/clk/CU x its
+    # peak engine clock
+    mhz = max_sclk_mhz(dev.index if dev.index is not None else 0)
+    env["max_sclk_mhz"] = mhz
+    env["peak_bf16_tflops_at_max_sclk"] = (
+        round(props.multi_processor_count * 4096 * mhz * 1e6 / 1e12, 1) if mhz else None)
     return env
 
 

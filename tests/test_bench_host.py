@@ -92,3 +92,21 @@ def test_kernel_label_of_plain_and_template_kernels():
         "split_combine_kernel<_Float16, 256>"
     assert bench.kernel_label("attn::sparse_compact_kernel(unsigned char const*)") == \
         "sparse_compact_kernel"
+
+
+def test_environment_starts_no_child_program(monkeypatch):
+    """bench.py's environment record is read from files and in-process calls:
+    under a profiler that preloads itself into every process, a child tool
+    would initialise the GPU and then exec."""
+    import subprocess
+
+    def refuse(*a, **k):
+        raise AssertionError("child process started")
+
+    monkeypatch.setattr(subprocess, "run", refuse)
+    monkeypatch.setattr(subprocess, "Popen", refuse)
+    v = bench.hip_version_string()
+    if os.path.exists("/opt/rocm/include/hip/hip_version.h"):
+        assert v.startswith("HIP version: ") and v.count(".") >= 2
+    mhz = bench.max_sclk_mhz(0)  # None without a GPU
+    assert mhz is None or mhz > 0
