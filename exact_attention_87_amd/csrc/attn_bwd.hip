@@ -51,9 +51,8 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 //    dQ kernel runs 3 at d = 64 and 2 at d = 128.  Against 2/2/1: +5% on the
 //    causal B=8 H=16 N=2048 d=64 backward.  d = 128 dK/dV at 2 waves (V in
 //    LDS, 32-query tiles) against 1 wave (V in registers, 64-query tiles):
-//    +4 to +10% on the d = 128 backward, but -7% on the small query-head
-//    split case B=1 Hq=32 Hkv=8 N=2048, where one round of workgroups cannot
-//    hide the shorter prefetch distance.
+//    +4 to +12% on the d = 128 backward, except on causal query-head splits
+//    (-9 to -11%), which keep the 1-wave layout.
 //  - Raised wave priority (s_setprio 1) in any matrix-core phase of the dQ
 //    kernel or of the dK/dV kernel at 1 or 3 waves per SIMD, or a priority
 //    falling with the remaining tiles: 0 to -3%, so they do not raise it.
@@ -102,17 +101,22 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <int D>
+// WIDE: one workgroup per CU with V in registers (the causal query-head
+// split at d = 128, below).
+template <int D, bool WIDE = false>
 struct DkdvCfg {
   static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
   // d = 128: V of the workgroup's keys sits in LDS (read as the dP
   // product's operand) instead of registers, and query tiles hold one
   // 32-query sub-block, so that registers (256) and LDS (64.5 KiB) allow two
-  // workgroups per CU.
-  static constexpr bool VLDS = D == 128;
+  // workgroups per CU.  Not for causal query-head splits: those grids are
+  // one or two rounds whose heaviest key blocks set the launch's length, and
+  // a key block sharing its CU with another workgroup runs longer (-9 to
+  // -11% on causal split shapes, +7% on a non-causal one).
+  static constexpr bool VLDS = D == 128 && !WIDE;
   static constexpr int BQ = VLDS ? 32 : 64;  // queries per tile (32-query sub-blocks)
   static constexpr int NBUF = D == 64 ? 3 : 2;
-  static constexpr int WPE = D == 64 ? 3 : D == 128 ? 2 : 1;  // waves per SIMD
+  static constexpr int WPE = D == 64 ? 3 : VLDS ? 2 : 1;  // waves per SIMD
   static constexpr int TILEB = BQ * D * 2;
   static constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q | dO | D | LSE*log2e
   static constexpr int VB = VLDS ? BKV * D * 2 : 0;       // V of the key block
@@ -120,14 +124,14 @@ struct DkdvCfg {
 };
 
 template <typename T, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D>::WPE, DkdvCfg<D>::WPE)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvCfg<D, CAUSAL && SPLIT>::WPE, DkdvCfg<D, CAUSAL && SPLIT>::WPE)))
 void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                      const T* __restrict__ V, const T* __restrict__ dO,
                      const float* __restrict__ stats, T* __restrict__ dK,
                      T* __restrict__ dV, int Hq, int Hkv, int Nmax, int nkb, int xg, int desc, Layout lay, float c,
                      float dk_scale, uint32_t qsign, const int* __restrict__ cu_seqlens,
                      int ntok, int nsplit_arg, float* __restrict__ part) {
-  using Cfg = DkdvCfg<D>;
+  using Cfg = DkdvCfg<D, CAUSAL && SPLIT>;
   const int nsplit = SPLIT ? nsplit_arg : 1;
   using V8 = typename Elem<T>::v8;
   constexpr int BKV = Cfg::BKV, BQ = Cfg::BQ, NBUF = Cfg::NBUF, TILEB = Cfg::TILEB;
@@ -927,10 +931,11 @@ static hipError_t dkdv_t(const BwdArgs& a) {
   const Layout lay = layout_of(a);
   const int desc = a.causal ? 1 : 0;  // descending query-tile walk (qtile_of)
   if (nsplit > 1) {
-    const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, true>, Cfg::LDS);
+    constexpr size_t lds = DkdvCfg<D, CAUSAL>::LDS;
+    const hipError_t e = allow_lds(bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, true>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, VARLEN, true>), dim3((unsigned)grid),
-                       dim3(256), Cfg::LDS, a.stream, (const T*)a.q, (const T*)a.k,
+                       dim3(256), lds, a.stream, (const T*)a.q, (const T*)a.k,
                        (const T*)a.v, (const T*)a.dout, a.stats, (T*)a.dk, (T*)a.dv, a.Hq,
                        a.Hkv, a.N, nkb, 0, desc, lay, k.c, a.scale, k.qsign, a.cu_seqlens, a.T, nsplit,
                        a.part);
