@@ -1,12 +1,14 @@
 // C ABI of the exact-attention library (declared in include/attn.h):
 // argument validation, the per-device architecture check and dispatch to the
-// gfx950 kernels.  Nothing here allocates device memory or synchronises.
+// gfx950 kernels.  Nothing here allocates device memory or synchronises
+// (unless ATTN_DEBUG is set, below).
 #include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <initializer_list>
 
@@ -42,6 +44,23 @@ attn_status check_device() {
     g_arch_state[dev].store(st, std::memory_order_relaxed);
   }
   return st == 1 ? ATTN_OK : ATTN_ERR_UNSUPPORTED_DEVICE;
+}
+
+// ATTN_DEBUG set to anything but "" or "0" in the environment (read at each
+// call): every entry point waits for the kernels it launched, so a kernel
+// that fails reports ATTN_ERR_HIP from the call that launched it instead of
+// from a later HIP call.  For debugging only: it serialises the caller's
+// stream, and a stream under graph capture cannot be synchronised.
+bool debug_sync() {
+  const char* v = std::getenv("ATTN_DEBUG");
+  return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+
+// Status of an entry point whose launches returned e on `stream`.
+attn_status launched(hipError_t e, hipStream_t stream) {
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  if (debug_sync() && hipStreamSynchronize(stream) != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
 }
 
 struct Range {
@@ -187,7 +206,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   if (st != ATTN_OK) return st;
   attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dt,
                   (hipStream_t)stream};
-  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_fwd(a), a.stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d, attn_dtype dtype) {
@@ -214,8 +233,7 @@ attn_status bwd_launch(attn::BwdArgs* a, const void* q, const void* k, const voi
   a->dq = dq, a->dk = dk, a->dv = dv, a->stats = (float*)workspace;
   set_split(a, workspace);
   if (attn::launch_bwd_dq_stats(*a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dkdv(*a) != hipSuccess) return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return launched(attn::launch_bwd_dkdv(*a), a->stream);
 }
 }  // namespace
 
@@ -246,9 +264,7 @@ attn_status attn_probe_clock(unsigned long long* out, int nwg, unsigned ticks, v
   if (nwg < 1 || nwg > 64 || ticks < 1 || ticks > 200000000u) return ATTN_ERR_INVALID_ARG;
   const attn_status st = check_device();
   if (st != ATTN_OK) return st;
-  return attn::launch_clock_probe(out, nwg, ticks, (hipStream_t)stream) == hipSuccess
-             ? ATTN_OK
-             : ATTN_ERR_HIP;
+  return launched(attn::launch_clock_probe(out, nwg, ticks, (hipStream_t)stream), (hipStream_t)stream);
 }
 
 attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
@@ -291,7 +307,7 @@ attn_status attn_bwd_dq_stats(const void* q, const void* k, const void* v, const
   if (st != ATTN_OK) return st;
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse, a.dout = dout;
   a.stats = stats, a.dq = dq;
-  return attn::launch_bwd_dq_stats(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_bwd_dq_stats(a), a.stream);
 }
 
 attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* lse, float* stats,
@@ -307,7 +323,7 @@ attn_status attn_bwd_preprocess(const void* o, const void* dout, const float* ls
   st = check_device();
   if (st != ATTN_OK) return st;
   a.o = o, a.dout = dout, a.lse = lse, a.stats = stats;
-  return attn::launch_bwd_pre(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_bwd_pre(a), a.stream);
 }
 
 attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
@@ -332,7 +348,7 @@ attn_status attn_bwd_dkdv(const void* q, const void* k, const void* v, const voi
   if (st != ATTN_OK) return st;
   a.q = q, a.k = k, a.v = v, a.dout = dout, a.stats = stats;
   a.dk = dk, a.dv = dv;
-  return attn::launch_bwd_dkdv(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_bwd_dkdv(a), a.stream);
 }
 
 attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
@@ -349,7 +365,7 @@ attn_status attn_bwd_dq(const void* q, const void* k, const void* v, const void*
   st = check_device();
   if (st != ATTN_OK) return st;
   a.q = q, a.k = k, a.v = v, a.dout = dout, a.stats = (float*)stats, a.dq = dq;
-  return attn::launch_bwd_dq(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_bwd_dq(a), a.stream);
 }
 
 }  // extern "C"
@@ -424,7 +440,7 @@ attn_status attn_fwd_splitkv(const void* q, const void* k, const void* v, void* 
   attn::SplitArgs a{q,  k,  v, o,           lse,   workspace,  B,
                     Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dt,
                     (hipStream_t)stream};
-  return attn::launch_fwd_split(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_fwd_split(a), a.stream);
 }
 
 }  // extern "C"
@@ -500,7 +516,7 @@ attn_status fwd_blocksparse_impl(const void* q, const void* k, const void* v, vo
   a.mask_heads = mask_heads;
   if (strides)
     a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
-  return attn::launch_fwd_sparse(a, block_mask, workspace) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_fwd_sparse(a, block_mask, workspace), a.stream);
 }
 
 }  // namespace
@@ -600,7 +616,7 @@ attn_status fwd_varlen_impl(const void* q, const void* k, const void* v, void* o
   a.cu_seqlens = cu_seqlens;
   a.T = T;
   if (strides) a.lay = varlen_layout(strides);
-  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_fwd(a), a.stream);
 }
 
 
@@ -682,8 +698,7 @@ attn_status bwd_varlen_impl(const void* q, const void* k, const void* v, const v
     a.part = s > 1 ? (float*)((char*)workspace + stats) : nullptr;
   }
   if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return launched(attn::launch_bwd_dkdv(a), a.stream);
 }
 
 }  // namespace
@@ -745,7 +760,7 @@ attn_status attn_fwd_splitkv_strided(const void* q, const void* k, const void* v
                     Hq, Hkv, Nq, Nk, d, causal == 1, scale, num_splits, (attn::Dtype)dt,
                     (hipStream_t)stream};
   a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
-  return attn::launch_fwd_split(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_fwd_split(a), a.stream);
 }
 
 attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -769,7 +784,7 @@ attn_status attn_fwd_strided(const void* q, const void* k, const void* v, void* 
   attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal == 1, scale, (attn::Dtype)dt,
                   (hipStream_t)stream};
   a.lay = attn::Layout{strides_at(strides, 0), strides_at(strides, 1), strides_at(strides, 2)};
-  return attn::launch_fwd(a) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched(attn::launch_fwd(a), a.stream);
 }
 
 attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const void* o,
@@ -814,8 +829,7 @@ attn_status attn_bwd_strided(const void* q, const void* k, const void* v, const 
   set_split(&a, workspace);
   // dQ first: it also writes the row statistics the dK/dV stage reads
   if (attn::launch_bwd_dq_stats(a) != hipSuccess) return ATTN_ERR_HIP;
-  if (attn::launch_bwd_dkdv(a) != hipSuccess) return ATTN_ERR_HIP;
-  return ATTN_OK;
+  return launched(attn::launch_bwd_dkdv(a), a.stream);
 }
 
 attn_status attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,

@@ -35,7 +35,11 @@
  *  - Outputs must not overlap inputs or each other.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the default stream).  The call returns once the kernels are launched;
- *    it never synchronises.
+ *    it never synchronises, unless the environment variable ATTN_DEBUG is
+ *    set (to anything but "" or "0"; read at every call): then every entry
+ *    point synchronises `stream` after its launches and returns
+ *    ATTN_ERR_HIP if they failed, so a failing kernel is reported by the
+ *    call that launched it (debugging only; not under graph capture).
  *  - Sizes: N <= 2^22 and B * Hq <= 2^24, and every launch must fit one
  *    dispatch of fewer than 2^32 work-items: B * Hq * (N rounded up to 128)
  *    * max(8, d / 8) < 2^32 (larger requests return ATTN_ERR_UNSUPPORTED).
