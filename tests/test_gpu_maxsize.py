@@ -96,7 +96,7 @@ def grad_ok(name, g, r):
     assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 2e-2, f"{name}: Frobenius"
 
 
-@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_forward_at_the_maximum_length(oracle_mod, d):
     host, q, k, v, _ = build(d, seed=60 + d)
     o, lse = ea.fwd(q, k, v, causal=True)
@@ -116,9 +116,10 @@ def test_forward_at_the_maximum_length(oracle_mod, d):
           al[0, 0, 1:], f"last rows d={d}")
 
 
-def test_backward_at_the_maximum_length(oracle_mod):
-    d = 64
-    host, q, k, v, do = build(d, seed=70, with_dout=True)
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_at_the_maximum_length(oracle_mod, d):
+    # d = 128: the dK/dV stage with V in LDS and 32-query tiles
+    host, q, k, v, do = build(d, seed=70 + d, with_dout=True)
     o, lse = ea.fwd(q, k, v, causal=True)
     dq, dk, dv = ea.bwd(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
