@@ -101,8 +101,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 }
 
 // ---------------------------------------------------------------- dK, dV
-// WIDE: one workgroup per CU with V in registers (the causal query-head
-// split at d = 128, below).
+// The kernel takes WIDE = CAUSAL && SPLIT: with it, d = 128 keeps V in
+// registers with 64-query tiles at one workgroup per CU (the layout d = 256
+// always uses).
 template <int D, bool WIDE = false>
 struct DkdvCfg {
   static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
