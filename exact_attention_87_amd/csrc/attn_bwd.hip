@@ -17,8 +17,9 @@
 //         cores return dP - D directly.
 //   dkdv: one workgroup per (batch, kv head, block of 128 keys); each wave
 //         keeps its 32 keys' K and V as matrix-core operands in registers
-//         (at d = 128 V stays in LDS, read per product, so that two
-//         workgroups fit on a CU) and
+//         (at d = 128 and 256 V stays in LDS, read per product, which lets
+//         two workgroups share a CU at d = 128 and frees registers at 256)
+//         and
 //         accumulates dK^T, dV^T over every query tile of every query head of
 //         the group (so grouped-query heads are summed on chip).  Query tiles
 //         (Q, dO and the statistics) stream through LDS.  When that grid is
@@ -47,7 +48,8 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 // Measured choices (same-box A/B each; the alternatives are not kept):
 //  - Waves per SIMD: the dK/dV kernel runs 3 at d = 64 (168 registers, with
 //    operand reads in pairs and fenced phases), 2 at d = 128 and 1 at d = 256
-//    (the dK, dV accumulators and resident K, V take 336-354 registers); the
+//    (with resident K and V, the dK, dV accumulators and K, V took 336-354
+//    registers at d = 128); the
 //    dQ kernel runs 3 at d = 64 and 2 at d = 128.  Against 2/2/1: +5% on the
 //    causal B=8 H=16 N=2048 d=64 backward.  d = 128 dK/dV at 2 waves (V in
 //    LDS, 32-query tiles) against 1 wave (V in registers, 64-query tiles):
@@ -102,22 +104,24 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 
 // ---------------------------------------------------------------- dK, dV
 // The kernel takes WIDE = CAUSAL && SPLIT: with it, d = 128 keeps V in
-// registers with 64-query tiles at one workgroup per CU (the layout d = 256
-// always uses).
+// registers with 64-query tiles at one workgroup per CU.
 template <int D, bool WIDE = false>
 struct DkdvCfg {
   static constexpr int BKV = 128;  // keys per workgroup (4 waves x 32)
-  // d = 128: V of the workgroup's keys sits in LDS (read as the dP
-  // product's operand) instead of registers, and query tiles hold one
-  // 32-query sub-block, so that registers (256) and LDS (64.5 KiB) allow two
-  // workgroups per CU.  Not for causal query-head splits: those grids are
-  // one or two rounds whose heaviest key blocks set the launch's length, and
-  // a key block sharing its CU with another workgroup runs longer (-9 to
-  // -11% on causal split shapes, +7% on a non-causal one).
-  static constexpr bool VLDS = D == 128 && !WIDE;
+  // VLDS: V of the workgroup's keys sits in LDS (read as the dP product's
+  // operand) instead of registers, and query tiles hold one 32-query
+  // sub-block.  d = 128: registers (256) and LDS (64.5 KiB) then allow two
+  // workgroups per CU; not for causal query-head splits, whose grids are one
+  // or two rounds with the heaviest key blocks setting the launch's length,
+  // where a key block sharing its CU with another workgroup runs longer (-9
+  // to -11% on causal split shapes, +7% on a non-causal one).  d = 256 (one
+  // workgroup per CU, 128.5 KiB of LDS): the 64 registers of V relieve the
+  // allocator (0-2 spilled values instead of 6-10), +4 to +9% on every d = 256
+  // shape measured, split or not.
+  static constexpr bool VLDS = (D == 128 && !WIDE) || D == 256;
   static constexpr int BQ = VLDS ? 32 : 64;  // queries per tile (32-query sub-blocks)
   static constexpr int NBUF = D == 64 ? 3 : 2;
-  static constexpr int WPE = D == 64 ? 3 : VLDS ? 2 : 1;  // waves per SIMD
+  static constexpr int WPE = D == 64 ? 3 : (VLDS && D == 128) ? 2 : 1;  // waves per SIMD
   static constexpr int TILEB = BQ * D * 2;
   static constexpr int STAGEB = 2 * TILEB + 2 * BQ * 4;  // Q | dO | D | LSE*log2e
   static constexpr int VB = VLDS ? BKV * D * 2 : 0;       // V of the key block
@@ -454,9 +458,9 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       uint32_t pk[8], dsk[8];
       // d = 128 (two workgroups per CU): the S and dP products run at raised
       // wave priority, so one wave's products overlap the other's exp work
-      if constexpr (VLDS) __builtin_amdgcn_s_setprio(1);
+      if constexpr (VLDS && D == 128) __builtin_amdgcn_s_setprio(1);
       phaseA(qtile, dotile, dsum, qs * 32, qs == 0 ? qf0 : qf1, sacc, pacc);
-      if constexpr (VLDS) __builtin_amdgcn_s_setprio(0);
+      if constexpr (VLDS && D == 128) __builtin_amdgcn_s_setprio(0);
       phaseV(lse2, qs * 32, qs == 0 ? qf0 : qf1, qs == 0 ? diag0 : diag1, sacc, pacc, pk, dsk);
       phaseC(qtile, dotile, qs * 32, pk, dsk);
     }

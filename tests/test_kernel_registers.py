@@ -17,7 +17,7 @@ from exact_attention_87_amd import _build
 
 CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                     "exact_attention_87_amd", "csrc")
-D256_MAX_SPILL = {"fwd_mfma_kernel": 0, "bwd_dkdv_kernel": 10, "bwd_dq_kernel": 0}
+D256_MAX_SPILL = {"fwd_mfma_kernel": 0, "bwd_dkdv_kernel": 2, "bwd_dq_kernel": 0}
 
 
 def kernel_table(source):
