@@ -294,6 +294,18 @@ def test_workload5_fwd_bwd_full_size_every_slice(oracle_mod):
     full_size_slices(oracle_mod, w, list(range(w.B * w.Hkv)))
 
 
+def test_gqa_backward_full_size_one_slice(oracle_mod):
+    """Workload 4's backward at its full size (B=1, Hq=32, Hkv=8, N=16384,
+    d=128, Q x 8, causal) in the launch the benchmark times: 128 key blocks x
+    8 kv heads fill the device, so the dK/dV stage runs unsplit, at two
+    waves per SIMD.  One (batch, kv head) slice, 4 query heads x 16384 rows
+    and 16384 keys, is compared whole (about 12 s of fp64 oracle)."""
+    w = attn_inputs.WORKLOADS[4].scaled(backward=True)
+    assert ea.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d, ea.ATTN_BF16) == \
+        w.B * w.Hq * 2 * w.N * 4  # statistics only: no query-head split
+    full_size_slices(oracle_mod, w, [5])
+
+
 def test_gqa_backward_reduced_length(oracle_mod):
     """Workload 4's heads (Hq=32, Hkv=8, d=128, Q x 8, causal) at N=2048."""
     w = attn_inputs.WORKLOADS[4].scaled(N=2048, backward=True, seed=41)
