@@ -306,6 +306,23 @@ def test_gqa_backward_full_size_one_slice(oracle_mod):
     full_size_slices(oracle_mod, w, [5])
 
 
+# The benchmark's other backward sweep shapes, with its seeds, at full size:
+# one (batch, head) slice each.
+SWEEP_SLICES = [
+    (attn_inputs.Workload("noncausal_bf16_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, False, "bf16",
+                          seed=6), 37),
+    (attn_inputs.Workload("causal_bf16_B4_H32_N4000_d128", 4, 32, 32, 4000, 128, True, "bf16",
+                          seed=3), 100),
+    (attn_inputs.Workload("noncausal_bf16_B1_H16_N8192_d256", 1, 16, 16, 8192, 256, False, "bf16",
+                          seed=9), 11),
+]
+
+
+@pytest.mark.parametrize("w,slice_", SWEEP_SLICES, ids=[w.name for w, _ in SWEEP_SLICES])
+def test_backward_sweep_shapes_full_size_one_slice(oracle_mod, w, slice_):
+    full_size_slices(oracle_mod, w, [slice_])
+
+
 def test_gqa_backward_reduced_length(oracle_mod):
     """Workload 4's heads (Hq=32, Hkv=8, d=128, Q x 8, causal) at N=2048."""
     w = attn_inputs.WORKLOADS[4].scaled(N=2048, backward=True, seed=41)
