@@ -216,6 +216,32 @@ def test_full_size_workload_sampled_rows(oracle_mod, wid):
     check_bf16(o_s, l_s, ro, rl, w.name)
 
 
+# The benchmark's other forward sweep shapes, with its seeds, at full size.
+SWEEP_SHAPES = [
+    attn_inputs.Workload("noncausal_bf16_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, False, "bf16",
+                         seed=6),
+    attn_inputs.Workload("noncausal_bf16_B1_H32_N8192_d128", 1, 32, 32, 8192, 128, False, "bf16",
+                         seed=7),
+    attn_inputs.Workload("causal_fp16_B1_H32_N8192_d128", 1, 32, 32, 8192, 128, True, "fp16",
+                         seed=8),
+    attn_inputs.Workload("noncausal_bf16_B1_H16_N8192_d256", 1, 16, 16, 8192, 256, False, "bf16",
+                         seed=9),
+]
+
+
+@pytest.mark.parametrize("w", SWEEP_SHAPES, ids=[w.name for w in SWEEP_SHAPES])
+def test_forward_sweep_shapes_sampled_rows(oracle_mod, w):
+    q, k, v = attn_inputs.make_workload(w, with_dout=False)
+    dev = gpu()
+    o, lse = ea.fwd(q.to(dev), k.to(dev), v.to(dev), causal=w.causal)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.B, w.Hq, w.N, 256, seed=w.seed)
+    o_s = o.reshape(-1, w.d)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+    l_s = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    ro, rl = oracle_mod.fwd_rows(q, k, v, rows, causal=w.causal)
+    check_bf16(o_s, l_s, ro, rl, w.name)  # a 16-bit bound, also for fp16 outputs
+
+
 def test_workload2_whole_output(oracle_mod):
     """Workload 2 (B=8 H=16 N=1024 d=64, non-causal) compared element by
     element over the whole output, in the launch the benchmark times."""
