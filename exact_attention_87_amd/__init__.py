@@ -326,7 +326,7 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
             raise ValueError(f"{name} must be [B, H, N, d]")
         if not t.is_cuda or t.stride(3) != 1:
             raise ValueError(f"{name} must be a device tensor with contiguous d")
-    if k.stride() != v.stride():
+    if not _same_strides(k, v):
         raise ValueError("k and v must share strides")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
@@ -378,7 +378,7 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
         for name, t in (("q", q), ("k", k), ("v", v)):
             if t.dim() != 4 or not t.is_cuda:
                 raise ValueError(f"{name} must be a 4-D device tensor [B, H, N, d]")
-        if k.stride() != v.stride() or k.shape != v.shape:
+        if not _same_strides(k, v):
             raise ValueError("k and v must share shape and strides")
         B, Hq, N, d = q.shape
         Hkv = k.shape[1]
@@ -445,7 +445,7 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
     Hkv = k.shape[0]
     if k.shape != v.shape or k.shape[1:] != (T, d):
         raise ValueError("k and v must be [Hkv, T, d] matching q")
-    if k.stride() != v.stride():
+    if not _same_strides(k, v):
         raise ValueError("k and v must share strides")
     _check_cu(cu_seqlens)
     if scale is None:
@@ -474,6 +474,16 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = False,
     return out, lse
 
 
+def _same_strides(a, b) -> bool:
+    """Whether two tensors of one shape lay out their elements alike.  The
+    stride of a dimension of size 1 never multiplies a nonzero index, so it is
+    not compared (torch gives such dimensions different strides depending on
+    how a tensor was made, e.g. a token-major [B, N, 1, d] tensor viewed as
+    [B, 1, N, d])."""
+    return tuple(a.shape) == tuple(b.shape) and all(
+        sa == sb for sa, sb, n in zip(a.stride(), b.stride(), a.shape) if n > 1)
+
+
 def _bhnd_strides(t):
     """(batch, head, row) element strides of a [B, H, N, d] view with a unit
     stride in d (any permutation of the first three axes in memory)."""
@@ -492,7 +502,7 @@ def fwd_strided(q, k, v, causal: bool = False, scale: float | None = None, out=N
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dim() != 4 or not t.is_cuda:
             raise ValueError(f"{name} must be a 4-D device tensor [B, H, N, d]")
-    if k.stride() != v.stride() or k.shape != v.shape:
+    if not _same_strides(k, v):
         raise ValueError("k and v must share shape and strides")
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -521,7 +531,7 @@ def bwd_strided(q, k, v, o, lse, dout, causal: bool = False, scale: float | None
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if t.dim() != 4 or not t.is_cuda:
             raise ValueError(f"{name} must be a 4-D device tensor [B, H, N, d]")
-    if k.stride() != v.stride() or o.stride() != dout.stride():
+    if not (_same_strides(k, v) and _same_strides(o, dout)):
         raise ValueError("k/v and o/dout must share strides")
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -530,7 +540,7 @@ def bwd_strided(q, k, v, o, lse, dout, causal: bool = False, scale: float | None
 
     def like(t, grad):
         if grad is not None:
-            if grad.stride() != t.stride() or grad.shape != t.shape:
+            if not _same_strides(grad, t):
                 raise ValueError("gradients must have their input's shape and strides")
             return grad
         return torch.empty_strided(t.shape, t.stride(), device=t.device, dtype=t.dtype)
@@ -563,7 +573,7 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool 
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if t.dim() != 3 or not t.is_cuda or t.stride(2) != 1:
             raise ValueError(f"{name} must be a device tensor [H, T, d] with contiguous d")
-    if k.stride() != v.stride() or o.stride() != dout.stride():
+    if not (_same_strides(k, v) and _same_strides(o, dout)):
         raise ValueError("k/v and o/dout must share strides")
     _check_cu(cu_seqlens)
     Hq, T, d = q.shape
@@ -574,7 +584,7 @@ def bwd_varlen(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, causal: bool 
 
     def like(t, grad):
         if grad is not None:
-            if grad.stride() != t.stride() or grad.shape != t.shape:
+            if not _same_strides(grad, t):
                 raise ValueError("gradients must have their input's shape and strides")
             return grad
         return torch.empty_strided(t.shape, t.stride(), device=t.device, dtype=t.dtype)

@@ -717,3 +717,18 @@ def test_noalloc_sizes():
 def test_noalloc_passes_validation():
     assert noalloc() == ea.ATTN_ERR_HIP  # no GPU here: stops at the device check
     assert noalloc(B=64, Hq=16, Hkv=16, N=4096) == ea.ATTN_ERR_INVALID_ARG  # fake buffers overlap
+
+
+def test_stride_comparison_ignores_size_one_dimensions():
+    """The binding compares the strides of tensors that must share a layout
+    only over dimensions of more than one element: a size-1 dimension's stride
+    is never used."""
+    import torch
+
+    a = torch.empty(2, 5, 1, 8).transpose(1, 2)   # [2, 1, 5, 8], token-major
+    b = torch.empty(2, 1, 5, 8)                   # dense: other size-1 stride
+    assert a.stride() != b.stride()
+    assert ea._same_strides(a, b)
+    c = torch.empty(2, 3, 5, 8).transpose(1, 2).contiguous().transpose(1, 2)  # [2, 5, 3, 8] -> view
+    assert not ea._same_strides(c, torch.empty(2, 3, 5, 8))  # real layout difference
+    assert not ea._same_strides(b, torch.empty(2, 1, 6, 8))  # shapes differ

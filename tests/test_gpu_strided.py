@@ -131,6 +131,27 @@ def test_backward_token_major(oracle_mod, d, causal):
         grads_ok(name, g, r)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_token_major_single_head_is_the_dense_backward_bitwise(d):
+    """One query and one kv head, token-major: torch gives the size-1 head
+    dimension of the forward's output and of dO different strides, which do
+    not change the layout (once rejected as a stride mismatch).  In memory the
+    layout is the dense one, so the gradients equal attn_bwd's bit for bit."""
+    dev = gpu()
+    q, k, v, do = attn_inputs.make(2, 1, 1, 211, d, "bf16", seed=50 + d, with_dout=True)
+    qt, kt, vt, dot = (t.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+                       for t in (q, k, v, do))
+    o, lse = ea.fwd_strided(qt, kt, vt, causal=True)
+    g1 = ea.bwd_strided(qt, kt, vt, o, lse, dot, causal=True)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    od, lsed = ea.fwd(qd, kd, vd, causal=True)
+    g2 = ea.bwd(qd, kd, vd, od, lsed, dod, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.contiguous(), od) and torch.equal(lse, lsed)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.contiguous(), b)
+
+
 def test_backward_packed_qkv(oracle_mod):
     # Q, K, V slices of one [B, N, Hq + 2 Hkv, d] buffer; dQ, dK, dV into
     # slices of one packed gradient buffer; O and dO token-major
