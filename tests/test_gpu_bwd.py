@@ -81,6 +81,19 @@ def test_bwd_head_maps(oracle_mod, heads, causal):
         check_grad(name, g, r)
 
 
+@pytest.mark.parametrize("heads,d", [((64, 1), 128), ((128, 8), 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_wide_head_groups(oracle_mod, heads, d, causal):
+    """64 query heads on one kv head, and 128 on 8: the dK/dV stage walks (or
+    splits) groups far wider than the workloads' 4."""
+    Hq, Hkv = heads
+    q, k, v, do = attn_inputs.make(1, Hq, Hkv, 200, d, "bf16", seed=Hq + d, with_dout=True)
+    dq, dk, dv = run(q, k, v, do, causal)
+    rq, rk, rv = oracle_mod.bwd(q, k, v, do, causal=causal)
+    for name, g, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check_grad(f"{name} Hq={Hq} Hkv={Hkv} d={d}", g, r)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.3])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_scales(oracle_mod, scale, causal):
