@@ -157,6 +157,9 @@ def counter_run(indir: str, run: str, timed: int = 30):
         with open(os.path.join(indir, f"{run}_{ctr}", "run_counter_collection.csv")) as f:
             for r in csv.DictReader(f):
                 agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        if COPY_KERNEL not in agg:
+            raise SystemExit(f"traffic: no calibration copy in {run}_{ctr} "
+                             "(profile the run with --copy-mib 512)")
         res = {k: sum(v) / len(v) for k, v in agg.items()}
         # the calibration copy is the run's largest copy (a run may hold smaller ones)
         res[COPY_KERNEL] = max(agg[COPY_KERNEL])

@@ -87,6 +87,20 @@ def test_traffic_from_counter_runs(tmp_path):
     assert set(k) == {"fwd", "bwd_dq", "bwd_dkdv"}  # only the runs that are there
 
 
+def test_traffic_from_needs_the_calibration_copy(tmp_path):
+    import pytest
+
+    kernel = "_ZN4attn15fwd_mfma_kernelIDF16bLi64ELb1ELi0EEEvPKT_"
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        _counter_csv(tmp_path / f"step_{ctr}", [(kernel, 1.0)])
+    tr = tmp_path / "step_trace"
+    tr.mkdir()
+    (tr / "run_kernel_trace.csv").write_text(
+        "Kernel_Name,Start_Timestamp,End_Timestamp\n" + kernel + ",0,1000\n")
+    with pytest.raises(SystemExit, match="calibration copy"):
+        bench.traffic_from(str(tmp_path), str(tmp_path / "traffic.json"))
+
+
 def test_kernel_label_of_plain_and_template_kernels():
     assert bench.kernel_label("_ZN4attn16split_combine_kernelIDF16_Li256EEEvPKf") == \
         "split_combine_kernel<_Float16, 256>"
