@@ -49,7 +49,11 @@
  *    the fp32 accumulators are at most 2^tau instead of 1.  bf16 outputs are
  *    therefore within range as long as (number of visible keys) * max|V| <
  *    2^98 (about 3e29; a plain online softmax allows up to 3.4e38).  fp16
- *    inputs cannot reach the limit (2^15 * 65504 * 2^22 < 2^128).
+ *    inputs cannot reach the limit (2^15 * 65504 * 2^22 < 2^128).  The
+ *    backward rounds P (at most 1 there) and dS = P * (dP - D) to the input
+ *    type for its dV, dK and dQ products (fp32 accumulation): with fp16 it
+ *    needs |dO_i . v_j - D_i| < 65504 wherever P_ij is not negligible, else
+ *    those gradients overflow; bf16 has fp32's range.
  *  - B == 0 or N == 0 is an empty problem: nothing is launched and ATTN_OK
  *    is returned (pointers may then be NULL).
  *  - Arguments are validated on the host before any HIP call.  On error no
