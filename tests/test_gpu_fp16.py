@@ -85,6 +85,31 @@ def test_backward(oracle_mod, N, d, causal):
         assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 2e-2, f"{name} Frobenius"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_large_magnitudes_within_range(oracle_mod, causal):
+    """fp16 rounds dS = P (dP - D) for the backward's products.  |V| up to
+    about 400 and |dO| up to 40 put dP - D in the tens of thousands, inside
+    fp16's 65504: the gradients stay finite and match the oracle."""
+    dev = gpu()
+    q, k, v, do = attn_inputs.make(2, 4, 2, 300, 64, "fp16", seed=460, with_dout=True)
+    v = (v.float() * 100).half()
+    do = (do.float() * 10).half()
+    qg, kg, vg, dog = (t.to(dev) for t in (q, k, v, do))
+    o, lse = ea.fwd(qg, kg, vg, causal=causal)
+    grads = ea.bwd(qg, kg, vg, o, lse, dog, causal=causal)
+    torch.cuda.synchronize()
+    refs = oracle_mod.bwd(q, k, v, do, causal=causal)
+    dp_max = np.abs(np.einsum("bhid,bhjd->bhij", do.double().numpy(),
+                              np.repeat(v.double().numpy(), 2, axis=1))).max()
+    assert 1e4 < dp_max < 65504, dp_max  # the case this test is about
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, refs):
+        g = g.float().cpu().numpy()
+        assert np.all(np.isfinite(g)), f"{name}: non-finite"
+        e, ref_max = np.abs(g - r).max(), np.abs(r).max()
+        assert e <= 5e-2 * ref_max, f"{name}: {e} vs {ref_max}"
+        assert np.linalg.norm(g - r) / np.linalg.norm(r) <= 2e-2, f"{name} Frobenius"
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_splitkv(oracle_mod, d):
     dev = gpu()
