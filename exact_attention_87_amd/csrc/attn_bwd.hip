@@ -57,7 +57,9 @@ constexpr float kTiny = 1.17549435e-38f;  // smallest normal fp32
 //    (-9 to -11%), which keep the 1-wave layout.
 //  - Raised wave priority (s_setprio 1) in any matrix-core phase of the dQ
 //    kernel or of the dK/dV kernel at 1 or 3 waves per SIMD, or a priority
-//    falling with the remaining tiles: 0 to -3%, so they do not raise it.
+//    falling with the remaining tiles: 0 to -3%, so they do not raise it;
+//    raised in their exp / dS (vector ALU) phase at d = 64 instead: -2 to
+//    +2% (dK/dV), -3% with the dQ kernel's too.
 //    At d = 128 (2 waves per SIMD) the dK/dV kernel raises it for the S and
 //    dP products: +1 to +3.6%; around the dV/dK products instead: +0 to
 //    +2.6%; fences between the dV/dK feature blocks: -1 to +1%.
