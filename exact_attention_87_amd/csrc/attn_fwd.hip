@@ -274,14 +274,18 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
   //     each block's LDS latency exposed);
   //   - the scores are copied once out of the accumulators into plain values
   //     for the mask and the softmax;
-  //   - a rescale of O (the running maximum moved) scales each O block just
-  //     before its first P V product, in a second copy of the product loop;
-  //     with the multiply in the tile's main path the compiler copied all of
-  //     O out and back on every tile (about 270 extra copies per tile).
+  //   - a rescale of O (the running maximum moved) multiplies O in place
+  //     behind an empty asm that pins O to the accumulation registers, so O
+  //     is copied out and back on that rare path only; written plainly, the
+  //     compiler kept a vector copy of all of O at hand and moved it on every
+  //     tile (about 270 extra copies per tile).
   // Same arithmetic, in the same order, as the generic body (bitwise-equal
   // results).  Measured against the generic body (same-box rotated A/B):
-  // non-causal B=1 H=16 N=8192 +17%, causal +8.6%, causal grouped-query B=2
-  // Hq=16 Hkv=2 N=4096 +7%, fp16 non-causal B=4 H=16 N=2048 +14%.
+  // non-causal B=1 H=16 N=8192 887 -> 1058 TFLOP/s (+19%), causal 843 -> 997
+  // (+18%), causal grouped-query B=2 Hq=16 Hkv=2 N=4096 804 -> 930 (+16%),
+  // fp16 non-causal B=4 H=16 N=2048 786 -> 914 (+16%).  (Scaling each O block
+  // inside a second copy of the P V loop instead measured 1% slower
+  // non-causal and 9% slower causal.)
   auto tile256 = [&](const char* kt, const char* vt, int j) __attribute__((always_inline)) {
     constexpr int NF = 2 * NQC, KLA = 4;  // score products; K fragments read ahead
     f32x16 sacc2[2];
@@ -363,8 +367,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     }
     lsum[0] += tsum;
     // O^T += V^T P^T; product i: O block mb = i/4, key block (i/2)%2, half i%2
-    auto pv = [&](auto scc) __attribute__((always_inline)) {
-      constexpr bool SCALE = decltype(scc)::value;
+    auto pv = [&]() __attribute__((always_inline)) {
       constexpr int NP = NMB * 4, VLA = 2;  // V^T fragment pairs read ahead
       u32x2 vlo[NP], vhi[NP];
       auto vread = [&](int i) __attribute__((always_inline)) {
@@ -383,14 +386,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
         const V8 a = bitcast<V8>(u32x4{vlo[i][0], vlo[i][1], vhi[i][0], vhi[i][1]});
         const V8 bp = bitcast<V8>(
             u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
-        if (SCALE && i % 4 == 0) {
-          // pinned in place here, so the copy out of the accumulator registers
-          // happens on this (rare) path only
-          f32x16 o = oacc[0][i / 4];
-          __asm__ volatile("" : "+a"(o));
-          oacc[0][i / 4] = mfma32(a, bp, o * alpha);
-        } else
-          oacc[0][i / 4] = mfma32(a, bp, oacc[0][i / 4]);
+        oacc[0][i / 4] = mfma32(a, bp, oacc[0][i / 4]);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * VLA, 0);
 #pragma unroll
@@ -401,10 +397,17 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_setprio(0);
     };
-    if (rescale)
-      pv(std::true_type{});
-    else
-      pv(std::false_type{});
+    // (after pv's definition on purpose: placed before it, the same code
+    // left the allocator spilling 10-80 registers)
+    if (rescale) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        f32x16 o = oacc[0][mb];
+        __asm__ volatile("" : "+a"(o));
+        oacc[0][mb] = o * alpha;
+      }
+    }
+    pv();
   };
 
   // One key tile; BUF (the LDS stage) is a compile-time constant so every LDS
