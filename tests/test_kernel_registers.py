@@ -3,8 +3,10 @@
 The d = 64 and d = 128 matrix-core kernels must not spill: a runtime test
 added to the scheduled tile body of the non-causal pipelined forward once
 made it spill 303 registers (scratch memory) and run 8x slower while every
-parity test still passed.  The d = 256 instances run at 512 registers with a
-few spills; their counts are bounded at the levels the kernels were tuned at.
+parity test still passed.  The d = 256 instances run at 512 registers; their
+spill counts are bounded at the levels the kernels were tuned at (none in the
+forward, split-K/V and dQ kernels, whose allocation at that size changed by
+tens of registers with the order of two statements).
 """
 import os
 import re
@@ -17,7 +19,8 @@ from exact_attention_87_amd import _build
 
 CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                     "exact_attention_87_amd", "csrc")
-D256_MAX_SPILL = {"fwd_mfma_kernel": 0, "bwd_dkdv_kernel": 2, "bwd_dq_kernel": 0}
+D256_MAX_SPILL = {"fwd_mfma_kernel": 0, "fwd_split_kernel": 0, "bwd_dkdv_kernel": 2, "bwd_dq_kernel": 0}
+MIN_KERNELS = {"attn_fwd.hip": 20, "attn_bwd.hip": 20, "attn_splitkv.hip": 12}
 
 
 def kernel_table(source):
@@ -39,13 +42,13 @@ def kernel_table(source):
     return rows
 
 
-@pytest.mark.parametrize("source", ["attn_fwd.hip", "attn_bwd.hip"])
+@pytest.mark.parametrize("source", ["attn_fwd.hip", "attn_bwd.hip", "attn_splitkv.hip"])
 def test_matrix_core_kernels_do_not_spill(source):
     rows = kernel_table(source)
     checked = 0
     for name, vgpr, spill, scratch in rows:
         base = re.match(r"_ZN4attn\d+(\w+?)I", name)
-        if not base or "mfma" not in name and "bwd_d" not in name:
+        if not base or not any(k in name for k in ("mfma", "bwd_d", "fwd_split")):
             continue
         kernel = base.group(1)
         if "Li256E" in name:
@@ -53,4 +56,4 @@ def test_matrix_core_kernels_do_not_spill(source):
         else:
             assert spill == 0 and scratch == 0, f"{name}: {spill} spilled registers, {scratch} B scratch"
         checked += 1
-    assert checked >= 20, f"only {checked} matrix-core kernels found in {source}"
+    assert checked >= MIN_KERNELS[source], f"only {checked} matrix-core kernels found in {source}"
