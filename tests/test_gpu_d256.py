@@ -2,8 +2,8 @@
 
 Forward tolerances are the 16-bit forward's: |O - O_ref| <= 2e-2 + 1e-2
 |O_ref|, |LSE - LSE_ref| <= 1e-3.  Covers the dense forward (tails, causal,
-GQA, extreme logits, bf16 and fp16), split-K/V, block-sparse and packed
-variable-length at d = 256.  Backward tolerances are the backward's: per
+GQA, extreme logits, bf16 and fp16), split-K/V (also with scores that force
+repeated rescales), block-sparse and packed variable-length at d = 256.  Backward tolerances are the backward's: per
 gradient, max |g - g_ref| <= 5e-2 max |g_ref| and relative Frobenius error
 <= 2e-2; covered: tails over several 128-key blocks, causal, GQA, fp16,
 extreme logits and a negative scale, the strided and packed
@@ -72,6 +72,30 @@ def test_splitkv(oracle_mod):
         torch.cuda.synchronize()
         ro, rl = oracle_mod.fwd_bottom_right(q, k, v, causal=causal)
         check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"split causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_splitkv_rising_scores_force_rescales(oracle_mod, dtype):
+    """Split-K/V with scores that climb by about 20 (base 2) per 64-key tile:
+    inside every split the running maximum moves past the rescale threshold
+    again and again (every tile at fp16's 15, every other tile at bf16's
+    30), so the rescale of the O accumulator runs many times per split."""
+    dev = gpu()
+    g = torch.Generator().manual_seed(2560)
+    B, Hq, Hkv, Nq, Nk = 1, 4, 2, 5, 1500
+    q = 1.0 + 0.3 * torch.randn(B, Hq, Nq, D, generator=g)
+    step = 20.0 / 64 / 1.4426950408889634 / D ** 0.5  # per key, in units of q.k
+    ramp = torch.arange(Nk, dtype=torch.float32)[None, None, :, None] * step
+    k = ramp + 0.3 * torch.randn(B, Hkv, Nk, D, generator=g)
+    v = torch.randn(B, Hkv, Nk, D, generator=g)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float16
+    q, k, v = (t.to(td) for t in (q, k, v))
+    for causal in (False, True):
+        o, lse = ea.fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), causal=causal, num_splits=3)
+        torch.cuda.synchronize()
+        ro, rl = oracle_mod.fwd_bottom_right(q, k, v, causal=causal)
+        assert rl.max() > 100  # the logits really span many thresholds
+        check(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, f"split rising {dtype} causal={causal}")
 
 
 def test_blocksparse(oracle_mod):

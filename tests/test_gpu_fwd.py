@@ -112,7 +112,7 @@ def test_bf16_extreme_logits(oracle_mod, mult, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rising_scores_force_rescales(oracle_mod, dtype, d, causal):
     """Scores that grow by about 20 (base 2) per 64-key tile: the running
