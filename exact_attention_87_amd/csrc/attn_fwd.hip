@@ -250,6 +250,21 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     for (int mb = 0; mb < NMB; ++mb) oacc[nb][mb] = f32x16{};
   }
 
+  // The running max after a wave's first tile: the row max of its (masked)
+  // scores, as the max path of the softmax would set it, without first
+  // forming p against a max that is not set yet (that pass always
+  // overflows and was thrown away).  The accumulators are still zero, so
+  // skipping their rescale changes nothing.
+  auto first_max = [&](const f32x16 (&sacc)[2], float m) {
+    float mloc = sacc[0][0];
+#pragma unroll
+    for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[kbk][r]);
+    mloc = __builtin_fmaxf(mloc, xor32(mloc));
+    return __builtin_fmaxf(m, mloc * c);
+  };
+
   // p = 2^(s*c - m) -> bf16 P^T operand and this lane's tile sum.
   auto softmax_exp = [&](const f32x16 (&sacc)[2], float m, uint32_t (&pk)[2][8]) {
     float tsum = 0.f;
@@ -329,6 +344,15 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
           const int key = k0 + kbk * 32 + acc_row(r, hf);
           if ((key >= N) || (CAUSAL && key > q0 + l32)) sv[kbk][r] = -__builtin_inff();
         }
+    }
+    if (j == 0) {  // first tile: the running maximum is set from it up front
+      float mloc = sv[0][0];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sv[kbk][r]);
+      mloc = __builtin_fmaxf(mloc, xor32(mloc));
+      ms[0] = __builtin_fmaxf(ms[0], mloc * c);
     }
     uint32_t pk[2][8];
     auto expo = [&](float m) __attribute__((always_inline)) {
@@ -473,8 +497,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
             }
       }
       // ---- p with the current running max.  A lane whose tile sum exceeds
-      // 2^kTau may hold a p above 2^kTau (or the max was never set): only
-      // then take the row max and, if it grew by more than kTau, rescale.
+      // 2^kTau may hold a p above 2^kTau: only then take the row max and, if
+      // it grew by more than kTau, rescale.  On a wave's first tile (loop
+      // position 0: its first tile with visible keys, also under a block-sparse
+      // list, which is ascending) the max is not set yet and is taken up front.
+      if (j == 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) ms[nb] = first_max(sacc[nb], ms[nb]);
+      }
       uint32_t pk[NB][2][8];
       float tsum[NB];
       bool redo = false;
@@ -787,6 +817,15 @@ __attribute__((amdgpu_waves_per_eu(PipeCfg<D>::WPE, PipeCfg<D>::WPE))) void fwd_
             const bool dead = (key >= N) || (CAUSAL && key > q0 + l32);
             if (dead) sc[kbk][r] = -__builtin_inff();
           }
+      }
+      if (j == 0) {  // a wave's first tile: the running max is taken up front
+        float mloc = sc[0][0];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sc[kbk][r]);
+        mloc = __builtin_fmaxf(mloc, xor32(mloc));
+        ms = __builtin_fmaxf(ms, mloc * c);
       }
       uint32_t pk[2][8];
       const char* vt = vstage(BUF);

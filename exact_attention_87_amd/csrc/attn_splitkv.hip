@@ -231,6 +231,15 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
           if ((key >= kend) || (CAUSAL && key > qi + off)) sv[kbk][rr] = -__builtin_inff();
         }
     }
+    if (j == 0) {  // the split's first tile: the running maximum is set from it up front
+      float mloc = sv[0][0];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) mloc = __builtin_fmaxf(mloc, sv[kbk][rr]);
+      mloc = __builtin_fmaxf(mloc, xor32(mloc));
+      ms = __builtin_fmaxf(ms, mloc * c);
+    }
     uint32_t pk[2][8];
     auto expo = [&]() __attribute__((always_inline)) {
       float ts = 0.f;
@@ -343,6 +352,15 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
             const bool dead = (key >= kend) || (CAUSAL && key > qi + off);
             if (dead) sacc[kbk][rr] = -__builtin_inff();
           }
+      }
+      if (j == 0) {  // the split's first tile: the running maximum is taken up front
+        float mloc = sacc[0][0];
+#pragma unroll
+        for (int kbk = 0; kbk < 2; ++kbk)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) mloc = __builtin_fmaxf(mloc, sacc[kbk][rr]);
+        mloc = __builtin_fmaxf(mloc, xor32(mloc));
+        ms = __builtin_fmaxf(ms, mloc * c);
       }
       uint32_t pk[2][8];
       float tsum = softmax_exp(sacc, pk);
