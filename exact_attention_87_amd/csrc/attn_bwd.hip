@@ -344,10 +344,18 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   //   A: S = Q K^T and dP - D = dO V^T - D on the matrix cores;
   //   V: P = 2^(S c - LSE), dS = P (dP - D), both packed to bf16 (vector ALU);
   //   C: dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.
-  // Operand chunks read per group: all at once at d = 128; two at a time,
-  // each group fenced off from the scheduler so the reads are not all
-  // hoisted, where registers are tight: d = 256 (K, V, dK and dV already
-  // hold 384) and d = 64 at three waves per SIMD (168 each).
+  // Operand chunks read per group: all at once at d = 128 (one wave per
+  // SIMD); two at a time, each group fenced off from the scheduler so the
+  // reads are not all hoisted, where registers are tight (d = 64 at three
+  // waves per SIMD, 168 each; d = 128 at two).  d = 256 (K, dK and dV
+  // already hold 384 registers, one wave per SIMD) streams its operand reads
+  // two products ahead in phases A and C instead: with fenced groups each
+  // group's LDS latency was exposed.  Measured (same-box rotated A/B of
+  // attn_bwd, bitwise-equal gradients, together with the same streaming in
+  // the dQ kernel): non-causal B=1 H=16 N=8192 661 -> 779 TFLOP/s (+18%),
+  // causal 655 -> 736 (+12%), causal B=2 N=4096 +10%, causal grouped-query
+  // Hq=32 Hkv=8 N=8192 +15%, a query-head split (B=2 Hq=16 Hkv=2 N=4096)
+  // +13%; one chunk ahead gained about half as much, three or four no more.
   constexpr int CG = (D > 128 || Cfg::WPE >= 2) ? 2 : NQC;
   constexpr bool FENCE_C = D > 128;  // a fence per feature block of the dV/dK products
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
@@ -371,6 +379,34 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
     }
     sacc = f32x16{};
+    if constexpr (D == 256) {
+      // d = 256 (one wave per SIMD): the operand chunks stream two products
+      // ahead; read in fenced groups, each group's LDS latency stayed exposed
+      constexpr int LA = 2;
+      u32x4 qa[NQC], da[NQC], va[NQC];
+      auto rd = [&](int cc) __attribute__((always_inline)) {
+        qa[cc] = lds_read16(qtile + qbase * ROWB + qo(cc));
+        da[cc] = lds_read16(dotile + qbase * ROWB + qo(cc));
+        va[cc] = lds_read16(vtile + w * 32 * ROWB + qo(cc));
+      };
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < LA; ++cc) rd(cc);
+#pragma unroll
+      for (int cc = 0; cc < NQC; ++cc) {
+        if (cc + LA < NQC) rd(cc + LA);
+        sacc = mfma32(bitcast<V8>(qa[cc]), kreg[cc], sacc);
+        pacc = mfma32(bitcast<V8>(da[cc]), bitcast<V8>(va[cc]), pacc);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 * LA, 0);
+#pragma unroll
+      for (int cc = 0; cc < NQC; ++cc) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (cc + LA < NQC) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
 #pragma unroll
     for (int c0 = 0; c0 < NQC; c0 += CG) {
       u32x4 qa[CG], da[CG], va[VLDS ? CG : 1];
@@ -419,6 +455,39 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   };
   auto phaseC = [&](const char* qtile, const char* dotile, int qbase, const uint32_t (&pk)[8],
                     const uint32_t (&dsk)[8]) {
+    if constexpr (D == 256) {
+      // d = 256: the transposed operand reads stream two product pairs ahead
+      constexpr int LA = 2, NI = 2 * NMB;  // pair i: half cp = i / NMB, block mb = i % NMB
+      u32x2 a0[NI], a1[NI], b0[NI], b1[NI];
+      auto rd = [&](int i) __attribute__((always_inline)) {
+        const int rows = (qbase + 16 * (i / NMB)) * ROWB, mb = i % NMB;
+        a0[i] = lds_read_tr(dotile + rows + tro(0, mb));
+        a1[i] = lds_read_tr(dotile + rows + tro(1, mb));
+        b0[i] = lds_read_tr(qtile + rows + tro(0, mb));
+        b1[i] = lds_read_tr(qtile + rows + tro(1, mb));
+      };
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < LA; ++i) rd(i);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (i + LA < NI) rd(i + LA);
+        const int cp = i / NMB, mb = i % NMB;
+        const V8 pb = bitcast<V8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
+        const V8 sb =
+            bitcast<V8>(u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
+        dvacc[mb] = mfma32(bitcast<V8>(u32x4{a0[i][0], a0[i][1], a1[i][0], a1[i][1]}), pb, dvacc[mb]);
+        dkacc[mb] = mfma32(bitcast<V8>(u32x4{b0[i][0], b0[i][1], b1[i][0], b1[i][1]}), sb, dkacc[mb]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * LA, 0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if (i + LA < NI) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
 #pragma unroll
     for (int cp = 0; cp < 2; ++cp) {
       const V8 pb = bitcast<V8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
@@ -771,8 +840,9 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
   // Under tight register budgets (three waves per SIMD at d = 64, two at
   // d = 128) the two key blocks of a tile are kept apart by a scheduling
-  // fence and their operands read two chunks at a time; otherwise the
-  // scheduler may overlap them freely.
+  // fence and their operands read two chunks at a time.  At d = 256 (one
+  // wave per SIMD) the operand reads of both products stream two products
+  // ahead of their use (see the dK/dV kernel's phases for the measurement).
   constexpr bool SEQ = D == 64 ? Cfg::WPE >= 3 : Cfg::WPE >= 2;
   constexpr int CG = SEQ ? 2 : NQC;
 
@@ -788,6 +858,31 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int kbk = 0; kbk < 2; ++kbk) {
         // S^T = K Q^T and dP^T - D = V dO^T - D for the tile's 32-key block kbk
         f32x16 sacc = f32x16{}, pacc = pinit;
+        if constexpr (D == 256) {
+          // d = 256 (one wave per SIMD): operand chunks stream two products ahead
+          constexpr int LA = 2;
+          u32x4 ka[NQC], va[NQC];
+          auto rd = [&](int cc) __attribute__((always_inline)) {
+            ka[cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
+            va[cc] = lds_read16(vt + kbk * 32 * ROWB + koff[cc]);
+          };
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int cc = 0; cc < LA; ++cc) rd(cc);
+#pragma unroll
+          for (int cc = 0; cc < NQC; ++cc) {
+            if (cc + LA < NQC) rd(cc + LA);
+            sacc = mfma32(bitcast<V8>(ka[cc]), qreg[cc], sacc);
+            pacc = mfma32(bitcast<V8>(va[cc]), doreg[cc], pacc);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+          for (int cc = 0; cc < NQC; ++cc) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (cc + LA < NQC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else
 #pragma unroll
         for (int c0 = 0; c0 < NQC; c0 += CG) {
           u32x4 ka[CG], va[CG];
@@ -819,6 +914,35 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
           dsk[r >> 1] = pack2<T>(pv[r] * pacc[r], pv[r + 1] * pacc[r + 1]);
         // dQ^T += K^T dS^T (per mb the same accumulation order as key block
         // by key block)
+        if constexpr (D == 256) {
+          // d = 256: the transposed K reads stream two products ahead
+          constexpr int LA = 2, NI = 2 * NMB;  // product i: block mb = i / 2, half cp = i % 2
+          u32x2 lo[NI], hi[NI];
+          auto rd = [&](int i) __attribute__((always_inline)) {
+            const int rows = (kbk * 32 + (i % 2) * 16) * ROWB;
+            lo[i] = lds_read_tr(kt + rows + troff[0][i / 2]);
+            hi[i] = lds_read_tr(kt + rows + troff[1][i / 2]);
+          };
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < LA; ++i) rd(i);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            if (i + LA < NI) rd(i + LA);
+            const int cp = i % 2;
+            const V8 a = bitcast<V8>(u32x4{lo[i][0], lo[i][1], hi[i][0], hi[i][1]});
+            const V8 sb = bitcast<V8>(
+                u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
+            dqacc[i / 2] = mfma32(a, sb, dqacc[i / 2]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i + LA < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
