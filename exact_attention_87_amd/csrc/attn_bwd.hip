@@ -347,15 +347,18 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // Operand chunks read per group: all at once at d = 128 (one wave per
   // SIMD); two at a time, each group fenced off from the scheduler so the
   // reads are not all hoisted, where registers are tight (d = 64 at three
-  // waves per SIMD, 168 each; d = 128 at two).  d = 256 (K, dK and dV
-  // already hold 384 registers, one wave per SIMD) streams its operand reads
-  // two products ahead in phases A and C instead: with fenced groups each
-  // group's LDS latency was exposed.  Measured (same-box rotated A/B of
-  // attn_bwd, bitwise-equal gradients, together with the same streaming in
-  // the dQ kernel): non-causal B=1 H=16 N=8192 661 -> 779 TFLOP/s (+18%),
+  // waves per SIMD, 168 each; d = 128 at two).  The one-wave layouts (d = 256,
+  // where K, dK and dV already hold 384 registers, and the split causal
+  // d = 128 stage) stream their operand reads two products ahead in phases
+  // A and C instead: one wave per SIMD leaves each group's LDS latency
+  // exposed.  Measured (same-box rotated A/B of attn_bwd, bitwise-equal
+  // gradients, at d = 256 together with the same streaming in the dQ
+  // kernel): d = 256 non-causal B=1 H=16 N=8192 661 -> 779 TFLOP/s (+18%),
   // causal 655 -> 736 (+12%), causal B=2 N=4096 +10%, causal grouped-query
   // Hq=32 Hkv=8 N=8192 +15%, a query-head split (B=2 Hq=16 Hkv=2 N=4096)
-  // +13%; one chunk ahead gained about half as much, three or four no more.
+  // +13%, with one chunk ahead about half of that and three or four no more;
+  // the split causal d = 128 shapes +0.4 to +1.2%.
+  constexpr bool STREAM = Cfg::WPE == 1;  // d = 256, and d = 128 split causal
   constexpr int CG = (D > 128 || Cfg::WPE >= 2) ? 2 : NQC;
   constexpr bool FENCE_C = D > 128;  // a fence per feature block of the dV/dK products
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
@@ -379,15 +382,15 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
     }
     sacc = f32x16{};
-    if constexpr (D == 256) {
-      // d = 256 (one wave per SIMD): the operand chunks stream two products
-      // ahead; read in fenced groups, each group's LDS latency stayed exposed
+    if constexpr (STREAM) {
+      // one wave per SIMD: the operand chunks stream two products ahead;
+      // read in fenced groups, each group's LDS latency stayed exposed
       constexpr int LA = 2;
-      u32x4 qa[NQC], da[NQC], va[NQC];
+      u32x4 qa[NQC], da[NQC], va[VLDS ? NQC : 1];
       auto rd = [&](int cc) __attribute__((always_inline)) {
         qa[cc] = lds_read16(qtile + qbase * ROWB + qo(cc));
         da[cc] = lds_read16(dotile + qbase * ROWB + qo(cc));
-        va[cc] = lds_read16(vtile + w * 32 * ROWB + qo(cc));
+        if constexpr (VLDS) va[cc] = lds_read16(vtile + w * 32 * ROWB + qo(cc));
       };
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -396,13 +399,17 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int cc = 0; cc < NQC; ++cc) {
         if (cc + LA < NQC) rd(cc + LA);
         sacc = mfma32(bitcast<V8>(qa[cc]), kreg[cc], sacc);
-        pacc = mfma32(bitcast<V8>(da[cc]), bitcast<V8>(va[cc]), pacc);
+        if constexpr (VLDS)
+          pacc = mfma32(bitcast<V8>(da[cc]), bitcast<V8>(va[cc]), pacc);
+        else
+          pacc = mfma32(bitcast<V8>(da[cc]), vreg[cc], pacc);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 3 * LA, 0);
+      constexpr int RPC = VLDS ? 3 : 2;  // LDS reads per chunk
+      __builtin_amdgcn_sched_group_barrier(0x100, RPC * LA, 0);
 #pragma unroll
       for (int cc = 0; cc < NQC; ++cc) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        if (cc + LA < NQC) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        if (cc + LA < NQC) __builtin_amdgcn_sched_group_barrier(0x100, RPC, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       return;
@@ -455,8 +462,9 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   };
   auto phaseC = [&](const char* qtile, const char* dotile, int qbase, const uint32_t (&pk)[8],
                     const uint32_t (&dsk)[8]) {
-    if constexpr (D == 256) {
-      // d = 256: the transposed operand reads stream two product pairs ahead
+    if constexpr (STREAM) {
+      // one wave per SIMD: the transposed operand reads stream two product
+      // pairs ahead
       constexpr int LA = 2, NI = 2 * NMB;  // pair i: half cp = i / NMB, block mb = i % NMB
       u32x2 a0[NI], a1[NI], b0[NI], b1[NI];
       auto rd = [&](int i) __attribute__((always_inline)) {
