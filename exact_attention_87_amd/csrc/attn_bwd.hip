@@ -344,23 +344,22 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   //   A: S = Q K^T and dP - D = dO V^T - D on the matrix cores;
   //   V: P = 2^(S c - LSE), dS = P (dP - D), both packed to bf16 (vector ALU);
   //   C: dV^T += dO^T P and dK^T += Q^T dS on the matrix cores.
-  // Operand chunks read per group: all at once at d = 128 (one wave per
-  // SIMD); two at a time, each group fenced off from the scheduler so the
-  // reads are not all hoisted, where registers are tight (d = 64 at three
-  // waves per SIMD, 168 each; d = 128 at two).  The one-wave layouts (d = 256,
-  // where K, dK and dV already hold 384 registers, and the split causal
-  // d = 128 stage) stream their operand reads two products ahead in phases
-  // A and C instead: one wave per SIMD leaves each group's LDS latency
-  // exposed.  Measured (same-box rotated A/B of attn_bwd, bitwise-equal
-  // gradients, at d = 256 together with the same streaming in the dQ
-  // kernel): d = 256 non-causal B=1 H=16 N=8192 661 -> 779 TFLOP/s (+18%),
-  // causal 655 -> 736 (+12%), causal B=2 N=4096 +10%, causal grouped-query
-  // Hq=32 Hkv=8 N=8192 +15%, a query-head split (B=2 Hq=16 Hkv=2 N=4096)
-  // +13%, with one chunk ahead about half of that and three or four no more;
-  // the split causal d = 128 shapes +0.4 to +1.2%.
-  constexpr bool STREAM = Cfg::WPE == 1;  // d = 256, and d = 128 split causal
-  constexpr int CG = (D > 128 || Cfg::WPE >= 2) ? 2 : NQC;
-  constexpr bool FENCE_C = D > 128;  // a fence per feature block of the dV/dK products
+  // Operand reads stream two products ahead of their use in phases A and C,
+  // pinned with scheduling groups.  Read in groups (all chunks at once, or
+  // two at a time behind scheduling fences where registers are tight), each
+  // group's LDS latency was exposed, fully so where one wave runs per SIMD.
+  // Measured (same-box rotated A/B of attn_bwd, bitwise-equal gradients):
+  //   - one wave per SIMD (d = 256, with the same streaming in the dQ
+  //     kernel): non-causal B=1 H=16 N=8192 661 -> 779 TFLOP/s (+18%), causal
+  //     655 -> 736 (+12%), causal B=2 N=4096 +10%, causal grouped-query
+  //     Hq=32 Hkv=8 N=8192 +15%, a query-head split (B=2 Hq=16 Hkv=2
+  //     N=4096) +13%; one chunk ahead gave about half of that, three or four
+  //     no more; the split causal d = 128 stage +0.4 to +1.2%;
+  //   - several waves per SIMD: causal B=8 H=16 N=2048 d=64 683 -> 697
+  //     (+2.0%), non-causal B=8 H=16 N=1024 d=64 +6.7%, causal grouped-query
+  //     d=64 +1.9%, causal B=4 H=32 N=4000 d=128 +3.4%, causal grouped-query
+  //     N=16384 d=128 +1.4%, non-causal B=2 H=32 N=4096 d=128 +0.3%; one
+  //     ahead in either phase gained less.
   auto phaseA = [&](const char* qtile, const char* dotile, const float* dsum, int qbase,
                     int qfirst, f32x16& sacc, f32x16& pacc) {
     // the dP accumulator starts at -D of each row (element 4*rg+e is row
@@ -382,10 +381,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int e = 0; e < 4; ++e) pacc[4 * rg + e] = nd[e];
     }
     sacc = f32x16{};
-    if constexpr (STREAM) {
-      // one wave per SIMD: the operand chunks stream two products ahead;
-      // read in fenced groups, each group's LDS latency stayed exposed
-      constexpr int LA = 2;
+    {
+      constexpr int LA = 2;  // chunks read ahead
       u32x4 qa[NQC], da[NQC], va[VLDS ? NQC : 1];
       auto rd = [&](int cc) __attribute__((always_inline)) {
         qa[cc] = lds_read16(qtile + qbase * ROWB + qo(cc));
@@ -412,26 +409,6 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         if (cc + LA < NQC) __builtin_amdgcn_sched_group_barrier(0x100, RPC, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      return;
-    }
-#pragma unroll
-    for (int c0 = 0; c0 < NQC; c0 += CG) {
-      u32x4 qa[CG], da[CG], va[VLDS ? CG : 1];
-#pragma unroll
-      for (int cc = 0; cc < CG; ++cc) {
-        qa[cc] = lds_read16(qtile + qbase * ROWB + qo(c0 + cc));
-        da[cc] = lds_read16(dotile + qbase * ROWB + qo(c0 + cc));
-        if constexpr (VLDS) va[cc] = lds_read16(vtile + w * 32 * ROWB + qo(c0 + cc));
-      }
-#pragma unroll
-      for (int cc = 0; cc < CG; ++cc) {
-        sacc = mfma32(bitcast<V8>(qa[cc]), kreg[c0 + cc], sacc);
-        if constexpr (VLDS)
-          pacc = mfma32(bitcast<V8>(da[cc]), bitcast<V8>(va[cc]), pacc);
-        else
-          pacc = mfma32(bitcast<V8>(da[cc]), vreg[c0 + cc], pacc);
-      }
-      if constexpr (CG < NQC) __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto phaseV = [&](const float* lse2, int qbase, int qfirst, bool diag, const f32x16& sacc,
@@ -462,10 +439,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   };
   auto phaseC = [&](const char* qtile, const char* dotile, int qbase, const uint32_t (&pk)[8],
                     const uint32_t (&dsk)[8]) {
-    if constexpr (STREAM) {
-      // one wave per SIMD: the transposed operand reads stream two product
-      // pairs ahead
-      constexpr int LA = 2, NI = 2 * NMB;  // pair i: half cp = i / NMB, block mb = i % NMB
+    {
+      constexpr int LA = 2, NI = 2 * NMB;  // pairs read ahead; pair i: half cp = i / NMB, block mb = i % NMB
       u32x2 a0[NI], a1[NI], b0[NI], b1[NI];
       auto rd = [&](int i) __attribute__((always_inline)) {
         const int rows = (qbase + 16 * (i / NMB)) * ROWB, mb = i % NMB;
@@ -494,24 +469,6 @@ void bwd_dkdv_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         if (i + LA < NI) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      return;
-    }
-#pragma unroll
-    for (int cp = 0; cp < 2; ++cp) {
-      const V8 pb = bitcast<V8>(u32x4{pk[4 * cp], pk[4 * cp + 1], pk[4 * cp + 2], pk[4 * cp + 3]});
-      const V8 sb =
-          bitcast<V8>(u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
-      const int rows = (qbase + 16 * cp) * ROWB;
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const u32x2 a0 = lds_read_tr(dotile + rows + tro(0, mb));
-        const u32x2 a1 = lds_read_tr(dotile + rows + tro(1, mb));
-        dvacc[mb] = mfma32(bitcast<V8>(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb, dvacc[mb]);
-        const u32x2 b0 = lds_read_tr(qtile + rows + tro(0, mb));
-        const u32x2 b1 = lds_read_tr(qtile + rows + tro(1, mb));
-        dkacc[mb] = mfma32(bitcast<V8>(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb, dkacc[mb]);
-        if constexpr (CG < NQC && FENCE_C) __builtin_amdgcn_sched_barrier(0);
-      }
     }
   };
 
@@ -846,13 +803,15 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dqacc[mb] = f32x16{};
 
-  // Under tight register budgets (three waves per SIMD at d = 64, two at
-  // d = 128) the two key blocks of a tile are kept apart by a scheduling
-  // fence and their operands read two chunks at a time.  At d = 256 (one
-  // wave per SIMD) the operand reads of both products stream two products
-  // ahead of their use (see the dK/dV kernel's phases for the measurement).
+  // The operand reads of both products stream two products ahead of their
+  // use, as in the dK/dV kernel (which gives the measurements of the one-wave
+  // layouts; here with several waves per SIMD, against reads two chunks at a
+  // time behind scheduling fences: causal B=4 H=32 N=4000 d=128 +1.3%,
+  // non-causal B=2 H=32 N=4096 d=128 +1.1%, d=64 +0.1 to +0.6%; one ahead
+  // lost 1%).  Under tight register budgets (three waves per SIMD at d = 64,
+  // two at d = 128) the two key blocks of a tile are also kept apart by a
+  // scheduling fence.
   constexpr bool SEQ = D == 64 ? Cfg::WPE >= 3 : Cfg::WPE >= 2;
-  constexpr int CG = SEQ ? 2 : NQC;
 
   auto tile = [&](auto bufc, int j) {
     constexpr int BUF = decltype(bufc)::value;
@@ -866,9 +825,8 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
       for (int kbk = 0; kbk < 2; ++kbk) {
         // S^T = K Q^T and dP^T - D = V dO^T - D for the tile's 32-key block kbk
         f32x16 sacc = f32x16{}, pacc = pinit;
-        if constexpr (D == 256) {
-          // d = 256 (one wave per SIMD): operand chunks stream two products ahead
-          constexpr int LA = 2;
+        {
+          constexpr int LA = 2;  // chunks read ahead
           u32x4 ka[NQC], va[NQC];
           auto rd = [&](int cc) __attribute__((always_inline)) {
             ka[cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
@@ -890,20 +848,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             if (cc + LA < NQC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
-        } else
-#pragma unroll
-        for (int c0 = 0; c0 < NQC; c0 += CG) {
-          u32x4 ka[CG], va[CG];
-#pragma unroll
-          for (int cc = 0; cc < CG; ++cc) {
-            ka[cc] = lds_read16(kt + kbk * 32 * ROWB + koff[c0 + cc]);
-            va[cc] = lds_read16(vt + kbk * 32 * ROWB + koff[c0 + cc]);
-          }
-#pragma unroll
-          for (int cc = 0; cc < CG; ++cc) {
-            sacc = mfma32(bitcast<V8>(ka[cc]), qreg[c0 + cc], sacc);
-            pacc = mfma32(bitcast<V8>(va[cc]), doreg[c0 + cc], pacc);
-          }
         }
         float pv[16];
 #pragma unroll
@@ -922,9 +866,8 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
           dsk[r >> 1] = pack2<T>(pv[r] * pacc[r], pv[r + 1] * pacc[r + 1]);
         // dQ^T += K^T dS^T (per mb the same accumulation order as key block
         // by key block)
-        if constexpr (D == 256) {
-          // d = 256: the transposed K reads stream two products ahead
-          constexpr int LA = 2, NI = 2 * NMB;  // product i: block mb = i / 2, half cp = i % 2
+        {
+          constexpr int LA = 2, NI = 2 * NMB;  // products read ahead; product i: block mb = i / 2, half cp = i % 2
           u32x2 lo[NI], hi[NI];
           auto rd = [&](int i) __attribute__((always_inline)) {
             const int rows = (kbk * 32 + (i % 2) * 16) * ROWB;
@@ -950,19 +893,7 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             if (i + LA < NI) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
-        } else
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-          for (int cp = 0; cp < 2; ++cp) {
-            const int rows = (kbk * 32 + cp * 16) * ROWB;
-            const u32x2 lo = lds_read_tr(kt + rows + troff[0][mb]);
-            const u32x2 hi = lds_read_tr(kt + rows + troff[1][mb]);
-            const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            const V8 sb = bitcast<V8>(
-                u32x4{dsk[4 * cp], dsk[4 * cp + 1], dsk[4 * cp + 2], dsk[4 * cp + 3]});
-            dqacc[mb] = mfma32(a, sb, dqacc[mb]);
-          }
+        }
         if constexpr (SEQ) __builtin_amdgcn_sched_barrier(0);
       }
     }
