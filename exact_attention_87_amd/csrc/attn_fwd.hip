@@ -62,9 +62,9 @@ constexpr int by_dim(int v64, int v128, int v256) {
 //     per workgroup, four workgroups per CU); three waves with three stages
 //     was 3-8% slower, and two 32-row blocks per wave (two waves per
 //     workgroup) 25-30% slower.
-//   d = 256: one wave per SIMD (256 VGPRs + 256 AGPRs), two stages (128 KiB),
-//     with a tile body of its own (tile256 below).  The software-pipelined
-//     kernel spills thousands of registers at this head dimension.
+//   d = 256: one wave per SIMD (256 VGPRs + 256 AGPRs), two stages (128 KiB).
+//     The software-pipelined kernel spills thousands of registers at this
+//     head dimension.
 template <int D>
 struct FwdCfg {
   static constexpr int NW = 4;             // waves per workgroup
@@ -250,59 +250,40 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     for (int mb = 0; mb < NMB; ++mb) oacc[nb][mb] = f32x16{};
   }
 
-  // The running max after a wave's first tile: the row max of its (masked)
-  // scores, as the max path of the softmax would set it, without first
-  // forming p against a max that is not set yet (that pass always
-  // overflows and was thrown away).  The accumulators are still zero, so
-  // skipping their rescale changes nothing.
-  auto first_max = [&](const f32x16 (&sacc)[2], float m) {
-    float mloc = sacc[0][0];
-#pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[kbk][r]);
-    mloc = __builtin_fmaxf(mloc, xor32(mloc));
-    return __builtin_fmaxf(m, mloc * c);
-  };
-
-  // p = 2^(s*c - m) -> bf16 P^T operand and this lane's tile sum.
-  auto softmax_exp = [&](const f32x16 (&sacc)[2], float m, uint32_t (&pk)[2][8]) {
-    float tsum = 0.f;
-#pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][r], c, -m));
-        const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][r + 1], c, -m));
-        pk[kbk][r >> 1] = pack2<T>(p0, p1);
-        tsum += p0 + p1;
-      }
-    return tsum;
-  };
-
-  // d = 256 tile body.  One wave per SIMD leaves nothing else to hide a
-  // wave's own stalls, and at 512 registers every product accumulator lives
-  // in the accumulation registers, which the vector ALU reaches only through
-  // copies.  So:
-  //   - K and V^T fragments are read a few products ahead of their use (4 and
-  //     2; reading all of a key block's K fragments before its products left
-  //     each block's LDS latency exposed);
-  //   - the scores are copied once out of the accumulators into plain values
-  //     for the mask and the softmax;
-  //   - a rescale of O (the running maximum moved) multiplies O in place
-  //     behind an empty asm that pins O to the accumulation registers, so O
-  //     is copied out and back on that rare path only; written plainly, the
-  //     compiler kept a vector copy of all of O at hand and moved it on every
-  //     tile (about 270 extra copies per tile).
-  // Same arithmetic, in the same order, as the generic body (bitwise-equal
-  // results).  Measured against the generic body (same-box rotated A/B):
-  // non-causal B=1 H=16 N=8192 887 -> 1058 TFLOP/s (+19%), causal 843 -> 997
-  // (+18%), causal grouped-query B=2 Hq=16 Hkv=2 N=4096 804 -> 930 (+16%),
-  // fp16 non-causal B=4 H=16 N=2048 786 -> 914 (+16%).  (Scaling each O block
-  // inside a second copy of the P V loop instead measured 1% slower
-  // non-causal and 9% slower causal.)
-  auto tile256 = [&](const char* kt, const char* vt, int j) __attribute__((always_inline)) {
-    constexpr int NF = 2 * NQC, KLA = 4;  // score products; K fragments read ahead
+  // One key tile of a wave (d = 64 and 256; d = 128 runs the
+  // software-pipelined kernel below):
+  //   - K and V^T fragments are read a few products ahead of their use (K 4
+  //     ahead at d = 256, 2 at d = 64; V^T pairs 2 ahead), pinned with
+  //     scheduling groups;
+  //   - the scores are copied once out of the product accumulators into
+  //     plain values for the mask and the softmax;
+  //   - on a wave's first tile (loop position 0: its first tile with visible
+  //     keys, also under a block-sparse list, which is ascending) the running
+  //     max, not set yet, is taken from the masked scores up front; forming p
+  //     against the unset max always overflowed and was thrown away;
+  //   - otherwise p is formed against the running max, and only a lane whose
+  //     tile sum exceeds 2^kTau takes the row max; if that grew by more than
+  //     kTau, O is rescaled.
+  // d = 256 runs one wave per SIMD, so nothing else hides a wave's own
+  // stalls, and at 512 registers every product accumulator lives in the
+  // accumulation registers, which the vector ALU reaches only through
+  // copies.  The O rescale therefore multiplies O in place behind an empty
+  // asm that pins O to those registers, so O is copied out and back on that
+  // rare path only; written plainly, the compiler kept a vector copy of all
+  // of O at hand and moved it on every tile (about 270 extra copies per
+  // tile).  Measured against the previous body (all K fragments of a key
+  // block read before its products, the V^T reads left to the compiler, the
+  // rescale written plainly; same arithmetic, bitwise-equal results,
+  // same-box rotated A/B): d = 256 non-causal B=1 H=16 N=8192 887 -> 1058
+  // TFLOP/s (+19%), causal 843 -> 997 (+18%), causal grouped-query B=2
+  // Hq=16 Hkv=2 N=4096 804 -> 930 (+16%), fp16 non-causal B=4 H=16 N=2048
+  // 786 -> 914 (+16%); d = 64 (four waves per SIMD) +0.2 to +1.4% (causal
+  // B=8 H=16 N=2048 812 -> 824).  (Scaling each O block inside a second copy
+  // of the P V loop instead measured 1% slower non-causal and 9% slower
+  // causal at d = 256.)
+  auto tile_body = [&](const char* kt, const char* vt, int j) __attribute__((always_inline)) {
+    static_assert(NB == 1, "the tile body serves one 32-row query block per wave");
+    constexpr int NF = 2 * NQC, KLA = D == 256 ? 4 : 2;  // score products; K fragments read ahead
     f32x16 sacc2[2];
     {
       u32x4 kf[NF];
@@ -310,7 +291,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
         kf[i] = lds_read16(kt + (i / NQC) * 32 * ROWB + koff(i % NQC));
       };
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(1);
+      if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < KLA; ++i) kread(i);
       sacc2[0] = f32x16{};
@@ -327,7 +308,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
         if (i + KLA < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
+      if (PRIO) __builtin_amdgcn_s_setprio(0);
     }
     float sv[2][16];
 #pragma unroll
@@ -400,7 +381,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
         vhi[i] = lds_read_tr(vt + rows + voff(1, i / 4));
       };
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(1);
+      if (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < VLA; ++i) vread(i);
 #pragma unroll
@@ -419,7 +400,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
         if (i + VLA < NP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
+      if (PRIO) __builtin_amdgcn_s_setprio(0);
     };
     // (after pv's definition on purpose: placed before it, the same code
     // left the allocator spilling 10-80 registers)
@@ -427,7 +408,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
         f32x16 o = oacc[0][mb];
-        __asm__ volatile("" : "+a"(o));
+        if constexpr (D == 256) __asm__ volatile("" : "+a"(o));
         oacc[0][mb] = o * alpha;
       }
     }
@@ -453,111 +434,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WPE, FwdCfg<D>::WPE))) void fwd_mf
     }
     if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (wave_active(j)) {
-      if constexpr (D == 256) {
-        tile256(kt, vt, j);
-      } else {
-      // ---- S^T = K Q^T for the tile's two 32-key blocks and every query block
-      // (all K fragments are read up front)
-      constexpr int KF = 2;  // key blocks whose fragments are held at once
-      f32x16 sacc[NB][2];
-#pragma unroll
-      for (int k0b = 0; k0b < 2; k0b += KF) {
-        u32x4 kfrag[KF][NQC];
-#pragma unroll
-        for (int kk = 0; kk < KF; ++kk)
-#pragma unroll
-          for (int cc = 0; cc < NQC; ++cc)
-            kfrag[kk][cc] = lds_read16(kt + (k0b + kk) * 32 * ROWB + koff(cc));
-        if (PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int kk = 0; kk < KF; ++kk)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            sacc[nb][k0b + kk] = f32x16{};
-#pragma unroll
-            for (int cc = 0; cc < NQC; ++cc)
-              sacc[nb][k0b + kk] = mfma32(bitcast<V8>(kfrag[kk][cc]), qreg[nb][cc], sacc[nb][k0b + kk]);
-          }
-        if (PRIO) __builtin_amdgcn_s_setprio(0);
-      }
-      // ---- mask (diagonal and tail tiles only; the branch is wave-uniform
-      // and kept as a branch rather than flattened into selects)
-      const int k0 = tile_of(j) * BC;
-      if ((k0 + BC > N) || (CAUSAL && (k0 + BC - 1 > q0))) {
-        __asm__ volatile("");
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kbk * 32 + acc_row(r, hf);
-              const bool dead = (key >= N) || (CAUSAL && key > q0 + nb * 32 + l32);
-              if (dead) sacc[nb][kbk][r] = -__builtin_inff();
-            }
-      }
-      // ---- p with the current running max.  A lane whose tile sum exceeds
-      // 2^kTau may hold a p above 2^kTau: only then take the row max and, if
-      // it grew by more than kTau, rescale.  On a wave's first tile (loop
-      // position 0: its first tile with visible keys, also under a block-sparse
-      // list, which is ascending) the max is not set yet and is taken up front.
-      if (j == 0) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) ms[nb] = first_max(sacc[nb], ms[nb]);
-      }
-      uint32_t pk[NB][2][8];
-      float tsum[NB];
-      bool redo = false;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        tsum[nb] = softmax_exp(sacc[nb], ms[nb], pk[nb]);
-        redo |= !(tsum[nb] <= kSumMax<T>);
-      }
-      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-        __asm__ volatile("");
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          float mloc = sacc[nb][0][0];
-#pragma unroll
-          for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mloc = __builtin_fmaxf(mloc, sacc[nb][kbk][r]);
-          mloc = __builtin_fmaxf(mloc, xor32(mloc));
-          const float tmax = mloc * c;
-          if (__builtin_amdgcn_ballot_w64(tmax > ms[nb] + kTau<T>) != 0) {
-            const float mnew = __builtin_fmaxf(ms[nb], tmax);
-            const float alpha = fast_exp2(ms[nb] - mnew);
-            ms[nb] = mnew;
-            lsum[nb] *= alpha;
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) oacc[nb][mb] *= alpha;
-            tsum[nb] = softmax_exp(sacc[nb], ms[nb], pk[nb]);
-          }
-        }
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) lsum[nb] += tsum[nb];
-      // ---- O^T += V^T P^T (each V^T fragment feeds every query block)
-      if (PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-          for (int cp = 0; cp < 2; ++cp) {
-            const int rows = (kbk * 32 + cp * 16) * ROWB;
-            const u32x2 lo = lds_read_tr(vt + rows + voff(0, mb));
-            const u32x2 hi = lds_read_tr(vt + rows + voff(1, mb));
-            const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              const V8 bp = bitcast<V8>(u32x4{pk[nb][kbk][4 * cp], pk[nb][kbk][4 * cp + 1],
-                                                      pk[nb][kbk][4 * cp + 2], pk[nb][kbk][4 * cp + 3]});
-              oacc[nb][mb] = mfma32(a, bp, oacc[nb][mb]);
-            }
-          }
-      if (PRIO) __builtin_amdgcn_s_setprio(0);
-      }
+      tile_body(kt, vt, j);
     }
     if (j + 1 < ntiles) {
       // tile j+1 must have landed; tile j+2 (three stages) may stay in flight
