@@ -808,10 +808,9 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
   // layouts; here with several waves per SIMD, against reads two chunks at a
   // time behind scheduling fences: causal B=4 H=32 N=4000 d=128 +1.3%,
   // non-causal B=2 H=32 N=4096 d=128 +1.1%, d=64 +0.1 to +0.6%; one ahead
-  // lost 1%).  Under tight register budgets (three waves per SIMD at d = 64,
-  // two at d = 128) the two key blocks of a tile are also kept apart by a
-  // scheduling fence.
-  constexpr bool SEQ = D == 64 ? Cfg::WPE >= 3 : Cfg::WPE >= 2;
+  // lost 1%).  A fence that kept a tile's two key blocks apart (for tight
+  // register budgets) is gone: with the streamed reads it cost 0.5-2.6% at
+  // d = 64 and nothing at d = 128, at the same register counts.
 
   auto tile = [&](auto bufc, int j) {
     constexpr int BUF = decltype(bufc)::value;
@@ -894,7 +893,6 @@ void bwd_dq_kernel(const T* __restrict__ Q, const T* __restrict__ K,
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (SEQ) __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (j + 1 < ntiles) {
