@@ -163,33 +163,23 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
 
-  auto softmax_exp = [&](const f32x16 (&sacc)[2], uint32_t (&pk)[2][8]) {
-    float tsum = 0.f;
-#pragma unroll
-    for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-      for (int rr = 0; rr < 16; rr += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(sacc[kbk][rr], c, -ms));
-        const float p1 = fast_exp2(__builtin_fmaf(sacc[kbk][rr + 1], c, -ms));
-        pk[kbk][rr >> 1] = pack2<T>(p0, p1);
-        tsum += p0 + p1;
-      }
-    return tsum;
-  };
-
-  // d = 256 tile body, as in the dense forward's: one wave per SIMD and every
-  // product accumulator in the accumulation registers, so K and V^T fragments
-  // are read a few products ahead, the scores are copied out once for the
-  // mask and the softmax, and an O rescale multiplies O in place behind an
-  // empty asm that pins it to the accumulation registers (written plainly,
-  // the compiler moved all of O out and back on every tile).  Same
-  // arithmetic and order as the generic body.  Measured against the generic
-  // body (same-box rotated A/B, d = 256, Hq=32 Hkv=8 unless stated): decode
-  // Nq=1 Nk=32768 B=8 +1%, causal append Nq=64 Nk=16384 B=4 621 -> 696
+  // One key tile of a wave, as in the dense forward: K and V^T fragments are
+  // read a few products ahead of their use (K 4 ahead at d = 256, 2 below;
+  // V^T pairs 2 ahead), the scores are copied once out of the product
+  // accumulators for the mask and the softmax, the split's first tile sets
+  // the running max up front, and a later rescale multiplies O in place.  At
+  // d = 256 (one wave per SIMD, every accumulator in the accumulation
+  // registers) an empty asm pins O to those registers for the rescale (written
+  // plainly, the compiler moved all of O out and back on every tile).  Same
+  // arithmetic and order as the previous body (all K fragments of a tile read
+  // before its products, the V^T reads left to the compiler).  Measured
+  // against it (same-box rotated A/B; Hq=32 Hkv=8 unless stated): d = 256
+  // decode Nq=1 Nk=32768 B=8 +1%, causal append Nq=64 Nk=16384 B=4 621 -> 696
   // TFLOP/s (+12%), causal chunk Nq=512 Nk=16384 B=1 Hq=16 Hkv=2 748 -> 896
-  // (+20%).
-  auto tile256 = [&](const char* kt, const char* vt, int j) __attribute__((always_inline)) {
-    constexpr int NF = 2 * NQC, KLA = 4;  // score products; K fragments read ahead
+  // (+20%); d = 128 causal chunk +1.4%, decode and append +0.2 to +0.4%; d = 64
+  // append +0.1%.
+  auto tile_body = [&](const char* kt, const char* vt, int j) __attribute__((always_inline)) {
+    constexpr int NF = 2 * NQC, KLA = D == 256 ? 4 : 2;  // score products; K fragments read ahead
     f32x16 sacc2[2];
     {
       u32x4 kf[NF];
@@ -311,7 +301,7 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
         f32x16 o = oacc[mb];
-        __asm__ volatile("" : "+a"(o));
+        if constexpr (D == 256) __asm__ volatile("" : "+a"(o));
         oacc[mb] = o * alpha;
       }
     }
@@ -324,81 +314,7 @@ __attribute__((amdgpu_waves_per_eu(SplitCfg<D>::WPE, SplitCfg<D>::WPE))) void fw
     const char* vt = kt + TILEB;
     if (j + NBUF - 1 < ntiles) issue(j + NBUF - 1);
     if (j < wtiles) {
-      if constexpr (D == 256) {
-        tile256(kt, vt, j);
-      } else {
-      u32x4 kfrag[2][NQC];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-        for (int cc = 0; cc < NQC; ++cc) kfrag[kbk][cc] = lds_read16(kt + kbk * 32 * ROWB + koff[cc]);
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) {
-        sacc[kbk] = f32x16{};
-#pragma unroll
-        for (int cc = 0; cc < NQC; ++cc)
-          sacc[kbk] = mfma32(bitcast<V8>(kfrag[kbk][cc]), qreg[cc], sacc[kbk]);
-      }
-      // mask: keys past the split / past Nk, and (causal) keys after the row's diagonal
-      const int k0 = kbeg + j * BC;
-      if ((k0 + BC > kend) || (CAUSAL && (k0 + BC - 1 > off))) {
-        __asm__ volatile("");
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int key = k0 + kbk * 32 + acc_row(rr, hf);
-            const bool dead = (key >= kend) || (CAUSAL && key > qi + off);
-            if (dead) sacc[kbk][rr] = -__builtin_inff();
-          }
-      }
-      if (j == 0) {  // the split's first tile: the running maximum is taken up front
-        float mloc = sacc[0][0];
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mloc = __builtin_fmaxf(mloc, sacc[kbk][rr]);
-        mloc = __builtin_fmaxf(mloc, xor32(mloc));
-        ms = __builtin_fmaxf(ms, mloc * c);
-      }
-      uint32_t pk[2][8];
-      float tsum = softmax_exp(sacc, pk);
-      if (__builtin_amdgcn_ballot_w64(!(tsum <= kSumMax<T>)) != 0) {
-        __asm__ volatile("");
-        float mloc = sacc[0][0];
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) mloc = __builtin_fmaxf(mloc, sacc[kbk][rr]);
-        mloc = __builtin_fmaxf(mloc, xor32(mloc));
-        const float tmax = mloc * c;
-        if (__builtin_amdgcn_ballot_w64(tmax > ms + kTau<T>) != 0) {
-          const float mnew = __builtin_fmaxf(ms, tmax);
-          const float alpha = fast_exp2(ms - mnew);
-          ms = mnew;
-          lsum *= alpha;
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
-          tsum = softmax_exp(sacc, pk);
-        }
-      }
-      lsum += tsum;
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int kbk = 0; kbk < 2; ++kbk)
-#pragma unroll
-          for (int cp = 0; cp < 2; ++cp) {
-            const int rows = (kbk * 32 + cp * 16) * ROWB;
-            const u32x2 lo = lds_read_tr(vt + rows + voff[0][mb]);
-            const u32x2 hi = lds_read_tr(vt + rows + voff[1][mb]);
-            const V8 a = bitcast<V8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            const V8 bp = bitcast<V8>(
-                u32x4{pk[kbk][4 * cp], pk[kbk][4 * cp + 1], pk[kbk][4 * cp + 2], pk[kbk][4 * cp + 3]});
-            oacc[mb] = mfma32(a, bp, oacc[mb]);
-          }
-      }
+      tile_body(kt, vt, j);
     }
     if (j + 1 < ntiles) wait_next(j + 1);
   };
